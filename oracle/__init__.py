@@ -1,0 +1,43 @@
+"""fp64 CPU oracle for the gated linear-attention state recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this package:
+only the tests, the smoke check and the benchmark's CPU-baseline leg call it.
+It shares no code with the HIP library.
+
+What it computes follows "Inference for linear attention and hybrid
+architectures", section "Two ways to write the same computation":
+
+* GLA:  S_t = alpha_t S_{t-1} + k_t^T v_t,  o_t = q_t S_t (state read after
+  the update).
+* Gated DeltaNet: S_t = alpha_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t
+  (the gate multiplies the old-state term only; that placement is a reading,
+  the page only says a decay gate is multiplied in as well).
+* the short causal convolution in front of the layer, with its per-request
+  cache of the last width-1 inputs (same section, last paragraph; section
+  "The real model's ledger" for the width-1 cache).
+
+The definition is the token-by-token recurrence (``recurrence``); the chunked
+forms in ``chunked`` restate the page's chunked algorithm (and a derived
+chunked form for Gated DeltaNet) and exist only to pin the recurrence.
+
+Parity status of every function is listed in ``PINS`` below: each entry names
+the pin tests that fix it against something other than itself.
+"""
+from .recurrence import (gla_sequence, gdn_sequence, gla_varlen, gdn_varlen,
+                         gla_decode, gdn_decode)
+from .conv import causal_conv1d
+from .chunked import gla_chunked, gdn_chunked
+
+PINS = {
+    "gla_sequence": "brute-force O(T^2) sum, alpha=1 masked matmul, scipy lfilter (d=1), "
+                    "page toy example recurrent==chunked at 1e-5, segmentation",
+    "gdn_sequence": "literal d_k x d_k matrix update, beta=0 closed form, orthogonal-key "
+                    "reduction to GLA, retrieval identity, chunked WY form",
+    "gla_varlen / gdn_varlen": "per-sequence equality with *_sequence, untouched slots, "
+                               "empty sequences",
+    "gla_decode / gdn_decode": "one step of *_sequence",
+    "causal_conv1d": "numpy.convolve per channel, segmented == one pass == token by token",
+    "gla_chunked": "page toy example; equality with the recurrence",
+    "gdn_chunked": "equality with the recurrence (the chunked GDN form itself is not on the "
+                   "page; it is pinned only through the recurrence)",
+}

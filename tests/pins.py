@@ -1,0 +1,208 @@
+"""Pins for the oracle: checks against facts that do not come from the
+oracle itself (brute-force sums, closed forms, textbook/library routines,
+the worked example of "Inference for linear attention and hybrid
+architectures").  Each check takes the implementation under test as an
+argument and returns the largest deviation it sees, so the same checks can
+be run on deliberately broken copies of the oracle (see
+test_oracle_mutants.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.signal import lfilter
+
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _inputs(seed, T=24, H=2, dk=6, dv=5, unit_k=False, state=True):
+    r = _rng(seed)
+    q = r.standard_normal((T, H, dk))
+    k = r.standard_normal((T, H, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    else:
+        k *= 0.5
+    v = r.standard_normal((T, H, dv))
+    a = 1.0 / (1.0 + np.exp(-(r.standard_normal((T, H)) + 2.0)))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal((T, H))))
+    S0 = r.standard_normal((H, dk, dv)) * 0.3 if state else np.zeros((H, dk, dv))
+    return q, k, v, a, b, S0
+
+
+# ---------------------------------------------------------------- GLA pins
+def gla_bruteforce(gla_sequence, seed=1):
+    """o_t = sum_{s<=t} (prod_{r=s+1..t} alpha_r)(q_t.k_s) v_s
+           + (prod_{r<=t} alpha_r) q_t S_0,  products taken directly."""
+    q, k, v, a, _, S0 = _inputs(seed, dk=5, dv=5)   # square heads: a transposed outer product stays shape-valid
+    o, S = gla_sequence(q, k, v, a, S0)
+    T, H, _ = q.shape
+    err = 0.0
+    for h in range(H):
+        for t in range(T):
+            ref = np.prod(a[: t + 1, h]) * (q[t, h] @ S0[h])
+            for s in range(t + 1):
+                ref = ref + np.prod(a[s + 1: t + 1, h]) * (q[t, h] @ k[s, h]) * v[s, h]
+            err = max(err, np.abs(o[t, h] - ref).max())
+        Sref = np.prod(a[:, h]) * S0[h]
+        for s in range(T):
+            Sref = Sref + np.prod(a[s + 1:, h]) * np.outer(k[s, h], v[s, h])
+        err = max(err, np.abs(S[h] - Sref).max())
+    return err
+
+
+def gla_linear_attention(gla_sequence, seed=2):
+    """alpha = 1, S_0 = 0: plain causal linear attention, tril(Q K^T) V."""
+    q, k, v, a, _, _ = _inputs(seed, state=False)
+    ones = np.ones_like(a)
+    o, S = gla_sequence(q, k, v, ones, None)
+    err = 0.0
+    for h in range(q.shape[1]):
+        ref = np.tril(q[:, h] @ k[:, h].T) @ v[:, h]
+        err = max(err, np.abs(o[:, h] - ref).max(), np.abs(S[h] - k[:, h].T @ v[:, h]).max())
+    return err
+
+
+def gla_lfilter(gla_sequence, seed=3):
+    """d_k = d_v = 1 with a constant gate: the state is the first-order IIR
+    filter y_t = a y_{t-1} + x_t (scipy.signal.lfilter) of x_t = k_t v_t."""
+    r = _rng(seed)
+    T = 40
+    k = r.standard_normal((T, 1, 1))
+    v = r.standard_normal((T, 1, 1))
+    q = r.standard_normal((T, 1, 1))
+    a0 = 0.87
+    o, S = gla_sequence(q, k, v, np.full((T, 1), a0), None)
+    y = lfilter([1.0], [1.0, -a0], (k * v)[:, 0, 0])
+    return max(np.abs(o[:, 0, 0] - q[:, 0, 0] * y).max(), abs(S[0, 0, 0] - y[-1]))
+
+
+# ---------------------------------------------------------------- GDN pins
+def gdn_matrix_form(gdn_sequence, seed=4):
+    """Literal update with the d_k x d_k matrix alpha (I - beta k^T k)."""
+    q, k, v, a, b, S0 = _inputs(seed)
+    o, S = gdn_sequence(q, k, v, a, b, S0)
+    T, H, dk = q.shape
+    err = 0.0
+    for h in range(H):
+        St = S0[h].copy()
+        for t in range(T):
+            kk = k[t, h][:, None]
+            M = a[t, h] * (np.eye(dk) - b[t, h] * (kk @ kk.T))
+            St = M @ St + b[t, h] * (kk @ v[t, h][None, :])
+            err = max(err, np.abs(o[t, h] - q[t, h] @ St).max())
+        err = max(err, np.abs(S[h] - St).max())
+    return err
+
+
+def gdn_unrolled(gdn_sequence, seed=5):
+    """Unrolled closed form S_T = M_T..M_1 S_0 + sum_t M_T..M_{t+1} beta_t k_t^T v_t,
+    with M_t = alpha_t (I - beta_t k_t^T k_t), products formed explicitly."""
+    q, k, v, a, b, S0 = _inputs(seed, T=10, H=1)
+    _, S = gdn_sequence(q, k, v, a, b, S0)
+    dk = q.shape[2]
+    Ms = [a[t, 0] * (np.eye(dk) - b[t, 0] * np.outer(k[t, 0], k[t, 0])) for t in range(q.shape[0])]
+
+    def prod(lo, hi):          # M_hi ... M_lo (inclusive), identity if empty
+        P = np.eye(dk)
+        for t in range(lo, hi + 1):
+            P = Ms[t] @ P
+        return P
+    T = q.shape[0]
+    ref = prod(0, T - 1) @ S0[0]
+    for t in range(T):
+        ref = ref + prod(t + 1, T - 1) @ (b[t, 0] * np.outer(k[t, 0], v[t, 0]))
+    return np.abs(S[0] - ref).max()
+
+
+def gdn_beta_zero(gdn_sequence, seed=6):
+    """beta = 0: no erase and no write, o_t = (prod_{r<=t} alpha_r) q_t S_0."""
+    q, k, v, a, _, S0 = _inputs(seed)
+    o, S = gdn_sequence(q, k, v, a, np.zeros_like(a), S0)
+    err = 0.0
+    for h in range(q.shape[1]):
+        for t in range(q.shape[0]):
+            err = max(err, np.abs(o[t, h] - np.prod(a[: t + 1, h]) * (q[t, h] @ S0[h])).max())
+    return err
+
+
+def _orthogonal_keys(seed, T, H, dk, unit=False):
+    r = _rng(seed)
+    k = np.zeros((T, H, dk))
+    for h in range(H):
+        Qm, _ = np.linalg.qr(r.standard_normal((dk, dk)))
+        scale = np.ones(T) if unit else r.uniform(0.5, 1.4, T)
+        k[:, h] = Qm[:T] * scale[:, None]
+    return k
+
+
+def gdn_orthogonal_keys(gdn_sequence, gla_sequence, seed=7):
+    """Mutually orthogonal keys and S_0 = 0: nothing is erased, so Gated
+    DeltaNet equals GLA fed with values beta_t v_t."""
+    q, _, v, a, b, _ = _inputs(seed, T=8, dk=8)
+    k = _orthogonal_keys(seed, 8, q.shape[1], 8)
+    o1, S1 = gdn_sequence(q, k, v, a, b, None)
+    o2, S2 = gla_sequence(q, k, b[:, :, None] * v, a, None)
+    return max(np.abs(o1 - o2).max(), np.abs(S1 - S2).max())
+
+
+def gdn_linear_attention(gdn_sequence, seed=8):
+    """Orthonormal keys, alpha = beta = 1, S_0 = 0: plain causal linear
+    attention tril(Q K^T) V."""
+    q, _, v, a, _, _ = _inputs(seed, T=8, dk=8)
+    k = _orthogonal_keys(seed, 8, q.shape[1], 8, unit=True)
+    ones = np.ones_like(a)
+    o, _ = gdn_sequence(q, k, v, ones, ones, None)
+    err = 0.0
+    for h in range(q.shape[1]):
+        err = max(err, np.abs(o[:, h] - np.tril(q[:, h] @ k[:, h].T) @ v[:, h]).max())
+    return err
+
+
+def gdn_retrieval(gdn_sequence, seed=9):
+    """k_t S_t = alpha_t (1 - beta_t |k_t|^2) k_t S_{t-1} + beta_t |k_t|^2 v_t at
+    every step, from states obtained by running one token at a time."""
+    q, k, v, a, b, S0 = _inputs(seed)
+    err = 0.0
+    S = S0.copy()
+    for t in range(q.shape[0]):
+        _, Sn = gdn_sequence(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1], S)
+        for h in range(q.shape[1]):
+            kk = k[t, h] @ k[t, h]
+            ref = a[t, h] * (1 - b[t, h] * kk) * (k[t, h] @ S[h]) + b[t, h] * kk * v[t, h]
+            err = max(err, np.abs(k[t, h] @ Sn[h] - ref).max())
+        S = Sn
+    return err
+
+
+def gdn_overwrite(gdn_sequence, seed=10):
+    """alpha = beta = 1 and |k| = 1: exact overwrite, k_t S_t = v_t."""
+    q, k, v, a, _, S0 = _inputs(seed, unit_k=True)
+    ones = np.ones_like(a)
+    err = 0.0
+    S = S0.copy()
+    for t in range(q.shape[0]):
+        _, S = gdn_sequence(q[t:t + 1], k[t:t + 1], v[t:t + 1], ones[t:t + 1], ones[t:t + 1], S)
+        for h in range(q.shape[1]):
+            err = max(err, np.abs(k[t, h] @ S[h] - v[t, h]).max())
+    return err
+
+
+# ---------------------------------------------------------------- conv pin
+def conv_numpy_convolve(causal_conv1d, seed=11):
+    """Zero cache: channel c is numpy.convolve(x[:, c], w[c, ::-1]) truncated
+    to the causal part (w[c, W-1] multiplies the current input)."""
+    r = _rng(seed)
+    N, Cch, W = 17, 5, 4
+    x = r.standard_normal((N, Cch))
+    w = r.standard_normal((Cch, W))
+    cache = np.zeros((1, W - 1, Cch))
+    y, cache_out = causal_conv1d(x, w, np.array([0, N]), cache, np.array([0]))
+    err = 0.0
+    for c in range(Cch):
+        ref = np.convolve(x[:, c], w[c, ::-1])[:N]
+        err = max(err, np.abs(y[:, c] - ref).max())
+    return max(err, np.abs(cache_out[0] - x[N - (W - 1):]).max())
