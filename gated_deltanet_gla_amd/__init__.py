@@ -1,0 +1,10 @@
+"""MI355X (gfx950) gated linear-attention state recurrence: GLA and Gated
+DeltaNet chunked prefill, slot-indexed decode, and the causal conv prelude.
+
+The computation runs in the HIP library ``libgla_mi355x.so`` (C ABI in
+include/gla.h); ``ops`` is its thin torch binding.
+"""
+from .ops import (gla_chunk_fwd, gdn_chunk_fwd, gla_decode_step, gdn_decode_step,  # noqa: F401
+                  causal_conv1d_fwd, workspace_bytes)
+
+__version__ = "0.1.0"

@@ -1,0 +1,172 @@
+// Host side of the C ABI declared in include/gla.h: argument validation
+// (nothing is enqueued when it fails) and dispatch to the kernel launchers.
+#include "gla.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <limits>
+
+#include "launch.h"
+
+namespace {
+
+bool is_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool is_chunk(int32_t c) { return c == 16 || c == 32 || c == 64; }
+bool is_dtype(int d) { return d == GLA_F32 || d == GLA_BF16; }
+
+// Largest grid the launchers build is (rows of work) x heads x (d_v tiles);
+// keep every product comfortably inside int32.
+constexpr long kMaxWork = 1L << 26;
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_EHIP; }
+
+int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
+                const float* beta, bool need_beta, const int32_t* cu_seqlens, int32_t n_seqs,
+                int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                int in_dtype, int out_dtype, const float* pool, int32_t n_slots,
+                const int32_t* slot_idx, uint32_t flags, const void* o) {
+    if (n_seqs < 0 || n_tokens < 0 || n_heads < 1) return GLA_ESHAPE;
+    if (!is_dim(dk) || !is_dim(dv)) return GLA_ESHAPE;
+    if (!is_chunk(chunk)) return GLA_ECHUNK;
+    if (!is_dtype(in_dtype) || !is_dtype(out_dtype)) return GLA_EDTYPE;
+    if (flags & ~static_cast<uint32_t>(GLA_ZERO_INIT)) return GLA_ESHAPE;
+    if (static_cast<long>(n_seqs) * n_heads > kMaxWork) return GLA_ESHAPE;
+    if (static_cast<long>(n_tokens) * n_heads > std::numeric_limits<int32_t>::max() / 128)
+        return GLA_ESHAPE;
+    if (n_seqs > 0) {
+        if (n_slots < 1) return GLA_ESHAPE;
+        if (!cu_seqlens || !pool || !slot_idx) return GLA_EPTR;
+    }
+    if (n_tokens > 0) {
+        if (n_seqs < 1) return GLA_ESHAPE;
+        if (!q || !k || !v || !alpha || !o) return GLA_EPTR;
+        if (need_beta && !beta) return GLA_EPTR;
+    }
+    return GLA_OK;
+}
+
+int check_decode(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, bool need_beta, int32_t n_req, int32_t n_heads, int32_t dk,
+                 int32_t dv, int in_dtype, int out_dtype, const float* pool, int32_t n_slots,
+                 const int32_t* slot_idx, const void* o) {
+    if (n_req < 0 || n_heads < 1) return GLA_ESHAPE;
+    if (!is_dim(dk) || !is_dim(dv)) return GLA_ESHAPE;
+    if (!is_dtype(in_dtype) || !is_dtype(out_dtype)) return GLA_EDTYPE;
+    if (static_cast<long>(n_req) * n_heads > kMaxWork) return GLA_ESHAPE;
+    if (n_req == 0) return GLA_OK;
+    if (n_slots < 1) return GLA_ESHAPE;
+    if (!q || !k || !v || !alpha || !pool || !slot_idx || !o) return GLA_EPTR;
+    if (need_beta && !beta) return GLA_EPTR;
+    return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gla_version(void) { return "0.1.0"; }
+
+const char* gla_status_string(int status) {
+    switch (status) {
+        case GLA_OK: return "ok";
+        case GLA_EPTR: return "a required pointer is NULL";
+        case GLA_ESHAPE: return "a size is negative, unsupported or inconsistent";
+        case GLA_EDTYPE: return "unsupported dtype";
+        case GLA_ECHUNK: return "unsupported chunk size";
+        case GLA_EWORKSPACE: return "workspace missing or too small";
+        case GLA_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t gla_chunk_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+size_t gdn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk,
+                                 int32_t dv, int32_t chunk) {
+    if (n_seqs < 0 || n_tokens < 0 || n_heads < 1 || !is_dim(dk) || !is_dim(dv) || !is_chunk(chunk))
+        return 0;
+    return gla::gdn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+}
+
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                  int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx, uint32_t flags,
+                  void* o, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_chunk(q, k, v, alpha, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads, dk,
+                         dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
+    if (st != GLA_OK) return st;
+    if (n_seqs == 0) return GLA_OK;
+    gla::ChunkArgs a{q, k, v, alpha, nullptr, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
+                     in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes};
+    return hip_status(gla::launch_gla_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype,
+                  gla_dtype out_dtype, float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_chunk(q, k, v, alpha, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
+                         chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
+    if (st != GLA_OK) return st;
+    const size_t need = gla::gdn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
+    if (n_seqs == 0) return GLA_OK;
+    gla::ChunkArgs a{q, k, v, alpha, beta, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
+                     in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes};
+    return hip_status(gla::launch_gdn_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+int gla_decode_step(const void* q, const void* k, const void* v, const float* alpha, int32_t n_req,
+                    int32_t n_heads, int32_t dk, int32_t dv, gla_dtype in_dtype,
+                    gla_dtype out_dtype, float* state_pool, int32_t n_slots,
+                    const int32_t* slot_idx, void* o, void* stream) {
+    int st = check_decode(q, k, v, alpha, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
+                          out_dtype, state_pool, n_slots, slot_idx, o);
+    if (st != GLA_OK || n_req == 0) return st;
+    gla::DecodeArgs a{q, k, v, alpha, nullptr, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
+                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o};
+    return hip_status(gla::launch_gla_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                    const float* beta, int32_t n_req, int32_t n_heads, int32_t dk, int32_t dv,
+                    gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool, int32_t n_slots,
+                    const int32_t* slot_idx, void* o, void* stream) {
+    int st = check_decode(q, k, v, alpha, beta, true, n_req, n_heads, dk, dv, in_dtype, out_dtype,
+                          state_pool, n_slots, slot_idx, o);
+    if (st != GLA_OK || n_req == 0) return st;
+    gla::DecodeArgs a{q, k, v, alpha, beta, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
+                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o};
+    return hip_status(gla::launch_gdn_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int causal_conv1d_fwd(const void* x, const float* w, const int32_t* cu_seqlens, int32_t n_seqs,
+                      int32_t n_tokens, int32_t channels, int32_t width, void* conv_cache,
+                      int32_t n_slots, const int32_t* slot_idx, uint32_t flags, void* y,
+                      gla_dtype dtype, void* stream) {
+    if (n_seqs < 0 || n_tokens < 0 || channels < 8 || (channels % 8) != 0) return GLA_ESHAPE;
+    if (width < 2 || width > 4) return GLA_ESHAPE;
+    if (!is_dtype(dtype)) return GLA_EDTYPE;
+    if (flags & ~static_cast<uint32_t>(GLA_ZERO_INIT)) return GLA_ESHAPE;
+    if (static_cast<long>(n_tokens) * channels > std::numeric_limits<int32_t>::max())
+        return GLA_ESHAPE;
+    if (static_cast<long>(n_seqs) * channels > kMaxWork * 8) return GLA_ESHAPE;
+    if (n_seqs > 0) {
+        if (n_slots < 1) return GLA_ESHAPE;
+        if (!cu_seqlens || !conv_cache || !slot_idx || !w) return GLA_EPTR;
+    }
+    if (n_tokens > 0) {
+        if (n_seqs < 1) return GLA_ESHAPE;
+        if (!x || !y) return GLA_EPTR;
+    }
+    if (n_seqs == 0) return GLA_OK;
+    gla::ConvArgs a{x, w, cu_seqlens, n_seqs, n_tokens, channels, width, conv_cache, n_slots,
+                    slot_idx, (flags & GLA_ZERO_INIT) ? 1 : 0, y, dtype == GLA_BF16};
+    return hip_status(gla::launch_conv1d(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Recurrent (decode) step of GLA and Gated DeltaNet on a slot-indexed fp32
+// state pool, in place.
+//
+// "Inference for linear attention and hybrid architectures", section "Two
+// ways to write the same computation": decode reads the state once and
+// applies one rank-one update, so each step costs the same whatever the
+// context length.  Section "Speculative decoding and PD disaggregation":
+// each request owns a fixed slot of the state pool and batched kernels read
+// and write by slot index.
+//
+// The step is HBM-bound (about 0.5 flop per byte): each workgroup owns one
+// (request, head), streams its d_k x d_v fp32 state from HBM exactly once
+// into registers, updates it there and streams it back.  Threads own 4
+// adjacent columns (one 16-byte vector) of RPT rows; the rows of a wave are
+// contiguous in memory, so every load and store is a full, coalesced
+// 16-byte-per-lane access.  The only cross-thread step is the reduction over
+// d_k for the outputs (and, for Gated DeltaNet, for p = k S), done in LDS.
+//
+// Gated DeltaNet uses the identity (exact in real arithmetic)
+//   o = q S_new = alpha (q S) + (q . k) u,   u = beta (v - alpha k S),
+// so q S, k S and q . k come out of ONE reduction over the old state and the
+// state is still touched once.
+#include "common.h"
+#include "launch.h"
+
+namespace gla {
+namespace {
+
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int NT_RAW = DK * DV / 64;
+    static constexpr int NT = NT_RAW < 64 ? 64 : (NT_RAW > 256 ? 256 : NT_RAW);  // threads
+    static constexpr int CG = DV / 4;          // 16-byte column groups per row
+    static constexpr int RG = NT / CG;         // row groups
+    static constexpr int RPT = DK / RG;        // rows per thread
+    static_assert(RG * CG == NT && RPT * RG == DK && RPT >= 1, "decode tiling");
+};
+
+template <int DK, int DV, class TI, class TO, bool GDN>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
+decode_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __restrict__ k,
+              const typename TI::T* __restrict__ v, const float* __restrict__ alpha,
+              const float* __restrict__ beta, float* __restrict__ pool, int n_heads,
+              int n_slots, const int32_t* __restrict__ slot_idx, typename TO::T* __restrict__ o) {
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int NT = Sh::NT, CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT;
+    constexpr int NRED = GDN ? 2 : 1;          // reduced vectors: (q S) [, k S]
+
+    const int h = blockIdx.x % n_heads;
+    const int r = blockIdx.x / n_heads;
+    const int t = threadIdx.x;
+    const int cg = t % CG;
+    const int rg = t / CG;
+
+    const int slot = slot_idx[r];
+    if (slot < 0 || slot >= n_slots) return;   // invalid slot: skip, never fault
+
+    __shared__ float s_q[DK];
+    __shared__ float s_k[DK];
+    __shared__ f32x4 s_red[NRED][RG][CG];
+    __shared__ float s_qk[RG];
+
+    float* __restrict__ S = pool + (static_cast<long>(slot) * n_heads + h) * (DK * DV);
+
+    // Issue the whole state tile first: RPT independent 16-byte loads/thread.
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV + cg * 4));
+    }
+
+    const long tok = static_cast<long>(r) * n_heads + h;
+    for (int i = t; i < DK; i += NT) {
+        s_q[i] = TI::load(q, tok * DK + i);
+        s_k[i] = TI::load(k, tok * DK + i);
+    }
+    const f32x4 v4 = Vec4<TI>::load(v + tok * DV + cg * 4);
+    const float a = alpha[tok];
+    __syncthreads();
+
+    if constexpr (!GDN) {
+        // S <- a S + k^T v ; partial (q S) over own rows
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + RG * i;
+            s[i] = a * s[i] + s_k[row] * v4;
+            acc += s_q[row] * s[i];
+            __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + row * DV + cg * 4));
+        }
+        s_red[0][rg][cg] = acc;
+        __syncthreads();
+        if (rg == 0) {
+            f32x4 tot = s_red[0][0][cg];
+#pragma unroll
+            for (int j = 1; j < RG; ++j) tot += s_red[0][j][cg];
+            Vec4<TO>::store(o + tok * DV + cg * 4, tot);
+        }
+    } else {
+        const float b = beta[tok];
+        f32x4 accq = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
+        float qk = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + RG * i;
+            accq += s_q[row] * s[i];
+            acck += s_k[row] * s[i];
+            qk += s_q[row] * s_k[row];
+        }
+        s_red[0][rg][cg] = accq;
+        s_red[1][rg][cg] = acck;
+        if (cg == 0) s_qk[rg] = qk;
+        __syncthreads();
+        f32x4 p = s_red[1][0][cg];
+#pragma unroll
+        for (int j = 1; j < RG; ++j) p += s_red[1][j][cg];
+        const f32x4 u = b * (v4 - a * p);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + RG * i;
+            s[i] = a * s[i] + s_k[row] * u;
+            __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + row * DV + cg * 4));
+        }
+        if (rg == 0) {
+            f32x4 qs = s_red[0][0][cg];
+            float qkt = s_qk[0];
+#pragma unroll
+            for (int j = 1; j < RG; ++j) {
+                qs += s_red[0][j][cg];
+                qkt += s_qk[j];
+            }
+            Vec4<TO>::store(o + tok * DV + cg * 4, a * qs + qkt * u);
+        }
+    }
+}
+
+template <int DK, int DV, class TI, class TO, bool GDN>
+hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
+    using Sh = DecodeShape<DK, DV>;
+    dim3 grid(a.n_heads * a.n_req);
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO, GDN>), grid, dim3(Sh::NT), 0, s,
+                       static_cast<const typename TI::T*>(a.q), static_cast<const typename TI::T*>(a.k),
+                       static_cast<const typename TI::T*>(a.v), a.alpha, a.beta, a.pool, a.n_heads,
+                       a.n_slots, a.slot_idx, static_cast<typename TO::T*>(a.o));
+    return hipGetLastError();
+}
+
+template <int DK, int DV, bool GDN>
+hipError_t launch_dt(const DecodeArgs& a, hipStream_t s) {
+    if (a.in_bf16) {
+        return a.out_bf16 ? launch4<DK, DV, BF16, BF16, GDN>(a, s) : launch4<DK, DV, BF16, F32, GDN>(a, s);
+    }
+    return a.out_bf16 ? launch4<DK, DV, F32, BF16, GDN>(a, s) : launch4<DK, DV, F32, F32, GDN>(a, s);
+}
+
+template <int DK, bool GDN>
+hipError_t launch_dv(const DecodeArgs& a, hipStream_t s) {
+    switch (a.dv) {
+        case 16: return launch_dt<DK, 16, GDN>(a, s);
+        case 32: return launch_dt<DK, 32, GDN>(a, s);
+        case 64: return launch_dt<DK, 64, GDN>(a, s);
+        case 128: return launch_dt<DK, 128, GDN>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool GDN>
+hipError_t launch(const DecodeArgs& a, hipStream_t s) {
+    if (a.n_req == 0 || a.n_heads == 0) return hipSuccess;
+    switch (a.dk) {
+        case 16: return launch_dv<16, GDN>(a, s);
+        case 32: return launch_dv<32, GDN>(a, s);
+        case 64: return launch_dv<64, GDN>(a, s);
+        case 128: return launch_dv<128, GDN>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s) { return launch<false>(a, s); }
+hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s) { return launch<true>(a, s); }
+
+}  // namespace gla

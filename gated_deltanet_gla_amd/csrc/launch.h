@@ -1,0 +1,63 @@
+// Internal launch interface between the host-side C ABI (api.cpp) and the
+// kernel translation units.  Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gla {
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;       // GDN only
+    int n_req, n_heads, dk, dv;
+    int in_bf16, out_bf16;
+    float* pool;
+    int n_slots;
+    const int32_t* slot_idx;
+    void* o;
+};
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;       // GDN only
+    const int32_t* cu_seqlens;
+    int n_seqs, n_tokens, n_heads, dk, dv, chunk;
+    int in_bf16, out_bf16;
+    float* pool;
+    int n_slots;
+    const int32_t* slot_idx;
+    int zero_init;
+    void* o;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+struct ConvArgs {
+    const void* x;
+    const float* w;
+    const int32_t* cu_seqlens;
+    int n_seqs, n_tokens, channels, width;
+    void* cache;
+    int n_slots;
+    const int32_t* slot_idx;
+    int zero_init;
+    void* y;
+    int bf16;
+};
+
+hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_gdn_chunk(const ChunkArgs& a, hipStream_t s);
+size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
+
+}  // namespace gla

@@ -1,0 +1,147 @@
+"""Python binding of the C ABI: torch tensors in, the same names out.
+
+Each function only checks tensor placement/dtype/layout, takes raw device
+pointers and the current HIP stream, and calls the library.  Every step of
+the computation runs in the HIP kernels; there is no other implementation
+here.  Shapes follow include/gla.h.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.GLA_F32, torch.bfloat16: _lib.GLA_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(t, name, dtype=None, dims=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, has {t.dim()}")
+
+
+def _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, out_dtype, o):
+    for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 3),
+                        (k, "k", (torch.float32, torch.bfloat16), 3),
+                        (v, "v", (torch.float32, torch.bfloat16), 3),
+                        (alpha, "alpha", torch.float32, 2), (cu_seqlens, "cu_seqlens", torch.int32, 1),
+                        (state_pool, "state_pool", torch.float32, 4), (slot_idx, "slot_idx", torch.int32, 1)]:
+        _check(t, n, d, nd)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    out_dtype = out_dtype or q.dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
+    _check(o, "o", out_dtype, 3)
+    return N, H, dk, dv, out_dtype, o
+
+
+def gla_chunk_fwd(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, *, chunk=64, out_dtype=None,
+                  zero_init=False, o=None, workspace=None):
+    """Chunked GLA prefill; updates state_pool[slot_idx] in place, returns o."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    B = cu_seqlens.shape[0] - 1
+    need = _lib.lib().gla_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _lib.call("gla_chunk_fwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              cu_seqlens.data_ptr(), B, N, H, dk, dv, chunk, _DT[q.dtype], _DT[out_dtype],
+              state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
+              _lib.GLA_ZERO_INIT if zero_init else 0, o.data_ptr(), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream(q.device))
+    return o
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, *, chunk=64,
+                  out_dtype=None, zero_init=False, o=None, workspace=None):
+    """Chunked Gated DeltaNet prefill; updates state_pool[slot_idx] in place, returns o."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    _check(beta, "beta", torch.float32, 2)
+    B = cu_seqlens.shape[0] - 1
+    need = _lib.lib().gdn_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _lib.call("gdn_chunk_fwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              beta.data_ptr(), cu_seqlens.data_ptr(), B, N, H, dk, dv, chunk, _DT[q.dtype],
+              _DT[out_dtype], state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
+              _lib.GLA_ZERO_INIT if zero_init else 0, o.data_ptr(), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream(q.device))
+    return o
+
+
+def workspace_bytes(kind, n_seqs, n_tokens, n_heads, dk, dv, chunk):
+    fn = {"gla": "gla_chunk_workspace_bytes", "gdn": "gdn_chunk_workspace_bytes"}[kind]
+    return getattr(_lib.lib(), fn)(n_seqs, n_tokens, n_heads, dk, dv, chunk)
+
+
+def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o):
+    for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 3),
+                        (k, "k", (torch.float32, torch.bfloat16), 3),
+                        (v, "v", (torch.float32, torch.bfloat16), 3),
+                        (alpha, "alpha", torch.float32, 2),
+                        (state_pool, "state_pool", torch.float32, 4), (slot_idx, "slot_idx", torch.int32, 1)]:
+        _check(t, n, d, nd)
+    R, H, dk = q.shape
+    dv = v.shape[2]
+    out_dtype = out_dtype or q.dtype
+    if o is None:
+        o = torch.empty((R, H, dv), dtype=out_dtype, device=q.device)
+    _check(o, "o", out_dtype, 3)
+    return R, H, dk, dv, out_dtype, o
+
+
+def gla_decode_step(q, k, v, alpha, state_pool, slot_idx, *, out_dtype=None, o=None):
+    """One GLA decode token per request, in place on state_pool[slot_idx]; returns o."""
+    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o)
+    _lib.call("gla_decode_step", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), R, H,
+              dk, dv, _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(), state_pool.shape[0],
+              slot_idx.data_ptr(), o.data_ptr(), _stream(q.device))
+    return o
+
+
+def gdn_decode_step(q, k, v, alpha, beta, state_pool, slot_idx, *, out_dtype=None, o=None):
+    """One Gated DeltaNet decode token per request, in place; returns o."""
+    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o)
+    _check(beta, "beta", torch.float32, 2)
+    _lib.call("gdn_decode_step", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              beta.data_ptr(), R, H, dk, dv, _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(),
+              state_pool.shape[0], slot_idx.data_ptr(), o.data_ptr(), _stream(q.device))
+    return o
+
+
+def causal_conv1d_fwd(x, w, cu_seqlens, conv_cache, slot_idx, *, zero_init=False, y=None):
+    """Depthwise causal conv with per-slot cache (updated in place); returns y."""
+    _check(x, "x", (torch.float32, torch.bfloat16), 2)
+    _check(w, "w", torch.float32, 2)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _check(conv_cache, "conv_cache", x.dtype, 3)
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    N, C = x.shape
+    W = w.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, 2)
+    _lib.call("causal_conv1d_fwd", x.data_ptr(), w.data_ptr(), cu_seqlens.data_ptr(),
+              cu_seqlens.shape[0] - 1, N, C, W, conv_cache.data_ptr(), conv_cache.shape[0],
+              slot_idx.data_ptr(), _lib.GLA_ZERO_INIT if zero_init else 0, y.data_ptr(),
+              _DT[x.dtype], _stream(x.device))
+    return y

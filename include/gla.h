@@ -1,0 +1,191 @@
+/*
+ * gla.h -- C ABI of the gated linear-attention state recurrence on MI355X
+ * (gfx950): GLA and Gated DeltaNet, chunked prefill and slot-indexed decode,
+ * plus the short causal convolution that precedes the layer.
+ *
+ * Source of the computation: "Inference for linear attention and hybrid
+ * architectures" (section "Two ways to write the same computation"):
+ *
+ *   GLA             S_t = a_t S_{t-1} + k_t^T v_t
+ *   Gated DeltaNet  S_t = a_t (I - b_t k_t^T k_t) S_{t-1} + b_t k_t^T v_t
+ *   output          o_t = q_t S_t            (state after the update)
+ *
+ * q_t, k_t are d_k row vectors, v_t is a d_v row vector, S is a d_k x d_v
+ * fp32 state per head, a_t (alpha, the decay gate) and b_t (beta) are one
+ * scalar per token per head.  There is no softmax, no normaliser and no
+ * scale: callers pre-scale q.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer (hipMalloc'ed or a tensor's
+ *    data) unless stated otherwise.  The library never allocates or frees
+ *    device memory and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; execution errors surface at the
+ *    caller's next synchronisation, as for any HIP launch.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    negative return value means nothing was enqueued and no output, state
+ *    slot or cache was touched.  GLA_EHIP reports a failed launch.
+ *  - No global state: calls are re-entrant.  No C++ exception crosses the
+ *    ABI.
+ *  - Packed variable-length layout: token n of sequence b is row
+ *    cu_seqlens[b] + n of the token-major arrays
+ *        q, k   [n_tokens, n_heads, dk]    (in_dtype)
+ *        v, o   [n_tokens, n_heads, dv]    (in_dtype / out_dtype)
+ *        alpha, beta  [n_tokens, n_heads]  fp32
+ *    cu_seqlens [n_seqs + 1] int32, non-decreasing, cu[0] = 0,
+ *    cu[n_seqs] = n_tokens.  Empty sequences are allowed.
+ *  - State pool [n_slots, n_heads, dk, dv] fp32, row-major (dv fastest).
+ *    Sequence / request b reads its initial state from
+ *    pool[slot_idx[b]] and writes its final state back to the same slot, in
+ *    place.  Slots not named by slot_idx are never read or written.
+ *    slot_idx entries must be distinct; an entry outside [0, n_slots)
+ *    makes the kernels skip that sequence (its outputs are left as they
+ *    were) instead of faulting.
+ *  - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}.
+ *    dtypes: in_dtype, out_dtype in {GLA_F32, GLA_BF16}.  bf16 outputs are
+ *    the fp32 result rounded to nearest even.
+ *  - Preconditions (undefined results, not faults, if violated):
+ *    alpha in (0, 1] and finite (the chunked form works with log alpha);
+ *    beta >= 0 with beta |k|^2 <= 2; q/k/v/o do not overlap the pool.
+ *    Token indices derived from cu_seqlens are clamped to [0, n_tokens),
+ *    so a malformed cu_seqlens gives wrong results, never an out-of-bounds
+ *    access.
+ */
+#ifndef GLA_MI355X_H
+#define GLA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GLA_API __attribute__((visibility("default")))
+#else
+#define GLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+enum {
+    GLA_OK = 0,
+    GLA_EPTR = -1,       /* a required pointer is NULL                        */
+    GLA_ESHAPE = -2,     /* a size is negative, unsupported or inconsistent   */
+    GLA_EDTYPE = -3,     /* unsupported dtype                                 */
+    GLA_ECHUNK = -4,     /* unsupported chunk size                            */
+    GLA_EWORKSPACE = -5, /* workspace missing or smaller than required        */
+    GLA_EHIP = -6        /* the HIP launch failed                             */
+};
+
+/* flags */
+enum { GLA_ZERO_INIT = 1u };  /* ignore the pool's contents: S_0 = 0 */
+
+/*
+ * gla_chunk_fwd -- GLA prefill by the chunked algorithm ("Two ways to write
+ * the same computation", the chunked form; chunks start at each sequence's
+ * first token of this call and the last one may be partial).  Per chunk of
+ * C tokens with g = running sum of log alpha inside the chunk:
+ *   O = ((Q K^T) .* D) V + diag(exp g) Q S,   D_ij = exp(g_i - g_j) [j <= i]
+ *   S <- exp(g_last) S + (diag(exp(g_last - g)) K)^T V
+ * The initial state is pool[slot_idx[b]] (zeros with GLA_ZERO_INIT); the
+ * final state is written back to that slot.  Splitting a prompt over
+ * several calls that pass the state through the pool gives the same result
+ * up to rounding ("Chunked prefill comes for free").
+ * `o` is fully overwritten for tokens of sequences with a valid slot.
+ * `workspace` may be NULL when gla_chunk_workspace_bytes() returns 0.
+ */
+GLA_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd -- Gated DeltaNet prefill, chunked.  Same contract as
+ * gla_chunk_fwd plus beta [n_tokens, n_heads] fp32.  The page gives no
+ * chunked form for DeltaNet (it only says the in-chunk corrections must be
+ * written in matrix form); the one used is derived from the update: with
+ * u_t = b_t (v_t - a_t k_t S_{t-1}) each step is a GLA step with value u_t,
+ * and inside a chunk entered with state S
+ *   (I + A) U = diag(b) V - diag(b exp g) K S,
+ *   A_tj = b_t exp(g_t - g_j) (k_t . k_j) for j < t,
+ * solved as U = T diag(b) V - (T diag(b exp g) K) S with T = (I + A)^-1,
+ * followed by the GLA chunk formulas with U in place of V.
+ * Requires workspace of gdn_chunk_workspace_bytes() bytes (may be 0).
+ */
+GLA_API int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes the chunked calls need for these sizes (an upper bound
+ * that does not depend on the contents of cu_seqlens).  0 = none. */
+GLA_API size_t gla_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                                 int32_t dk, int32_t dv, int32_t chunk);
+GLA_API size_t gdn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                                 int32_t dk, int32_t dv, int32_t chunk);
+
+/*
+ * gla_decode_step -- one GLA token per request, recurrent form ("Two ways
+ * to write the same computation": the state is read once and updated by one
+ * rank-one term; "Speculative decoding and PD disaggregation": batched
+ * decode reads and writes each request's fixed pool slot).
+ *   S = pool[slot_idx[r]];  S <- alpha_r S + k_r^T v_r;  o_r = q_r S;
+ *   pool[slot_idx[r]] <- S          (in place)
+ * q, k [n_req, n_heads, dk]; v, o [n_req, n_heads, dv]; alpha [n_req, n_heads].
+ */
+GLA_API int gla_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                    int32_t n_req, int32_t n_heads, int32_t dk, int32_t dv,
+                    gla_dtype in_dtype, gla_dtype out_dtype,
+                    float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                    void* o, void* stream);
+
+/*
+ * gdn_decode_step -- one Gated DeltaNet token per request, in place:
+ *   p = k S;  u = beta (v - alpha p);  S <- alpha S + k^T u;  o = q S
+ * (equal to alpha (I - beta k^T k) S + beta k^T v).  beta [n_req, n_heads].
+ */
+GLA_API int gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                    const float* beta,
+                    int32_t n_req, int32_t n_heads, int32_t dk, int32_t dv,
+                    gla_dtype in_dtype, gla_dtype out_dtype,
+                    float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                    void* o, void* stream);
+
+/*
+ * causal_conv1d_fwd -- depthwise causal convolution of width W with a
+ * per-request cache of the last W-1 inputs ("Two ways to write the same
+ * computation", last paragraph; "The real model's ledger": an engine keeps
+ * W-1 columns).  For sequence b with cache rows c = conv_cache[slot_idx[b]]
+ * (zeros with GLA_ZERO_INIT) and xx = [c ; x_b]:
+ *   y[t, ch] = sum_{i<W} w[ch, i] * xx[t + i, ch]     (w[:, W-1] = current token)
+ * then conv_cache[slot_idx[b]] <- the last W-1 rows of xx.  No bias, no
+ * activation.  x, y [n_tokens, channels] (dtype); w [channels, W] fp32;
+ * conv_cache [n_slots, W-1, channels] (dtype).  W in {2, 3, 4}; channels a
+ * multiple of 8.  x and y must not overlap.
+ */
+GLA_API int causal_conv1d_fwd(const void* x, const float* w, const int32_t* cu_seqlens,
+                      int32_t n_seqs, int32_t n_tokens, int32_t channels, int32_t width,
+                      void* conv_cache, int32_t n_slots, const int32_t* slot_idx,
+                      uint32_t flags, void* y, gla_dtype dtype, void* stream);
+
+/* Static description of a status code. */
+GLA_API const char* gla_status_string(int status);
+
+/* Library version, "major.minor.patch". */
+GLA_API const char* gla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_MI355X_H */

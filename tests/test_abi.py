@@ -1,0 +1,119 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry
+point declared in include/gla.h, and rejects bad arguments with the
+documented status before any HIP call (so these run without a GPU)."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+from gated_deltanet_gla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"GLA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert {"gla_chunk_fwd", "gdn_chunk_fwd", "gla_decode_step", "gdn_decode_step",
+            "causal_conv1d_fwd"} <= set(names)
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    assert _lib.status_string(0) == "ok"
+    for st in (-1, -2, -3, -4, -5, -6):
+        assert _lib.status_string(st) not in ("ok", "unknown status")
+    assert _lib.lib().gla_version().decode().count(".") == 2
+
+
+FAKE = 0x1000   # never dereferenced: validation fails before any launch
+
+
+def _chunk_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, cu=FAKE, B=2, N=10, H=4, dk=128, dv=128, C=64,
+             idt=1, odt=1, pool=FAKE, n_slots=4, slots=FAKE, flags=0, o=FAKE, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return a
+
+
+def _gla_chunk(a):
+    return _lib.lib().gla_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["cu"], a["B"], a["N"],
+                                    a["H"], a["dk"], a["dv"], a["C"], a["idt"], a["odt"], a["pool"],
+                                    a["n_slots"], a["slots"], a["flags"], a["o"], a["ws"], a["wsb"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.GLA_EPTR), (dict(pool=None), _lib.GLA_EPTR), (dict(cu=None), _lib.GLA_EPTR),
+    (dict(dk=96), _lib.GLA_ESHAPE), (dict(dv=256), _lib.GLA_ESHAPE), (dict(H=0), _lib.GLA_ESHAPE),
+    (dict(N=-1), _lib.GLA_ESHAPE), (dict(B=-3), _lib.GLA_ESHAPE), (dict(n_slots=0), _lib.GLA_ESHAPE),
+    (dict(C=48), _lib.GLA_ECHUNK), (dict(C=128), _lib.GLA_ECHUNK), (dict(idt=2), _lib.GLA_EDTYPE),
+    (dict(odt=-1), _lib.GLA_EDTYPE), (dict(flags=8), _lib.GLA_ESHAPE), (dict(B=0), _lib.GLA_ESHAPE),
+])
+def test_gla_chunk_validation(kw, status):
+    assert _gla_chunk(_chunk_args(**kw)) == status
+
+
+def test_empty_calls_are_noops():
+    # nothing to do -> OK without touching any pointer
+    assert _gla_chunk(_chunk_args(B=0, N=0, q=None, k=None, v=None, pool=None, cu=None)) == 0
+    L = _lib.lib()
+    assert L.gla_decode_step(None, None, None, None, 0, 16, 128, 128, 1, 1, None, 4, None, None,
+                             None) == 0
+
+
+def test_gdn_chunk_validation():
+    L = _lib.lib()
+    a = _chunk_args()
+    args = [a["q"], a["k"], a["v"], a["alpha"], None, a["cu"], a["B"], a["N"], a["H"], a["dk"],
+            a["dv"], a["C"], a["idt"], a["odt"], a["pool"], a["n_slots"], a["slots"], 0, a["o"],
+            None, 0, None]
+    assert L.gdn_chunk_fwd(*args) == _lib.GLA_EPTR          # beta missing
+    need = L.gdn_chunk_workspace_bytes(2, 10, 4, 128, 128, 64)
+    args[4] = FAKE
+    if need:
+        assert L.gdn_chunk_fwd(*args) == _lib.GLA_EWORKSPACE
+        args[19], args[20] = FAKE, need - 1
+        assert L.gdn_chunk_fwd(*args) == _lib.GLA_EWORKSPACE
+    assert L.gdn_chunk_workspace_bytes(2, 10, 4, 100, 128, 64) == 0
+
+
+def test_decode_validation():
+    L = _lib.lib()
+    base = [FAKE, FAKE, FAKE, FAKE, 8, 16, 128, 128, 1, 1, FAKE, 32, FAKE, FAKE, None]
+    for i, bad, st in [(0, None, -1), (10, None, -1), (12, None, -1), (13, None, -1),
+                       (6, 100, -2), (7, 8, -2), (8, 5, -3), (11, 0, -2), (4, -1, -2)]:
+        args = list(base)
+        args[i] = bad
+        assert L.gla_decode_step(*args) == st, (i, bad)
+    gargs = base[:4] + [None] + base[4:]
+    assert L.gdn_decode_step(*gargs) == -1
+
+
+def test_conv_validation():
+    L = _lib.lib()
+    base = [FAKE, FAKE, FAKE, 2, 10, 2048, 4, FAKE, 8, FAKE, 0, FAKE, 1, None]
+    for i, bad, st in [(0, None, -1), (1, None, -1), (5, 12, -2), (6, 5, -2), (6, 1, -2),
+                       (12, 3, -3), (8, 0, -2), (10, 4, -2), (11, None, -1)]:
+        args = list(base)
+        args[i] = bad
+        assert L.causal_conv1d_fwd(*args) == st, (i, bad)
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """The package never imports the oracle and has no CPU path."""
+    pkg = os.path.join(ROOT, "gated_deltanet_gla_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("no oracle", ""), fn
