@@ -1,0 +1,226 @@
+// Building blocks of the chunked prefill kernels (GLA and Gated DeltaNet).
+//
+// MFMA operands are read from LDS matrices stored "k-contiguous": the
+// element (line, k) of an operand sits at base[line * ld + k].  An A
+// operand's lines are its rows, a B operand's lines are its columns (the
+// matrix is kept transposed).  With that single convention every 16x16
+// output tile is one call of mma() whatever the contraction.
+//
+// Two operand formats:
+//  * bf16 inputs: matrices are bf16.  Inputs q, k, v are exact in bf16;
+//    every fp32-derived operand (decay-masked scores, the state, decayed or
+//    beta-scaled values, the inverse T, ...) is stored as a hi + lo pair of
+//    bf16 matrices and contracted with two (or three) MFMAs, which keeps the
+//    product accurate to about 2^-16 relative instead of bf16's 2^-8.
+//  * fp32 inputs: matrices are fp32 and the 16x16x4 fp32 MFMA is used;
+//    there is no lo part.
+//
+// Lines are padded by 16 bytes, so the 16 lines a ds_read_b128 wave touches
+// start in 16 different 4-bank groups (no bank conflicts).
+#pragma once
+
+#include "common.h"
+
+namespace gla {
+
+template <bool F32> struct Op;
+
+template <> struct Op<false> {               // bf16 operands
+    using E = uint16_t;
+    static constexpr int PAD = 8;
+    static constexpr bool kHasLo = true;
+
+    __device__ __forceinline__ static void mma(f32x4& acc, const E* A, int lda, const E* B, int ldb,
+                                               int K) {
+        const int lane = threadIdx.x & 63;
+        const int line = lane & 15;
+        const int grp = lane >> 4;
+        const E* a = A + line * lda + grp * 8;
+        const E* b = B + line * ldb + grp * 8;
+        int k0 = 0;
+        for (; k0 + 32 <= K; k0 += 32) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(a + k0);
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(b + k0);
+            acc = mfma_bf16(as_bf16x8(av), as_bf16x8(bv), acc);
+        }
+        if (k0 < K) {   // 16-wide tail: 16x16x16 MFMA, 4 k-values per lane
+            typedef __attribute__((ext_vector_type(4))) short s16x4;
+            const E* a4 = A + line * lda + k0 + grp * 4;
+            const E* b4 = B + line * ldb + k0 + grp * 4;
+            const u32x2 av = *reinterpret_cast<const u32x2*>(a4);
+            const u32x2 bv = *reinterpret_cast<const u32x2*>(b4);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av),
+                                                            __builtin_bit_cast(s16x4, bv), acc, 0, 0, 0);
+        }
+    }
+
+    // Store 4 consecutive values (v.x..v.w at p[0..3]) as hi (+ lo).
+    __device__ __forceinline__ static void store4(E* hi, E* lo, f32x4 v) {
+        uint16_t h[4], l[4];
+        split_bf16(v.x, h[0], l[0]);
+        split_bf16(v.y, h[1], l[1]);
+        split_bf16(v.z, h[2], l[2]);
+        split_bf16(v.w, h[3], l[3]);
+        u32x2 wh, wl;
+        wh.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+        wh.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+        wl.x = l[0] | (static_cast<uint32_t>(l[1]) << 16);
+        wl.y = l[2] | (static_cast<uint32_t>(l[3]) << 16);
+        *reinterpret_cast<u32x2*>(hi) = wh;
+        *reinterpret_cast<u32x2*>(lo) = wl;
+    }
+    __device__ __forceinline__ static void store1(E* hi, E* lo, float x) {
+        uint16_t h, l;
+        split_bf16(x, h, l);
+        *hi = h;
+        *lo = l;
+    }
+    __device__ __forceinline__ static void store1_exact(E* p, float x) { *p = f32_to_bf16_bits(x); }
+    __device__ __forceinline__ static float load1(const E* p) { return bf16_bits_to_f32(*p); }
+};
+
+template <> struct Op<true> {                // fp32 operands
+    using E = float;
+    static constexpr int PAD = 4;
+    static constexpr bool kHasLo = false;
+
+    __device__ __forceinline__ static void mma(f32x4& acc, const E* A, int lda, const E* B, int ldb,
+                                               int K) {
+        const int lane = threadIdx.x & 63;
+        const int line = lane & 15;
+        const int grp = lane >> 4;
+        const E* a = A + line * lda + grp * 4;
+        const E* b = B + line * ldb + grp * 4;
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(a + k0);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(b + k0);
+            acc = mfma_f32(av.x, bv.x, acc);
+            acc = mfma_f32(av.y, bv.y, acc);
+            acc = mfma_f32(av.z, bv.z, acc);
+            acc = mfma_f32(av.w, bv.w, acc);
+        }
+    }
+    __device__ __forceinline__ static void store4(E* hi, E*, f32x4 v) {
+        *reinterpret_cast<f32x4*>(hi) = v;
+    }
+    __device__ __forceinline__ static void store1(E* hi, E*, float x) { *hi = x; }
+    __device__ __forceinline__ static void store1_exact(E* p, float x) { *p = x; }
+    __device__ __forceinline__ static float load1(const E* p) { return *p; }
+};
+
+// acc += A_hi.B (+ A_lo.B): A fp32-derived (hi/lo), B exact.
+template <bool F32>
+__device__ __forceinline__ void mma_sx(f32x4& acc, const typename Op<F32>::E* Ahi,
+                                       const typename Op<F32>::E* Alo, int lda,
+                                       const typename Op<F32>::E* B, int ldb, int K) {
+    Op<F32>::mma(acc, Ahi, lda, B, ldb, K);
+    if constexpr (!F32) Op<F32>::mma(acc, Alo, lda, B, ldb, K);
+}
+// acc += A.B_hi (+ A.B_lo): A exact, B fp32-derived.
+template <bool F32>
+__device__ __forceinline__ void mma_xs(f32x4& acc, const typename Op<F32>::E* A, int lda,
+                                       const typename Op<F32>::E* Bhi,
+                                       const typename Op<F32>::E* Blo, int ldb, int K) {
+    Op<F32>::mma(acc, A, lda, Bhi, ldb, K);
+    if constexpr (!F32) Op<F32>::mma(acc, A, lda, Blo, ldb, K);
+}
+// acc += (A_hi + A_lo)(B_hi + B_lo) without the lo.lo term.
+template <bool F32>
+__device__ __forceinline__ void mma_ss(f32x4& acc, const typename Op<F32>::E* Ahi,
+                                       const typename Op<F32>::E* Alo, int lda,
+                                       const typename Op<F32>::E* Bhi,
+                                       const typename Op<F32>::E* Blo, int ldb, int K) {
+    Op<F32>::mma(acc, Ahi, lda, Bhi, ldb, K);
+    if constexpr (!F32) {
+        Op<F32>::mma(acc, Ahi, lda, Blo, ldb, K);
+        Op<F32>::mma(acc, Alo, lda, Bhi, ldb, K);
+    }
+}
+
+// Lane position inside a 16x16 accumulator tile: column (lane % 16), rows
+// 4 * (lane / 16) + {0..3}.
+struct AccPos {
+    int col, row0;
+    __device__ __forceinline__ AccPos() {
+        const int lane = threadIdx.x & 63;
+        col = lane & 15;
+        row0 = (lane >> 4) * 4;
+    }
+};
+
+// ------------------------------------------------------------------ staging
+// Copy rows [0, n) of a [rows x W] slice of a token-major tensor (row j at
+// src + j * stride) into LDS, natural layout dst[j * ld + c]; rows >= n are
+// zero.  16-byte vectors; TI is the input storage type (F32 or BF16) and the
+// LDS element has the same width.
+template <class TI, int ROWS, int W, int NT>
+__device__ __forceinline__ void stage_natural(typename TI::T* dst, int ld, const typename TI::T* src,
+                                              long stride, int n) {
+    constexpr int VE = 16 / TI::bytes;
+    constexpr int VPR = W / VE;
+    for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+        const int row = idx / VPR;
+        const int vc = idx % VPR;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (row < n) val = *reinterpret_cast<const u32x4*>(src + row * stride + vc * VE);
+        *reinterpret_cast<u32x4*>(dst + row * ld + vc * VE) = val;
+    }
+}
+
+// Same source, transposed into LDS: dst[c * ld + j] = src[j][c].  Optionally
+// also the natural copy (natural != nullptr).
+template <class TI, int ROWS, int W, int NT>
+__device__ __forceinline__ void stage_transposed(typename TI::T* dst, int ld, typename TI::T* natural,
+                                                 int ldn, const typename TI::T* src, long stride,
+                                                 int n) {
+    using T = typename TI::T;
+    constexpr int VE = 16 / TI::bytes;
+    constexpr int VPR = W / VE;
+    for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+        const int row = idx / VPR;
+        const int vc = idx % VPR;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (row < n) val = *reinterpret_cast<const u32x4*>(src + row * stride + vc * VE);
+        if (natural) *reinterpret_cast<u32x4*>(natural + row * ldn + vc * VE) = val;
+        const T* e = reinterpret_cast<const T*>(&val);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) dst[(vc * VE + i) * ld + row] = e[i];
+    }
+}
+
+// ------------------------------------------------------------------ decay scan
+// Wave 0 computes, for the chunk rows j < C (rows >= n behave as alpha = 1):
+//   g[j]   = sum_{r <= j} log alpha_r   (inclusive, restarted at the chunk)
+//   eg[j]  = exp(g[j]),  dec[j] = exp(g[C-1] - g[j]),  *gamma = exp(g[C-1]).
+// Every exponent is <= 0.  Requires C <= 64.
+template <int C>
+__device__ __forceinline__ void decay_scan(const float* alpha, long astride, int n, float* g,
+                                           float* eg, float* dec, float* gamma) {
+    const int lane = threadIdx.x;
+    if (lane >= 64) return;
+    float x = 0.f;
+    if (lane < n && lane < C) x = __logf(alpha[lane * astride]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    const float last = __shfl(x, C - 1, 64);
+    if (lane < C) {
+        g[lane] = x;
+        eg[lane] = __expf(x);
+        dec[lane] = __expf(last - x);
+    }
+    if (lane == 0) *gamma = __expf(last);
+}
+
+// blockIdx -> logical work id, grouping consecutive logical ids on one XCD
+// (blocks are dealt to the 8 XCDs round-robin) so that work sharing inputs
+// through L2 lands on the same XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    if ((nblocks & 7) != 0) return bid;
+    const int per = nblocks >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace gla

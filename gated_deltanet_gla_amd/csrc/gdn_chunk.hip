@@ -1,0 +1,486 @@
+// Chunked Gated DeltaNet prefill on gfx950.
+//
+// "Inference for linear attention and hybrid architectures", section "Two
+// ways to write the same computation": DeltaNet's update
+// (I - b_t k_t^T k_t) S + b_t k_t^T v_t with a decay gate a_t multiplied in
+// (on the old state), and the remark that the in-chunk error-correcting
+// updates must first be written in matrix form.  That matrix form is not on
+// the page; the one used here is derived from the update itself:
+//
+//   u_t = b_t (v_t - a_t k_t S_{t-1})  makes every step a GLA step with
+//   value u_t:  S_t = a_t S_{t-1} + k_t^T u_t.
+//
+// Inside a chunk entered with state S, with g the running sum of log a,
+//   (I + A) U = diag(b) (V - diag(exp g) K S),
+//   A_tj = b_t exp(g_t - g_j) (k_t . k_j)  for j < t, 0 otherwise,
+// so U = T diag(b) Y with T = (I + A)^-1 and Y = V - diag(exp g) (K S).
+// Then the GLA chunk formulas apply with U in place of V:
+//   O = diag(exp g) Q S + ((Q K^T) .* D) U
+//   S <- exp(g_last) S + K^T diag(exp(g_last - g)) U.
+//
+// Kernels:
+//  1. gdn_chunk_offsets: exclusive scan of ceil(L_b / C) -> first chunk of
+//     every sequence (one workgroup).
+//  2. gdn_prep: one workgroup per (chunk, head), all chunks at once: A from
+//     K K^T on MFMA, then the unit-lower-triangular inverse T in fp32
+//     (16x16 diagonal blocks by forward substitution, off-diagonal blocks
+//     T_ij = -T_ii sum_k A_ik T_kj along successive block diagonals).  T does
+//     not depend on the state, so this latency-heavy step runs fully
+//     parallel instead of on the serial chain.  Written to the workspace.
+//  3. gdn_chunk: one workgroup per (sequence, head, d_v tile), the serial
+//     chunk loop with the state slice in MFMA accumulators.
+#include "chunk_common.h"
+#include "launch.h"
+
+namespace gla {
+namespace {
+
+constexpr int NW = 4;
+constexpr int NT = NW * 64;
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ constexpr long max_chunks(int n_seqs, int n_tokens, int C) {
+    return static_cast<long>(n_tokens) / C + n_seqs;
+}
+
+// ------------------------------------------------------------------ 1. offsets
+__global__ void __launch_bounds__(1024)
+gdn_chunk_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int C,
+                  int32_t* __restrict__ off) {
+    __shared__ int part[1024];
+    const int t = threadIdx.x;
+    const int per = (n_seqs + 1023) / 1024;
+    const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int s = clampi(cu[b], 0, n_tokens);
+        const int e = clampi(cu[b + 1], s, n_tokens);
+        sum += (e - s + C - 1) / C;
+    }
+    part[t] = sum;
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int i = 0; i < 1024; ++i) {
+            const int x = part[i];
+            part[i] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    int run = part[t];
+    for (int b = b0; b < b1; ++b) {
+        off[b] = run;
+        const int s = clampi(cu[b], 0, n_tokens);
+        const int e = clampi(cu[b + 1], s, n_tokens);
+        run += (e - s + C - 1) / C;
+    }
+    if (b1 == n_seqs && b0 < b1) off[n_seqs] = run;
+    if (n_seqs == 0 && t == 0) off[0] = 0;
+}
+
+// ------------------------------------------------------------------ 2. prep
+template <int DK, int C, bool F32>
+struct PrepSmem {
+    using E = typename Op<F32>::E;
+    static constexpr int LQ = DK + Op<F32>::PAD;
+    static constexpr int LA = C + 4;           // fp32 lines of A and T (16-byte aligned)
+    alignas(16) E k[C][LQ];
+    alignas(16) float a[C][LA];
+    alignas(16) float t[C][LA];
+    alignas(16) float x[NW][16][20];           // per-wave 16x16 scratch (padded)
+    float g[C], eg[C], dec[C], beta[C];
+    float gamma;
+};
+
+template <int DK, int C, class TI>
+__global__ void __launch_bounds__(NT)
+gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
+         const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
+         int H, const int32_t* __restrict__ off, float* __restrict__ Tws) {
+    constexpr bool F32 = (TI::bytes == 4);
+    using O = Op<F32>;
+    using Sm = PrepSmem<DK, C, F32>;
+    constexpr int LQ = Sm::LQ;
+    constexpr int NB = C / 16;
+    __shared__ Sm sm;
+
+    const int h = blockIdx.x % H;
+    const int ci = blockIdx.x / H;
+    if (ci >= off[n_seqs]) return;
+    // sequence of this chunk: largest b with off[b] <= ci
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= ci) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int s0 = clampi(cu[b], 0, n_tokens);
+    const int s1 = clampi(cu[b + 1], s0, n_tokens);
+    const int c0 = (ci - off[b]) * C;
+    const int n = min(C, s1 - s0 - c0);
+    if (c0 < 0 || n <= 0) return;   // only with a malformed cu_seqlens
+    const long tok0 = s0 + c0;
+    const long tstride = static_cast<long>(H) * DK;
+
+    stage_natural<TI, C, DK, NT>(&sm.k[0][0], LQ, k + tok0 * tstride + h * DK, tstride, n);
+    decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g, sm.eg, sm.dec, &sm.gamma);
+    for (int j = threadIdx.x; j < C; j += NT) sm.beta[j] = j < n ? beta[(tok0 + j) * H + h] : 0.f;
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const AccPos ap;
+    // A = strictly-lower(diag(beta) (K K^T .* D)), fp32
+    for (int t = wave; t < NB * NB; t += NW) {
+        const int tt = t / NB, jt = t % NB;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (jt <= tt) O::mma(acc, &sm.k[tt * 16][0], LQ, &sm.k[jt * 16][0], LQ, DK);
+        const int j = jt * 16 + ap.col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = tt * 16 + ap.row0 + r;
+            sm.a[i][j] = (j < i) ? sm.beta[i] * __expf(sm.g[i] - sm.g[j]) * acc[r] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // diagonal blocks: forward substitution, one column per lane
+    if (wave < NB && lane < 16) {
+        const int base = wave * 16;
+        const int c = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) acc -= sm.a[base + r][base + m] * x[m];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.t[base + r][base + c] = x[r];
+    }
+    // blocks above the diagonal are zero
+    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+        const int r = idx / C, c = idx % C;
+        if ((c >> 4) > (r >> 4)) sm.t[r][c] = 0.f;
+    }
+    __syncthreads();
+
+    // off-diagonal blocks, one block diagonal at a time: T_ij = -T_ii sum_k A_ik T_kj
+    const int rr = lane >> 2;          // row inside the block
+    const int cc = (lane & 3) * 4;     // first of 4 columns
+    for (int d = 1; d < NB; ++d) {
+        const int i = d + wave;        // this wave's block row (block column i - d)
+        if (i < NB) {
+            const int j = i - d;
+            f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = j; kb < i; ++kb) {
+#pragma unroll 4
+                for (int m = 0; m < 16; ++m) {
+                    const float aim = sm.a[i * 16 + rr][kb * 16 + m];
+                    const f32x4 tk = *reinterpret_cast<const f32x4*>(&sm.t[kb * 16 + m][j * 16 + cc]);
+                    xs += aim * tk;
+                }
+            }
+            *reinterpret_cast<f32x4*>(&sm.x[wave][rr][cc]) = xs;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int m = 0; m < 16; ++m) {
+                const float tim = sm.t[i * 16 + rr][i * 16 + m];
+                const f32x4 xm = *reinterpret_cast<const f32x4*>(&sm.x[wave][m][cc]);
+                y += tim * xm;
+            }
+            *reinterpret_cast<f32x4*>(&sm.t[i * 16 + rr][j * 16 + cc]) = -y;
+        }
+        __syncthreads();
+    }
+
+    // T -> workspace, row-major C x C
+    float* dst = Tws + (static_cast<long>(ci) * H + h) * C * C;
+    for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
+        const int r = (idx * 4) / C, c = (idx * 4) % C;
+        *reinterpret_cast<f32x4*>(dst + r * C + c) = *reinterpret_cast<const f32x4*>(&sm.t[r][c]);
+    }
+}
+
+// ------------------------------------------------------------------ 3. serial chunk loop
+template <int DK, int BV, int C, bool F32>
+struct GdnSmem {
+    using E = typename Op<F32>::E;
+    static constexpr int PAD = Op<F32>::PAD;
+    static constexpr int LQ = DK + PAD;
+    static constexpr int LT = C + PAD;
+    static constexpr int HL = F32 ? 1 : 2;      // hi (+ lo) planes
+    alignas(16) E q[C][LQ];
+    alignas(16) E k[C][LQ];
+    alignas(16) E kt[DK][LT];
+    alignas(16) E p[HL][C][LT];
+    alignas(16) E st[HL][BV][LQ];
+    alignas(16) E t1[HL][C][LT];      // T diag(beta)
+    alignas(16) E yt[HL][BV][LT];     // (V - diag(exp g) K S)^T
+    alignas(16) E ut[HL][BV][LT];     // U^T
+    alignas(16) E udt[HL][BV][LT];    // (diag(exp(g_last - g)) U)^T
+    float g[C], eg[C], dec[C], beta[C];
+    float gamma;
+};
+
+template <int DK, int DV, int BV, int C, class TI, class TO>
+__global__ void __launch_bounds__(NT)
+gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __restrict__ k,
+                 const typename TI::T* __restrict__ v, const float* __restrict__ alpha,
+                 const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs,
+                 int n_tokens, int H, float* __restrict__ pool, int n_slots,
+                 const int32_t* __restrict__ slot_idx, int zero_init,
+                 const int32_t* __restrict__ off, long n_chunks_max, const float* __restrict__ Tws,
+                 typename TO::T* __restrict__ o) {
+    constexpr bool F32 = (TI::bytes == 4);
+    using O = Op<F32>;
+    using Sm = GdnSmem<DK, BV, C, F32>;
+    constexpr int LQ = Sm::LQ, LT = Sm::LT;
+    constexpr int LO = F32 ? 0 : 1;              // index of the lo plane
+    constexpr int NVT = DV / BV;
+    constexpr int CT = C / 16;
+    constexpr int BT = BV / 16;
+    constexpr int ST = (DK / 16) * BT;
+    constexpr int SPW = (ST + NW - 1) / NW;
+    static_assert(DV % BV == 0 && BV % 16 == 0 && C % 16 == 0 && C <= 64, "tiling");
+
+    __shared__ Sm sm;
+
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int vt = work % NVT;
+    const int bh = work / NVT;
+    const int h = bh % H;
+    const int b = bh / H;
+    if (b >= n_seqs) return;
+    const int slot = slot_idx[b];
+    if (slot < 0 || slot >= n_slots) return;
+    const int s0 = clampi(cu[b], 0, n_tokens);
+    const int s1 = clampi(cu[b + 1], s0, n_tokens);
+    const int L = s1 - s0;
+    const int chunk_base = off[b];
+
+    const int wave = threadIdx.x >> 6;
+    const AccPos ap;
+    const int col0 = vt * BV;
+
+    float* Sg = pool + (static_cast<long>(slot) * H + h) * DK * DV;
+    f32x4 S[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int t = wave + NW * i;
+        const int mt = t / BT, nt = t % BT;
+        S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < ST && !zero_init) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[i][r] = Sg[(mt * 16 + ap.row0 + r) * DV + col0 + nt * 16 + ap.col];
+        }
+    }
+
+    const long tstride = static_cast<long>(H) * DK;
+    const long vstride = static_cast<long>(H) * DV;
+    for (int c0 = 0, ci = chunk_base; c0 < L; c0 += C, ++ci) {
+        const int n = min(C, L - c0);
+        const long tok0 = s0 + c0;
+        if (ci < 0 || ci >= n_chunks_max) break;   // only reachable with a malformed cu_seqlens
+        __syncthreads();
+
+        // ---- phase 0: stage inputs, decay scan, state slice -> st
+        stage_natural<TI, C, DK, NT>(&sm.q[0][0], LQ, q + tok0 * tstride + h * DK, tstride, n);
+        stage_transposed<TI, C, DK, NT>(&sm.kt[0][0], LT, &sm.k[0][0], LQ,
+                                        k + tok0 * tstride + h * DK, tstride, n);
+        decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g, sm.eg, sm.dec, &sm.gamma);
+        for (int j = threadIdx.x; j < C; j += NT) sm.beta[j] = j < n ? beta[(tok0 + j) * H + h] : 0.f;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int t = wave + NW * i;
+            if (t < ST) {
+                const int mt = t / BT, nt = t % BT;
+                const int ln = nt * 16 + ap.col;
+                O::store4(&sm.st[0][ln][mt * 16 + ap.row0], &sm.st[LO][ln][mt * 16 + ap.row0], S[i]);
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 1: T diag(beta); P; X = K S -> Y = V - diag(exp g) X
+        {
+            const float* Tc = Tws + (static_cast<long>(ci) * H + h) * C * C;
+            for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
+                const int r = (idx * 4) / C, m = (idx * 4) % C;
+                f32x4 tv = *reinterpret_cast<const f32x4*>(Tc + r * C + m);
+                tv.x *= sm.beta[m];
+                tv.y *= sm.beta[m + 1];
+                tv.z *= sm.beta[m + 2];
+                tv.w *= sm.beta[m + 3];
+                O::store4(&sm.t1[0][r][m], &sm.t1[LO][r][m], tv);
+            }
+        }
+        for (int t = wave; t < CT * CT; t += NW) {
+            const int jt = t / CT, it = t % CT;
+            const int i = it * 16 + ap.col;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (jt <= it) {
+                O::mma(acc, &sm.k[jt * 16][0], LQ, &sm.q[it * 16][0], LQ, DK);
+                const float gi = sm.g[i];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = jt * 16 + ap.row0 + r;
+                    acc[r] = (j <= i) ? acc[r] * __expf(gi - sm.g[j]) : 0.f;
+                }
+            }
+            O::store4(&sm.p[0][i][jt * 16 + ap.row0], &sm.p[LO][i][jt * 16 + ap.row0], acc);
+        }
+        for (int t = wave; t < CT * BT; t += NW) {
+            const int tt = t / BT, nt = t % BT;
+            const int ln = nt * 16 + ap.col;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_xs<F32>(acc, &sm.k[tt * 16][0], LQ, &sm.st[0][nt * 16][0], &sm.st[LO][nt * 16][0], LQ, DK);
+            f32x4 y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = tt * 16 + ap.row0 + r;
+                const float vv = row < n ? TI::load(v, (tok0 + row) * vstride + h * DV + col0 + ln) : 0.f;
+                y[r] = vv - sm.eg[row] * acc[r];
+            }
+            O::store4(&sm.yt[0][ln][tt * 16 + ap.row0], &sm.yt[LO][ln][tt * 16 + ap.row0], y);
+        }
+        __syncthreads();
+
+        // ---- phase 2: U = T diag(beta) Y
+        for (int t = wave; t < CT * BT; t += NW) {
+            const int tt = t / BT, nt = t % BT;
+            const int ln = nt * 16 + ap.col;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_ss<F32>(acc, &sm.t1[0][tt * 16][0], &sm.t1[LO][tt * 16][0], LT, &sm.yt[0][nt * 16][0],
+                        &sm.yt[LO][nt * 16][0], LT, C);
+            O::store4(&sm.ut[0][ln][tt * 16 + ap.row0], &sm.ut[LO][ln][tt * 16 + ap.row0], acc);
+            f32x4 ud;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ud[r] = acc[r] * sm.dec[tt * 16 + ap.row0 + r];
+            O::store4(&sm.udt[0][ln][tt * 16 + ap.row0], &sm.udt[LO][ln][tt * 16 + ap.row0], ud);
+        }
+        __syncthreads();
+
+        // ---- phase 3: outputs and state hand-off
+        for (int t = wave; t < CT * BT; t += NW) {
+            const int it = t / BT, nt = t % BT;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_xs<F32>(acc, &sm.q[it * 16][0], LQ, &sm.st[0][nt * 16][0], &sm.st[LO][nt * 16][0], LQ, DK);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= sm.eg[it * 16 + ap.row0 + r];
+            mma_ss<F32>(acc, &sm.p[0][it * 16][0], &sm.p[LO][it * 16][0], LT, &sm.ut[0][nt * 16][0],
+                        &sm.ut[LO][nt * 16][0], LT, C);
+            const int colg = col0 + nt * 16 + ap.col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = it * 16 + ap.row0 + r;
+                if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + colg, acc[r]);
+            }
+        }
+        const float gam = sm.gamma;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int t = wave + NW * i;
+            if (t < ST) {
+                const int mt = t / BT, nt = t % BT;
+                S[i] *= gam;
+                mma_xs<F32>(S[i], &sm.kt[mt * 16][0], LT, &sm.udt[0][nt * 16][0],
+                            &sm.udt[LO][nt * 16][0], LT, C);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int t = wave + NW * i;
+        if (t < ST) {
+            const int mt = t / BT, nt = t % BT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sg[(mt * 16 + ap.row0 + r) * DV + col0 + nt * 16 + ap.col] = S[i][r];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+template <int DK, int DV, int C, class TI, class TO>
+hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
+    using T = typename TI::T;
+    constexpr bool F32 = (TI::bytes == 4);
+    constexpr int BV = F32 ? 16 : (DV >= 32 ? 32 : DV);
+    int32_t* off = static_cast<int32_t*>(a.workspace);
+    float* Tws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                          align256(sizeof(int32_t) * (a.n_seqs + 1)));
+    hipLaunchKernelGGL(gdn_chunk_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
+                       a.n_tokens, C, off);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
+    if (a.n_tokens > 0) {
+        hipLaunchKernelGGL((gdn_prep<DK, C, TI>), dim3(static_cast<unsigned>(mc * a.n_heads)), dim3(NT),
+                           0, s, static_cast<const T*>(a.k), a.alpha, a.beta, a.cu_seqlens, a.n_seqs,
+                           a.n_tokens, a.n_heads, off, Tws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
+    hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV, BV, C, TI, TO>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens,
+                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, mc, Tws,
+                       static_cast<typename TO::T*>(a.o));
+    return hipGetLastError();
+}
+
+template <int DK, int DV, class TI, class TO>
+hipError_t launch_c(const ChunkArgs& a, hipStream_t s) {
+    switch (a.chunk) {
+        case 16: return launch_inst<DK, DV, 16, TI, TO>(a, s);
+        case 32: return launch_inst<DK, DV, 32, TI, TO>(a, s);
+        case 64: return launch_inst<DK, DV, 64, TI, TO>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DK, int DV>
+hipError_t launch_dt(const ChunkArgs& a, hipStream_t s) {
+    if (a.in_bf16) return a.out_bf16 ? launch_c<DK, DV, BF16, BF16>(a, s) : launch_c<DK, DV, BF16, F32>(a, s);
+    return a.out_bf16 ? launch_c<DK, DV, F32, BF16>(a, s) : launch_c<DK, DV, F32, F32>(a, s);
+}
+
+template <int DK>
+hipError_t launch_dv(const ChunkArgs& a, hipStream_t s) {
+    switch (a.dv) {
+        case 16: return launch_dt<DK, 16>(a, s);
+        case 32: return launch_dt<DK, 32>(a, s);
+        case 64: return launch_dt<DK, 64>(a, s);
+        case 128: return launch_dt<DK, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int, int, int chunk) {
+    return align256(sizeof(int32_t) * (n_seqs + 1)) +
+           static_cast<size_t>(max_chunks(n_seqs, n_tokens, chunk)) * n_heads * chunk * chunk *
+               sizeof(float);
+}
+
+hipError_t launch_gdn_chunk(const ChunkArgs& a, hipStream_t s) {
+    switch (a.dk) {
+        case 16: return launch_dv<16>(a, s);
+        case 32: return launch_dv<32>(a, s);
+        case 64: return launch_dv<64>(a, s);
+        case 128: return launch_dv<128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gla

@@ -1,0 +1,196 @@
+"""GPU parity of the chunked prefill kernels (GLA and Gated DeltaNet)
+against the fp64 oracle.
+
+GLA: "Inference for linear attention and hybrid architectures", section
+"Two ways to write the same computation" (chunked form, state hand-off,
+segmented prefill).  Gated DeltaNet: the same section's update with the
+decay gate; the chunked form is derived (the page has none) and is checked
+here only through the recurrence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import DEV, check, dev, host, note, rel_err, rne_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_chunk(kind, w, *, out_dtype="f32", pool=None, chunk=None, cu=None, slots=None,
+              zero_init=None, rows=None):
+    """Run gla/gdn_chunk_fwd on workload w; returns (o tensor, pool tensor)."""
+    import gated_deltanet_gla_amd as G
+    sl = slice(None) if rows is None else slice(*rows)
+    tin = w.dtype
+    q, k, v = dev(w.q[sl], tin), dev(w.k[sl], tin), dev(w.v[sl], tin)
+    a = dev(w.alpha[sl])
+    pool = dev(w.pool) if pool is None else pool
+    cu = dev(w.cu_seqlens) if cu is None else dev(cu)
+    slots = dev(w.slot_idx) if slots is None else dev(slots)
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    zi = w.zero_init if zero_init is None else zero_init
+    C = chunk or w.chunk
+    if kind == "gla":
+        o = G.gla_chunk_fwd(q, k, v, a, cu, pool, slots, chunk=C, out_dtype=od, zero_init=zi)
+    else:
+        o = G.gdn_chunk_fwd(q, k, v, a, dev(w.beta[sl]), cu, pool, slots, chunk=C, out_dtype=od,
+                            zero_init=zi)
+    torch.cuda.synchronize()
+    return o, pool
+
+
+def run_oracle(kind, w):
+    if kind == "gla":
+        return oracle.gla_varlen(w.q, w.k, w.v, w.alpha, w.cu_seqlens, w.pool, w.slot_idx,
+                                 w.zero_init)
+    return oracle.gdn_varlen(w.q, w.k, w.v, w.alpha, w.beta, w.cu_seqlens, w.pool, w.slot_idx,
+                             w.zero_init)
+
+
+def test_page_toy_example_chunked():
+    """The page's worked example (T=64, d=16, C=16, fp32, zero state):
+    outputs and final state within 1e-5 of the recurrence."""
+    w = synth.page_toy_workload()
+    note("gla chunk toy")
+    o, pool = run_chunk("gla", w)
+    o_ref, S_ref = oracle.gla_sequence(w.q, w.k, w.v, w.alpha)
+    check(host(o), o_ref, "f32", "o")
+    check(host(pool)[0, 0], S_ref[0], "f32", "state")
+
+
+LENS = [1, 2, 15, 16, 17, 63, 0, 64, 65, 129, 200]
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (128, 128), (64, 32), (32, 128)])
+def test_chunk_varlen_parity(kind, dtype, C, dk, dv):
+    zero_init = (C == 32)
+    note(f"chunk {kind} {dtype} C={C} dk={dk} dv={dv} zero_init={zero_init}")
+    w = synth.random_varlen(1000 + C + dk + dv, LENS, 2, dk, dv, dtype=dtype, gdn=(kind == "gdn"),
+                            n_slots=14, zero_init=zero_init, chunk=C)
+    o, pool = run_chunk(kind, w)
+    o_ref, pool_ref = run_oracle(kind, w)
+    check(host(o), o_ref, dtype, "o")
+    p = pool.cpu().numpy()
+    check(p[w.slot_idx], pool_ref[w.slot_idx], dtype, "state")
+    untouched = sorted(set(range(14)) - set(w.slot_idx.tolist()))
+    assert np.array_equal(p[untouched], w.pool[untouched])
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+def test_bf16_output_is_rne_of_fp32(kind):
+    w = synth.random_varlen(11, [70, 5, 130], 3, 128, 128, dtype="bf16", gdn=(kind == "gdn"))
+    note(f"chunk {kind} bf16 out")
+    o32, p32 = run_chunk(kind, w, out_dtype="f32")
+    o16, p16 = run_chunk(kind, w, out_dtype="bf16")
+    assert torch.equal(o16.cpu(), rne_bf16(o32))
+    assert torch.equal(p16, p32)
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+def test_deterministic_and_batch_invariant(kind):
+    """Two runs are bitwise equal, and a sequence's output and final state do
+    not depend on what else is in the batch."""
+    w = synth.random_varlen(12, [40, 100, 7], 2, 64, 64, dtype="bf16", gdn=(kind == "gdn"), n_slots=5)
+    note(f"chunk {kind} determinism")
+    o1, p1 = run_chunk(kind, w)
+    o2, p2 = run_chunk(kind, w)
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
+    # sequence 1 alone
+    s, e = int(w.cu_seqlens[1]), int(w.cu_seqlens[2])
+    o3, p3 = run_chunk(kind, w, rows=(s, e), cu=np.array([0, e - s], np.int32),
+                       slots=w.slot_idx[1:2])
+    assert torch.equal(o3, o1[s:e])
+    sl = int(w.slot_idx[1])
+    assert torch.equal(p3[sl], p1[sl])
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+def test_invalid_slot_skips_sequence(kind):
+    w = synth.random_varlen(13, [20, 30], 2, 32, 32, dtype="f32", gdn=(kind == "gdn"), n_slots=3)
+    w.slot_idx = np.array([5, 1], np.int32)
+    note(f"chunk {kind} invalid slot")
+    import gated_deltanet_gla_amd as G
+    q, k, v, a = dev(w.q), dev(w.k), dev(w.v), dev(w.alpha)
+    pool = dev(w.pool)
+    o = torch.full((50, 2, 32), 7.0, device=DEV)
+    if kind == "gla":
+        G.gla_chunk_fwd(q, k, v, a, dev(w.cu_seqlens), pool, dev(w.slot_idx), chunk=16, o=o)
+    else:
+        G.gdn_chunk_fwd(q, k, v, a, dev(w.beta), dev(w.cu_seqlens), pool, dev(w.slot_idx),
+                        chunk=16, o=o)
+    torch.cuda.synchronize()
+    assert torch.all(o[:20] == 7.0)
+    assert np.array_equal(pool.cpu().numpy()[[0, 2]], w.pool[[0, 2]])
+    o_ref, _ = run_oracle(kind, synth.Workload(**{**w.__dict__, "slot_idx": np.array([0, 1], np.int32)}))
+    check(host(o)[20:], o_ref[20:], "f32", "o")
+
+
+def test_gla_prefill_full_size():
+    """GLA prefill: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 inputs,
+    zero initial state: every output and final state against the oracle."""
+    w = synth.prefill_gla()
+    note("gla prefill full size")
+    o, pool = run_chunk("gla", w)
+    o_ref, pool_ref = run_oracle("gla", w)
+    e_o = check(host(o), o_ref, "bf16", "o")
+    e_s = check(host(pool), pool_ref, "bf16", "state")
+    print(f"gla full: rel err o {e_o:.2e} state {e_s:.2e}")
+    o16, _ = run_chunk("gla", w, out_dtype="bf16")
+    print(f"gla full: bf16-stored o rel err {rel_err(host(o16), o_ref):.2e} (information)")
+
+
+def test_gdn_prefill_full_size_and_segments():
+    """Gated DeltaNet prefill: 2 x 8192 tokens, 16 heads, d=128, C=64, bf16,
+    initial states ~ N(0, 0.05); one pass, and three calls over tokens
+    [0,2000), [2000,5000), [5000,8192) that pass only the state."""
+    w = synth.prefill_gdn()
+    note("gdn prefill full size")
+    o, pool = run_chunk("gdn", w)
+    o_ref, pool_ref = run_oracle("gdn", w)
+    e_o = check(host(o), o_ref, "bf16", "o")
+    e_s = check(host(pool), pool_ref, "bf16", "state")
+    print(f"gdn full: rel err o {e_o:.2e} state {e_s:.2e}")
+    note("gdn prefill segmented")
+    T = 8192
+    segs = w.extra["segments"]
+    pool_s = dev(w.pool)
+    outs = []
+    for a_, b_ in zip(segs[:-1], segs[1:]):
+        # the same token range of both sequences, packed
+        idx = np.concatenate([np.arange(a_, b_), T + np.arange(a_, b_)])
+        ws = synth.Workload(**{**w.__dict__, "q": w.q[idx], "k": w.k[idx], "v": w.v[idx],
+                               "alpha": w.alpha[idx], "beta": w.beta[idx],
+                               "cu_seqlens": np.array([0, b_ - a_, 2 * (b_ - a_)], np.int32)})
+        os_, pool_s = run_chunk("gdn", ws, pool=pool_s)
+        outs.append((idx, host(os_)))
+    o_seg = np.zeros_like(o_ref)
+    for idx, x in outs:
+        o_seg[idx] = x
+    check(o_seg, o_ref, "bf16", "o (segments)")
+    check(host(pool_s), pool_ref, "bf16", "state (segments)")
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+def test_prefill_then_decode(kind):
+    """Prefill T tokens, then decode token T+1 from the same slot: equal to
+    the recurrence over T+1 tokens."""
+    import gated_deltanet_gla_amd as G
+    w = synth.random_varlen(14, [97], 2, 128, 128, dtype="bf16", gdn=(kind == "gdn"), n_slots=2)
+    note(f"{kind} prefill then decode")
+    wp = synth.Workload(**{**w.__dict__, "cu_seqlens": np.array([0, 96], np.int32)})
+    _, pool = run_chunk(kind, wp, rows=(0, 96))
+    t = slice(96, 97)
+    args = [dev(w.q[t], "bf16"), dev(w.k[t], "bf16"), dev(w.v[t], "bf16"), dev(w.alpha[t])]
+    if kind == "gla":
+        od = G.gla_decode_step(*args, pool, dev(w.slot_idx), out_dtype=torch.float32)
+    else:
+        od = G.gdn_decode_step(*args, dev(w.beta[t]), pool, dev(w.slot_idx), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = run_oracle(kind, w)
+    check(host(od)[0], o_ref[96], "bf16", "decode o")
+    check(host(pool)[w.slot_idx], pool_ref[w.slot_idx], "bf16", "state")
