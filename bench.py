@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated linear-attention state recurrence on one MI355X.
+
+Headline (``value``): chunked GLA prefill tokens/s on 4 sequences x 4096
+tokens, 16 heads, d_k = d_v = 128, chunk 64, bf16 q/k/v/o, fp32 gates and
+states, zero initial state (a token = one sequence position with all 16
+heads).  One step = one ``gla_chunk_fwd`` over the whole batch with the
+inputs resident in HBM.  The same JSON line also carries the decode-step
+HBM GB/s (256 requests x 16 heads of 128x128 fp32 states in a 1024-slot
+pool, GLA and Gated DeltaNet), the Gated DeltaNet prefill (2 x 8192 tokens)
+and the mixed varlen Gated DeltaNet step (conv prelude + 48 prompts + 512
+decodes), each timed the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunked prefill tokens/s + decode-step HBM GB/s, 128×128 fp32 state heads"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only", default="all",
+                   choices=["all", "gla_prefill", "gdn_prefill", "decode", "mixed"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--cpu-sample-seqs", type=int, default=1)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline_child(n_seqs: int):
+    """The fp64 oracle, single-threaded on one core, on a bounded sample of
+    the headline workload: n_seqs whole sequences (4096 tokens x 16 heads)."""
+    os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    import numpy as np  # noqa: F401  (threads pinned by the parent's env)
+    import oracle
+    import synth
+    w = synth.prefill_gla()
+    T = int(w.cu_seqlens[1])
+    n = T * n_seqs
+    t0 = time.perf_counter()
+    oracle.gla_varlen(w.q[:n], w.k[:n], w.v[:n], w.alpha[:n], w.cu_seqlens[: n_seqs + 1], w.pool,
+                      w.slot_idx[:n_seqs], True)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                      "seconds": dt,
+                      "sample": f"{n_seqs} of 4 sequences (4096 tokens x 16 heads each), "
+                                f"fp64 token-by-token recurrence, numpy, 1 pinned core"}))
+
+
+def run_cpu_baseline(n_seqs: int):
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               NUMEXPR_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
+                          "--cpu-sample-seqs", str(n_seqs)], env=env, capture_output=True, text=True,
+                         timeout=600)
+    if res.returncode != 0:
+        raise RuntimeError(f"cpu baseline failed: {res.stderr[-2000:]}")
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+# ---------------------------------------------------------------- GPU timing
+def timed(torch, fn, steps, warmup):
+    """Run fn(i) warmup times, then time exactly `steps` calls between two
+    HIP events on the current stream (synchronised on both sides)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps   # ms per call
+
+
+def bench_gla_prefill(torch, G, synth, dev, steps, warmup):
+    w = synth.prefill_gla()
+    N, H, d = w.n_tokens, w.n_heads, w.dk
+    sets = []
+    for r in range(2):   # two resident copies, alternated: the working set exceeds the MALL
+        sets.append((dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha)))
+    cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
+    pool = dev(w.pool)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+
+    def step(i):
+        q, k, v, a = sets[i % 2]
+        G.gla_chunk_fwd(q, k, v, a, cu, pool, slots, chunk=w.chunk, zero_init=True, o=o)
+    ms = timed(torch, step, steps, warmup)
+    nbytes = (3 * N * H * d * 2) + N * H * 4 + N * H * d * 2 + w.n_seqs * H * d * d * 4
+    flops = N * H * (2 * w.chunk * (2 * d) + 4 * d * d)
+    return {"workload": w.name, "ms": ms, "tokens_per_s": N / (ms * 1e-3), "bytes": nbytes,
+            "flops": flops, "n_tokens": N, "batch": w.n_seqs, "seq_len": N // w.n_seqs, "heads": H,
+            "d": d, "chunk": w.chunk}
+
+
+def bench_gdn_prefill(torch, G, synth, dev, steps, warmup):
+    w = synth.prefill_gdn()
+    N, H, d = w.n_tokens, w.n_heads, w.dk
+    sets = [(dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha), dev(w.beta))
+            for _ in range(2)]
+    cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
+    pool = dev(w.pool)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(G.workspace_bytes("gdn", w.n_seqs, N, H, d, d, w.chunk), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def step(i):
+        q, k, v, a, b = sets[i % 2]
+        G.gdn_chunk_fwd(q, k, v, a, b, cu, pool, slots, chunk=w.chunk, o=o, workspace=ws)
+    ms = timed(torch, step, steps, warmup)
+    nbytes = 3 * N * H * d * 2 + 2 * N * H * 4 + N * H * d * 2 + 2 * w.n_seqs * H * d * d * 4
+    C = w.chunk
+    flops = N * H * (2 * C * (3 * d + 2 * d) + C * C // 3 + 6 * d * d)
+    return {"workload": w.name, "ms": ms, "tokens_per_s": N / (ms * 1e-3), "bytes": nbytes,
+            "flops": flops}
+
+
+def bench_decode(torch, G, synth, dev, steps, warmup, gdn):
+    w = synth.decode(seed=3, gdn=gdn)
+    R, H, d = w.q.shape
+    q, k, v, a = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha)
+    b = dev(w.beta) if gdn else None
+    pool = dev(w.pool)
+    perm = w.extra["perm"]
+    quarters = [dev(perm[i * R:(i + 1) * R].copy()) for i in range(len(perm) // R)]
+    o = torch.empty((R, H, d), dtype=torch.bfloat16, device="cuda:0")
+
+    def step(i):
+        sl = quarters[i % len(quarters)]   # disjoint slot sets: no MALL reuse between steps
+        if gdn:
+            G.gdn_decode_step(q, k, v, a, b, pool, sl, o=o)
+        else:
+            G.gla_decode_step(q, k, v, a, pool, sl, o=o)
+    ms = timed(torch, step, steps, warmup)
+    nbytes = R * H * (2 * d * d * 4 + 4 * d * 2 + (8 if gdn else 4))
+    return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
+
+
+def bench_mixed(torch, G, synth, dev, steps, warmup):
+    import numpy as np
+    from gated_deltanet_gla_amd.step import MixedStep
+    w = synth.mixed_varlen()
+    x = w.extra["x"]
+    P, D = w.extra["n_prefill"], w.extra["n_decode"]
+    lens = w.extra["lengths"]
+    NP = int(lens[:P].sum())
+    N, H, d = w.q.shape
+    cu_p = np.concatenate([[0], np.cumsum(lens[:P])]).astype(np.int32)
+    step_obj = MixedStep(dev(x, "bf16"), dev(w.extra["w"]), dev(w.extra["conv_cache"], "bf16"),
+                         dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.alpha), dev(w.beta),
+                         dev(w.cu_seqlens), dev(cu_p), dev(w.pool), dev(w.slot_idx), P, NP)
+    ms = timed(torch, lambda i: step_obj(), steps, warmup)
+    nbytes = (N * H * d * 2 * 3 + N * H * 8            # q, k, o; alpha, beta
+              + N * H * d * 2 * 2                       # conv x in, y out (= v)
+              + N * H * d * 2                           # v read by the recurrence
+              + len(lens) * H * d * d * 4 * 2           # state read + write
+              + len(lens) * 3 * H * d * 2 * 2)          # conv cache read + write
+    return {"workload": w.name, "ms": ms, "tokens_per_s": N / (ms * 1e-3), "n_tokens": N,
+            "prefill_tokens": NP, "longest_prompt": int(lens[:P].max()), "bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
+def calib_copy(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    ms = timed(torch, lambda i: b.copy_(a), 5, 2)
+    return {"bytes_each_way": n, "ms": ms, "GBps": 2 * n / (ms * 1e-3) / 1e9}
+
+
+def main():
+    args = parse()
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.cpu_sample_seqs)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(every (sequence, head) is independent, so N GPUs would each run this workload "
+              f"on their own share)", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline and args.only in ("all", "gla_prefill"):
+        cpu = run_cpu_baseline(args.cpu_sample_seqs)      # before this process touches the GPU
+
+    import torch
+    import gated_deltanet_gla_amd as G
+    import synth
+    from gated_deltanet_gla_amd import _lib
+    _lib.lib()   # fail loudly if the HIP library is missing
+
+    def dev(x, dtype="f32"):
+        import numpy as np
+        if dtype == "bf16":
+            bits = synth.bf16_bits(np.asarray(x, np.float32)).view(np.int16)
+            return torch.from_numpy(bits.copy()).to("cuda:0").view(torch.bfloat16)
+        if x.dtype in (np.int32, np.int64):
+            return torch.from_numpy(np.ascontiguousarray(x.astype(np.int32))).to("cuda:0")
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda:0")
+
+    res = {}
+    K, W = args.steps, args.warmup
+    if args.only in ("all", "gla_prefill"):
+        res["gla_prefill"] = bench_gla_prefill(torch, G, synth, dev, K, W)
+        print(f"# gla prefill {res['gla_prefill']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    if args.only in ("all", "decode"):
+        res["gla_decode"] = bench_decode(torch, G, synth, dev, K, W, gdn=False)
+        res["gdn_decode"] = bench_decode(torch, G, synth, dev, K, W, gdn=True)
+        print(f"# decode {res['gla_decode']['ms']:.3f} / {res['gdn_decode']['ms']:.3f} ms",
+              file=sys.stderr, flush=True)
+    if args.only in ("all", "gdn_prefill"):
+        res["gdn_prefill"] = bench_gdn_prefill(torch, G, synth, dev, K, W)
+        print(f"# gdn prefill {res['gdn_prefill']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    if args.only in ("all", "mixed"):
+        res["mixed"] = bench_mixed(torch, G, synth, dev, max(3, K // 4), max(1, W // 2))
+        print(f"# mixed {res['mixed']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    if args.calib_copy:
+        res["copy"] = calib_copy(torch)
+
+    head = res.get("gla_prefill")
+    out = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    if head:
+        ach = head["bytes"] / (head["ms"] * 1e-3) / 1e9
+        out.update({
+            "value": head["tokens_per_s"], "ms_per_step": head["ms"],
+            "config": {"workload": head["workload"], "global_batch": head["batch"],
+                       "seq_len": head["seq_len"], "heads": head["heads"], "dk": head["d"],
+                       "dv": head["d"], "chunk": head["chunk"], "state": "fp32",
+                       "io": "bf16 q/k/v/o, fp32 alpha"},
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "gla_chunk_kernel", "algorithmic_bytes": head["bytes"],
+                         "mfma_frac": head["flops"] / (head["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        })
+    else:
+        out.update({"value": None, "ms_per_step": None, "config": {"workload": args.only}})
+    if "gla_decode" in res:
+        out["decode_hbm_GBps"] = {
+            "gla": res["gla_decode"]["GBps"], "gdn": res["gdn_decode"]["GBps"],
+            "frac_of_peak": {"gla": res["gla_decode"]["GBps"] / HBM_PEAK_GBPS,
+                             "gdn": res["gdn_decode"]["GBps"] / HBM_PEAK_GBPS},
+            "ms": {"gla": res["gla_decode"]["ms"], "gdn": res["gdn_decode"]["ms"]},
+            "workload": "256 requests x 16 heads, 128x128 fp32 states, 1024-slot pool, in place"}
+    other = {}
+    if "gdn_prefill" in res:
+        r = res["gdn_prefill"]
+        ach = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        other["gdn_prefill"] = {"workload": r["workload"], "tokens_per_s": r["tokens_per_s"],
+                                "ms": r["ms"], "hbm_frac": ach / HBM_PEAK_GBPS,
+                                "mfma_frac": r["flops"] / (r["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    if "mixed" in res:
+        r = res["mixed"]
+        other["mixed_gdn_step"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s", "n_tokens",
+                                                     "prefill_tokens", "longest_prompt", "GBps")}
+        other["mixed_gdn_step"]["hbm_frac"] = r["GBps"] / HBM_PEAK_GBPS
+    if other:
+        out["other_workloads"] = other
+    if "copy" in res:
+        out["copy_calibration"] = res["copy"]
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

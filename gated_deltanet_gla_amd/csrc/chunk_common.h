@@ -56,18 +56,11 @@ template <> struct Op<false> {               // bf16 operands
 
     // Store 4 consecutive values (v.x..v.w at p[0..3]) as hi (+ lo).
     __device__ __forceinline__ static void store4(E* hi, E* lo, f32x4 v) {
-        uint16_t h[4], l[4];
-        split_bf16(v.x, h[0], l[0]);
-        split_bf16(v.y, h[1], l[1]);
-        split_bf16(v.z, h[2], l[2]);
-        split_bf16(v.w, h[3], l[3]);
-        u32x2 wh, wl;
-        wh.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
-        wh.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-        wl.x = l[0] | (static_cast<uint32_t>(l[1]) << 16);
-        wl.y = l[2] | (static_cast<uint32_t>(l[3]) << 16);
-        *reinterpret_cast<u32x2*>(hi) = wh;
-        *reinterpret_cast<u32x2*>(lo) = wl;
+        uint32_t h0, h1, l0, l1;
+        split_bf16x2(v.x, v.y, h0, l0);
+        split_bf16x2(v.z, v.w, h1, l1);
+        *reinterpret_cast<u32x2*>(hi) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(lo) = u32x2{l0, l1};
     }
     __device__ __forceinline__ static void store1(E* hi, E* lo, float x) {
         uint16_t h, l;
@@ -214,6 +207,16 @@ __device__ __forceinline__ void decay_scan(const float* alpha, long astride, int
     if (lane == 0) *gamma = __expf(last);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences
+// global memory, which makes every wave drain its outstanding global loads
+// (the next chunk's prefetch) and stores at each barrier; the chunk loops
+// exchange data between waves through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // blockIdx -> logical work id, grouping consecutive logical ids on one XCD
 // (blocks are dealt to the 8 XCDs round-robin) so that work sharing inputs
 // through L2 lands on the same XCD.
@@ -221,6 +224,83 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     if ((nblocks & 7) != 0) return bid;
     const int per = nblocks >> 3;
     return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace gla
+
+namespace gla {
+
+// ------------------------------------------------------------------ operand fragments (bf16)
+// A 16x16x32 operand fragment: 8 bf16 per lane.  "KC" storage keeps k
+// contiguous along a line (line = operand row for A, column for B); "KM"
+// storage is k-major (row = k, the 16 operand lines contiguous), which is
+// the natural token-major layout of q/k/v chunks when the contraction runs
+// over tokens.  KM fragments are read with ds_read_b64_tr_b16: within each
+// 16-lane group, lane i points at row (k0 + i/4) and 4 consecutive lines
+// starting at m0 + 4 (i % 4); lane j then receives line m0 + j of the 4
+// consecutive rows.  Two such reads give the 8 k-values of a lane group.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 ld_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 cat8(s16x4 a, s16x4 b) {
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    s16x8 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+}
+// KC: line (lane % 16) of the 16 lines starting at `line0`, k-values
+// k0 + 8 g .. k0 + 8 g + 7 (g = lane / 16).
+__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* base, int ld, int line0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (line0 + (lane & 15)) * ld + k0 + (lane >> 4) * 8);
+    return as_bf16x8(v);
+}
+// KC with the split k order {k0 + 4g .. +3} u {k0 + 16 + 4g .. +3}.
+__device__ __forceinline__ bf16x8 frag_kc_split(const uint16_t* base, int ld, int line0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* p = base + (line0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+    return cat8(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b));
+}
+// KM: lines m0 .. m0 + 15 (contiguous within a row), k-values k0 + 8 g .. +7.
+__device__ __forceinline__ bf16x8 frag_km(const uint16_t* base, int ld, int m0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const uint16_t* p = base + (k0 + (lane >> 4) * 8 + (i >> 2)) * ld + m0 + 4 * (i & 3);
+    return cat8(ld_tr16(p), ld_tr16(p + 4 * ld));
+}
+// KM with the split k order {k0 + 4g .. +3} u {k0 + 16 + 4g .. +3}.
+__device__ __forceinline__ bf16x8 frag_km_split(const uint16_t* base, int ld, int m0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const uint16_t* p = base + (k0 + (lane >> 4) * 4 + (i >> 2)) * ld + m0 + 4 * (i & 3);
+    return cat8(ld_tr16(p), ld_tr16(p + 16 * ld));
+}
+// 16-wide k tail (16x16x16 MFMA, 4 k-values k0 + 4 g .. +3 per lane).
+__device__ __forceinline__ s16x4 frag_kc4(const uint16_t* base, int ld, int line0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(base + (line0 + (lane & 15)) * ld + k0 + (lane >> 4) * 4);
+    return __builtin_bit_cast(s16x4, v);
+}
+__device__ __forceinline__ s16x4 frag_km4(const uint16_t* base, int ld, int m0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    return ld_tr16(base + (k0 + (lane >> 4) * 4 + (i >> 2)) * ld + m0 + 4 * (i & 3));
+}
+__device__ __forceinline__ f32x4 mfma_bf16_k16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// fp32 values -> packed bf16 hi and lo halves (4 values -> 2 dwords each)
+__device__ __forceinline__ void split4(f32x4 v, s16x4& hi, s16x4& lo) {
+    uint32_t h0, h1, l0, l1;
+    split_bf16x2(v.x, v.y, h0, l0);
+    split_bf16x2(v.z, v.w, h1, l1);
+    hi = __builtin_bit_cast(s16x4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(s16x4, u32x2{l0, l1});
 }
 
 }  // namespace gla

@@ -22,12 +22,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 with the hardware converter (v_cvt_pk_bf16_f32): round to
+// nearest even, NaN stays NaN.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Split x into hi + lo, both bf16: hi = RNE(x), lo = RNE(x - hi).  hi + lo
@@ -36,6 +39,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
     hi = f32_to_bf16_bits(x);
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+// Two values at once: packed hi pair and lo pair.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16x2(a, b);
+    const float ha = __uint_as_float(hi << 16);
+    const float hb = __uint_as_float(hi & 0xffff0000u);
+    lo = pack_bf16x2(a - ha, b - hb);
 }
 
 // ---------------------------------------------------------------- storage types
@@ -70,8 +80,8 @@ template <> struct Vec4<BF16> {
     }
     __device__ __forceinline__ static void store(uint16_t* p, f32x4 x) {
         u32x2 w;
-        w.x = static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16);
-        w.y = static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16);
+        w.x = pack_bf16x2(x.x, x.y);
+        w.y = pack_bf16x2(x.z, x.w);
         *reinterpret_cast<u32x2*>(p) = w;
     }
 };

@@ -59,7 +59,7 @@ gdn_chunk_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int 
         sum += (e - s + C - 1) / C;
     }
     part[t] = sum;
-    __syncthreads();
+    lds_barrier();
     if (t == 0) {
         int run = 0;
         for (int i = 0; i < 1024; ++i) {
@@ -68,7 +68,7 @@ gdn_chunk_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int 
             run += x;
         }
     }
-    __syncthreads();
+    lds_barrier();
     int run = part[t];
     for (int b = b0; b < b1; ++b) {
         off[b] = run;
@@ -127,7 +127,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
     stage_natural<TI, C, DK, NT>(&sm.k[0][0], LQ, k + tok0 * tstride + h * DK, tstride, n);
     decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g, sm.eg, sm.dec, &sm.gamma);
     for (int j = threadIdx.x; j < C; j += NT) sm.beta[j] = j < n ? beta[(tok0 + j) * H + h] : 0.f;
-    __syncthreads();
+    lds_barrier();
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -144,7 +144,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
             sm.a[i][j] = (j < i) ? sm.beta[i] * __expf(sm.g[i] - sm.g[j]) * acc[r] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // diagonal blocks: forward substitution, one column per lane
     if (wave < NB && lane < 16) {
@@ -166,7 +166,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
         const int r = idx / C, c = idx % C;
         if ((c >> 4) > (r >> 4)) sm.t[r][c] = 0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // off-diagonal blocks, one block diagonal at a time: T_ij = -T_ii sum_k A_ik T_kj
     const int rr = lane >> 2;          // row inside the block
@@ -197,7 +197,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
             }
             *reinterpret_cast<f32x4*>(&sm.t[i * 16 + rr][j * 16 + cc]) = -y;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // T -> workspace, row-major C x C
@@ -289,7 +289,7 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
         const int n = min(C, L - c0);
         const long tok0 = s0 + c0;
         if (ci < 0 || ci >= n_chunks_max) break;   // only reachable with a malformed cu_seqlens
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 0: stage inputs, decay scan, state slice -> st
         stage_natural<TI, C, DK, NT>(&sm.q[0][0], LQ, q + tok0 * tstride + h * DK, tstride, n);
@@ -306,7 +306,7 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                 O::store4(&sm.st[0][ln][mt * 16 + ap.row0], &sm.st[LO][ln][mt * 16 + ap.row0], S[i]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 1: T diag(beta); P; X = K S -> Y = V - diag(exp g) X
         {
@@ -350,7 +350,7 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
             }
             O::store4(&sm.yt[0][ln][tt * 16 + ap.row0], &sm.yt[LO][ln][tt * 16 + ap.row0], y);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 2: U = T diag(beta) Y
         for (int t = wave; t < CT * BT; t += NW) {
@@ -365,7 +365,7 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
             for (int r = 0; r < 4; ++r) ud[r] = acc[r] * sm.dec[tt * 16 + ap.row0 + r];
             O::store4(&sm.udt[0][ln][tt * 16 + ap.row0], &sm.udt[LO][ln][tt * 16 + ap.row0], ud);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 3: outputs and state hand-off
         for (int t = wave; t < CT * BT; t += NW) {

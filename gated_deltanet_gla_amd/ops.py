@@ -44,7 +44,7 @@ def _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, out_dtype, o
         raise ValueError("q, k, v must share a dtype")
     N, H, dk = q.shape
     dv = v.shape[2]
-    out_dtype = out_dtype or q.dtype
+    out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
     _check(o, "o", out_dtype, 3)
@@ -102,7 +102,7 @@ def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o):
         _check(t, n, d, nd)
     R, H, dk = q.shape
     dv = v.shape[2]
-    out_dtype = out_dtype or q.dtype
+    out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
     if o is None:
         o = torch.empty((R, H, dv), dtype=out_dtype, device=q.device)
     _check(o, "o", out_dtype, 3)

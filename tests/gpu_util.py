@@ -67,3 +67,16 @@ def check(x, ref, dtype, what):
         e = rel_err(x, ref)
         assert e <= TOL_BF16_REL, f"{what}: rel err {e:.3e} > {TOL_BF16_REL}"
     return e
+
+
+def check_bf16_storage(x, ref, what, slack=1e-5):
+    """A bf16-stored result must be within one bf16 rounding of the exact
+    value: |x - r| <= 2^-8 |r| elementwise (bf16 keeps 8 significant bits, so
+    round-to-nearest moves a value by at most half an ulp = 2^-8 relative to
+    the bottom of its binade), plus a small slack for fp32 arithmetic."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    excess = np.abs(x - ref) - 2.0 ** -8 * np.abs(ref)
+    worst = float(excess.max() / max(np.abs(ref).max(), 1e-30))
+    assert worst <= slack, f"{what}: exceeds one bf16 rounding by {worst:.3e} (relative to max)"
+    return worst
