@@ -8,32 +8,37 @@
 // and only the state is handed from one chunk to the next (and, through the
 // pool, from one call to the next).
 //
-// Work split: one workgroup (4 waves) per (sequence, head, d_v tile of BV
-// columns).  Columns of the state evolve independently under this update,
-// so tiling d_v is exact; the tiles of one (sequence, head) re-read the same
-// q/k chunk, which the XCD-aware block order keeps in one L2.  The BV-column
-// slice of the fp32 state stays in MFMA accumulators for the whole sequence.
+// Work split: one workgroup per (sequence, head, d_v tile of BV columns).
+// State columns evolve independently under this update, so tiling d_v is
+// exact; the tiles of one (sequence, head) re-read the same q/k chunk, which
+// the XCD-aware block order keeps in one L2.  The BV-column slice of the
+// fp32 state stays in MFMA accumulators for the whole sequence.
 //
-// Per chunk, wave w owns the 16 output rows 16w..16w+15:
-//   P^T = K Q^T for its rows (accumulators), masked and decayed; the P^T
-//         accumulator tile already has the lane layout of an MFMA A operand
-//         (lane = row i, 4 consecutive j), so P never goes through LDS;
-//   O   = diag(exp g) (Q S) + P V  for its rows, stored straight to HBM;
-// and a share of the state tiles:
-//   S   = exp(g_last) S + K^T (diag(exp(g_last - g)) V).
-// q, k, v are staged in LDS in their natural token-major layout; the
-// contractions over tokens read them with the LDS transpose read, so
-// nothing is transposed on the way in.  Chunk c+1 is fetched from HBM into
-// registers while chunk c computes, and written to the second LDS buffer
-// after it; one barrier per chunk (fp32 inputs use one buffer and two).
+// Eight waves with two roles, one of each per SIMD, so that the VALU work of
+// one role overlaps the MFMA work of the other:
+//  * output waves 0..3: wave w owns chunk rows 16w..16w+15.  It forms
+//    P^T = K Q^T for its rows in accumulators, decays and masks it; the P^T
+//    accumulator tile already has the lane layout of an MFMA A operand
+//    (lane = row, 4 consecutive tokens), so P never goes through LDS.  Then
+//    O = diag(exp g) (Q S) + P V for its rows, stored straight to HBM.
+//  * state waves 4..7: each owns a share of the state tiles (weighted so
+//    every SIMD gets about the same MFMA count) and applies
+//    S = exp(g_last) S + K^T (diag(exp(g_last - g)) V); then they write the
+//    updated slice for the next chunk's Q S, stage the next chunk (already
+//    in registers) into the other LDS buffer and prefetch the one after.
+// q, k, v sit in LDS in their natural token-major layout; contractions over
+// tokens read them with the LDS transpose read.  One LDS-only barrier per
+// chunk (fp32 inputs use a single buffer and two).
 #include "chunk_common.h"
 #include "launch.h"
 
 namespace gla {
 namespace {
 
-constexpr int NW = 4;
+constexpr int NW = 8;
 constexpr int NT = NW * 64;
+constexpr int NO = 4;            // output waves
+constexpr int NS = NW - NO;      // state waves
 
 template <int DK, int BV, int C, bool F32>
 struct GlaBuf {
@@ -47,26 +52,60 @@ struct GlaBuf {
     alignas(16) E v[C][LV];
     alignas(16) E vd[HL][C][LV];    // diag(exp(g_last - g)) V  (hi, lo)
     alignas(16) E st[HL][BV][LQ];   // state slice, line = column n, k = d (hi, lo)
-    float g[C];
-    float eg[C];
-    float gamma;
+    float g2[C];                    // log2 of the cumulative decay
+    float eg[C];                    // exp(g)
+    float gamma;                    // exp(g_last)
+};
+
+// Split of the state tiles over the state waves.  State wave s shares a SIMD
+// with output wave s, whose MFMA count grows with its row block; tiles go
+// greedily to the SIMD with the least work.
+template <int DK, int BV, int C>
+struct StateSplit {
+    static constexpr int KT = DK / 16, BT = BV / 16, CT = C / 16, ST = KT * BT;
+    struct Tab { int beg[NS + 1]; int maxcnt; };
+    static constexpr Tab make() {
+        Tab t{};
+        int load[NS] = {};
+        int cnt[NS] = {};
+        const int kd = DK >= 32 ? DK / 32 : 1;
+        const int kc = C >= 32 ? C / 32 : 1;
+        for (int s = 0; s < NS; ++s) {
+            if (s < CT) load[s] = (s + 1) * kd + BT * 2 * kd + BT * 2 * (s / 2 + 1);
+        }
+        for (int i = 0; i < ST; ++i) {
+            int best = 0;
+            for (int s = 1; s < NS; ++s)
+                if (load[s] < load[best]) best = s;
+            load[best] += 2 * kc;
+            cnt[best] += 1;
+        }
+        t.beg[0] = 0;
+        t.maxcnt = 0;
+        for (int s = 0; s < NS; ++s) {
+            t.beg[s + 1] = t.beg[s] + cnt[s];
+            if (cnt[s] > t.maxcnt) t.maxcnt = cnt[s];
+        }
+        return t;
+    }
+    static constexpr Tab tab = make();
 };
 
 template <class TI, int C, int DK, int BV>
 struct Prefetch {
+    static constexpr int NTS = NS * 64;                  // staging threads
     static constexpr int VE = 16 / TI::bytes;            // elements per 16-byte vector
-    static constexpr int NQ = (C * DK / VE + NT - 1) / NT;
-    static constexpr int NV = (C * BV / VE + NT - 1) / NT;
+    static constexpr int NQ = (C * DK / VE + NTS - 1) / NTS;
+    static constexpr int NV = (C * BV / VE + NTS - 1) / NTS;
     u32x4 q[NQ], k[NQ], v[NV];
-    float a;   // alpha of row (lane) in every wave; 1 for rows >= n
+    float a;   // alpha of row (lane) in every state wave; 1 for rows >= n
 
-    __device__ __forceinline__ void load(const typename TI::T* qg, const typename TI::T* kg,
+    __device__ __forceinline__ void load(int st, const typename TI::T* qg, const typename TI::T* kg,
                                          const typename TI::T* vg, const float* ag, long tstride,
                                          long vstride, long astride, int n) {
-        const int tid = threadIdx.x;
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
-            const int x = tid + u * NT;
+            const int x = st + u * NTS;
             const int row = x / (DK / VE), vc = x % (DK / VE);
             q[u] = u32x4{0u, 0u, 0u, 0u};
             k[u] = u32x4{0u, 0u, 0u, 0u};
@@ -77,12 +116,12 @@ struct Prefetch {
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int x = tid + u * NT;
+            const int x = st + u * NTS;
             const int row = x / (BV / VE), vc = x % (BV / VE);
             v[u] = u32x4{0u, 0u, 0u, 0u};
             if (x < C * BV / VE && row < n) v[u] = *reinterpret_cast<const u32x4*>(vg + row * vstride + vc * VE);
         }
-        const int lane = tid & 63;
+        const int lane = st & 63;
         a = (lane < n && lane < C) ? ag[lane * astride] : 1.f;
     }
 };
@@ -99,16 +138,17 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     using E = typename O::E;
     using Buf = GlaBuf<DK, BV, C, F32>;
     using PF = Prefetch<TI, C, DK, BV>;
+    using SS = StateSplit<DK, BV, C>;
     constexpr int NBUF = F32 ? 1 : 2;
     constexpr int LQ = Buf::LQ, LV = Buf::LV;
     constexpr int LO = F32 ? 0 : 1;
     constexpr int NVT = DV / BV;
     constexpr int CT = C / 16;                   // 16-row tiles per chunk
     constexpr int BT = BV / 16;                  // 16-col tiles per d_v tile
-    constexpr int ST = (DK / 16) * BT;           // state tiles
-    constexpr int SPW = (ST + NW - 1) / NW;      // state tiles per wave
+    constexpr int KSD = DK / 32;                 // 32-wide k steps over d_k (0 when DK = 16)
+    constexpr int SMAX = SS::tab.maxcnt > 0 ? SS::tab.maxcnt : 1;
     constexpr int VE = PF::VE;
-    static_assert(DV % BV == 0 && BV % 16 == 0 && C % 16 == 0 && C <= 64 && CT <= NW, "tiling");
+    static_assert(DV % BV == 0 && BV % 16 == 0 && C % 16 == 0 && C <= 64 && CT <= NO, "tiling");
 
     __shared__ Buf buf[NBUF];
 
@@ -128,20 +168,25 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
+    const bool is_state = wave >= NO;
+    const int sw = wave - NO;                    // state wave index
+    const int stid = tid - NO * 64;              // staging thread index
     const AccPos ap;
     const int col0 = vt * BV;
     const long tstride = static_cast<long>(H) * DK;
     const long vstride = static_cast<long>(H) * DV;
 
-    // ---- initial state slice -> accumulators
+    // ---- this state wave's tiles; initial state slice -> accumulators
+    const int tbeg = is_state ? SS::tab.beg[sw] : 0;
+    const int tcnt = is_state ? SS::tab.beg[sw + 1] - SS::tab.beg[sw] : 0;
     float* Sg = pool + (static_cast<long>(slot) * H + h) * DK * DV;
-    f32x4 S[SPW];
+    f32x4 S[SMAX];
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int t = wave + NW * i;
-        const int mt = t / BT, nt = t % BT;
+    for (int i = 0; i < SMAX; ++i) {
         S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (t < ST && !zero_init) {
+        if (i < tcnt && !zero_init) {
+            const int t = tbeg + i;
+            const int mt = t / BT, nt = t % BT;
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[i][r] = Sg[(mt * 16 + ap.row0 + r) * DV + col0 + nt * 16 + ap.col];
         }
@@ -150,27 +195,27 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     PF pf;
     auto fetch = [&](int c) {
         const long tok0 = s0 + static_cast<long>(c) * C;
-        pf.load(q + tok0 * tstride + h * DK, k + tok0 * tstride + h * DK, v + tok0 * vstride + h * DV + col0,
-                alpha + tok0 * H + h, tstride, vstride, H, min(C, L - c * C));
+        pf.load(stid, q + tok0 * tstride + h * DK, k + tok0 * tstride + h * DK,
+                v + tok0 * vstride + h * DV + col0, alpha + tok0 * H + h, tstride, vstride, H,
+                min(C, L - c * C));
     };
-    // Write the prefetched chunk and the current state slice into buffer bb.
+    // State waves: write the prefetched chunk and the current state slice into bb.
     auto stage = [&](Buf& bb) {
-        // in-wave scan of log alpha (every wave keeps its own copy)
-        float x = __logf(pf.a);
+        float x = __log2f(pf.a);                 // in-wave scan, log2 domain
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);
             if (lane >= off) x += y;
         }
         const float glast = __shfl(x, C - 1, 64);
-        if (wave == 0 && lane < C) {
-            bb.g[lane] = x;
-            bb.eg[lane] = __expf(x);
+        if (sw == 0 && lane < C) {
+            bb.g2[lane] = x;
+            bb.eg[lane] = exp2f(x);
         }
-        if (tid == 0) bb.gamma = __expf(glast);
+        if (stid == 0) bb.gamma = exp2f(glast);
 #pragma unroll
         for (int u = 0; u < PF::NQ; ++u) {
-            const int xx = tid + u * NT;
+            const int xx = stid + u * PF::NTS;
             if (xx < C * DK / VE) {
                 const int row = xx / (DK / VE), vc = xx % (DK / VE);
                 *reinterpret_cast<u32x4*>(&bb.q[row][vc * VE]) = pf.q[u];
@@ -179,9 +224,9 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int xx = tid + u * NT;
+            const int xx = stid + u * PF::NTS;
             const int row = xx / (BV / VE), vc = xx % (BV / VE);
-            const float dec = __expf(glast - __shfl(x, row & 63, 64));
+            const float dec = exp2f(glast - __shfl(x, row & 63, 64));
             if (xx < C * BV / VE) {
                 *reinterpret_cast<u32x4*>(&bb.v[row][vc * VE]) = pf.v[u];
                 const E* e = reinterpret_cast<const E*>(&pf.v[u]);
@@ -194,11 +239,10 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                 }
             }
         }
-        // state slice as the B operand of Q S: st[n][d]
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int t = wave + NW * i;
-            if (t < ST) {
+        for (int i = 0; i < SMAX; ++i) {
+            if (i < tcnt) {
+                const int t = tbeg + i;
                 const int mt = t / BT, nt = t % BT;
                 const int ln = nt * 16 + ap.col;
                 O::store4(&bb.st[0][ln][mt * 16 + ap.row0], &bb.st[LO][ln][mt * 16 + ap.row0], S[i]);
@@ -206,7 +250,7 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
         }
     };
 
-    if (nchunks > 0) {
+    if (is_state && nchunks > 0) {
         fetch(0);
         stage(buf[0]);
         if (nchunks > 1) fetch(1);
@@ -217,112 +261,160 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
         Buf& bb = buf[c % NBUF];
         const int n = min(C, L - c * C);
         const long tok0 = s0 + static_cast<long>(c) * C;
-        const float gam = bb.gamma;
 
-        f32x4 ov[BT];                             // this wave's output tiles, stored after staging
-        if (wave < CT) {
-            const int it = wave;                  // this wave's 16 rows of the chunk
-            const int i = it * 16 + ap.col;       // row index held by this lane in P^T tiles
-            // ---- P^T tiles (rows j, cols i), masked and decayed
-            f32x4 pt[CT];
-#pragma unroll
-            for (int jt = 0; jt < CT; ++jt) {
-                pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (jt <= it) {
-                    O::mma(pt[jt], &bb.k[jt * 16][0], LQ, &bb.q[it * 16][0], LQ, DK);
-                    const float gi = bb.g[i];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = jt * 16 + ap.row0 + r;
-                        pt[jt][r] = (j <= i) ? pt[jt][r] * __expf(gi - bb.g[j]) : 0.f;
-                    }
-                }
-            }
-            // ---- O tiles of this wave's rows
-#pragma unroll
-            for (int nt = 0; nt < BT; ++nt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                mma_xs<F32>(acc, &bb.q[it * 16][0], LQ, &bb.st[0][nt * 16][0], &bb.st[LO][nt * 16][0], LQ, DK);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] *= bb.eg[it * 16 + ap.row0 + r];
+        if (!is_state) {
+            const int it = wave;
+            if (it < CT) {
+                const int i = it * 16 + ap.col;       // row held by this lane in the P^T tiles
+                const float gi = bb.g2[i];
+                // ---- P^T tiles (rows j, cols i) and Q S for this wave's rows
+                f32x4 pt[CT];
+                f32x4 ov[BT];
                 if constexpr (F32) {
 #pragma unroll
                     for (int jt = 0; jt < CT; ++jt) {
+                        pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (jt <= it) O::mma(pt[jt], &bb.k[jt * 16][0], LQ, &bb.q[it * 16][0], LQ, DK);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < BT; ++nt) {
+                        ov[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        O::mma(ov[nt], &bb.q[it * 16][0], LQ, &bb.st[0][nt * 16][0], LQ, DK);
+                    }
+                } else if constexpr (KSD == 0) {
+                    const s16x4 qf = frag_kc4(&bb.q[0][0], LQ, it * 16, 0);
+#pragma unroll
+                    for (int jt = 0; jt < CT; ++jt) {
+                        pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (jt <= it) pt[jt] = mfma_bf16_k16(frag_kc4(&bb.k[0][0], LQ, jt * 16, 0), qf, pt[jt]);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < BT; ++nt) {
+                        ov[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        ov[nt] = mfma_bf16_k16(qf, frag_kc4(&bb.st[0][0][0], LQ, nt * 16, 0), ov[nt]);
+                        ov[nt] = mfma_bf16_k16(qf, frag_kc4(&bb.st[LO][0][0], LQ, nt * 16, 0), ov[nt]);
+                    }
+                } else {
+                    bf16x8 qf[KSD];                   // this wave's q rows: B of P^T, A of Q S
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks) qf[ks] = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
+#pragma unroll
+                    for (int jt = 0; jt < CT; ++jt) {
+                        pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
                         if (jt <= it) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                acc = mfma_f32(pt[jt][r], bb.v[jt * 16 + ap.row0 + r][nt * 16 + ap.col], acc);
+                            for (int ks = 0; ks < KSD; ++ks)
+                                pt[jt] = mfma_bf16(frag_kc(&bb.k[0][0], LQ, jt * 16, 32 * ks), qf[ks], pt[jt]);
                         }
                     }
-                } else if constexpr (CT == 1) {
-                    s16x4 hi, lo;
-                    split4(pt[0], hi, lo);
-                    const s16x4 bv = frag_km4(&bb.v[0][0], LV, nt * 16, 0);
-                    acc = mfma_bf16_k16(hi, bv, acc);
-                    acc = mfma_bf16_k16(lo, bv, acc);
-                } else {
 #pragma unroll
-                    for (int s = 0; s < CT / 2; ++s) {
-                        if (2 * s <= it) {
-                            s16x4 h0, l0, h1, l1;
-                            split4(pt[2 * s], h0, l0);
-                            split4(pt[2 * s + 1], h1, l1);
-                            const bf16x8 bv = frag_km_split(&bb.v[0][0], LV, nt * 16, 32 * s);
-                            acc = mfma_bf16(cat8(h0, h1), bv, acc);
-                            acc = mfma_bf16(cat8(l0, l1), bv, acc);
+                    for (int nt = 0; nt < BT; ++nt) {
+                        ov[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < KSD; ++ks) {
+                            ov[nt] = mfma_bf16(qf[ks], frag_kc(&bb.st[0][0][0], LQ, nt * 16, 32 * ks), ov[nt]);
+                            ov[nt] = mfma_bf16(qf[ks], frag_kc(&bb.st[LO][0][0], LQ, nt * 16, 32 * ks), ov[nt]);
                         }
                     }
                 }
-                ov[nt] = acc;
-            }
-        }
-        // ---- state hand-off for this wave's state tiles
+                // decay exp(g_i - g_j) on tiles below the diagonal; mask j > i on the diagonal one
 #pragma unroll
-        for (int si = 0; si < SPW; ++si) {
-            const int t = wave + NW * si;
-            if (t < ST) {
-                const int mt = t / BT, nt = t % BT;
-                S[si] *= gam;
-                if constexpr (F32) {
+                for (int jt = 0; jt < CT; ++jt) {
+                    if (jt < it) {
 #pragma unroll
-                    for (int jb = 0; jb < C; jb += 16) {
+                        for (int r = 0; r < 4; ++r) pt[jt][r] *= exp2f(gi - bb.g2[jt * 16 + ap.row0 + r]);
+                    } else if (jt == it) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int j = jb + (lane >> 4) * 4 + e;
-                            S[si] = mfma_f32(bb.k[j][mt * 16 + (lane & 15)], bb.vd[0][j][nt * 16 + (lane & 15)], S[si]);
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = jt * 16 + ap.row0 + r;
+                            pt[jt][r] = (j <= i) ? pt[jt][r] * exp2f(gi - bb.g2[j]) : 0.f;
                         }
                     }
-                } else if constexpr (C == 16) {
-                    const s16x4 a = frag_km4(&bb.k[0][0], LQ, mt * 16, 0);
-                    S[si] = mfma_bf16_k16(a, frag_km4(&bb.vd[0][0][0], LV, nt * 16, 0), S[si]);
-                    S[si] = mfma_bf16_k16(a, frag_km4(&bb.vd[LO][0][0], LV, nt * 16, 0), S[si]);
-                } else {
+                }
+                // ---- O = diag(exp g) Q S + P V
 #pragma unroll
-                    for (int k0 = 0; k0 < C; k0 += 32) {
-                        const bf16x8 a = frag_km(&bb.k[0][0], LQ, mt * 16, k0);
-                        S[si] = mfma_bf16(a, frag_km(&bb.vd[0][0][0], LV, nt * 16, k0), S[si]);
-                        S[si] = mfma_bf16(a, frag_km(&bb.vd[LO][0][0], LV, nt * 16, k0), S[si]);
+                for (int nt = 0; nt < BT; ++nt) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ov[nt][r] *= bb.eg[it * 16 + ap.row0 + r];
+                    if constexpr (F32) {
+#pragma unroll
+                        for (int jt = 0; jt < CT; ++jt) {
+                            if (jt <= it) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    ov[nt] = mfma_f32(pt[jt][r], bb.v[jt * 16 + ap.row0 + r][nt * 16 + ap.col], ov[nt]);
+                            }
+                        }
+                    } else if constexpr (CT == 1) {
+                        s16x4 hi, lo;
+                        split4(pt[0], hi, lo);
+                        const s16x4 bv = frag_km4(&bb.v[0][0], LV, nt * 16, 0);
+                        ov[nt] = mfma_bf16_k16(hi, bv, ov[nt]);
+                        ov[nt] = mfma_bf16_k16(lo, bv, ov[nt]);
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < CT / 2; ++s) {
+                            if (2 * s <= it) {
+                                s16x4 h0, l0, h1, l1;
+                                split4(pt[2 * s], h0, l0);
+                                split4(pt[2 * s + 1], h1, l1);
+                                const bf16x8 bv = frag_km_split(&bb.v[0][0], LV, nt * 16, 32 * s);
+                                ov[nt] = mfma_bf16(cat8(h0, h1), bv, ov[nt]);
+                                ov[nt] = mfma_bf16(cat8(l0, l1), bv, ov[nt]);
+                            }
+                        }
+                    }
+                    const int colg = col0 + nt * 16 + ap.col;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = it * 16 + ap.row0 + r;
+                        if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + colg, ov[nt][r]);
                     }
                 }
             }
-        }
-
-        if (c + 1 < nchunks) {
-            if constexpr (NBUF == 1) lds_barrier();   // everyone done with the single buffer
-            stage(buf[(c + 1) % NBUF]);
-            if (c + 2 < nchunks) fetch(c + 2);
-        }
-        // Outputs go out after the prefetch is issued: loads and stores share
-        // one counter, so stores issued earlier would make the staging of the
-        // next chunk wait for them.
-        if (wave < CT) {
+        } else {
+            // ---- state hand-off for this wave's tiles
+            const float gam = bb.gamma;
 #pragma unroll
-            for (int nt = 0; nt < BT; ++nt) {
-                const int colg = col0 + nt * 16 + ap.col;
+            for (int si = 0; si < SMAX; ++si) {
+                if (si < tcnt) {
+                    const int t = tbeg + si;
+                    const int mt = t / BT, nt = t % BT;
+                    S[si] *= gam;
+                    if constexpr (F32) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wave * 16 + ap.row0 + r;
-                    if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + colg, ov[nt][r]);
+                        for (int jb = 0; jb < C; jb += 16) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int j = jb + (lane >> 4) * 4 + e;
+                                S[si] = mfma_f32(bb.k[j][mt * 16 + (lane & 15)], bb.vd[0][j][nt * 16 + (lane & 15)], S[si]);
+                            }
+                        }
+                    } else if constexpr (C == 16) {
+                        const s16x4 a = frag_km4(&bb.k[0][0], LQ, mt * 16, 0);
+                        S[si] = mfma_bf16_k16(a, frag_km4(&bb.vd[0][0][0], LV, nt * 16, 0), S[si]);
+                        S[si] = mfma_bf16_k16(a, frag_km4(&bb.vd[LO][0][0], LV, nt * 16, 0), S[si]);
+                    } else {
+#pragma unroll
+                        for (int k0 = 0; k0 < C; k0 += 32) {
+                            const bf16x8 a = frag_km_split(&bb.k[0][0], LQ, mt * 16, k0);
+                            S[si] = mfma_bf16(a, frag_km_split(&bb.vd[0][0][0], LV, nt * 16, k0), S[si]);
+                            S[si] = mfma_bf16(a, frag_km_split(&bb.vd[LO][0][0], LV, nt * 16, k0), S[si]);
+                        }
+                    }
+                }
+            }
+            if (c + 1 < nchunks && NBUF == 2) {
+                stage(buf[(c + 1) % NBUF]);
+                if (c + 2 < nchunks) fetch(c + 2);
+            }
+        }
+        if constexpr (NBUF == 1) {
+            if (c + 1 < nchunks) {
+                lds_barrier();                 // everyone done with the single buffer
+                if (is_state) {
+                    stage(buf[0]);
+                    if (c + 2 < nchunks) fetch(c + 2);
                 }
             }
         }
@@ -331,9 +423,9 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
 
     // ---- final state slice -> pool (zeros for an empty sequence with zero-init)
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int t = wave + NW * i;
-        if (t < ST) {
+    for (int i = 0; i < SMAX; ++i) {
+        if (i < tcnt) {
+            const int t = tbeg + i;
             const int mt = t / BT, nt = t % BT;
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * DV + col0 + nt * 16 + ap.col] = S[i][r];
