@@ -27,8 +27,11 @@
 //     T_ij = -T_ii sum_k A_ik T_kj along successive block diagonals).  T does
 //     not depend on the state, so this latency-heavy step runs fully
 //     parallel instead of on the serial chain.  Written to the workspace.
-//  3. gdn_chunk: one workgroup per (sequence, head, d_v tile), the serial
-//     chunk loop with the state slice in MFMA accumulators.
+//  3. the serial chunk loop with the state slice in MFMA accumulators, one
+//     workgroup per (sequence, head, d_v tile): gdn_fast_kernel for bf16
+//     inputs with chunks of 32/64 and d_k >= 32 (the prep kernel then also
+//     emits T diag(beta) and P as bf16 hi/lo planes), gdn_chunk_kernel for
+//     the rest (fp32 inputs, 16-wide shapes).
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -81,12 +84,13 @@ gdn_chunk_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int 
 }
 
 // ------------------------------------------------------------------ 2. prep
-template <int DK, int C, bool F32>
+template <int DK, int C, bool F32, bool TP>
 struct PrepSmem {
     using E = typename Op<F32>::E;
     static constexpr int LQ = DK + Op<F32>::PAD;
     static constexpr int LA = C + 4;           // fp32 lines of A and T (16-byte aligned)
     alignas(16) E k[C][LQ];
+    alignas(16) E q[TP ? C : 1][LQ];
     alignas(16) float a[C][LA];
     alignas(16) float t[C][LA];
     alignas(16) float x[NW][16][20];           // per-wave 16x16 scratch (padded)
@@ -94,14 +98,19 @@ struct PrepSmem {
     float gamma;
 };
 
-template <int DK, int C, class TI>
+// TP = false: write T (fp32, C x C) per (chunk, head).
+// TP = true (bf16 inputs): write four bf16 C x C planes per (chunk, head):
+//   T diag(beta) hi, lo, and P = (Q K^T) .* D (lower, decayed) hi, lo.
+template <int DK, int C, class TI, bool TP>
 __global__ void __launch_bounds__(NT)
-gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
-         const float* __restrict__ beta, const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
-         int H, const int32_t* __restrict__ off, float* __restrict__ Tws) {
+gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict__ q,
+         const float* __restrict__ alpha, const float* __restrict__ beta,
+         const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
+         const int32_t* __restrict__ off, void* __restrict__ Tws) {
     constexpr bool F32 = (TI::bytes == 4);
+    static_assert(!(TP && F32), "planes are bf16");
     using O = Op<F32>;
-    using Sm = PrepSmem<DK, C, F32>;
+    using Sm = PrepSmem<DK, C, F32, TP>;
     constexpr int LQ = Sm::LQ;
     constexpr int NB = C / 16;
     __shared__ Sm sm;
@@ -125,6 +134,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
     const long tstride = static_cast<long>(H) * DK;
 
     stage_natural<TI, C, DK, NT>(&sm.k[0][0], LQ, k + tok0 * tstride + h * DK, tstride, n);
+    if constexpr (TP) stage_natural<TI, C, DK, NT>(&sm.q[0][0], LQ, q + tok0 * tstride + h * DK, tstride, n);
     decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g, sm.eg, sm.dec, &sm.gamma);
     for (int j = threadIdx.x; j < C; j += NT) sm.beta[j] = j < n ? beta[(tok0 + j) * H + h] : 0.f;
     lds_barrier();
@@ -200,11 +210,38 @@ gdn_prep(const typename TI::T* __restrict__ k, const float* __restrict__ alpha,
         lds_barrier();
     }
 
-    // T -> workspace, row-major C x C
-    float* dst = Tws + (static_cast<long>(ci) * H + h) * C * C;
-    for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
-        const int r = (idx * 4) / C, c = (idx * 4) % C;
-        *reinterpret_cast<f32x4*>(dst + r * C + c) = *reinterpret_cast<const f32x4*>(&sm.t[r][c]);
+    if constexpr (!TP) {
+        // T -> workspace, row-major C x C
+        float* dst = static_cast<float*>(Tws) + (static_cast<long>(ci) * H + h) * C * C;
+        for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
+            const int r = (idx * 4) / C, c = (idx * 4) % C;
+            *reinterpret_cast<f32x4*>(dst + r * C + c) = *reinterpret_cast<const f32x4*>(&sm.t[r][c]);
+        }
+    } else {
+        uint16_t* dst = static_cast<uint16_t*>(Tws) + (static_cast<long>(ci) * H + h) * 4 * C * C;
+        // T diag(beta) -> planes 0 (hi), 1 (lo)
+        for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
+            const int r = (idx * 4) / C, c = (idx * 4) % C;
+            f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.t[r][c]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tv[e] *= sm.beta[c + e];
+            O::store4(dst + r * C + c, dst + C * C + r * C + c, tv);
+        }
+        // P = (Q K^T) .* D as P^T tiles (lane: 4 consecutive j of row i) -> planes 2, 3
+        for (int t = wave; t < NB * NB; t += NW) {
+            const int jt = t / NB, it = t % NB;
+            const int i = it * 16 + ap.col;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (jt <= it) {
+                O::mma(acc, &sm.k[jt * 16][0], LQ, &sm.q[it * 16][0], LQ, DK);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = jt * 16 + ap.row0 + r;
+                    acc[r] = (j <= i) ? acc[r] * __expf(sm.g[i] - sm.g[j]) : 0.f;
+                }
+            }
+            O::store4(dst + 2 * C * C + i * C + jt * 16 + ap.row0, dst + 3 * C * C + i * C + jt * 16 + ap.row0, acc);
+        }
     }
 }
 
@@ -408,11 +445,313 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     }
 }
 
+// ------------------------------------------------------------------ 3b. serial chunk loop, bf16
+// The bf16 path for chunks of 32 or 64 tokens and d_k >= 32.  One
+// workgroup (4 waves) per (sequence, head, 16-column d_v tile); wave w owns
+// chunk rows 16w..16w+15.  T diag(beta) and P come precomputed from
+// gdn_prep as bf16 hi/lo planes and are read straight from HBM/L2 into MFMA
+// operand registers one chunk ahead, so the serial chain only carries the
+// state-dependent work:
+//   A: X = K S and Q S (state slice from LDS), Y = V - diag(exp g) X  -> LDS
+//   B: U = T diag(beta) Y                                             -> LDS
+//   C: O = diag(exp g) Q S + P U; S <- gamma S + K^T diag(dec) U; the new
+//      state slice -> LDS for the next chunk.
+// q, k, v are double-buffered in LDS and prefetched into registers two
+// chunks ahead; three LDS-only barriers per chunk.
+template <int DK, int C>
+struct GdnFastSmem {
+    static constexpr int BV = 16;
+    static constexpr int LQ = DK + 8;
+    static constexpr int LV = BV + 8;
+    static constexpr int LT = C + 8;
+    struct Buf {
+        alignas(16) uint16_t q[C][LQ];
+        alignas(16) uint16_t k[C][LQ];
+        alignas(16) uint16_t v[C][LV];
+        float eg[C];
+        float dec[C];
+        float gamma;
+    };
+    Buf buf[2];
+    alignas(16) uint16_t st[2][BV][LQ];    // state slice: line = column, k = d (hi, lo)
+    alignas(16) uint16_t yt[2][BV][LT];    // Y^T (hi, lo)
+    alignas(16) uint16_t ut[2][BV][LT];    // U^T (hi, lo)
+    alignas(16) uint16_t udt[2][BV][LT];   // (diag(dec) U)^T (hi, lo)
+};
+
+template <int C, int DK>
+struct GdnFastPrefetch {
+    static constexpr int NQ = (C * DK / 8 + NT - 1) / NT;
+    static constexpr int NV = (C * 16 / 8 + NT - 1) / NT;
+    u32x4 q[NQ], k[NQ], v[NV];
+    float a;
+};
+
+template <int DK, int DV, int C, class TO>
+__global__ void __launch_bounds__(NT)
+gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+                const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
+                float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
+                int zero_init, const int32_t* __restrict__ off, long n_chunks_max,
+                const uint16_t* __restrict__ TP, typename TO::T* __restrict__ o) {
+    using Sm = GdnFastSmem<DK, C>;
+    using PF = GdnFastPrefetch<C, DK>;
+    using O = Op<false>;
+    constexpr int BV = Sm::BV, LQ = Sm::LQ, LV = Sm::LV, LT = Sm::LT;
+    constexpr int NVT = DV / BV;
+    constexpr int CT = C / 16;
+    constexpr int KSD = DK / 32;                 // k steps over d_k
+    constexpr int KSC = C / 32;                  // k steps over the chunk
+    constexpr int KT = DK / 16;                  // state tiles (one column tile)
+    constexpr int SPW = (KT + NW - 1) / NW;
+    static_assert(C >= 32 && DK >= 32 && DV % BV == 0, "fast path shapes");
+
+    __shared__ Sm sm;
+
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int vt = work % NVT;
+    const int bh = work / NVT;
+    const int h = bh % H;
+    const int b = bh / H;
+    if (b >= n_seqs) return;
+    const int slot = slot_idx[b];
+    if (slot < 0 || slot >= n_slots) return;
+    const int s0 = clampi(cu[b], 0, n_tokens);
+    const int s1 = clampi(cu[b + 1], s0, n_tokens);
+    const int L = s1 - s0;
+    int nchunks = (L + C - 1) / C;
+    const long cbase = off[b];
+    if (cbase < 0) nchunks = 0;                                  // malformed cu_seqlens only
+    if (cbase + nchunks > n_chunks_max) nchunks = static_cast<int>(max(0L, n_chunks_max - cbase));
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const AccPos ap;
+    const int col0 = vt * BV;
+    const long tstride = static_cast<long>(H) * DK;
+    const long vstride = static_cast<long>(H) * DV;
+    const int it = wave;                         // this wave's row block (if it < CT)
+
+    float* Sg = pool + (static_cast<long>(slot) * H + h) * DK * DV;
+    f32x4 S[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int mt = wave + NW * i;
+        S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (mt < KT && !zero_init) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[i][r] = Sg[(mt * 16 + ap.row0 + r) * DV + col0 + ap.col];
+        }
+    }
+
+    PF pf;
+    auto fetch = [&](int c) {
+        const long tok0 = s0 + static_cast<long>(c) * C;
+        const int n = min(C, L - c * C);
+        const uint16_t* qg = q + tok0 * tstride + h * DK;
+        const uint16_t* kg = k + tok0 * tstride + h * DK;
+        const uint16_t* vg = v + tok0 * vstride + h * DV + col0;
+#pragma unroll
+        for (int u = 0; u < PF::NQ; ++u) {
+            const int x = tid + u * NT;
+            const int row = x / (DK / 8), vc = x % (DK / 8);
+            pf.q[u] = u32x4{0u, 0u, 0u, 0u};
+            pf.k[u] = u32x4{0u, 0u, 0u, 0u};
+            if (x < C * DK / 8 && row < n) {
+                pf.q[u] = *reinterpret_cast<const u32x4*>(qg + row * tstride + vc * 8);
+                pf.k[u] = *reinterpret_cast<const u32x4*>(kg + row * tstride + vc * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PF::NV; ++u) {
+            const int x = tid + u * NT;
+            const int row = x / 2, vc = x % 2;
+            pf.v[u] = u32x4{0u, 0u, 0u, 0u};
+            if (x < C * 2 && row < n) pf.v[u] = *reinterpret_cast<const u32x4*>(vg + row * vstride + vc * 8);
+        }
+        pf.a = (lane < n && lane < C) ? alpha[(tok0 + lane) * H + h] : 1.f;
+    };
+    auto stage = [&](typename Sm::Buf& bb) {
+        float x = __log2f(pf.a);
+#pragma unroll
+        for (int offs = 1; offs < 64; offs <<= 1) {
+            const float y = __shfl_up(x, offs, 64);
+            if (lane >= offs) x += y;
+        }
+        const float glast = __shfl(x, C - 1, 64);
+        if (wave == 0 && lane < C) {
+            bb.eg[lane] = exp2f(x);
+            bb.dec[lane] = exp2f(glast - x);
+        }
+        if (tid == 0) bb.gamma = exp2f(glast);
+#pragma unroll
+        for (int u = 0; u < PF::NQ; ++u) {
+            const int xx = tid + u * NT;
+            if (xx < C * DK / 8) {
+                const int row = xx / (DK / 8), vc = xx % (DK / 8);
+                *reinterpret_cast<u32x4*>(&bb.q[row][vc * 8]) = pf.q[u];
+                *reinterpret_cast<u32x4*>(&bb.k[row][vc * 8]) = pf.k[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PF::NV; ++u) {
+            const int xx = tid + u * NT;
+            if (xx < C * 2) *reinterpret_cast<u32x4*>(&bb.v[xx / 2][(xx % 2) * 8]) = pf.v[u];
+        }
+    };
+    auto write_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int mt = wave + NW * i;
+            if (mt < KT) O::store4(&sm.st[0][ap.col][mt * 16 + ap.row0], &sm.st[1][ap.col][mt * 16 + ap.row0], S[i]);
+        }
+    };
+    // this wave's rows of T diag(beta) and P (hi, lo) for a chunk: A operands
+    u32x4 tpc[4][KSC], tpn[4][KSC];
+    auto load_tp = [&](u32x4 (&dst)[4][KSC], int c) {
+        if (it >= CT) return;
+        const uint16_t* base = TP + (cbase + c) * static_cast<long>(H) * 4 * C * C + static_cast<long>(h) * 4 * C * C;
+#pragma unroll
+        for (int pl = 0; pl < 4; ++pl) {
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                dst[pl][ks] = u32x4{0u, 0u, 0u, 0u};
+                if (32 * ks <= it * 16 + 15)
+                    dst[pl][ks] = *reinterpret_cast<const u32x4*>(base + pl * C * C + (it * 16 + (lane & 15)) * C +
+                                                                  32 * ks + (lane >> 4) * 8);
+            }
+        }
+    };
+
+    if (nchunks > 0) {
+        fetch(0);
+        stage(sm.buf[0]);
+        write_state();
+        load_tp(tpc, 0);
+        if (nchunks > 1) {
+            fetch(1);
+            load_tp(tpn, 1);
+        }
+    }
+    lds_barrier();
+
+    for (int c = 0; c < nchunks; ++c) {
+        typename Sm::Buf& bb = sm.buf[c & 1];
+        const int n = min(C, L - c * C);
+        const long tok0 = s0 + static_cast<long>(c) * C;
+        f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+
+        // ---- phase A: X = K S, Q S, Y = V - diag(exp g) X
+        if (it < CT) {
+            f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, 0, 32 * ks);
+                const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, 0, 32 * ks);
+                const bf16x8 kf = frag_kc(&bb.k[0][0], LQ, it * 16, 32 * ks);
+                const bf16x8 qf = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
+                xs = mfma_bf16(kf, sh, xs);
+                xs = mfma_bf16(kf, sl, xs);
+                qs = mfma_bf16(qf, sh, qs);
+                qs = mfma_bf16(qf, sl, qs);
+            }
+            f32x4 y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = it * 16 + ap.row0 + r;
+                y[r] = bf16_bits_to_f32(bb.v[row][ap.col]) - bb.eg[row] * xs[r];
+            }
+            O::store4(&sm.yt[0][ap.col][it * 16 + ap.row0], &sm.yt[1][ap.col][it * 16 + ap.row0], y);
+        }
+        if (c + 1 < nchunks) stage(sm.buf[(c + 1) & 1]);
+        if (c + 2 < nchunks) fetch(c + 2);
+        lds_barrier();
+
+        // ---- phase B: U = T diag(beta) Y
+        if (it < CT) {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                if (32 * ks <= it * 16 + 15) {
+                    const bf16x8 yh = frag_kc(&sm.yt[0][0][0], LT, 0, 32 * ks);
+                    const bf16x8 yl = frag_kc(&sm.yt[1][0][0], LT, 0, 32 * ks);
+                    u = mfma_bf16(as_bf16x8(tpc[0][ks]), yh, u);
+                    u = mfma_bf16(as_bf16x8(tpc[0][ks]), yl, u);
+                    u = mfma_bf16(as_bf16x8(tpc[1][ks]), yh, u);
+                }
+            }
+            O::store4(&sm.ut[0][ap.col][it * 16 + ap.row0], &sm.ut[1][ap.col][it * 16 + ap.row0], u);
+            f32x4 ud;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ud[r] = u[r] * bb.dec[it * 16 + ap.row0 + r];
+            O::store4(&sm.udt[0][ap.col][it * 16 + ap.row0], &sm.udt[1][ap.col][it * 16 + ap.row0], ud);
+        }
+        lds_barrier();
+
+        // ---- phase C: outputs and the state hand-off
+        if (it < CT) {
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = qs[r] * bb.eg[it * 16 + ap.row0 + r];
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                if (32 * ks <= it * 16 + 15) {
+                    const bf16x8 uh = frag_kc(&sm.ut[0][0][0], LT, 0, 32 * ks);
+                    const bf16x8 ul = frag_kc(&sm.ut[1][0][0], LT, 0, 32 * ks);
+                    acc = mfma_bf16(as_bf16x8(tpc[2][ks]), uh, acc);
+                    acc = mfma_bf16(as_bf16x8(tpc[2][ks]), ul, acc);
+                    acc = mfma_bf16(as_bf16x8(tpc[3][ks]), uh, acc);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = it * 16 + ap.row0 + r;
+                if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + col0 + ap.col, acc[r]);
+            }
+        }
+        const float gam = bb.gamma;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int mt = wave + NW * i;
+            if (mt < KT) {
+                S[i] *= gam;
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    const bf16x8 a = frag_km_split(&bb.k[0][0], LQ, mt * 16, 32 * ks);
+                    S[i] = mfma_bf16(a, frag_kc_split(&sm.udt[0][0][0], LT, 0, 32 * ks), S[i]);
+                    S[i] = mfma_bf16(a, frag_kc_split(&sm.udt[1][0][0], LT, 0, 32 * ks), S[i]);
+                }
+            }
+        }
+        write_state();
+        if (c + 1 < nchunks) {
+#pragma unroll
+            for (int pl = 0; pl < 4; ++pl)
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) tpc[pl][ks] = tpn[pl][ks];
+            if (c + 2 < nchunks) load_tp(tpn, c + 2);
+        }
+        lds_barrier();
+    }
+
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int mt = wave + NW * i;
+        if (mt < KT) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * DV + col0 + ap.col] = S[i][r];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 template <int DK, int DV, int C, class TI, class TO>
 hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     using T = typename TI::T;
     constexpr bool F32 = (TI::bytes == 4);
+    constexpr bool FAST = !F32 && C >= 32 && DK >= 32;
     constexpr int BV = F32 ? 16 : (DV >= 32 ? 32 : DV);
     int32_t* off = static_cast<int32_t*>(a.workspace);
     float* Tws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
@@ -423,19 +762,30 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
     if (a.n_tokens > 0) {
-        hipLaunchKernelGGL((gdn_prep<DK, C, TI>), dim3(static_cast<unsigned>(mc * a.n_heads)), dim3(NT),
-                           0, s, static_cast<const T*>(a.k), a.alpha, a.beta, a.cu_seqlens, a.n_seqs,
-                           a.n_tokens, a.n_heads, off, Tws);
+        hipLaunchKernelGGL((gdn_prep<DK, C, TI, FAST>), dim3(static_cast<unsigned>(mc * a.n_heads)),
+                           dim3(NT), 0, s, static_cast<const T*>(a.k), static_cast<const T*>(a.q),
+                           a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, off,
+                           static_cast<void*>(Tws));
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
-    hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV, BV, C, TI, TO>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens,
-                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, mc, Tws,
-                       static_cast<typename TO::T*>(a.o));
-    return hipGetLastError();
+    if constexpr (FAST) {
+        const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / 16);
+        hipLaunchKernelGGL((gdn_fast_kernel<DK, DV, C, TO>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
+                           0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs,
+                           a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, mc,
+                           reinterpret_cast<const uint16_t*>(Tws), static_cast<typename TO::T*>(a.o));
+        return hipGetLastError();
+    } else {
+        const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
+        hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV, BV, C, TI, TO>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens,
+                           a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, mc, Tws,
+                           static_cast<typename TO::T*>(a.o));
+        return hipGetLastError();
+    }
 }
 
 template <int DK, int DV, class TI, class TO>
@@ -468,9 +818,9 @@ hipError_t launch_dv(const ChunkArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int, int, int chunk) {
+    // per (chunk, head): T in fp32 (generic path) or four bf16 planes (bf16 path): 8 C^2 bytes
     return align256(sizeof(int32_t) * (n_seqs + 1)) +
-           static_cast<size_t>(max_chunks(n_seqs, n_tokens, chunk)) * n_heads * chunk * chunk *
-               sizeof(float);
+           static_cast<size_t>(max_chunks(n_seqs, n_tokens, chunk)) * n_heads * chunk * chunk * 8;
 }
 
 hipError_t launch_gdn_chunk(const ChunkArgs& a, hipStream_t s) {
