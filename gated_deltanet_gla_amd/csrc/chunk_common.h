@@ -304,3 +304,36 @@ __device__ __forceinline__ void split4(f32x4 v, s16x4& hi, s16x4& lo) {
 }
 
 }  // namespace gla
+
+namespace gla {
+
+// Raw buffer resource over [base, base + nbytes): loads past the end return
+// zero and stores past the end are dropped by the hardware.  Used to guard
+// partial chunks without branches, so every loop iteration issues the same
+// sequence of memory instructions (which keeps the compiler's waits on the
+// shared load/store counter precise across iterations).
+struct BufRsrc {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ BufRsrc(const void* base, uint32_t nbytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(nbytes), 0x00020000)) {}
+    __device__ __forceinline__ u32x4 load16(uint32_t off) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    __device__ __forceinline__ float loadf(uint32_t off) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+    __device__ __forceinline__ void store_b16(uint16_t v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+    }
+    __device__ __forceinline__ void store_b32(uint32_t v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+    }
+};
+
+// Bytes covered by rows [0, n) of a row-strided slice whose rows are
+// `width` bytes wide, `stride` bytes apart (0 when n <= 0).
+__device__ __forceinline__ uint32_t rows_extent(int n, long stride, int width) {
+    return n > 0 ? static_cast<uint32_t>((n - 1) * stride + width) : 0u;
+}
+
+}  // namespace gla

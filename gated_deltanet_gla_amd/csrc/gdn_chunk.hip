@@ -498,7 +498,7 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     using Sm = GdnFastSmem<DK, C>;
     using PF = GdnFastPrefetch<C, DK>;
     using O = Op<false>;
-    constexpr int BV = Sm::BV, LQ = Sm::LQ, LV = Sm::LV, LT = Sm::LT;
+    constexpr int BV = Sm::BV, LQ = Sm::LQ, LT = Sm::LT;
     constexpr int NVT = DV / BV;
     constexpr int CT = C / 16;
     constexpr int KSD = DK / 32;                 // k steps over d_k
@@ -532,7 +532,8 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int col0 = vt * BV;
     const long tstride = static_cast<long>(H) * DK;
     const long vstride = static_cast<long>(H) * DV;
-    const int it = wave;                         // this wave's row block (if it < CT)
+    const int it = wave;                         // this wave's row block
+    const bool rows_here = (CT == NW) || it < CT;
 
     float* Sg = pool + (static_cast<long>(slot) * H + h) * DK * DV;
     f32x4 S[SPW];
@@ -546,32 +547,33 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
     }
 
+    // rows of chunk c that belong to the sequence (<= 0 past its end)
+    auto chunk_rows = [&](int c) { return c < nchunks ? min(C, L - c * C) : 0; };
     PF pf;
+    // Global -> registers for chunk c, with no branches: rows past the
+    // chunk's valid ones (or chunks past the end) read as zero.
     auto fetch = [&](int c) {
-        const long tok0 = s0 + static_cast<long>(c) * C;
-        const int n = min(C, L - c * C);
-        const uint16_t* qg = q + tok0 * tstride + h * DK;
-        const uint16_t* kg = k + tok0 * tstride + h * DK;
-        const uint16_t* vg = v + tok0 * vstride + h * DV + col0;
+        const int n = chunk_rows(c);
+        const long tok0 = s0 + static_cast<long>(c < nchunks ? c : 0) * C;
+        const BufRsrc rq(q + tok0 * tstride + h * DK, rows_extent(n, tstride * 2, DK * 2));
+        const BufRsrc rk(k + tok0 * tstride + h * DK, rows_extent(n, tstride * 2, DK * 2));
+        const BufRsrc rv(v + tok0 * vstride + h * DV + col0, rows_extent(n, vstride * 2, BV * 2));
+        const BufRsrc ra(alpha + tok0 * H + h, rows_extent(n, static_cast<long>(H) * 4, 4));
 #pragma unroll
         for (int u = 0; u < PF::NQ; ++u) {
             const int x = tid + u * NT;
             const int row = x / (DK / 8), vc = x % (DK / 8);
-            pf.q[u] = u32x4{0u, 0u, 0u, 0u};
-            pf.k[u] = u32x4{0u, 0u, 0u, 0u};
-            if (x < C * DK / 8 && row < n) {
-                pf.q[u] = *reinterpret_cast<const u32x4*>(qg + row * tstride + vc * 8);
-                pf.k[u] = *reinterpret_cast<const u32x4*>(kg + row * tstride + vc * 8);
-            }
+            const uint32_t offb = static_cast<uint32_t>((row * tstride + vc * 8) * 2);
+            pf.q[u] = rq.load16(offb);
+            pf.k[u] = rk.load16(offb);
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int x = tid + u * NT;
-            const int row = x / 2, vc = x % 2;
-            pf.v[u] = u32x4{0u, 0u, 0u, 0u};
-            if (x < C * 2 && row < n) pf.v[u] = *reinterpret_cast<const u32x4*>(vg + row * vstride + vc * 8);
+            pf.v[u] = rv.load16(static_cast<uint32_t>(((x / 2) * vstride + (x % 2) * 8) * 2));
         }
-        pf.a = (lane < n && lane < C) ? alpha[(tok0 + lane) * H + h] : 1.f;
+        const float a = ra.loadf(static_cast<uint32_t>(lane * H * 4));
+        pf.a = (lane < n && lane < C) ? a : 1.f;
     };
     auto stage = [&](typename Sm::Buf& bb) {
         float x = __log2f(pf.a);
@@ -608,43 +610,40 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             if (mt < KT) O::store4(&sm.st[0][ap.col][mt * 16 + ap.row0], &sm.st[1][ap.col][mt * 16 + ap.row0], S[i]);
         }
     };
-    // this wave's rows of T diag(beta) and P (hi, lo) for a chunk: A operands
+    // This wave's rows of T diag(beta) and P (hi, lo) for chunk c, as MFMA A
+    // operands; zero past the end.  Row blocks beyond the chunk read rows
+    // they never use.
     u32x4 tpc[4][KSC], tpn[4][KSC];
     auto load_tp = [&](u32x4 (&dst)[4][KSC], int c) {
-        if (it >= CT) return;
-        const uint16_t* base = TP + (cbase + c) * static_cast<long>(H) * 4 * C * C + static_cast<long>(h) * 4 * C * C;
+        const bool ok = c < nchunks;
+        const BufRsrc rt(TP + (cbase + (ok ? c : 0)) * static_cast<long>(H) * 4 * C * C +
+                             static_cast<long>(h) * 4 * C * C,
+                         ok ? 4u * C * C * 2u : 0u);
 #pragma unroll
         for (int pl = 0; pl < 4; ++pl) {
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                dst[pl][ks] = u32x4{0u, 0u, 0u, 0u};
-                if (32 * ks <= it * 16 + 15)
-                    dst[pl][ks] = *reinterpret_cast<const u32x4*>(base + pl * C * C + (it * 16 + (lane & 15)) * C +
-                                                                  32 * ks + (lane >> 4) * 8);
-            }
+            for (int ks = 0; ks < KSC; ++ks)
+                dst[pl][ks] = rt.load16(static_cast<uint32_t>(
+                    (pl * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2));
         }
     };
 
-    if (nchunks > 0) {
-        fetch(0);
-        stage(sm.buf[0]);
-        write_state();
-        load_tp(tpc, 0);
-        if (nchunks > 1) {
-            fetch(1);
-            load_tp(tpn, 1);
-        }
-    }
+    fetch(0);
+    stage(sm.buf[0]);
+    write_state();
+    load_tp(tpc, 0);
+    fetch(1);
+    load_tp(tpn, 1);
     lds_barrier();
 
     for (int c = 0; c < nchunks; ++c) {
         typename Sm::Buf& bb = sm.buf[c & 1];
-        const int n = min(C, L - c * C);
+        const int n = chunk_rows(c);
         const long tok0 = s0 + static_cast<long>(c) * C;
         f32x4 qs = {0.f, 0.f, 0.f, 0.f};
 
-        // ---- phase A: X = K S, Q S, Y = V - diag(exp g) X
-        if (it < CT) {
+        // ---- phase A: X = K S, Q S, Y = V - diag(exp g) X; stage chunk c+1
+        if (rows_here) {
             f32x4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
@@ -665,12 +664,12 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             }
             O::store4(&sm.yt[0][ap.col][it * 16 + ap.row0], &sm.yt[1][ap.col][it * 16 + ap.row0], y);
         }
-        if (c + 1 < nchunks) stage(sm.buf[(c + 1) & 1]);
-        if (c + 2 < nchunks) fetch(c + 2);
+        stage(sm.buf[(c + 1) & 1]);
+        fetch(c + 2);
         lds_barrier();
 
         // ---- phase B: U = T diag(beta) Y
-        if (it < CT) {
+        if (rows_here) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
@@ -691,7 +690,7 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         lds_barrier();
 
         // ---- phase C: outputs and the state hand-off
-        if (it < CT) {
+        if (rows_here) {
             f32x4 acc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = qs[r] * bb.eg[it * 16 + ap.row0 + r];
@@ -705,10 +704,14 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     acc = mfma_bf16(as_bf16x8(tpc[3][ks]), uh, acc);
                 }
             }
+            // rows past the chunk's valid ones fall outside the resource
+            const BufRsrc ro(o + tok0 * vstride + h * DV + col0, rows_extent(n, vstride * TO::bytes, BV * TO::bytes));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = it * 16 + ap.row0 + r;
-                if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + col0 + ap.col, acc[r]);
+                const uint32_t offb = static_cast<uint32_t>((row * vstride + ap.col) * TO::bytes);
+                if constexpr (TO::bytes == 2) ro.store_b16(f32_to_bf16_bits(acc[r]), offb);
+                else ro.store_b32(__float_as_uint(acc[r]), offb);
             }
         }
         const float gam = bb.gamma;
@@ -726,13 +729,11 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             }
         }
         write_state();
-        if (c + 1 < nchunks) {
 #pragma unroll
-            for (int pl = 0; pl < 4; ++pl)
+        for (int pl = 0; pl < 4; ++pl)
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) tpc[pl][ks] = tpn[pl][ks];
-            if (c + 2 < nchunks) load_tp(tpn, c + 2);
-        }
+            for (int ks = 0; ks < KSC; ++ks) tpc[pl][ks] = tpn[pl][ks];
+        load_tp(tpn, c + 2);
         lds_barrier();
     }
 
