@@ -108,10 +108,13 @@ def bench_gla_prefill(torch, G, synth, dev, steps, warmup):
     cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
     pool = dev(w.pool)
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(max(1, G.workspace_bytes("gla", w.n_seqs, N, H, d, d, w.chunk)),
+                     dtype=torch.uint8, device="cuda:0")
 
     def step(i):
         q, k, v, a = sets[i % 2]
-        G.gla_chunk_fwd(q, k, v, a, cu, pool, slots, chunk=w.chunk, zero_init=True, o=o)
+        G.gla_chunk_fwd(q, k, v, a, cu, pool, slots, chunk=w.chunk, zero_init=True, o=o,
+                        workspace=ws)
     ms = timed(torch, step, steps, warmup)
     nbytes = (3 * N * H * d * 2) + N * H * 4 + N * H * d * 2 + w.n_seqs * H * d * d * 4
     flops = N * H * (2 * w.chunk * (2 * d) + 4 * d * d)

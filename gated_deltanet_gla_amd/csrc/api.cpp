@@ -79,7 +79,12 @@ const char* gla_status_string(int status) {
     return "unknown status";
 }
 
-size_t gla_chunk_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gla_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk,
+                                 int32_t dv, int32_t chunk) {
+    if (n_seqs < 0 || n_tokens < 0 || n_heads < 1 || !is_dim(dk) || !is_dim(dv) || !is_chunk(chunk))
+        return 0;
+    return gla::gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+}
 
 size_t gdn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk,
                                  int32_t dv, int32_t chunk) {
@@ -97,6 +102,8 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
                          dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (n_seqs == 0) return GLA_OK;
+    const size_t need = gla::gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
     gla::ChunkArgs a{q, k, v, alpha, nullptr, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                      in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
                      (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes};
@@ -111,9 +118,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
     int st = check_chunk(q, k, v, alpha, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
                          chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
+    if (n_seqs == 0) return GLA_OK;
     const size_t need = gla::gdn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
-    if (n_seqs == 0) return GLA_OK;
     gla::ChunkArgs a{q, k, v, alpha, beta, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                      in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
                      (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes};

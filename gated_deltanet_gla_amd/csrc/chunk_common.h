@@ -337,3 +337,58 @@ __device__ __forceinline__ uint32_t rows_extent(int n, long stride, int width) {
 }
 
 }  // namespace gla
+
+namespace gla {
+namespace {
+
+// Exclusive scan of max(min_count, ceil(L_b / span)) over the sequences (L_b
+// from the clamped cu_seqlens): off[b] = first span index of sequence b,
+// off[n_seqs] = total.  One workgroup of 1024 threads; each thread sums a contiguous
+// range of sequences, one thread scans the 1024 partial sums.
+__global__ void __launch_bounds__(1024)
+span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span, int min_count,
+             int32_t* __restrict__ off) {
+    __shared__ int part[1024];
+    const int t = threadIdx.x;
+    const int per = (n_seqs + 1023) / 1024;
+    const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int s = clampi(cu[b], 0, n_tokens);
+        const int e = clampi(cu[b + 1], s, n_tokens);
+        sum += max(min_count, (e - s + span - 1) / span);
+    }
+    part[t] = sum;
+    lds_barrier();
+    if (t == 0) {
+        int run = 0;
+        for (int i = 0; i < 1024; ++i) {
+            const int x = part[i];
+            part[i] = run;
+            run += x;
+        }
+    }
+    lds_barrier();
+    int run = part[t];
+    for (int b = b0; b < b1; ++b) {
+        off[b] = run;
+        const int s = clampi(cu[b], 0, n_tokens);
+        const int e = clampi(cu[b + 1], s, n_tokens);
+        run += max(min_count, (e - s + span - 1) / span);
+    }
+    if (b1 == n_seqs && b0 < b1) off[n_seqs] = run;
+    if (n_seqs == 0 && t == 0) off[0] = 0;
+}
+
+// Largest b in [0, n_seqs) with off[b] <= idx (off non-decreasing).
+__device__ __forceinline__ int find_span_owner(const int32_t* off, int n_seqs, int idx) {
+    int lo = 0, hi = n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= idx) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace
+}  // namespace gla

@@ -19,8 +19,8 @@
 //   S <- exp(g_last) S + K^T diag(exp(g_last - g)) U.
 //
 // Kernels:
-//  1. gdn_chunk_offsets: exclusive scan of ceil(L_b / C) -> first chunk of
-//     every sequence (one workgroup).
+//  1. span_offsets: exclusive scan of ceil(L_b / C) -> first chunk of every
+//     sequence (one workgroup).
 //  2. gdn_prep: one workgroup per (chunk, head), all chunks at once: A from
 //     K K^T on MFMA, then the unit-lower-triangular inverse T in fp32
 //     (16x16 diagonal blocks by forward substitution, off-diagonal blocks
@@ -45,42 +45,6 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~si
 
 __host__ __device__ constexpr long max_chunks(int n_seqs, int n_tokens, int C) {
     return static_cast<long>(n_tokens) / C + n_seqs;
-}
-
-// ------------------------------------------------------------------ 1. offsets
-__global__ void __launch_bounds__(1024)
-gdn_chunk_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int C,
-                  int32_t* __restrict__ off) {
-    __shared__ int part[1024];
-    const int t = threadIdx.x;
-    const int per = (n_seqs + 1023) / 1024;
-    const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
-    int sum = 0;
-    for (int b = b0; b < b1; ++b) {
-        const int s = clampi(cu[b], 0, n_tokens);
-        const int e = clampi(cu[b + 1], s, n_tokens);
-        sum += (e - s + C - 1) / C;
-    }
-    part[t] = sum;
-    lds_barrier();
-    if (t == 0) {
-        int run = 0;
-        for (int i = 0; i < 1024; ++i) {
-            const int x = part[i];
-            part[i] = run;
-            run += x;
-        }
-    }
-    lds_barrier();
-    int run = part[t];
-    for (int b = b0; b < b1; ++b) {
-        off[b] = run;
-        const int s = clampi(cu[b], 0, n_tokens);
-        const int e = clampi(cu[b + 1], s, n_tokens);
-        run += (e - s + C - 1) / C;
-    }
-    if (b1 == n_seqs && b0 < b1) off[n_seqs] = run;
-    if (n_seqs == 0 && t == 0) off[0] = 0;
 }
 
 // ------------------------------------------------------------------ 2. prep
@@ -757,8 +721,8 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     int32_t* off = static_cast<int32_t*>(a.workspace);
     float* Tws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
                                           align256(sizeof(int32_t) * (a.n_seqs + 1)));
-    hipLaunchKernelGGL(gdn_chunk_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
-                       a.n_tokens, C, off);
+    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
+                       a.n_tokens, C, 0, off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long mc = max_chunks(a.n_seqs, a.n_tokens, C);

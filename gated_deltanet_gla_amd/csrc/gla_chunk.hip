@@ -480,7 +480,16 @@ hipError_t launch_dv(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk) {
+    // the segmented bf16 path (d_k = d_v = 128, chunk 64) keeps per-segment
+    // states in the workspace; the dtype is not known here, so the bound
+    // covers both dtypes
+    if (dk == 128 && dv == 128 && chunk == 64) return gla_seg_workspace(n_seqs, n_tokens, n_heads);
+    return 0;
+}
+
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s) {
+    if (gla_seg_supported(a)) return launch_gla_seg(a, s);
     switch (a.dk) {
         case 16: return launch_dv<16>(a, s);
         case 32: return launch_dv<32>(a, s);

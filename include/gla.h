@@ -95,7 +95,13 @@ enum { GLA_ZERO_INIT = 1u };  /* ignore the pool's contents: S_0 = 0 */
  * several calls that pass the state through the pool gives the same result
  * up to rounding ("Chunked prefill comes for free").
  * `o` is fully overwritten for tokens of sequences with a valid slot.
- * `workspace` may be NULL when gla_chunk_workspace_bytes() returns 0.
+ * Requires workspace of gla_chunk_workspace_bytes() bytes (may be 0; NULL is
+ * then accepted).  For bf16 inputs with d_k = d_v = 128 and C = 64 the
+ * sequences are also cut into segments of whole chunks that run in
+ * parallel: a first pass writes each segment's state contribution and total
+ * decay to the workspace, and each segment folds its entry state from them
+ * (the same hand-off of the state, inside one call).  Contents of the
+ * workspace are scratch; it must not be shared by calls that overlap.
  */
 GLA_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                   const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,

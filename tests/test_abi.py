@@ -64,6 +64,19 @@ def test_gla_chunk_validation(kw, status):
     assert _gla_chunk(_chunk_args(**kw)) == status
 
 
+def test_gla_chunk_workspace_contract():
+    L = _lib.lib()
+    need = L.gla_chunk_workspace_bytes(2, 10, 4, 128, 128, 64)
+    assert need > 0                                     # segmented path keeps per-segment states
+    assert _gla_chunk(_chunk_args()) == _lib.GLA_EWORKSPACE
+    assert _gla_chunk(_chunk_args(ws=FAKE, wsb=need - 1)) == _lib.GLA_EWORKSPACE
+    # bound grows with the token count and covers one 128x128 fp32 state per segment and head
+    big = L.gla_chunk_workspace_bytes(4, 16384, 16, 128, 128, 64)
+    assert big >= (16384 // 1024 + 4 - 1) * 16 * 128 * 128 * 4
+    assert L.gla_chunk_workspace_bytes(2, 10, 4, 64, 64, 64) == 0
+    assert L.gla_chunk_workspace_bytes(2, 10, 4, 100, 128, 64) == 0
+
+
 def test_empty_calls_are_noops():
     # nothing to do -> OK without touching any pointer
     assert _gla_chunk(_chunk_args(B=0, N=0, q=None, k=None, v=None, pool=None, cu=None)) == 0
