@@ -328,6 +328,34 @@ struct BufRsrc {
     __device__ __forceinline__ void store_b32(uint32_t v, uint32_t off) const {
         __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
     }
+    __device__ __forceinline__ void store_b64(u32x2 v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    }
+    __device__ __forceinline__ void store_b128(u32x4 v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    }
+    // Streaming (nontemporal) variants for data touched once per pass: on
+    // this memory system they sustain about twice the bandwidth of the
+    // default policy for the strided token-major tiles read here.
+    static constexpr int kNT = 2;
+    __device__ __forceinline__ u32x4 load16_nt(uint32_t off) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+    }
+    __device__ __forceinline__ float loadf_nt(uint32_t off) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNT));
+    }
+    __device__ __forceinline__ void store_b16_nt(uint16_t v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kNT);
+    }
+    __device__ __forceinline__ void store_b32_nt(uint32_t v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kNT);
+    }
+    __device__ __forceinline__ void store_b64_nt(u32x2 v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kNT);
+    }
+    __device__ __forceinline__ void store_b128_nt(u32x4 v, uint32_t off) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNT);
+    }
 };
 
 // Bytes covered by rows [0, n) of a row-strided slice whose rows are

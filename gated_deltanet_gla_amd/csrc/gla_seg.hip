@@ -20,15 +20,26 @@
 // Within a workgroup (8 waves) each wave owns 16 columns of the 128x128
 // fp32 state (held in MFMA accumulators).  Q S, P V and the state update are
 // then column-local; only P = (Q K^T) .* D is shared, computed once per
-// chunk by all waves and passed through LDS.  Per chunk:
-//   phase 1: P tiles (split over the waves) -> LDS; this wave's columns of
-//            Q S (state operand straight from its accumulators);
-//   phase 2: + P V; outputs; S <- exp(g_last) S + K^T (diag(dec) V); stage
-//            the next chunk (prefetched into registers) into the other LDS
-//            buffer and prefetch the one after.
-// q, k, v stay token-major in LDS; contractions over tokens use the LDS
-// transpose read.  Global accesses go through buffer resources sized to the
-// valid rows, so the loop has no guarded memory instructions.
+// chunk by all waves and passed through LDS.  Outputs are formed transposed
+// (O^T = S^T Q^T + V^T P^T): the state accumulator tile is already an MFMA
+// operand in that orientation, and each lane ends up holding 4 consecutive
+// columns of one token, stored as one 8-byte write.
+//
+// One workgroup per compute unit; chunks are double-buffered in LDS and the
+// chunk after next is prefetched into registers, so each chunk costs two
+// barriers.  Pass 2, per chunk:
+//   phase 1: P tiles (split over the waves) -> LDS; this wave's Q S;
+//   phase 2: + P V; outputs; S <- exp(g_last) S + K^T (diag(dec) V);
+//            stage the prefetched chunk into the other buffer, prefetch the
+//            one after.
+// Pass 1 runs the state update alone.  q, k, v stay token-major in LDS;
+// contractions over tokens use the LDS transpose read.  Each step issues all
+// of its LDS operand reads first, then the VALU work that does not depend on
+// them (splits, decays), then the MFMAs, so the read latency is hidden
+// behind that work instead of stalling every MFMA.
+// Global accesses go through buffer resources sized to the valid rows, so
+// the loops have no guarded memory instructions; the token streams use the
+// nontemporal policy.
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -39,22 +50,36 @@ constexpr int SW = 8;              // waves
 constexpr int ST = SW * 64;        // threads
 constexpr int SD = 128;            // d_k = d_v
 constexpr int SC = 64;             // chunk
-constexpr int SL = SD + 8;         // LDS line of a q/k/v row (16-byte pad)
-constexpr int SP = SC + 8;         // LDS line of a P row
+// LDS row strides (bf16 elements).  q is read only along rows (16 lanes on
+// 16 rows, same column): a stride of 4 banks mod 64 spreads them over all
+// banks.  k and v are mostly read with the transpose read, where 8 rows of
+// 32 bytes go out together: a stride of 8 banks mod 64 keeps those apart.
+constexpr int LQ = SD + 8;         // 68 dwords
+constexpr int LK = SD + 16;        // 72 dwords
+constexpr int SP = SC + 8;         // LDS line of a P row (36 dwords)
+constexpr int kSegBlocks = 256;    // one workgroup on each of the 256 compute units
 
-struct SegBuf {
-    alignas(16) uint16_t q[SC][SL];
-    alignas(16) uint16_t k[SC][SL];
-    alignas(16) uint16_t v[SC][SL];
-    alignas(16) float g2[SC];      // running log2 decay
-    alignas(16) float eg[SC];      // 2^g2
+struct KVBuf {                     // pass 1 staging
+    alignas(16) uint16_t k[SC][LK];
+    alignas(16) uint16_t v[SC][LK];
     alignas(16) float dec[SC];     // 2^(g2_last - g2)
     float gamma;                   // 2^g2_last
 };
 
+struct QKVBuf {                    // pass 2 staging
+    alignas(16) uint16_t q[SC][LQ];
+    alignas(16) uint16_t k[SC][LK];
+    alignas(16) uint16_t v[SC][LK];
+    alignas(16) float g2[SC];      // running log2 decay inside the chunk
+    alignas(16) float eg[SC];      // 2^g2
+    alignas(16) float dec[SC];
+    float gamma;
+};
+
+template <bool WQ>
 struct SegPrefetch {
     static constexpr int NV = SC * SD / 8 / ST;    // 16-byte vectors per thread per tensor
-    u32x4 q[NV], k[NV], v[NV];
+    u32x4 q[WQ ? NV : 1], k[NV], v[NV];
     float a;
 };
 
@@ -65,25 +90,64 @@ struct SegGeom {
     long ws_first;     // slot of the sequence's first segment
 };
 
-// Which (sequence, segment, head) this block works on; false if none.
+// Which (sequence, segment, head) this block works on; false (for the whole
+// block) if none.  Segment s of the call belongs to the sequence b whose
+// exclusive prefix sum of max(1, ceil(L_b / lseg)) covers s; the block
+// computes that prefix sum itself (threads sum contiguous ranges of
+// sequences, then a wave scan and a scan of the wave totals).
 __device__ __forceinline__ bool seg_geometry(SegGeom& sg, const int32_t* cu, int n_seqs, int n_tokens,
-                                             int H, int lseg, const int32_t* soff, const int32_t* slot_idx,
-                                             int n_slots) {
+                                             int H, int lseg, const int32_t* slot_idx, int n_slots,
+                                             int* sh) {
     const int h = blockIdx.x % H;
     const int si = blockIdx.x / H;
     const int maxseg = gridDim.x / H;
-    if (si >= soff[n_seqs]) return false;
-    const int b = find_span_owner(soff, n_seqs, si);
-    const int g = si - soff[b];
-    const int nseg = soff[b + 1] - soff[b];
-    if (g < 0 || g >= nseg) return false;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    auto count = [&](int b) {
+        const int s = clampi(cu[b], 0, n_tokens);
+        const int e = clampi(cu[b + 1], s, n_tokens);
+        return max(1, (e - s + lseg - 1) / lseg);
+    };
+    const int per = (n_seqs + ST - 1) / ST;
+    const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += count(b);
+    int x = sum;
+#pragma unroll
+    for (int offs = 1; offs < 64; offs <<= 1) {
+        const int y = __shfl_up(x, offs, 64);
+        if (lane >= offs) x += y;
+    }
+    if (lane == 63) sh[wave] = x;
+    if (t == 0) sh[SW] = -1;
+    lds_barrier();
+    int run = x - sum;
+    for (int w = 0; w < wave; ++w) run += sh[w];
+    if (sum > 0 && run <= si && si < run + sum) {
+        for (int b = b0; b < b1; ++b) {
+            const int c = count(b);
+            if (si < run + c) {
+                sh[SW] = b;
+                sh[SW + 1] = run;
+                sh[SW + 2] = c;
+                break;
+            }
+            run += c;
+        }
+    }
+    lds_barrier();
+    // block-uniform from here on: keep it in scalar registers
+    const int b = __builtin_amdgcn_readfirstlane(sh[SW]);
+    if (b < 0) return false;
+    const int first = __builtin_amdgcn_readfirstlane(sh[SW + 1]);
+    const int nseg = __builtin_amdgcn_readfirstlane(sh[SW + 2]);
     // cu_seqlens that are not non-decreasing can claim more segments than
     // the workspace holds; such sequences are skipped rather than overrun it
-    if (soff[b + 1] > maxseg) return false;
+    if (first + nseg > maxseg) return false;
     const int slot = slot_idx[b];
     if (slot < 0 || slot >= n_slots) return false;
     const int s0 = clampi(cu[b], 0, n_tokens);
     const int s1 = clampi(cu[b + 1], s0, n_tokens);
+    const int g = si - first;
     sg.b = b;
     sg.g = g;
     sg.nseg = nseg;
@@ -91,76 +155,115 @@ __device__ __forceinline__ bool seg_geometry(SegGeom& sg, const int32_t* cu, int
     sg.slot = slot;
     sg.t0 = min(s0 + g * lseg, s1);
     sg.t1 = min(sg.t0 + lseg, s1);
-    sg.ws_first = static_cast<long>(soff[b]) * H + h;
+    sg.ws_first = static_cast<long>(first) * H + h;
     sg.ws_slot = static_cast<long>(si) * H + h;
     return true;
 }
 
+// A state slot in the workspace holds the 128x128 state as the MFMA
+// accumulator fragments of the 8 waves: lane l of wave w keeps its 8 tiles x
+// 4 values (32 floats, 128 contiguous bytes) at ((w * 64 + l) * 32), so a
+// slot is written and read with 16-byte accesses.
+__device__ __forceinline__ float* frag_slot(float* ws, long slot) {
+    return ws + slot * SD * SD + threadIdx.x * 32;
+}
+__device__ __forceinline__ const float* frag_slot(const float* ws, long slot) {
+    return ws + slot * SD * SD + threadIdx.x * 32;
+}
+
+// This wave's 8 state tiles read from a row-major [d][n] state.
+__device__ __forceinline__ void load_state_rowmajor(f32x4 (&S)[8], const float* src, int col) {
+    const AccPos ap;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[mt][r] = src[(mt * 16 + ap.row0 + r) * SD + col + ap.col];
+    }
+}
+
 // One chunk's global slices (rows past n read as zero) into registers.
-__device__ __forceinline__ void seg_fetch(SegPrefetch& pf, const uint16_t* q, const uint16_t* k,
+template <bool WQ>
+__device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q, const uint16_t* k,
                                           const uint16_t* v, const float* alpha, long tok0, int n, int h,
-                                          int H, bool with_q) {
+                                          int H) {
     const long stride = static_cast<long>(H) * SD;
     const uint32_t ext = rows_extent(n, stride * 2, SD * 2);
-    const BufRsrc rq(q + tok0 * stride + h * SD, with_q ? ext : 0u);
     const BufRsrc rk(k + tok0 * stride + h * SD, ext);
     const BufRsrc rv(v + tok0 * stride + h * SD, ext);
-    const BufRsrc ra(alpha + tok0 * H + h, rows_extent(n, static_cast<long>(H) * 4, 4));
+    // only wave 0 scans the decays: the other waves' alpha loads are out of
+    // range (no memory traffic) and read as zero
+    const bool w0 = threadIdx.x < 64;
+    const BufRsrc ra(alpha + tok0 * H + h, w0 ? rows_extent(n, static_cast<long>(H) * 4, 4) : 0u);
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < SegPrefetch::NV; ++u) {
+    for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
         const int x = tid + u * ST;
         const uint32_t offb = static_cast<uint32_t>(((x / (SD / 8)) * stride + (x % (SD / 8)) * 8) * 2);
-        if (with_q) pf.q[u] = rq.load16(offb);
-        pf.k[u] = rk.load16(offb);
-        pf.v[u] = rv.load16(offb);
+        if constexpr (WQ) pf.q[u] = BufRsrc(q + tok0 * stride + h * SD, ext).load16_nt(offb);
+        pf.k[u] = rk.load16_nt(offb);
+        pf.v[u] = rv.load16_nt(offb);
     }
     const int lane = tid & 63;
-    const float a = ra.loadf(static_cast<uint32_t>(lane * H * 4));
+    const float a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
     pf.a = (lane < n && lane < SC) ? a : 1.f;
 }
 
-// Registers -> LDS buffer; every wave scans log2(alpha) itself and returns
-// the chunk's total log2 decay.
-__device__ __forceinline__ float seg_stage(SegBuf& bb, const SegPrefetch& pf, bool with_q) {
+// Registers -> LDS; wave 0 scans log2(alpha), writes the per-token tables and
+// gets the chunk's total log2 decay back (other waves get 0).
+template <bool WQ, class Buf>
+__device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    float x = __log2f(pf.a);
+    float glast = 0.f;
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
+        float x = __log2f(pf.a);
 #pragma unroll
-    for (int offs = 1; offs < 64; offs <<= 1) {
-        const float y = __shfl_up(x, offs, 64);
-        if (lane >= offs) x += y;
-    }
-    const float glast = __shfl(x, SC - 1, 64);
-    if ((tid >> 6) == 0) {
-        bb.g2[lane] = x;
-        bb.eg[lane] = exp2f(x);
+        for (int offs = 1; offs < 64; offs <<= 1) {
+            const float y = __shfl_up(x, offs, 64);
+            if (lane >= offs) x += y;
+        }
+        glast = __shfl(x, SC - 1, 64);
+        if constexpr (WQ) {
+            bb.g2[lane] = x;
+            bb.eg[lane] = exp2f(x);
+        }
         bb.dec[lane] = exp2f(glast - x);
+        if (lane == 0) bb.gamma = exp2f(glast);
     }
-    if (tid == 0) bb.gamma = exp2f(glast);
 #pragma unroll
-    for (int u = 0; u < SegPrefetch::NV; ++u) {
+    for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
         const int xx = tid + u * ST;
         const int row = xx / (SD / 8), vc = (xx % (SD / 8)) * 8;
-        if (with_q) *reinterpret_cast<u32x4*>(&bb.q[row][vc]) = pf.q[u];
+        if constexpr (WQ) *reinterpret_cast<u32x4*>(&bb.q[row][vc]) = pf.q[u];
         *reinterpret_cast<u32x4*>(&bb.k[row][vc]) = pf.k[u];
         *reinterpret_cast<u32x4*>(&bb.v[row][vc]) = pf.v[u];
     }
     return glast;
 }
 
+// V^T operand of this wave's 16 columns for the two 32-token halves of the
+// chunk (split k order, so the same registers serve P V and the state update).
+template <class Buf>
+__device__ __forceinline__ void load_vt(bf16x8 (&vf)[2], const Buf& bb, int col) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&bb.v[0][0], LK, col, 32 * ks);
+}
+
 // S (this wave's 16 columns, all 8 row tiles) <- gamma S + K^T diag(dec) V.
-__device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const SegBuf& bb, int col) {
-    const int lane = threadIdx.x & 63;
-    const float gam = bb.gamma;
+template <class Buf>
+__device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
+    bf16x8 kf[2][8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] *= gam;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < SC / 32; ++ks) {
-        // decayed values for tokens {32ks + 4g + e} u {32ks + 16 + 4g + e}
-        const bf16x8 vf = frag_km_split(&bb.v[0][0], SL, col, 32 * ks);
-        const u32x4 vw = __builtin_bit_cast(u32x4, vf);
-        const int g = lane >> 4;
+        for (int mt = 0; mt < 8; ++mt) kf[ks][mt] = frag_km_split(&bb.k[0][0], LK, mt * 16, 32 * ks);
+    __builtin_amdgcn_sched_barrier(0);
+    // decayed values for tokens {32ks + 4g + e} u {32ks + 16 + 4g + e}, split
+    const int g = (threadIdx.x & 63) >> 4;
+    bf16x8 vh[2], vl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 vw = __builtin_bit_cast(u32x4, vf[ks]);
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(&bb.dec[32 * ks + 4 * g]);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(&bb.dec[32 * ks + 16 + 4 * g]);
         uint32_t hw[4], lw[4];
@@ -168,15 +271,20 @@ __device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const SegBuf& bb
         split_bf16x2(__uint_as_float(vw.y << 16) * d0.z, __uint_as_float(vw.y & 0xffff0000u) * d0.w, hw[1], lw[1]);
         split_bf16x2(__uint_as_float(vw.z << 16) * d1.x, __uint_as_float(vw.z & 0xffff0000u) * d1.y, hw[2], lw[2]);
         split_bf16x2(__uint_as_float(vw.w << 16) * d1.z, __uint_as_float(vw.w & 0xffff0000u) * d1.w, hw[3], lw[3]);
-        const bf16x8 vh = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-        const bf16x8 vl = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+        vh[ks] = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
+        vl[ks] = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+    }
+    const float gam = bb.gamma;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] *= gam;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const bf16x8 kf = frag_km_split(&bb.k[0][0], SL, mt * 16, 32 * ks);
-            S[mt] = mfma_bf16(kf, vh, S[mt]);
-            S[mt] = mfma_bf16(kf, vl, S[mt]);
+            S[mt] = mfma_bf16(kf[ks][mt], vh[ks], S[mt]);
+            S[mt] = mfma_bf16(kf[ks][mt], vl[ks], S[mt]);
         }
-    }
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -185,48 +293,46 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
               const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs,
               int n_tokens, int H, const float* __restrict__ pool, int n_slots,
               const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
-              const int32_t* __restrict__ soff, float* __restrict__ wstate, float* __restrict__ wlam) {
+              float* __restrict__ wstate, float* __restrict__ wlam) {
+    __shared__ int sh[SW + 4];
     SegGeom sg;
-    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, soff, slot_idx, n_slots)) return;
+    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
     if (sg.nseg <= 1) return;                      // no split: pass 2 reads the pool itself
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const AccPos ap;
     const int col = wave * 16;
-    float* dst = wstate + sg.ws_slot * SD * SD;
-    if (sg.g == sg.nseg - 1) {                     // last segment's slot: copy of the initial state
-        const float* src = pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD;
-        for (int i = threadIdx.x; i < SD * SD / 4; i += ST) {
-            const f32x4 x = zero_init ? f32x4{0.f, 0.f, 0.f, 0.f} : reinterpret_cast<const f32x4*>(src)[i];
-            reinterpret_cast<f32x4*>(dst)[i] = x;
-        }
-        return;
-    }
-
-    __shared__ SegBuf buf[2];
+    float* dst = frag_slot(wstate, sg.ws_slot);
     f32x4 S[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (sg.g == sg.nseg - 1) {                     // last segment's slot: copy of the initial state
+        if (!zero_init) load_state_rowmajor(S, pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD, col);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
+        return;
+    }
+
+    __shared__ KVBuf buf[2];
     const int nch = (sg.t1 - sg.t0 + SC - 1) / SC;
     auto rows = [&](int c) { return c < nch ? min(SC, sg.t1 - sg.t0 - c * SC) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * SC; };
-    SegPrefetch pf;
+    SegPrefetch<false> pf;
     float lam = 0.f;
-    seg_fetch(pf, nullptr, k, v, alpha, tok(0), rows(0), sg.h, H, false);
-    lam += seg_stage(buf[0], pf, false);
-    seg_fetch(pf, nullptr, k, v, alpha, tok(1), rows(1), sg.h, H, false);
+    seg_fetch(pf, nullptr, k, v, alpha, tok(0), rows(0), sg.h, H);
+    lam += seg_stage(buf[0], pf);
+    seg_fetch(pf, nullptr, k, v, alpha, tok(1), rows(1), sg.h, H);
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
-        seg_state_update(S, buf[c & 1], col);
-        const float gl = seg_stage(buf[(c + 1) & 1], pf, false);
+        bf16x8 vf[2];
+        load_vt(vf, buf[c & 1], col);
+        seg_state_update(S, buf[c & 1], vf);
+        const float gl = seg_stage(buf[(c + 1) & 1], pf);
         if (c + 1 < nch) lam += gl;
-        seg_fetch(pf, nullptr, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H, false);
+        seg_fetch(pf, nullptr, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(mt * 16 + ap.row0 + r) * SD + col + ap.col] = S[mt][r];
-    }
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
     if (threadIdx.x == 0) wlam[sg.ws_slot] = lam;
 }
 
@@ -236,48 +342,47 @@ __global__ void __launch_bounds__(ST)
 gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
             const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
             int H, float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
-            int zero_init, int lseg, const int32_t* __restrict__ soff, const float* __restrict__ wstate,
-            const float* __restrict__ wlam, typename TO::T* __restrict__ o) {
+            int zero_init, int lseg, const float* __restrict__ wstate, const float* __restrict__ wlam,
+            typename TO::T* __restrict__ o) {
+    __shared__ int sh[SW + 4];
     SegGeom sg;
-    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, soff, slot_idx, n_slots)) return;
-    __shared__ SegBuf buf[2];
+    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
+    __shared__ QKVBuf buf[2];
     __shared__ uint16_t pbuf[2][SC][SP];           // P = (Q K^T) .* D, hi and lo planes
+    // bf16 outputs of the previous chunk, stored to HBM as whole rows
+    __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LQ];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const AccPos ap;
     const int col = wave * 16;
     const long stride = static_cast<long>(H) * SD;
 
-    // ---- entry state of this segment
-    f32x4 S[8];
-    float* Sg = pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD;
-    auto load_tile = [&](const float* base, int mt) {
-        f32x4 x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = base[(mt * 16 + ap.row0 + r) * SD + col + ap.col];
-        return x;
-    };
-    if (sg.nseg <= 1) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = zero_init ? f32x4{0.f, 0.f, 0.f, 0.f} : load_tile(Sg, mt);
-    } else {
-        const float* s0 = wstate + (sg.ws_first + static_cast<long>(sg.nseg - 1) * H) * SD * SD;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = load_tile(s0, mt);
-        for (int j = 0; j < sg.g; ++j) {
-            const long sj = sg.ws_first + static_cast<long>(j) * H;
-            const float dcy = exp2f(wlam[sj]);
-            const float* dS = wstate + sj * SD * SD;
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + load_tile(dS, mt);
-        }
-    }
-
     const int nch = (sg.t1 - sg.t0 + SC - 1) / SC;
     auto rows = [&](int c) { return c < nch ? min(SC, sg.t1 - sg.t0 - c * SC) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * SC; };
+    SegPrefetch<true> pf;
+    seg_fetch(pf, q, k, v, alpha, tok(0), rows(0), sg.h, H);     // in flight during the fold
+
+    // ---- entry state of this segment
+    f32x4 S[8];
+    float* Sg = pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD;
+    if (sg.nseg <= 1) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!zero_init) load_state_rowmajor(S, Sg, col);
+    } else {
+        const float* s0 = frag_slot(wstate, sg.ws_first + static_cast<long>(sg.nseg - 1) * H);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
+        for (int j = 0; j < sg.g; ++j) {
+            const long sj = sg.ws_first + static_cast<long>(j) * H;
+            const float dcy = exp2f(wlam[sj]);
+            const float* dS = frag_slot(wstate, sj);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
+        }
+    }
     // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
     // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
     for (int idx = tid; idx < 2 * 256; idx += ST) {
@@ -286,89 +391,138 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         pbuf[0][row][cx] = 0;
         pbuf[1][row][cx] = 0;
     }
-    SegPrefetch pf;
-    seg_fetch(pf, q, k, v, alpha, tok(0), rows(0), sg.h, H, true);
-    seg_stage(buf[0], pf, true);
-    seg_fetch(pf, q, k, v, alpha, tok(1), rows(1), sg.h, H, true);
+    seg_stage(buf[0], pf);
+    seg_fetch(pf, q, k, v, alpha, tok(1), rows(1), sg.h, H);
     lds_barrier();
 
+    // P tile t of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3):
+    // operand reads, then the MFMAs and the decay / mask / split epilogue
+    auto tile_it = [](int t) { return t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3)); };
+    auto p_load = [&](const QKVBuf& bb, int t, bf16x8 (&pa)[4], bf16x8 (&pb)[4]) {
+        const int it = tile_it(t), jt = t - it * (it + 1) / 2;
+#pragma unroll
+        for (int ks = 0; ks < SD / 32; ++ks) {
+            pa[ks] = frag_kc(&bb.k[0][0], LK, jt * 16, 32 * ks);
+            pb[ks] = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
+        }
+    };
+    auto p_finish = [&](const QKVBuf& bb, int t, const bf16x8 (&pa)[4], const bf16x8 (&pb)[4]) {
+        const int it = tile_it(t), jt = t - it * (it + 1) / 2;
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < SD / 32; ++ks) pt = mfma_bf16(pa[ks], pb[ks], pt);
+        const int i = it * 16 + ap.col;
+        const float gi = bb.g2[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = jt * 16 + ap.row0 + r;
+            pt[r] = (j <= i) ? pt[r] * exp2f(gi - bb.g2[j]) : 0.f;
+        }
+        Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
+    };
+
+    // chunk cc's bf16 outputs: LDS -> HBM, 16 lanes per 256-byte row
+    auto flush_o = [&](int cc) {
+        if constexpr (TO::bytes == 2) {
+            const BufRsrc ro(o + tok(cc) * stride + sg.h * SD, rows_extent(rows(cc), stride * 2, SD * 2));
+#pragma unroll
+            for (int u = 0; u < SC * SD / 8 / ST; ++u) {
+                const int x = tid + u * ST, row = x / (SD / 8), vc = (x % (SD / 8)) * 8;
+                ro.store_b128(*reinterpret_cast<const u32x4*>(&obuf[row][vc]),
+                              static_cast<uint32_t>((row * stride + vc) * 2));
+            }
+        }
+    };
+
     for (int c = 0; c < nch; ++c) {
-        SegBuf& bb = buf[c & 1];
+        const QKVBuf& bb = buf[c & 1];
         const int n = rows(c);
         const long tok0 = tok(c);
+        if (c > 0) flush_o(c - 1);
 
-        // ---- phase 1: P tiles (lower triangle, split over the waves) -> LDS
-        for (int t = wave; t < 10; t += SW) {
-            // tile t of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-            const int it = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-            const int jt = t - it * (it + 1) / 2;
-            f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 1: P tiles (split over the waves) -> LDS, and
+        // O^T = S^T Q^T for this wave's columns (the state accumulator tiles
+        // serve as the A operand directly: rows = columns of S)
+        bf16x8 pa[4], pb[4], qf[4][4];
+        p_load(bb, wave, pa, pb);
 #pragma unroll
-            for (int ks = 0; ks < SD / 32; ++ks)
-                pt = mfma_bf16(frag_kc(&bb.k[0][0], SL, jt * 16, 32 * ks), frag_kc(&bb.q[0][0], SL, it * 16, 32 * ks), pt);
-            const int i = it * 16 + ap.col;
-            const float gi = bb.g2[i];
+        for (int s = 0; s < SD / 32; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = jt * 16 + ap.row0 + r;
-                pt[r] = (j <= i) ? pt[r] * exp2f(gi - bb.g2[j]) : 0.f;
-            }
-            Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
-        }
-        // ---- this wave's columns of Q S, the state operand from its accumulators
-        f32x4 oacc[4];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) oacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int it = 0; it < 4; ++it) qf[s][it] = frag_kc_split(&bb.q[0][0], LQ, it * 16, 32 * s);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 sh8[4], sl8[4];
 #pragma unroll
         for (int s = 0; s < SD / 32; ++s) {
             s16x4 h0, l0, h1, l1;
             split4(S[2 * s], h0, l0);
             split4(S[2 * s + 1], h1, l1);
-            const bf16x8 sh = cat8(h0, h1), sl = cat8(l0, l1);
+            sh8[s] = cat8(h0, h1);
+            sl8[s] = cat8(l0, l1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 ot[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) ot[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < SD / 32; ++s)
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
-                const bf16x8 qf = frag_kc_split(&bb.q[0][0], SL, it * 16, 32 * s);
-                oacc[it] = mfma_bf16(qf, sh, oacc[it]);
-                oacc[it] = mfma_bf16(qf, sl, oacc[it]);
+                ot[it] = mfma_bf16(sh8[s], qf[s][it], ot[it]);
+                ot[it] = mfma_bf16(sl8[s], qf[s][it], ot[it]);
             }
+        p_finish(bb, wave, pa, pb);
+        if (wave + SW < 10) {
+            p_load(bb, wave + SW, pa, pb);
+            p_finish(bb, wave + SW, pa, pb);
         }
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(&bb.eg[it * 16 + ap.row0]);
-            oacc[it] *= e;
-        }
+        for (int it = 0; it < 4; ++it) ot[it] *= bb.eg[it * 16 + ap.col];
         lds_barrier();
 
-        // ---- phase 2: + P V, outputs, state update, next chunk
+        // ---- phase 2: + V^T P^T (split k order on both operands), outputs,
+        // state update, next chunk
+        bf16x8 vf[2], pp[6][2];
+        load_vt(vf, bb, col);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-#pragma unroll
-            for (int s = 0; s < SC / 32; ++s) {
-                if (32 * s <= it * 16 + 15) {
-                    const bf16x8 vf = frag_km(&bb.v[0][0], SL, col, 32 * s);
-                    oacc[it] = mfma_bf16(frag_kc(&pbuf[0][0][0], SP, it * 16, 32 * s), vf, oacc[it]);
-                    oacc[it] = mfma_bf16(frag_kc(&pbuf[1][0][0], SP, it * 16, 32 * s), vf, oacc[it]);
-                }
-            }
+            pp[it][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 0);
+            pp[it][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 0);
         }
-        {
-            const BufRsrc ro(o + tok0 * stride + sg.h * SD, rows_extent(n, stride * TO::bytes, SD * TO::bytes));
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t offb =
-                        static_cast<uint32_t>(((it * 16 + ap.row0 + r) * stride + col + ap.col) * TO::bytes);
-                    if constexpr (TO::bytes == 2) ro.store_b16(f32_to_bf16_bits(oacc[it][r]), offb);
-                    else ro.store_b32(__float_as_uint(oacc[it][r]), offb);
-                }
-            }
+        for (int it = 2; it < 4; ++it) {
+            pp[it + 2][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 32);
+            pp[it + 2][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 32);
         }
-        seg_state_update(S, bb, col);
-        seg_stage(buf[(c + 1) & 1], pf, true);
-        seg_fetch(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H, true);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
+            ot[it] = mfma_bf16(vf[0], pp[it][1], ot[it]);
+        }
+#pragma unroll
+        for (int it = 2; it < 4; ++it) {
+            ot[it] = mfma_bf16(vf[1], pp[it + 2][0], ot[it]);
+            ot[it] = mfma_bf16(vf[1], pp[it + 2][1], ot[it]);
+        }
+        // lane: token it*16 + (lane % 16), columns col + 4 (lane / 16) .. +3
+        if constexpr (TO::bytes == 2) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                *reinterpret_cast<u32x2*>(&obuf[it * 16 + ap.col][col + ap.row0]) =
+                    u32x2{pack_bf16x2(ot[it][0], ot[it][1]), pack_bf16x2(ot[it][2], ot[it][3])};
+        } else {
+            const BufRsrc ro(o + tok0 * stride + sg.h * SD, rows_extent(n, stride * 4, SD * 4));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
+                              static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
+        }
+        seg_state_update(S, bb, vf);
+        seg_stage(buf[(c + 1) & 1], pf);
+        seg_fetch(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
+    if (nch > 0) flush_o(nch - 1);
 
     if (sg.g == sg.nseg - 1) {
 #pragma unroll
@@ -377,20 +531,21 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * SD + col + ap.col] = S[mt][r];
         }
     }
-    (void)lane;
 }
 
 // Every sequence gets at least one segment (an empty one still writes its
-// state back).  Segment length: whole chunks, at least 4 of them, about 256 workgroups in
-// total (one per compute unit; LDS allows one workgroup per CU).
+// state back).  Segment length: whole chunks, at least 4 of them, about
+// kSegBlocks workgroups in total.
 int seg_len(int n_tokens, int n_heads) {
-    const long target = n_heads >= 256 ? 1 : 256 / n_heads;
+    const long target = n_heads >= kSegBlocks ? 1 : kSegBlocks / n_heads;
     long L = (n_tokens + target - 1) / target;
     L = ((L + SC - 1) / SC) * SC;
     return static_cast<int>(L < 4 * SC ? 4 * SC : L);
 }
 
 __host__ __device__ constexpr size_t align256s(size_t x) { return (x + 255) & ~size_t(255); }
+
+long seg_count_bound(int n_seqs, int n_tokens, int lseg) { return n_tokens / lseg + n_seqs; }
 
 }  // namespace
 
@@ -399,40 +554,33 @@ bool gla_seg_supported(const ChunkArgs& a) {
 }
 
 size_t gla_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
-    const long lseg = seg_len(n_tokens, n_heads);
-    const long maxseg = n_tokens / lseg + n_seqs;
-    return align256s(sizeof(int32_t) * (n_seqs + 1)) + align256s(sizeof(float) * maxseg * n_heads) +
+    const long maxseg = seg_count_bound(n_seqs, n_tokens, seg_len(n_tokens, n_heads));
+    return align256s(sizeof(float) * maxseg * n_heads) +
            static_cast<size_t>(maxseg) * n_heads * SD * SD * sizeof(float);
 }
 
 hipError_t launch_gla_seg(const ChunkArgs& a, hipStream_t s) {
     const int lseg = seg_len(a.n_tokens, a.n_heads);
-    const long maxseg = a.n_tokens / lseg + a.n_seqs;
+    const long maxseg = seg_count_bound(a.n_seqs, a.n_tokens, lseg);
     char* ws = static_cast<char*>(a.workspace);
-    int32_t* soff = reinterpret_cast<int32_t*>(ws);
-    ws += align256s(sizeof(int32_t) * (a.n_seqs + 1));
     float* wlam = reinterpret_cast<float*>(ws);
-    ws += align256s(sizeof(float) * maxseg * a.n_heads);
-    float* wstate = reinterpret_cast<float*>(ws);
-    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 1, soff);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    float* wstate = reinterpret_cast<float*>(ws + align256s(sizeof(float) * maxseg * a.n_heads));
     const dim3 grid(static_cast<unsigned>(maxseg * a.n_heads));
     hipLaunchKernelGGL(gla_seg_state, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
-                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, soff, wstate, wlam);
-    e = hipGetLastError();
+                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.out_bf16) {
         hipLaunchKernelGGL((gla_seg_out<BF16>), grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
                            a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, soff, wstate, wlam, static_cast<uint16_t*>(a.o));
+                           a.zero_init, lseg, wstate, wlam, static_cast<uint16_t*>(a.o));
     } else {
         hipLaunchKernelGGL((gla_seg_out<F32>), grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
                            a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, soff, wstate, wlam, static_cast<float*>(a.o));
+                           a.zero_init, lseg, wstate, wlam, static_cast<float*>(a.o));
     }
     return hipGetLastError();
 }
