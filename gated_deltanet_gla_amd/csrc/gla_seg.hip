@@ -181,6 +181,33 @@ __device__ __forceinline__ void load_state_rowmajor(f32x4 (&S)[8], const float* 
     }
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then row 0's total broadcast into row 1 (and
+// row 2's into row 3), then rows 0-1's total into rows 2-3.  Lanes without a
+// source read 0.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    auto dpp = [](float a, int ctrl_sel) {
+        const int ai = __builtin_bit_cast(int, a);
+        int r = 0;
+        switch (ctrl_sel) {
+            case 1: r = __builtin_amdgcn_update_dpp(0, ai, 0x111, 0xf, 0xf, true); break;   // row_shr:1
+            case 2: r = __builtin_amdgcn_update_dpp(0, ai, 0x112, 0xf, 0xf, true); break;   // row_shr:2
+            case 4: r = __builtin_amdgcn_update_dpp(0, ai, 0x114, 0xf, 0xf, true); break;   // row_shr:4
+            case 8: r = __builtin_amdgcn_update_dpp(0, ai, 0x118, 0xf, 0xf, true); break;   // row_shr:8
+            case 15: r = __builtin_amdgcn_update_dpp(0, ai, 0x142, 0xa, 0xf, false); break; // row_bcast:15
+            default: r = __builtin_amdgcn_update_dpp(0, ai, 0x143, 0xc, 0xf, false); break; // row_bcast:31
+        }
+        return __builtin_bit_cast(float, r);
+    };
+    v += dpp(v, 1);
+    v += dpp(v, 2);
+    v += dpp(v, 4);
+    v += dpp(v, 8);
+    v += dpp(v, 15);
+    v += dpp(v, 31);
+    return v;
+}
+
 // One chunk's global slices (rows past n read as zero) into registers.
 template <bool WQ>
 __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q, const uint16_t* k,
@@ -192,7 +219,7 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
     const BufRsrc rv(v + tok0 * stride + h * SD, ext);
     // only wave 0 scans the decays: the other waves' alpha loads are out of
     // range (no memory traffic) and read as zero
-    const bool w0 = threadIdx.x < 64;
+    const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
     const BufRsrc ra(alpha + tok0 * H + h, w0 ? rows_extent(n, static_cast<long>(H) * 4, 4) : 0u);
     const int tid = threadIdx.x;
 #pragma unroll
@@ -216,13 +243,8 @@ __device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int lane = tid & 63;
     float glast = 0.f;
     if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
-        float x = __log2f(pf.a);
-#pragma unroll
-        for (int offs = 1; offs < 64; offs <<= 1) {
-            const float y = __shfl_up(x, offs, 64);
-            if (lane >= offs) x += y;
-        }
-        glast = __shfl(x, SC - 1, 64);
+        const float x = wave_inclusive_sum(__log2f(pf.a));
+        glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), SC - 1));
         if constexpr (WQ) {
             bb.g2[lane] = x;
             bb.eg[lane] = exp2f(x);
