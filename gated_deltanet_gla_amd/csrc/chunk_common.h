@@ -155,7 +155,7 @@ __device__ __forceinline__ void stage_natural(typename TI::T* dst, int ld, const
         const int row = idx / VPR;
         const int vc = idx % VPR;
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (row < n) val = *reinterpret_cast<const u32x4*>(src + row * stride + vc * VE);
+        if (row < n) val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * stride + vc * VE));
         *reinterpret_cast<u32x4*>(dst + row * ld + vc * VE) = val;
     }
 }
@@ -173,7 +173,7 @@ __device__ __forceinline__ void stage_transposed(typename TI::T* dst, int ld, ty
         const int row = idx / VPR;
         const int vc = idx % VPR;
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (row < n) val = *reinterpret_cast<const u32x4*>(src + row * stride + vc * VE);
+        if (row < n) val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + row * stride + vc * VE));
         if (natural) *reinterpret_cast<u32x4*>(natural + row * ldn + vc * VE) = val;
         const T* e = reinterpret_cast<const T*>(&val);
 #pragma unroll
@@ -192,7 +192,7 @@ __device__ __forceinline__ void decay_scan(const float* alpha, long astride, int
     const int lane = threadIdx.x;
     if (lane >= 64) return;
     float x = 0.f;
-    if (lane < n && lane < C) x = __logf(alpha[lane * astride]);
+    if (lane < n && lane < C) x = __logf(__builtin_nontemporal_load(alpha + lane * astride));
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -357,6 +357,33 @@ struct BufRsrc {
         __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNT);
     }
 };
+
+// Inclusive prefix sum over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then row 0's total broadcast into row 1 (and
+// row 2's into row 3), then rows 0-1's total into rows 2-3.  Lanes without a
+// source read 0.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    auto dpp = [](float a, int ctrl_sel) {
+        const int ai = __builtin_bit_cast(int, a);
+        int r = 0;
+        switch (ctrl_sel) {
+            case 1: r = __builtin_amdgcn_update_dpp(0, ai, 0x111, 0xf, 0xf, true); break;   // row_shr:1
+            case 2: r = __builtin_amdgcn_update_dpp(0, ai, 0x112, 0xf, 0xf, true); break;   // row_shr:2
+            case 4: r = __builtin_amdgcn_update_dpp(0, ai, 0x114, 0xf, 0xf, true); break;   // row_shr:4
+            case 8: r = __builtin_amdgcn_update_dpp(0, ai, 0x118, 0xf, 0xf, true); break;   // row_shr:8
+            case 15: r = __builtin_amdgcn_update_dpp(0, ai, 0x142, 0xa, 0xf, false); break; // row_bcast:15
+            default: r = __builtin_amdgcn_update_dpp(0, ai, 0x143, 0xc, 0xf, false); break; // row_bcast:31
+        }
+        return __builtin_bit_cast(float, r);
+    };
+    v += dpp(v, 1);
+    v += dpp(v, 2);
+    v += dpp(v, 4);
+    v += dpp(v, 8);
+    v += dpp(v, 15);
+    v += dpp(v, 31);
+    return v;
+}
 
 // Bytes covered by rows [0, n) of a row-strided slice whose rows are
 // `width` bytes wide, `stride` bytes apart (0 when n <= 0).

@@ -528,30 +528,28 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const int x = tid + u * NT;
             const int row = x / (DK / 8), vc = x % (DK / 8);
             const uint32_t offb = static_cast<uint32_t>((row * tstride + vc * 8) * 2);
-            pf.q[u] = rq.load16(offb);
-            pf.k[u] = rk.load16(offb);
+            pf.q[u] = rq.load16_nt(offb);
+            pf.k[u] = rk.load16_nt(offb);
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int x = tid + u * NT;
-            pf.v[u] = rv.load16(static_cast<uint32_t>(((x / 2) * vstride + (x % 2) * 8) * 2));
+            pf.v[u] = rv.load16_nt(static_cast<uint32_t>(((x / 2) * vstride + (x % 2) * 8) * 2));
         }
-        const float a = ra.loadf(static_cast<uint32_t>(lane * H * 4));
+        const float a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
         pf.a = (lane < n && lane < C) ? a : 1.f;
     };
     auto stage = [&](typename Sm::Buf& bb) {
-        float x = __log2f(pf.a);
-#pragma unroll
-        for (int offs = 1; offs < 64; offs <<= 1) {
-            const float y = __shfl_up(x, offs, 64);
-            if (lane >= offs) x += y;
+        if (__builtin_amdgcn_readfirstlane(wave) == 0) {
+            const float x = wave_inclusive_sum(__log2f(pf.a));
+            const float glast =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), C - 1));
+            if (lane < C) {
+                bb.eg[lane] = exp2f(x);
+                bb.dec[lane] = exp2f(glast - x);
+            }
+            if (lane == 0) bb.gamma = exp2f(glast);
         }
-        const float glast = __shfl(x, C - 1, 64);
-        if (wave == 0 && lane < C) {
-            bb.eg[lane] = exp2f(x);
-            bb.dec[lane] = exp2f(glast - x);
-        }
-        if (tid == 0) bb.gamma = exp2f(glast);
 #pragma unroll
         for (int u = 0; u < PF::NQ; ++u) {
             const int xx = tid + u * NT;
@@ -587,7 +585,7 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int pl = 0; pl < 4; ++pl) {
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks)
-                dst[pl][ks] = rt.load16(static_cast<uint32_t>(
+                dst[pl][ks] = rt.load16_nt(static_cast<uint32_t>(
                     (pl * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2));
         }
     };

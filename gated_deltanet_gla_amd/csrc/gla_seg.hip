@@ -181,33 +181,6 @@ __device__ __forceinline__ void load_state_rowmajor(f32x4 (&S)[8], const float* 
     }
 }
 
-// Inclusive prefix sum over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8
-// inside each row of 16 lanes, then row 0's total broadcast into row 1 (and
-// row 2's into row 3), then rows 0-1's total into rows 2-3.  Lanes without a
-// source read 0.
-__device__ __forceinline__ float wave_inclusive_sum(float v) {
-    auto dpp = [](float a, int ctrl_sel) {
-        const int ai = __builtin_bit_cast(int, a);
-        int r = 0;
-        switch (ctrl_sel) {
-            case 1: r = __builtin_amdgcn_update_dpp(0, ai, 0x111, 0xf, 0xf, true); break;   // row_shr:1
-            case 2: r = __builtin_amdgcn_update_dpp(0, ai, 0x112, 0xf, 0xf, true); break;   // row_shr:2
-            case 4: r = __builtin_amdgcn_update_dpp(0, ai, 0x114, 0xf, 0xf, true); break;   // row_shr:4
-            case 8: r = __builtin_amdgcn_update_dpp(0, ai, 0x118, 0xf, 0xf, true); break;   // row_shr:8
-            case 15: r = __builtin_amdgcn_update_dpp(0, ai, 0x142, 0xa, 0xf, false); break; // row_bcast:15
-            default: r = __builtin_amdgcn_update_dpp(0, ai, 0x143, 0xc, 0xf, false); break; // row_bcast:31
-        }
-        return __builtin_bit_cast(float, r);
-    };
-    v += dpp(v, 1);
-    v += dpp(v, 2);
-    v += dpp(v, 4);
-    v += dpp(v, 8);
-    v += dpp(v, 15);
-    v += dpp(v, 31);
-    return v;
-}
-
 // One chunk's global slices (rows past n read as zero) into registers.
 template <bool WQ>
 __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q, const uint16_t* k,
