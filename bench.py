@@ -280,9 +280,13 @@ def main():
                        "seq_len": head["seq_len"], "heads": head["heads"], "dk": head["d"],
                        "dv": head["d"], "chunk": head["chunk"], "state": "fp32",
                        "io": "bf16 q/k/v/o, fp32 alpha"},
+            # one gla_chunk_fwd call = two dependent launches (gla_seg_state,
+            # then gla_seg_out); both are timed together by the events around
+            # the call, and the traffic is the sum of their counters
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic("gla_chunk_kernel"),
-                         "kernel": "gla_chunk_kernel", "algorithmic_bytes": head["bytes"],
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic("gla_chunk_fwd"),
+                         "kernel": "gla_chunk_fwd (gla_seg_state + gla_seg_out)",
+                         "algorithmic_bytes": head["bytes"],
                          "mfma_frac": head["flops"] / (head["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         })
     else:

@@ -396,43 +396,69 @@ __device__ __forceinline__ uint32_t rows_extent(int n, long stride, int width) {
 namespace gla {
 namespace {
 
+// Integer form of wave_inclusive_sum.
+__device__ __forceinline__ int wave_inclusive_sum_i(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Up to this many sequences get a longest-first order (rank by a pairwise
+// count in LDS); larger batches keep their own order.
+constexpr int kOrderMax = 1024;
+
 // Exclusive scan of max(min_count, ceil(L_b / span)) over the sequences (L_b
 // from the clamped cu_seqlens): off[b] = first span index of sequence b,
-// off[n_seqs] = total.  One workgroup of 1024 threads; each thread sums a contiguous
-// range of sequences, one thread scans the 1024 partial sums.
+// off[n_seqs] = total.  One workgroup of 1024 threads; each thread sums a
+// contiguous range of sequences, then wave scans and a scan of the 16 wave
+// totals.  With order != nullptr also writes the sequences by decreasing
+// length (ties by index): order[r] = sequence of rank r.
 __global__ void __launch_bounds__(1024)
 span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span, int min_count,
-             int32_t* __restrict__ off) {
-    __shared__ int part[1024];
-    const int t = threadIdx.x;
+             int32_t* __restrict__ off, int32_t* __restrict__ order) {
+    __shared__ int wsum[16];
+    __shared__ int lens[kOrderMax];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    auto length = [&](int b) {
+        const int s = clampi(cu[b], 0, n_tokens);
+        return clampi(cu[b + 1], s, n_tokens) - s;
+    };
+    auto count = [&](int b) { return max(min_count, (length(b) + span - 1) / span); };
     const int per = (n_seqs + 1023) / 1024;
     const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
     int sum = 0;
-    for (int b = b0; b < b1; ++b) {
-        const int s = clampi(cu[b], 0, n_tokens);
-        const int e = clampi(cu[b + 1], s, n_tokens);
-        sum += max(min_count, (e - s + span - 1) / span);
-    }
-    part[t] = sum;
+    for (int b = b0; b < b1; ++b) sum += count(b);
+    const int incl = wave_inclusive_sum_i(sum);
+    if (lane == 63) wsum[wave] = incl;
     lds_barrier();
-    if (t == 0) {
-        int run = 0;
-        for (int i = 0; i < 1024; ++i) {
-            const int x = part[i];
-            part[i] = run;
-            run += x;
-        }
-    }
-    lds_barrier();
-    int run = part[t];
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
     for (int b = b0; b < b1; ++b) {
         off[b] = run;
-        const int s = clampi(cu[b], 0, n_tokens);
-        const int e = clampi(cu[b + 1], s, n_tokens);
-        run += max(min_count, (e - s + span - 1) / span);
+        run += count(b);
     }
     if (b1 == n_seqs && b0 < b1) off[n_seqs] = run;
     if (n_seqs == 0 && t == 0) off[0] = 0;
+    if (order == nullptr) return;
+    if (n_seqs <= kOrderMax) {
+        for (int b = t; b < n_seqs; b += 1024) lens[b] = length(b);
+        lds_barrier();
+        for (int b = t; b < n_seqs; b += 1024) {
+            const int lb = lens[b];
+            int r = 0;
+            for (int j = 0; j < n_seqs; ++j) {
+                const int lj = lens[j];
+                r += (lj > lb || (lj == lb && j < b)) ? 1 : 0;
+            }
+            order[r] = b;
+        }
+    } else {
+        for (int b = t; b < n_seqs; b += 1024) order[b] = b;
+    }
 }
 
 // Largest b in [0, n_seqs) with off[b] <= idx (off non-decreasing).

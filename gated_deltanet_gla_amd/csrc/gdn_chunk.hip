@@ -457,8 +457,8 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const float* __restrict__ alpha,
                 const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
                 float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
-                int zero_init, const int32_t* __restrict__ off, long n_chunks_max,
-                const uint16_t* __restrict__ TP, typename TO::T* __restrict__ o) {
+                int zero_init, const int32_t* __restrict__ off, const int32_t* __restrict__ order,
+                long n_chunks_max, const uint16_t* __restrict__ TP, typename TO::T* __restrict__ o) {
     using Sm = GdnFastSmem<DK, C>;
     using PF = GdnFastPrefetch<C, DK>;
     using O = Op<false>;
@@ -473,12 +473,16 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     __shared__ Sm sm;
 
-    const int work = xcd_remap(blockIdx.x, gridDim.x);
-    const int vt = work % NVT;
-    const int bh = work / NVT;
-    const int h = bh % H;
-    const int b = bh / H;
-    if (b >= n_seqs) return;
+    // (sequence, head) groups in longest-first order, dealt round-robin to
+    // the 8 XCDs (blockIdx mod 8 picks the XCD); the d_v tiles of one group
+    // are consecutive blocks of one XCD, so they share q and k through its L2
+    const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+    const int vt = pos % NVT;
+    const int gi = (pos / NVT) * 8 + xcd;
+    if (gi >= n_seqs * H) return;
+    const int h = gi % H;
+    const int b = order[gi / H];
+    if (b < 0 || b >= n_seqs) return;
     const int slot = slot_idx[b];
     if (slot < 0 || slot >= n_slots) return;
     const int s0 = clampi(cu[b], 0, n_tokens);
@@ -716,11 +720,14 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     constexpr bool F32 = (TI::bytes == 4);
     constexpr bool FAST = !F32 && C >= 32 && DK >= 32;
     constexpr int BV = F32 ? 16 : (DV >= 32 ? 32 : DV);
-    int32_t* off = static_cast<int32_t*>(a.workspace);
-    float* Tws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
-                                          align256(sizeof(int32_t) * (a.n_seqs + 1)));
+    char* ws = static_cast<char*>(a.workspace);
+    int32_t* off = reinterpret_cast<int32_t*>(ws);
+    ws += align256(sizeof(int32_t) * (a.n_seqs + 1));
+    int32_t* order = reinterpret_cast<int32_t*>(ws);
+    ws += align256(sizeof(int32_t) * a.n_seqs);
+    float* Tws = reinterpret_cast<float*>(ws);
     hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
-                       a.n_tokens, C, 0, off);
+                       a.n_tokens, C, 0, off, FAST ? order : nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
@@ -733,12 +740,13 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if constexpr (FAST) {
-        const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / 16);
+        const long groups = (static_cast<long>(a.n_seqs) * a.n_heads + 7) / 8 * 8;
+        const long blocks = groups * (DV / 16);
         hipLaunchKernelGGL((gdn_fast_kernel<DK, DV, C, TO>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
                            0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs,
-                           a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, mc,
-                           reinterpret_cast<const uint16_t*>(Tws), static_cast<typename TO::T*>(a.o));
+                           a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, order,
+                           mc, reinterpret_cast<const uint16_t*>(Tws), static_cast<typename TO::T*>(a.o));
         return hipGetLastError();
     } else {
         const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
@@ -782,7 +790,8 @@ hipError_t launch_dv(const ChunkArgs& a, hipStream_t s) {
 
 size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int, int, int chunk) {
     // per (chunk, head): T in fp32 (generic path) or four bf16 planes (bf16 path): 8 C^2 bytes
-    return align256(sizeof(int32_t) * (n_seqs + 1)) +
+    // plus chunk offsets and the longest-first sequence order
+    return align256(sizeof(int32_t) * (n_seqs + 1)) + align256(sizeof(int32_t) * n_seqs) +
            static_cast<size_t>(max_chunks(n_seqs, n_tokens, chunk)) * n_heads * chunk * chunk * 8;
 }
 
