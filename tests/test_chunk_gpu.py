@@ -130,6 +130,30 @@ def test_invalid_slot_skips_sequence(kind):
     check(host(o)[20:], o_ref[20:], "f32", "o")
 
 
+@pytest.mark.parametrize("zero_init", [False, True])
+def test_gla_segmented_many_sequences(zero_init):
+    """The segmented bf16 path (d=128, C=64) with 600 short sequences
+    (lengths 0..40, so each thread of a workgroup's segment lookup sums
+    several sequences) around three long ones that split into 4, 6 and 7
+    segments of 256 tokens (the last one 1 token long): outputs and final
+    states against the recurrence, fp32 and bf16 outputs."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    short = rng.integers(0, 41, size=600).tolist()
+    lens = short[:200] + [1500] + short[200:400] + [1537] + short[400:] + [900]
+    w = synth.random_varlen(15 + zero_init, lens, 2, 128, 128, dtype="bf16", zero_init=zero_init)
+    note(f"gla segmented, {len(lens)} sequences, zero_init={zero_init}")
+    o, pool = run_chunk("gla", w)
+    o_ref, pool_ref = run_oracle("gla", w)
+    check(host(o), o_ref, "bf16", "o")
+    p = pool.cpu().numpy()
+    check(p[w.slot_idx], pool_ref[w.slot_idx], "bf16", "state")
+    spare = sorted(set(range(p.shape[0])) - set(w.slot_idx.tolist()))
+    assert np.array_equal(p[spare], w.pool[spare])
+    o16, p16 = run_chunk("gla", w, out_dtype="bf16")
+    assert torch.equal(o16.cpu(), rne_bf16(o))
+    assert torch.equal(p16, pool)
+
+
 def test_gla_prefill_full_size():
     """GLA prefill: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 inputs,
     zero initial state: every output and final state against the oracle."""
