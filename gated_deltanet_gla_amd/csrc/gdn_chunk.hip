@@ -411,8 +411,10 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
 
 // ------------------------------------------------------------------ 3b. serial chunk loop, bf16
 // The bf16 path for chunks of 32 or 64 tokens and d_k >= 32.  One
-// workgroup (4 waves) per (sequence, head, 16-column d_v tile); wave w owns
-// chunk rows 16w..16w+15.  T diag(beta) and P come precomputed from
+// workgroup (8 waves) per (sequence, head, 16-column d_v tile).  Waves 0-3
+// own a 16-row block of the chunk for X, Y and U, waves 4-7 the same blocks
+// for Q S and the outputs, and wave w owns state tile w (rows 16w..16w+15),
+// which halves each wave's MFMA chain on the serial path.  T diag(beta) and P come precomputed from
 // gdn_prep as bf16 hi/lo planes and are read straight from HBM/L2 into MFMA
 // operand registers one chunk ahead, so the serial chain only carries the
 // state-dependent work:
@@ -443,16 +445,19 @@ struct GdnFastSmem {
     alignas(16) uint16_t udt[2][BV][LT];   // (diag(dec) U)^T (hi, lo)
 };
 
+constexpr int FW = 8;                 // waves of the bf16 serial kernel
+constexpr int FT = FW * 64;
+
 template <int C, int DK>
 struct GdnFastPrefetch {
-    static constexpr int NQ = (C * DK / 8 + NT - 1) / NT;
-    static constexpr int NV = (C * 16 / 8 + NT - 1) / NT;
+    static constexpr int NQ = (C * DK / 8 + FT - 1) / FT;
+    static constexpr int NV = (C * 16 / 8 + FT - 1) / FT;
     u32x4 q[NQ], k[NQ], v[NV];
     float a;
 };
 
 template <int DK, int DV, int C, class TO>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(FT)
 gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const float* __restrict__ alpha,
                 const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
@@ -464,12 +469,11 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     using O = Op<false>;
     constexpr int BV = Sm::BV, LQ = Sm::LQ, LT = Sm::LT;
     constexpr int NVT = DV / BV;
-    constexpr int CT = C / 16;
+    constexpr int CT = C / 16;                   // 16-row blocks per chunk
     constexpr int KSD = DK / 32;                 // k steps over d_k
     constexpr int KSC = C / 32;                  // k steps over the chunk
-    constexpr int KT = DK / 16;                  // state tiles (one column tile)
-    constexpr int SPW = (KT + NW - 1) / NW;
-    static_assert(C >= 32 && DK >= 32 && DV % BV == 0, "fast path shapes");
+    constexpr int KT = DK / 16;                  // state tiles (one column tile), at most FW
+    static_assert(C >= 32 && DK >= 32 && DV % BV == 0 && KT <= FW && CT <= 4, "fast path shapes");
 
     __shared__ Sm sm;
 
@@ -494,25 +498,24 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (cbase + nchunks > n_chunks_max) nchunks = static_cast<int>(max(0L, n_chunks_max - cbase));
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const AccPos ap;
     const int col0 = vt * BV;
     const long tstride = static_cast<long>(H) * DK;
     const long vstride = static_cast<long>(H) * DV;
-    const int it = wave;                         // this wave's row block
-    const bool rows_here = (CT == NW) || it < CT;
+    // roles: waves 0..3 own row block `it` for X, Y and U; waves 4..7 own row
+    // block `it` for Q S and the outputs; every wave owns state tile `wave`
+    const bool xrole = wave < 4 && wave < CT;
+    const bool qrole = wave >= 4 && wave - 4 < CT;
+    const int it = wave & 3;
+    const bool has_tile = wave < KT;
 
     float* Sg = pool + (static_cast<long>(slot) * H + h) * DK * DV;
-    f32x4 S[SPW];
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    if (has_tile && !zero_init) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int mt = wave + NW * i;
-        S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (mt < KT && !zero_init) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[i][r] = Sg[(mt * 16 + ap.row0 + r) * DV + col0 + ap.col];
-        }
+        for (int r = 0; r < 4; ++r) S[r] = Sg[(wave * 16 + ap.row0 + r) * DV + col0 + ap.col];
     }
 
     // rows of chunk c that belong to the sequence (<= 0 past its end)
@@ -526,10 +529,10 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const BufRsrc rq(q + tok0 * tstride + h * DK, rows_extent(n, tstride * 2, DK * 2));
         const BufRsrc rk(k + tok0 * tstride + h * DK, rows_extent(n, tstride * 2, DK * 2));
         const BufRsrc rv(v + tok0 * vstride + h * DV + col0, rows_extent(n, vstride * 2, BV * 2));
-        const BufRsrc ra(alpha + tok0 * H + h, rows_extent(n, static_cast<long>(H) * 4, 4));
+        const BufRsrc ra(alpha + tok0 * H + h, wave == 0 ? rows_extent(n, static_cast<long>(H) * 4, 4) : 0u);
 #pragma unroll
         for (int u = 0; u < PF::NQ; ++u) {
-            const int x = tid + u * NT;
+            const int x = tid + u * FT;
             const int row = x / (DK / 8), vc = x % (DK / 8);
             const uint32_t offb = static_cast<uint32_t>((row * tstride + vc * 8) * 2);
             pf.q[u] = rq.load16_nt(offb);
@@ -537,14 +540,14 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int x = tid + u * NT;
+            const int x = tid + u * FT;
             pf.v[u] = rv.load16_nt(static_cast<uint32_t>(((x / 2) * vstride + (x % 2) * 8) * 2));
         }
         const float a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
         pf.a = (lane < n && lane < C) ? a : 1.f;
     };
     auto stage = [&](typename Sm::Buf& bb) {
-        if (__builtin_amdgcn_readfirstlane(wave) == 0) {
+        if (wave == 0) {
             const float x = wave_inclusive_sum(__log2f(pf.a));
             const float glast =
                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), C - 1));
@@ -556,7 +559,7 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
 #pragma unroll
         for (int u = 0; u < PF::NQ; ++u) {
-            const int xx = tid + u * NT;
+            const int xx = tid + u * FT;
             if (xx < C * DK / 8) {
                 const int row = xx / (DK / 8), vc = xx % (DK / 8);
                 *reinterpret_cast<u32x4*>(&bb.q[row][vc * 8]) = pf.q[u];
@@ -565,32 +568,28 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int xx = tid + u * NT;
+            const int xx = tid + u * FT;
             if (xx < C * 2) *reinterpret_cast<u32x4*>(&bb.v[xx / 2][(xx % 2) * 8]) = pf.v[u];
         }
     };
     auto write_state = [&]() {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int mt = wave + NW * i;
-            if (mt < KT) O::store4(&sm.st[0][ap.col][mt * 16 + ap.row0], &sm.st[1][ap.col][mt * 16 + ap.row0], S[i]);
-        }
+        if (has_tile) O::store4(&sm.st[0][ap.col][wave * 16 + ap.row0], &sm.st[1][ap.col][wave * 16 + ap.row0], S);
     };
-    // This wave's rows of T diag(beta) and P (hi, lo) for chunk c, as MFMA A
-    // operands; zero past the end.  Row blocks beyond the chunk read rows
-    // they never use.
-    u32x4 tpc[4][KSC], tpn[4][KSC];
-    auto load_tp = [&](u32x4 (&dst)[4][KSC], int c) {
-        const bool ok = c < nchunks;
+    // This wave's rows of T diag(beta) (x role) or P (q role), hi and lo, for
+    // chunk c, as MFMA A operands; zero past the end.
+    const int plane0 = qrole ? 2 : 0;
+    u32x4 tpc[2][KSC], tpn[2][KSC];
+    auto load_tp = [&](u32x4 (&dst)[2][KSC], int c) {
+        const bool ok = c < nchunks && (xrole || qrole);
         const BufRsrc rt(TP + (cbase + (ok ? c : 0)) * static_cast<long>(H) * 4 * C * C +
                              static_cast<long>(h) * 4 * C * C,
                          ok ? 4u * C * C * 2u : 0u);
 #pragma unroll
-        for (int pl = 0; pl < 4; ++pl) {
+        for (int pl = 0; pl < 2; ++pl) {
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks)
                 dst[pl][ks] = rt.load16_nt(static_cast<uint32_t>(
-                    (pl * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2));
+                    ((plane0 + pl) * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2));
         }
     };
 
@@ -608,19 +607,17 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const long tok0 = s0 + static_cast<long>(c) * C;
         f32x4 qs = {0.f, 0.f, 0.f, 0.f};
 
-        // ---- phase A: X = K S, Q S, Y = V - diag(exp g) X; stage chunk c+1
-        if (rows_here) {
+        // ---- phase A: X = K S, Y = V - diag(exp g) X (x role); Q S (q role);
+        // stage chunk c+1
+        if (xrole) {
             f32x4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
                 const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, 0, 32 * ks);
                 const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, 0, 32 * ks);
                 const bf16x8 kf = frag_kc(&bb.k[0][0], LQ, it * 16, 32 * ks);
-                const bf16x8 qf = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
                 xs = mfma_bf16(kf, sh, xs);
                 xs = mfma_bf16(kf, sl, xs);
-                qs = mfma_bf16(qf, sh, qs);
-                qs = mfma_bf16(qf, sl, qs);
             }
             f32x4 y;
 #pragma unroll
@@ -629,13 +626,22 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 y[r] = bf16_bits_to_f32(bb.v[row][ap.col]) - bb.eg[row] * xs[r];
             }
             O::store4(&sm.yt[0][ap.col][it * 16 + ap.row0], &sm.yt[1][ap.col][it * 16 + ap.row0], y);
+        } else if (qrole) {
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, 0, 32 * ks);
+                const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, 0, 32 * ks);
+                const bf16x8 qf = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
+                qs = mfma_bf16(qf, sh, qs);
+                qs = mfma_bf16(qf, sl, qs);
+            }
         }
         stage(sm.buf[(c + 1) & 1]);
         fetch(c + 2);
         lds_barrier();
 
-        // ---- phase B: U = T diag(beta) Y
-        if (rows_here) {
+        // ---- phase B: U = T diag(beta) Y (x role)
+        if (xrole) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
@@ -655,8 +661,8 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
         lds_barrier();
 
-        // ---- phase C: outputs and the state hand-off
-        if (rows_here) {
+        // ---- phase C: outputs (q role) and the state hand-off (every wave)
+        if (qrole) {
             f32x4 acc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = qs[r] * bb.eg[it * 16 + ap.row0 + r];
@@ -665,9 +671,9 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 if (32 * ks <= it * 16 + 15) {
                     const bf16x8 uh = frag_kc(&sm.ut[0][0][0], LT, 0, 32 * ks);
                     const bf16x8 ul = frag_kc(&sm.ut[1][0][0], LT, 0, 32 * ks);
-                    acc = mfma_bf16(as_bf16x8(tpc[2][ks]), uh, acc);
-                    acc = mfma_bf16(as_bf16x8(tpc[2][ks]), ul, acc);
-                    acc = mfma_bf16(as_bf16x8(tpc[3][ks]), uh, acc);
+                    acc = mfma_bf16(as_bf16x8(tpc[0][ks]), uh, acc);
+                    acc = mfma_bf16(as_bf16x8(tpc[0][ks]), ul, acc);
+                    acc = mfma_bf16(as_bf16x8(tpc[1][ks]), uh, acc);
                 }
             }
             // rows past the chunk's valid ones fall outside the resource
@@ -680,36 +686,27 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 else ro.store_b32(__float_as_uint(acc[r]), offb);
             }
         }
-        const float gam = bb.gamma;
+        if (has_tile) {
+            S *= bb.gamma;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int mt = wave + NW * i;
-            if (mt < KT) {
-                S[i] *= gam;
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) {
-                    const bf16x8 a = frag_km_split(&bb.k[0][0], LQ, mt * 16, 32 * ks);
-                    S[i] = mfma_bf16(a, frag_kc_split(&sm.udt[0][0][0], LT, 0, 32 * ks), S[i]);
-                    S[i] = mfma_bf16(a, frag_kc_split(&sm.udt[1][0][0], LT, 0, 32 * ks), S[i]);
-                }
+            for (int ks = 0; ks < KSC; ++ks) {
+                const bf16x8 a = frag_km_split(&bb.k[0][0], LQ, wave * 16, 32 * ks);
+                S = mfma_bf16(a, frag_kc_split(&sm.udt[0][0][0], LT, 0, 32 * ks), S);
+                S = mfma_bf16(a, frag_kc_split(&sm.udt[1][0][0], LT, 0, 32 * ks), S);
             }
         }
         write_state();
 #pragma unroll
-        for (int pl = 0; pl < 4; ++pl)
+        for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) tpc[pl][ks] = tpn[pl][ks];
         load_tp(tpn, c + 2);
         lds_barrier();
     }
 
+    if (has_tile) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int mt = wave + NW * i;
-        if (mt < KT) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * DV + col0 + ap.col] = S[i][r];
-        }
+        for (int r = 0; r < 4; ++r) Sg[(wave * 16 + ap.row0 + r) * DV + col0 + ap.col] = S[r];
     }
 }
 
@@ -742,7 +739,7 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     if constexpr (FAST) {
         const long groups = (static_cast<long>(a.n_seqs) * a.n_heads + 7) / 8 * 8;
         const long blocks = groups * (DV / 16);
-        hipLaunchKernelGGL((gdn_fast_kernel<DK, DV, C, TO>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
+        hipLaunchKernelGGL((gdn_fast_kernel<DK, DV, C, TO>), dim3(static_cast<unsigned>(blocks)), dim3(FT),
                            0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs,
                            a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, order,
