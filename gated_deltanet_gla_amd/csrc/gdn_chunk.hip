@@ -142,34 +142,33 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
     }
     lds_barrier();
 
-    // off-diagonal blocks, one block diagonal at a time: T_ij = -T_ii sum_k A_ik T_kj
-    const int rr = lane >> 2;          // row inside the block
-    const int cc = (lane & 3) * 4;     // first of 4 columns
+    // off-diagonal blocks, one block diagonal at a time: T_ij = -T_ii sum_k A_ik T_kj,
+    // each 16x16x16 product on the fp32 MFMA (16x16x4: A lane = row, B lane =
+    // column, k = lane / 16 within each group of 4; C lane = column, rows
+    // 4 (lane / 16) .. +3)
+    const int l16 = lane & 15, lg = lane >> 4;
     for (int d = 1; d < NB; ++d) {
         const int i = d + wave;        // this wave's block row (block column i - d)
         if (i < NB) {
             const int j = i - d;
             f32x4 xs = {0.f, 0.f, 0.f, 0.f};
             for (int kb = j; kb < i; ++kb) {
-#pragma unroll 4
-                for (int m = 0; m < 16; ++m) {
-                    const float aim = sm.a[i * 16 + rr][kb * 16 + m];
-                    const f32x4 tk = *reinterpret_cast<const f32x4*>(&sm.t[kb * 16 + m][j * 16 + cc]);
-                    xs += aim * tk;
-                }
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    xs = mfma_f32(sm.a[i * 16 + l16][kb * 16 + 4 * s4 + lg],
+                                  sm.t[kb * 16 + 4 * s4 + lg][j * 16 + l16], xs);
             }
-            *reinterpret_cast<f32x4*>(&sm.x[wave][rr][cc]) = xs;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.x[wave][4 * lg + r][l16] = xs[r];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int m = 0; m < 16; ++m) {
-                const float tim = sm.t[i * 16 + rr][i * 16 + m];
-                const f32x4 xm = *reinterpret_cast<const f32x4*>(&sm.x[wave][m][cc]);
-                y += tim * xm;
-            }
-            *reinterpret_cast<f32x4*>(&sm.t[i * 16 + rr][j * 16 + cc]) = -y;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                y = mfma_f32(sm.t[i * 16 + l16][i * 16 + 4 * s4 + lg], sm.x[wave][4 * s4 + lg][l16], y);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.t[i * 16 + 4 * lg + r][j * 16 + l16] = -y[r];
         }
         lds_barrier();
     }
