@@ -192,7 +192,7 @@ __device__ __forceinline__ void decay_scan(const float* alpha, long astride, int
     const int lane = threadIdx.x;
     if (lane >= 64) return;
     float x = 0.f;
-    if (lane < n && lane < C) x = __logf(__builtin_nontemporal_load(alpha + lane * astride));
+    if (lane < n && lane < C) x = __logf(fmaxf(__builtin_nontemporal_load(alpha + lane * astride), kMinDecay));
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);

@@ -48,6 +48,12 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uin
     lo = pack_bf16x2(a - ha, b - hb);
 }
 
+// Smallest decay the chunked kernels take the logarithm of: a gate of exactly
+// 0 (a complete reset) becomes 2^-126, whose contribution is below fp32
+// resolution of any state it multiplies, instead of log(0) = -inf turning
+// differences of log decays into NaN.
+constexpr float kMinDecay = 1.17549435e-38f;
+
 // ---------------------------------------------------------------- storage types
 struct F32 {
     using T = float;

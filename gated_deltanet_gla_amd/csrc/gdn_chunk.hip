@@ -547,7 +547,7 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     };
     auto stage = [&](typename Sm::Buf& bb) {
         if (wave == 0) {
-            const float x = wave_inclusive_sum(__log2f(pf.a));
+            const float x = wave_inclusive_sum(__log2f(fmaxf(pf.a, kMinDecay)));
             const float glast =
                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), C - 1));
             if (lane < C) {

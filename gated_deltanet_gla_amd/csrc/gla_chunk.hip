@@ -201,7 +201,7 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     };
     // State waves: write the prefetched chunk and the current state slice into bb.
     auto stage = [&](Buf& bb) {
-        float x = __log2f(pf.a);                 // in-wave scan, log2 domain
+        float x = __log2f(fmaxf(pf.a, kMinDecay));   // in-wave scan, log2 domain
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(x, off, 64);

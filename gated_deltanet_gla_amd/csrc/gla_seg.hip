@@ -216,7 +216,7 @@ __device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int lane = tid & 63;
     float glast = 0.f;
     if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
-        const float x = wave_inclusive_sum(__log2f(pf.a));
+        const float x = wave_inclusive_sum(__log2f(fmaxf(pf.a, kMinDecay)));
         glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), SC - 1));
         if constexpr (WQ) {
             bb.g2[lane] = x;

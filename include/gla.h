@@ -46,7 +46,8 @@
  *    dtypes: in_dtype, out_dtype in {GLA_F32, GLA_BF16}.  bf16 outputs are
  *    the fp32 result rounded to nearest even.
  *  - Preconditions (undefined results, not faults, if violated):
- *    alpha in (0, 1] and finite (the chunked form works with log alpha);
+ *    alpha in [0, 1] and finite (the chunked form works with log alpha;
+ *    alpha = 0, a complete reset, is taken as 2^-126);
  *    beta >= 0 with beta |k|^2 <= 2; q/k/v/o do not overlap the pool.
  *    Token indices derived from cu_seqlens are clamped to [0, n_tokens),
  *    so a malformed cu_seqlens gives wrong results, never an out-of-bounds

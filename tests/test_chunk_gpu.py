@@ -218,3 +218,35 @@ def test_prefill_then_decode(kind):
     o_ref, pool_ref = run_oracle(kind, w)
     check(host(od)[0], o_ref[96], "bf16", "decode o")
     check(host(pool)[w.slot_idx], pool_ref[w.slot_idx], "bf16", "state")
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+@pytest.mark.parametrize("dtype,d,C", [("bf16", 128, 64), ("f32", 32, 16)])
+def test_degenerate_gates(kind, dtype, d, C):
+    """Gates at the ends of their range: alpha exactly 0 (a complete reset)
+    or 1 (no decay) on a tenth of the tokens each, and for Gated DeltaNet
+    beta exactly 0 (no write) or 1; against the recurrence."""
+    w = synth.random_varlen(21 + d, [300, 77, 129], 2, d, d, dtype=dtype, gdn=(kind == "gdn"),
+                            chunk=C)
+    rng = np.random.Generator(np.random.PCG64(22))
+    u = rng.random(w.alpha.shape)
+    w.alpha = np.where(u < 0.1, 0.0, np.where(u > 0.9, 1.0, w.alpha)).astype(np.float32)
+    if kind == "gdn":
+        u = rng.random(w.beta.shape)
+        w.beta = np.where(u < 0.1, 0.0, np.where(u > 0.9, 1.0, w.beta)).astype(np.float32)
+    note(f"chunk {kind} {dtype} d={d} C={C} degenerate gates")
+    o, pool = run_chunk(kind, w)
+    o_ref, pool_ref = run_oracle(kind, w)
+    p = pool.cpu().numpy()[w.slot_idx]
+    assert np.all(np.isfinite(host(o))) and np.all(np.isfinite(p))
+    if dtype == "f32":
+        # A zero gate is taken as 2^-126, which shifts the chunk's running
+        # log2 decay by -126 per reset; fp32 keeps log values near 126..252
+        # to 2^-17..2^-16, so decays between later tokens of that chunk carry
+        # ~1e-5 relative error: the absolute bar here is 5e-5 instead of 1e-5.
+        e_o = float(np.max(np.abs(host(o) - o_ref)))
+        e_s = float(np.max(np.abs(p - pool_ref[w.slot_idx])))
+        assert e_o <= 5e-5 and e_s <= 5e-5, (e_o, e_s)
+    else:
+        check(host(o), o_ref, dtype, "o")
+        check(p, pool_ref[w.slot_idx], dtype, "state")
