@@ -207,6 +207,21 @@ __device__ __forceinline__ void decay_scan(const float* alpha, long astride, int
     if (lane == 0) *gamma = __expf(last);
 }
 
+// The running log-decay alone: g[j] = sum_{i <= j} ln a_i (rows past n: a = 1).
+template <int C>
+__device__ __forceinline__ void log_decay_scan(const float* alpha, long astride, int n, float* g) {
+    const int lane = threadIdx.x;
+    if (lane >= 64) return;
+    float x = 0.f;
+    if (lane < n && lane < C) x = __logf(fmaxf(__builtin_nontemporal_load(alpha + lane * astride), kMinDecay));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane < C) g[lane] = x;
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences
 // global memory, which makes every wave drain its outstanding global loads
 // (the next chunk's prefetch) and stores at each barrier; the chunk loops

@@ -48,18 +48,29 @@ __host__ __device__ constexpr long max_chunks(int n_seqs, int n_tokens, int C) {
 }
 
 // ------------------------------------------------------------------ 2. prep
+// LDS: the staged k (and q) and the fp32 A / T tiles are never live at the
+// same time, so they share one region; with the per-wave scratch and the
+// gate tables a workgroup fits in 40 KiB and four of them share a compute
+// unit, which overlaps one workgroup's loads with the others' arithmetic.
 template <int DK, int C, bool F32, bool TP>
 struct PrepSmem {
     using E = typename Op<F32>::E;
     static constexpr int LQ = DK + Op<F32>::PAD;
     static constexpr int LA = C + 4;           // fp32 lines of A and T (16-byte aligned)
-    alignas(16) E k[C][LQ];
-    alignas(16) E q[TP ? C : 1][LQ];
-    alignas(16) float a[C][LA];
-    alignas(16) float t[C][LA];
+    struct In {
+        alignas(16) E k[C][LQ];
+        alignas(16) E q[TP ? C : 1][LQ];
+    };
+    struct Tri {
+        alignas(16) float a[C][LA];
+        alignas(16) float t[C][LA];
+    };
+    union {
+        In in;
+        Tri tri;
+    };
     alignas(16) float x[NW][16][20];           // per-wave 16x16 scratch (padded)
-    float g[C], eg[C], dec[C], beta[C];
-    float gamma;
+    float g[C], beta[C];
 };
 
 // TP = false: write T (fp32, C x C) per (chunk, head).
@@ -77,6 +88,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
     using Sm = PrepSmem<DK, C, F32, TP>;
     constexpr int LQ = Sm::LQ;
     constexpr int NB = C / 16;
+    constexpr int TPW = (NB * NB + NW - 1) / NW;   // 16x16 tiles per wave
     __shared__ Sm sm;
 
     const int h = blockIdx.x % H;
@@ -97,26 +109,66 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
     const long tok0 = s0 + c0;
     const long tstride = static_cast<long>(H) * DK;
 
-    stage_natural<TI, C, DK, NT>(&sm.k[0][0], LQ, k + tok0 * tstride + h * DK, tstride, n);
-    if constexpr (TP) stage_natural<TI, C, DK, NT>(&sm.q[0][0], LQ, q + tok0 * tstride + h * DK, tstride, n);
-    decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g, sm.eg, sm.dec, &sm.gamma);
+    stage_natural<TI, C, DK, NT>(&sm.in.k[0][0], LQ, k + tok0 * tstride + h * DK, tstride, n);
+    if constexpr (TP) stage_natural<TI, C, DK, NT>(&sm.in.q[0][0], LQ, q + tok0 * tstride + h * DK, tstride, n);
+    log_decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g);
     for (int j = threadIdx.x; j < C; j += NT) sm.beta[j] = j < n ? beta[(tok0 + j) * H + h] : 0.f;
     lds_barrier();
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const AccPos ap;
-    // A = strictly-lower(diag(beta) (K K^T .* D)), fp32
-    for (int t = wave; t < NB * NB; t += NW) {
-        const int tt = t / NB, jt = t % NB;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (jt <= tt) O::mma(acc, &sm.k[tt * 16][0], LQ, &sm.k[jt * 16][0], LQ, DK);
-        const int j = jt * 16 + ap.col;
+    uint16_t* planes = static_cast<uint16_t*>(Tws) + (static_cast<long>(ci) * H + h) * 4 * C * C;
+    // A = strictly-lower(diag(beta) (K K^T .* D)), fp32, held in registers
+    // until k (and q) are no longer read; P = (Q K^T) .* D as P^T tiles (lane:
+    // 4 consecutive j of row i) straight to planes 2, 3
+    f32x4 areg[TPW];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = tt * 16 + ap.row0 + r;
-            sm.a[i][j] = (j < i) ? sm.beta[i] * __expf(sm.g[i] - sm.g[j]) * acc[r] : 0.f;
+    for (int m = 0; m < TPW; ++m) {
+        const int t = wave + NW * m;
+        areg[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < NB * NB) {
+            const int tt = t / NB, jt = t % NB;
+            if (jt <= tt) {
+                O::mma(areg[m], &sm.in.k[tt * 16][0], LQ, &sm.in.k[jt * 16][0], LQ, DK);
+                const int j = jt * 16 + ap.col;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = tt * 16 + ap.row0 + r;
+                    areg[m][r] = (j < i) ? sm.beta[i] * __expf(sm.g[i] - sm.g[j]) * areg[m][r] : 0.f;
+                }
+            }
+            if constexpr (TP) {
+                const int pj = t / NB, pi = t % NB;
+                const int i = pi * 16 + ap.col;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (pj <= pi) {
+                    O::mma(acc, &sm.in.k[pj * 16][0], LQ, &sm.in.q[pi * 16][0], LQ, DK);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = pj * 16 + ap.row0 + r;
+                        acc[r] = (j <= i) ? acc[r] * __expf(sm.g[i] - sm.g[j]) : 0.f;
+                    }
+                }
+                O::store4(planes + 2 * C * C + i * C + pj * 16 + ap.row0,
+                          planes + 3 * C * C + i * C + pj * 16 + ap.row0, acc);
+            }
         }
+    }
+    lds_barrier();                       // k, q dead: their space becomes A and T
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+        const int t = wave + NW * m;
+        if (t < NB * NB) {
+            const int tt = t / NB, jt = t % NB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.tri.a[tt * 16 + ap.row0 + r][jt * 16 + ap.col] = areg[m][r];
+        }
+    }
+    // blocks above the diagonal of T are zero
+    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
+        const int r = idx / C, c = idx % C;
+        if ((c >> 4) > (r >> 4)) sm.tri.t[r][c] = 0.f;
     }
     lds_barrier();
 
@@ -129,16 +181,11 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
         for (int r = 0; r < 16; ++r) {
             float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc -= sm.a[base + r][base + m] * x[m];
+            for (int m = 0; m < r; ++m) acc -= sm.tri.a[base + r][base + m] * x[m];
             x[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.t[base + r][base + c] = x[r];
-    }
-    // blocks above the diagonal are zero
-    for (int idx = threadIdx.x; idx < C * C; idx += NT) {
-        const int r = idx / C, c = idx % C;
-        if ((c >> 4) > (r >> 4)) sm.t[r][c] = 0.f;
+        for (int r = 0; r < 16; ++r) sm.tri.t[base + r][base + c] = x[r];
     }
     lds_barrier();
 
@@ -155,8 +202,8 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
             for (int kb = j; kb < i; ++kb) {
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
-                    xs = mfma_f32(sm.a[i * 16 + l16][kb * 16 + 4 * s4 + lg],
-                                  sm.t[kb * 16 + 4 * s4 + lg][j * 16 + l16], xs);
+                    xs = mfma_f32(sm.tri.a[i * 16 + l16][kb * 16 + 4 * s4 + lg],
+                                  sm.tri.t[kb * 16 + 4 * s4 + lg][j * 16 + l16], xs);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.x[wave][4 * lg + r][l16] = xs[r];
@@ -166,9 +213,9 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
-                y = mfma_f32(sm.t[i * 16 + l16][i * 16 + 4 * s4 + lg], sm.x[wave][4 * s4 + lg][l16], y);
+                y = mfma_f32(sm.tri.t[i * 16 + l16][i * 16 + 4 * s4 + lg], sm.x[wave][4 * s4 + lg][l16], y);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.t[i * 16 + 4 * lg + r][j * 16 + l16] = -y[r];
+            for (int r = 0; r < 4; ++r) sm.tri.t[i * 16 + 4 * lg + r][j * 16 + l16] = -y[r];
         }
         lds_barrier();
     }
@@ -178,32 +225,16 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
         float* dst = static_cast<float*>(Tws) + (static_cast<long>(ci) * H + h) * C * C;
         for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
             const int r = (idx * 4) / C, c = (idx * 4) % C;
-            *reinterpret_cast<f32x4*>(dst + r * C + c) = *reinterpret_cast<const f32x4*>(&sm.t[r][c]);
+            *reinterpret_cast<f32x4*>(dst + r * C + c) = *reinterpret_cast<const f32x4*>(&sm.tri.t[r][c]);
         }
     } else {
-        uint16_t* dst = static_cast<uint16_t*>(Tws) + (static_cast<long>(ci) * H + h) * 4 * C * C;
         // T diag(beta) -> planes 0 (hi), 1 (lo)
         for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
             const int r = (idx * 4) / C, c = (idx * 4) % C;
-            f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.t[r][c]);
+            f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.tri.t[r][c]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) tv[e] *= sm.beta[c + e];
-            O::store4(dst + r * C + c, dst + C * C + r * C + c, tv);
-        }
-        // P = (Q K^T) .* D as P^T tiles (lane: 4 consecutive j of row i) -> planes 2, 3
-        for (int t = wave; t < NB * NB; t += NW) {
-            const int jt = t / NB, it = t % NB;
-            const int i = it * 16 + ap.col;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (jt <= it) {
-                O::mma(acc, &sm.k[jt * 16][0], LQ, &sm.q[it * 16][0], LQ, DK);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = jt * 16 + ap.row0 + r;
-                    acc[r] = (j <= i) ? acc[r] * __expf(sm.g[i] - sm.g[j]) : 0.f;
-                }
-            }
-            O::store4(dst + 2 * C * C + i * C + jt * 16 + ap.row0, dst + 3 * C * C + i * C + jt * 16 + ap.row0, acc);
+            O::store4(planes + r * C + c, planes + C * C + r * C + c, tv);
         }
     }
 }
@@ -423,16 +454,22 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
 //      state slice -> LDS for the next chunk.
 // q, k, v are double-buffered in LDS and prefetched into registers two
 // chunks ahead; three LDS-only barriers per chunk.
+constexpr int FW = 8;                 // waves of the bf16 serial kernel
+constexpr int FT = FW * 64;
+
 template <int DK, int C>
 struct GdnFastSmem {
     static constexpr int BV = 16;
+    // rows of the v tile buffer: every thread stages one dword (FT / 8 rows
+    // of 16 values), so the staging has no thread-dependent branch
+    static constexpr int VR = FT / 8 > C ? FT / 8 : C;
     static constexpr int LQ = DK + 8;
     static constexpr int LV = BV + 8;
     static constexpr int LT = C + 8;
     struct Buf {
         alignas(16) uint16_t q[C][LQ];
         alignas(16) uint16_t k[C][LQ];
-        alignas(16) uint16_t v[C][LV];
+        alignas(16) uint16_t v[VR][LV];
         float eg[C];
         float dec[C];
         float gamma;
@@ -444,15 +481,13 @@ struct GdnFastSmem {
     alignas(16) uint16_t udt[2][BV][LT];   // (diag(dec) U)^T (hi, lo)
 };
 
-constexpr int FW = 8;                 // waves of the bf16 serial kernel
-constexpr int FT = FW * 64;
-
 template <int C, int DK>
 struct GdnFastPrefetch {
     static constexpr int NQ = (C * DK / 8 + FT - 1) / FT;
-    static constexpr int NV = (C * 16 / 8 + FT - 1) / FT;
-    u32x4 q[NQ], k[NQ], v[NV];
-    float a;
+    u32x4 q[NQ], k[NQ];
+    uint32_t v;        // two values of row tid / 8 of the v tile
+    float a;           // raw gate of token `lane`; only the first n are valid
+    int n;
 };
 
 template <int DK, int DV, int C, class TO>
@@ -537,17 +572,16 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             pf.q[u] = rq.load16_nt(offb);
             pf.k[u] = rk.load16_nt(offb);
         }
-#pragma unroll
-        for (int u = 0; u < PF::NV; ++u) {
-            const int x = tid + u * FT;
-            pf.v[u] = rv.load16_nt(static_cast<uint32_t>(((x / 2) * vstride + (x % 2) * 8) * 2));
-        }
-        const float a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
-        pf.a = (lane < n && lane < C) ? a : 1.f;
+        pf.v = __float_as_uint(rv.loadf_nt(static_cast<uint32_t>(((tid >> 3) * vstride + (tid & 7) * 2) * 2)));
+        // rows past n get a gate of 1 when staged: a select on the loaded
+        // value here would make the wave wait for this load right away
+        pf.a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
+        pf.n = n;
     };
     auto stage = [&](typename Sm::Buf& bb) {
         if (wave == 0) {
-            const float x = wave_inclusive_sum(__log2f(fmaxf(pf.a, kMinDecay)));
+            const float a = lane < pf.n ? pf.a : 1.f;
+            const float x = wave_inclusive_sum(__log2f(fmaxf(a, kMinDecay)));
             const float glast =
                 __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), C - 1));
             if (lane < C) {
@@ -559,17 +593,15 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int u = 0; u < PF::NQ; ++u) {
             const int xx = tid + u * FT;
-            if (xx < C * DK / 8) {
+            // (a constant condition when the threads cover the tile exactly;
+            // a branch here would blur the compiler's load-counter waits)
+            if (C * DK / 8 == PF::NQ * FT || xx < C * DK / 8) {
                 const int row = xx / (DK / 8), vc = xx % (DK / 8);
                 *reinterpret_cast<u32x4*>(&bb.q[row][vc * 8]) = pf.q[u];
                 *reinterpret_cast<u32x4*>(&bb.k[row][vc * 8]) = pf.k[u];
             }
         }
-#pragma unroll
-        for (int u = 0; u < PF::NV; ++u) {
-            const int xx = tid + u * FT;
-            if (xx < C * 2) *reinterpret_cast<u32x4*>(&bb.v[xx / 2][(xx % 2) * 8]) = pf.v[u];
-        }
+        *reinterpret_cast<uint32_t*>(&bb.v[tid >> 3][(tid & 7) * 2]) = pf.v;
     };
     auto write_state = [&]() {
         if (has_tile) O::store4(&sm.st[0][ap.col][wave * 16 + ap.row0], &sm.st[1][ap.col][wave * 16 + ap.row0], S);
@@ -577,7 +609,10 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // This wave's rows of T diag(beta) (x role) or P (q role), hi and lo, for
     // chunk c, as MFMA A operands; zero past the end.
     const int plane0 = qrole ? 2 : 0;
-    u32x4 tpc[2][KSC], tpn[2][KSC];
+    // two register sets used alternately (even / odd chunks): each is
+    // reloaded for chunk c + 2 right after chunk c used it, so no copy ever
+    // waits on a load that was just issued
+    u32x4 tpa[2][KSC], tpb[2][KSC];
     auto load_tp = [&](u32x4 (&dst)[2][KSC], int c) {
         const bool ok = c < nchunks && (xrole || qrole);
         const BufRsrc rt(TP + (cbase + (ok ? c : 0)) * static_cast<long>(H) * 4 * C * C +
@@ -595,12 +630,12 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     fetch(0);
     stage(sm.buf[0]);
     write_state();
-    load_tp(tpc, 0);
+    load_tp(tpa, 0);
     fetch(1);
-    load_tp(tpn, 1);
+    load_tp(tpb, 1);
     lds_barrier();
 
-    for (int c = 0; c < nchunks; ++c) {
+    auto chunk_step = [&](int c, u32x4 (&tpc)[2][KSC]) {
         typename Sm::Buf& bb = sm.buf[c & 1];
         const int n = chunk_rows(c);
         const long tok0 = s0 + static_cast<long>(c) * C;
@@ -695,13 +730,17 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             }
         }
         write_state();
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) tpc[pl][ks] = tpn[pl][ks];
-        load_tp(tpn, c + 2);
+        load_tp(tpc, c + 2);
         lds_barrier();
+    };
+    // pairs of chunks with no path that skips the odd one, so the compiler
+    // sees the same load sequence on every trip round the loop
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        chunk_step(c, tpa);
+        chunk_step(c + 1, tpb);
     }
+    if (c < nchunks) chunk_step(c, tpa);
 
     if (has_tile) {
 #pragma unroll

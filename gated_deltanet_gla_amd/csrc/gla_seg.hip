@@ -80,7 +80,8 @@ template <bool WQ>
 struct SegPrefetch {
     static constexpr int NV = SC * SD / 8 / ST;    // 16-byte vectors per thread per tensor
     u32x4 q[WQ ? NV : 1], k[NV], v[NV];
-    float a;
+    float a;           // raw gate of token `lane`; only the first n are valid
+    int n;
 };
 
 struct SegGeom {
@@ -204,8 +205,10 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
         pf.v[u] = rv.load16_nt(offb);
     }
     const int lane = tid & 63;
-    const float a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
-    pf.a = (lane < n && lane < SC) ? a : 1.f;
+    // The gates of rows past n are replaced by 1 when staged, not here: a
+    // select on the loaded value would make this wave wait for the load now.
+    pf.a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
+    pf.n = n;
 }
 
 // Registers -> LDS; wave 0 scans log2(alpha), writes the per-token tables and
@@ -216,7 +219,8 @@ __device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int lane = tid & 63;
     float glast = 0.f;
     if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
-        const float x = wave_inclusive_sum(__log2f(fmaxf(pf.a, kMinDecay)));
+        const float a = lane < pf.n ? pf.a : 1.f;
+        const float x = wave_inclusive_sum(__log2f(fmaxf(a, kMinDecay)));
         glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), SC - 1));
         if constexpr (WQ) {
             bb.g2[lane] = x;
