@@ -607,7 +607,9 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         if (has_tile) O::store4(&sm.st[0][ap.col][wave * 16 + ap.row0], &sm.st[1][ap.col][wave * 16 + ap.row0], S);
     };
     // This wave's rows of T diag(beta) (x role) or P (q role), hi and lo, for
-    // chunk c, as MFMA A operands; zero past the end.
+    // chunk c, as MFMA A operands; zero past the end.  The planes were just
+    // written by gdn_prep and are shared by the d_v tiles of the group, so
+    // they are read with the default policy (kept in L2).
     const int plane0 = qrole ? 2 : 0;
     // two register sets used alternately (even / odd chunks): each is
     // reloaded for chunk c + 2 right after chunk c used it, so no copy ever
@@ -622,7 +624,7 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int pl = 0; pl < 2; ++pl) {
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks)
-                dst[pl][ks] = rt.load16_nt(static_cast<uint32_t>(
+                dst[pl][ks] = rt.load16(static_cast<uint32_t>(
                     ((plane0 + pl) * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2));
         }
     };
