@@ -46,6 +46,9 @@
 namespace gla {
 namespace {
 
+#ifndef SEG_OVERLAP
+#define SEG_OVERLAP 1
+#endif
 constexpr int SW = 8;              // waves
 constexpr int ST = SW * 64;        // threads
 constexpr int SD = 128;            // d_k = d_v
@@ -200,9 +203,14 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
     for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
         const int x = tid + u * ST;
         const uint32_t offb = static_cast<uint32_t>(((x / (SD / 8)) * stride + (x % (SD / 8)) * 8) * 2);
-        if constexpr (WQ) pf.q[u] = BufRsrc(q + tok0 * stride + h * SD, ext).load16_nt(offb);
-        pf.k[u] = rk.load16_nt(offb);
-        pf.v[u] = rv.load16_nt(offb);
+        if constexpr (WQ) {
+            pf.q[u] = BufRsrc(q + tok0 * stride + h * SD, ext).load16_nt(offb);
+            pf.k[u] = rk.load16_nt(offb);
+            pf.v[u] = rv.load16_nt(offb);
+        } else {
+            pf.k[u] = rk.load16(offb);
+            pf.v[u] = rv.load16(offb);
+        }
     }
     const int lane = tid & 63;
     // The gates of rows past n are replaced by 1 when staged, not here: a
@@ -211,10 +219,24 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
     pf.n = n;
 }
 
-// Registers -> LDS; wave 0 scans log2(alpha), writes the per-token tables and
-// gets the chunk's total log2 decay back (other waves get 0).
+// Registers -> LDS: the q, k, v rows.
 template <bool WQ, class Buf>
-__device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
+__device__ __forceinline__ void seg_stage_rows(Buf& bb, const SegPrefetch<WQ>& pf) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
+        const int xx = tid + u * ST;
+        const int row = xx / (SD / 8), vc = (xx % (SD / 8)) * 8;
+        if constexpr (WQ) *reinterpret_cast<u32x4*>(&bb.q[row][vc]) = pf.q[u];
+        *reinterpret_cast<u32x4*>(&bb.k[row][vc]) = pf.k[u];
+        *reinterpret_cast<u32x4*>(&bb.v[row][vc]) = pf.v[u];
+    }
+}
+
+// Wave 0 scans log2(alpha), writes the per-token tables and gets the chunk's
+// total log2 decay back (other waves get 0).
+template <bool WQ, class Buf>
+__device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     float glast = 0.f;
@@ -229,14 +251,15 @@ __device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
         bb.dec[lane] = exp2f(glast - x);
         if (lane == 0) bb.gamma = exp2f(glast);
     }
-#pragma unroll
-    for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
-        const int xx = tid + u * ST;
-        const int row = xx / (SD / 8), vc = (xx % (SD / 8)) * 8;
-        if constexpr (WQ) *reinterpret_cast<u32x4*>(&bb.q[row][vc]) = pf.q[u];
-        *reinterpret_cast<u32x4*>(&bb.k[row][vc]) = pf.k[u];
-        *reinterpret_cast<u32x4*>(&bb.v[row][vc]) = pf.v[u];
-    }
+    return glast;
+}
+
+// Registers -> LDS (rows and gate tables); returns the chunk's total log2
+// decay on wave 0.
+template <bool WQ, class Buf>
+__device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
+    const float glast = seg_stage_gates(bb, pf);
+    seg_stage_rows(bb, pf);
     return glast;
 }
 
@@ -248,18 +271,22 @@ __device__ __forceinline__ void load_vt(bf16x8 (&vf)[2], const Buf& bb, int col)
     for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&bb.v[0][0], LK, col, 32 * ks);
 }
 
-// S (this wave's 16 columns, all 8 row tiles) <- gamma S + K^T diag(dec) V.
-template <class Buf>
-__device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
+// State update S (this wave's 16 columns, all 8 row tiles) <- gamma S +
+// K^T diag(dec) V, in two parts: the operand reads and the VALU work
+// (decayed, split values; the gamma scaling), then the MFMAs.
+struct SegUpd {
     bf16x8 kf[2][8];
+    bf16x8 vh[2], vl[2];
+};
+template <class Buf>
+__device__ __forceinline__ void seg_update_prep(SegUpd& up, f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) kf[ks][mt] = frag_km_split(&bb.k[0][0], LK, mt * 16, 32 * ks);
+        for (int mt = 0; mt < 8; ++mt) up.kf[ks][mt] = frag_km_split(&bb.k[0][0], LK, mt * 16, 32 * ks);
     __builtin_amdgcn_sched_barrier(0);
     // decayed values for tokens {32ks + 4g + e} u {32ks + 16 + 4g + e}, split
     const int g = (threadIdx.x & 63) >> 4;
-    bf16x8 vh[2], vl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const u32x4 vw = __builtin_bit_cast(u32x4, vf[ks]);
@@ -270,20 +297,30 @@ __device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, c
         split_bf16x2(__uint_as_float(vw.y << 16) * d0.z, __uint_as_float(vw.y & 0xffff0000u) * d0.w, hw[1], lw[1]);
         split_bf16x2(__uint_as_float(vw.z << 16) * d1.x, __uint_as_float(vw.z & 0xffff0000u) * d1.y, hw[2], lw[2]);
         split_bf16x2(__uint_as_float(vw.w << 16) * d1.z, __uint_as_float(vw.w & 0xffff0000u) * d1.w, hw[3], lw[3]);
-        vh[ks] = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
-        vl[ks] = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
+        up.vh[ks] = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
+        up.vl[ks] = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
     const float gam = bb.gamma;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] *= gam;
+}
+__device__ __forceinline__ void seg_update_mfma_half(f32x4 (&S)[8], const SegUpd& up, int ks) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        S[mt] = mfma_bf16(up.kf[ks][mt], up.vh[ks], S[mt]);
+        S[mt] = mfma_bf16(up.kf[ks][mt], up.vl[ks], S[mt]);
+    }
+}
+__device__ __forceinline__ void seg_update_mfma(f32x4 (&S)[8], const SegUpd& up) {
+    seg_update_mfma_half(S, up, 0);
+    seg_update_mfma_half(S, up, 1);
+}
+template <class Buf>
+__device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
+    SegUpd up;
+    seg_update_prep(up, S, bb, vf);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            S[mt] = mfma_bf16(kf[ks][mt], vh[ks], S[mt]);
-            S[mt] = mfma_bf16(kf[ks][mt], vl[ks], S[mt]);
-        }
+    seg_update_mfma(S, up);
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -458,7 +495,9 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             sh8[s] = cat8(h0, h1);
             sl8[s] = cat8(l0, l1);
         }
+#if !SEG_OVERLAP
         __builtin_amdgcn_sched_barrier(0);
+#endif
         f32x4 ot[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) ot[it] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -493,6 +532,12 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             pp[it + 2][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 32);
         }
         __builtin_amdgcn_sched_barrier(0);
+#if SEG_OVERLAP
+        // the state update's operand reads and VALU work go ahead of the
+        // P V MFMAs, which do not depend on them, so they can overlap
+        SegUpd up;
+        seg_update_prep(up, S, bb, vf);
+#endif
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
@@ -516,8 +561,17 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
                 ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
                               static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
         }
+#if SEG_OVERLAP
+        // the next chunk's rows go to LDS between the two halves of the
+        // update's MFMAs, the gate scan after them
+        seg_update_mfma_half(S, up, 0);
+        seg_stage_rows(buf[(c + 1) & 1], pf);
+        seg_update_mfma_half(S, up, 1);
+        seg_stage_gates(buf[(c + 1) & 1], pf);
+#else
         seg_state_update(S, bb, vf);
         seg_stage(buf[(c + 1) & 1], pf);
+#endif
         seg_fetch(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
