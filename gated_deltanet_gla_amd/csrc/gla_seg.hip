@@ -34,21 +34,21 @@
 //            one after.
 // Pass 1 runs the state update alone.  q, k, v stay token-major in LDS;
 // contractions over tokens use the LDS transpose read.  Each step issues all
-// of its LDS operand reads first, then the VALU work that does not depend on
-// them (splits, decays), then the MFMAs, so the read latency is hidden
-// behind that work instead of stalling every MFMA.
+// of its LDS operand reads first, so the read latency is hidden behind the
+// VALU work that does not depend on them (splits, decays); that VALU work is
+// placed next to MFMAs it does not feed (the state update's split before
+// the P V products, the next chunk's LDS writes between the update's
+// products), so the matrix and vector units run side by side.
 // Global accesses go through buffer resources sized to the valid rows, so
-// the loops have no guarded memory instructions; the token streams use the
-// nontemporal policy.
+// the loops have no guarded memory instructions; the output pass streams
+// q, k, v with the nontemporal policy (pass 1 reads k, v with the default
+// one, which leaves them in the last-level cache for pass 2).
 #include "chunk_common.h"
 #include "launch.h"
 
 namespace gla {
 namespace {
 
-#ifndef SEG_OVERLAP
-#define SEG_OVERLAP 1
-#endif
 constexpr int SW = 8;              // waves
 constexpr int ST = SW * 64;        // threads
 constexpr int SD = 128;            // d_k = d_v
@@ -495,9 +495,6 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             sh8[s] = cat8(h0, h1);
             sl8[s] = cat8(l0, l1);
         }
-#if !SEG_OVERLAP
-        __builtin_amdgcn_sched_barrier(0);
-#endif
         f32x4 ot[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) ot[it] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -532,12 +529,10 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             pp[it + 2][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 32);
         }
         __builtin_amdgcn_sched_barrier(0);
-#if SEG_OVERLAP
         // the state update's operand reads and VALU work go ahead of the
         // P V MFMAs, which do not depend on them, so they can overlap
         SegUpd up;
         seg_update_prep(up, S, bb, vf);
-#endif
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
@@ -561,17 +556,12 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
                 ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
                               static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
         }
-#if SEG_OVERLAP
         // the next chunk's rows go to LDS between the two halves of the
         // update's MFMAs, the gate scan after them
         seg_update_mfma_half(S, up, 0);
         seg_stage_rows(buf[(c + 1) & 1], pf);
         seg_update_mfma_half(S, up, 1);
         seg_stage_gates(buf[(c + 1) & 1], pf);
-#else
-        seg_state_update(S, bb, vf);
-        seg_stage(buf[(c + 1) & 1], pf);
-#endif
         seg_fetch(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
