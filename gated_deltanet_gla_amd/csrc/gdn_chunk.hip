@@ -32,6 +32,8 @@
 //     inputs with chunks of 32/64 and d_k >= 32 (the prep kernel then also
 //     emits T diag(beta) and P as bf16 hi/lo planes), gdn_chunk_kernel for
 //     the rest (fp32 inputs, 16-wide shapes).
+#include <algorithm>
+
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -40,6 +42,7 @@ namespace {
 
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
+constexpr long kPrepBlocks = 768;    // 256 compute units x 3 resident prep workgroups
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -73,11 +76,30 @@ struct PrepSmem {
     float g[C], beta[C];
 };
 
+// One work item = one (chunk, head).  The kernel is persistent: a fixed grid
+// of workgroups strides over the items, and while one item's arithmetic runs
+// (latency-bound: the triangular inverse), the k / q rows and gates of the
+// workgroup's next item are already loading into registers.
+struct PrepItem {
+    int ci, h, n;      // chunk (global index), head, valid rows
+    long tok0;         // first token
+    bool ok;
+};
+
+template <class TI, int C, int DK, bool TP>
+struct PrepPrefetch {
+    static constexpr int VE = 16 / TI::bytes;          // elements per 16-byte vector
+    static constexpr int NV = (C * DK / VE + NT - 1) / NT;
+    u32x4 k[NV];
+    u32x4 q[TP ? NV : 1];
+    float a;           // gate (wave 0) / beta (wave 1) of token `lane`, raw
+};
+
 // TP = false: write T (fp32, C x C) per (chunk, head).
 // TP = true (bf16 inputs): write four bf16 C x C planes per (chunk, head):
 //   T diag(beta) hi, lo, and P = (Q K^T) .* D (lower, decayed) hi, lo.
 template <int DK, int C, class TI, bool TP>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, 3)       // three resident workgroups per compute unit
 gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict__ q,
          const float* __restrict__ alpha, const float* __restrict__ beta,
          const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
@@ -86,37 +108,94 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
     static_assert(!(TP && F32), "planes are bf16");
     using O = Op<F32>;
     using Sm = PrepSmem<DK, C, F32, TP>;
+    using PF = PrepPrefetch<TI, C, DK, TP>;
     constexpr int LQ = Sm::LQ;
     constexpr int NB = C / 16;
     constexpr int TPW = (NB * NB + NW - 1) / NW;   // 16x16 tiles per wave
+    constexpr int VE = PF::VE;
+    constexpr int VPR = DK / VE;                   // vectors per row
     __shared__ Sm sm;
 
-    const int h = blockIdx.x % H;
-    const int ci = blockIdx.x / H;
-    if (ci >= off[n_seqs]) return;
-    // sequence of this chunk: largest b with off[b] <= ci
-    int lo = 0, hi = n_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= ci) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int s0 = clampi(cu[b], 0, n_tokens);
-    const int s1 = clampi(cu[b + 1], s0, n_tokens);
-    const int c0 = (ci - off[b]) * C;
-    const int n = min(C, s1 - s0 - c0);
-    if (c0 < 0 || n <= 0) return;   // only with a malformed cu_seqlens
-    const long tok0 = s0 + c0;
-    const long tstride = static_cast<long>(H) * DK;
-
-    stage_natural<TI, C, DK, NT>(&sm.in.k[0][0], LQ, k + tok0 * tstride + h * DK, tstride, n);
-    if constexpr (TP) stage_natural<TI, C, DK, NT>(&sm.in.q[0][0], LQ, q + tok0 * tstride + h * DK, tstride, n);
-    log_decay_scan<C>(alpha + tok0 * H + h, H, n, sm.g);
-    for (int j = threadIdx.x; j < C; j += NT) sm.beta[j] = j < n ? beta[(tok0 + j) * H + h] : 0.f;
-    lds_barrier();
-
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const long tstride = static_cast<long>(H) * DK;
+    const long n_items = static_cast<long>(off[n_seqs]) * H;
+
+    auto locate = [&](long item) {
+        PrepItem it{0, 0, 0, 0, false};
+        if (item >= n_items) return it;
+        it.h = static_cast<int>(item % H);
+        it.ci = static_cast<int>(item / H);
+        // sequence of this chunk: largest b with off[b] <= ci
+        int lo = 0, hi = n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= it.ci) lo = mid; else hi = mid - 1;
+        }
+        const int s0 = clampi(cu[lo], 0, n_tokens);
+        const int s1 = clampi(cu[lo + 1], s0, n_tokens);
+        const int c0 = (it.ci - off[lo]) * C;
+        it.n = min(C, s1 - s0 - c0);
+        it.ok = c0 >= 0 && it.n > 0;      // false only with a malformed cu_seqlens
+        if (!it.ok) it.n = 0;
+        it.tok0 = s0 + max(c0, 0);
+        return it;
+    };
+    // item rows -> registers; rows past n (and items that do not exist) read
+    // as zero through the buffer resource
+    auto fetch = [&](PF& pf, const PrepItem& it) {
+        const uint32_t ext = rows_extent(it.n, tstride * TI::bytes, DK * TI::bytes);
+        const BufRsrc rk(k + it.tok0 * tstride + it.h * DK, ext);
+        const BufRsrc rq(q + it.tok0 * tstride + it.h * DK, TP ? ext : 0u);
+#pragma unroll
+        for (int u = 0; u < PF::NV; ++u) {
+            const int x = threadIdx.x + u * NT;
+            const uint32_t offb = static_cast<uint32_t>(((x / VPR) * tstride + (x % VPR) * VE) * TI::bytes);
+            pf.k[u] = rk.load16_nt(offb);
+            if constexpr (TP) pf.q[u] = rq.load16_nt(offb);
+        }
+        const float* gsrc = wave == 0 ? alpha : beta;
+        const BufRsrc rg(gsrc + it.tok0 * H + it.h, wave < 2 ? rows_extent(it.n, static_cast<long>(H) * 4, 4) : 0u);
+        pf.a = rg.loadf_nt(static_cast<uint32_t>(lane * H * 4));
+    };
+    auto stage = [&](const PF& pf, const PrepItem& it) {
+#pragma unroll
+        for (int u = 0; u < PF::NV; ++u) {
+            const int x = threadIdx.x + u * NT;
+            if (C * DK / VE == PF::NV * NT || x < C * DK / VE) {
+                const int row = x / VPR, vc = x % VPR;
+                *reinterpret_cast<u32x4*>(&sm.in.k[row][vc * VE]) = pf.k[u];
+                if constexpr (TP) *reinterpret_cast<u32x4*>(&sm.in.q[row][vc * VE]) = pf.q[u];
+            }
+        }
+        if (wave == 0) {
+            // running log-decay g_j = sum_{i <= j} ln a_i (rows past n: a = 1)
+            float x = lane < it.n ? __logf(fmaxf(pf.a, kMinDecay)) : 0.f;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            if (lane < C) sm.g[lane] = x;
+        } else if (wave == 1) {
+            if (lane < C) sm.beta[lane] = lane < it.n ? pf.a : 0.f;
+        }
+    };
+
+    PF pf;
+    long item = blockIdx.x;
+    PrepItem cur = locate(item);
+    fetch(pf, cur);
+    for (; item < n_items; item += gridDim.x) {
+    stage(pf, cur);
+    lds_barrier();
+    const PrepItem nxt = locate(item + gridDim.x);
+    fetch(pf, nxt);                      // in flight during this item's arithmetic
+    if (cur.ok) {
+    const int h = cur.h;
+    const int ci = cur.ci;
+    const int n = cur.n;
+    (void)n;
     const AccPos ap;
     uint16_t* planes = static_cast<uint16_t*>(Tws) + (static_cast<long>(ci) * H + h) * 4 * C * C;
     // A = strictly-lower(diag(beta) (K K^T .* D)), fp32, held in registers
@@ -237,6 +316,10 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
             O::store4(planes + r * C + c, planes + C * C + r * C + c, tv);
         }
     }
+    }  // cur.ok
+    lds_barrier();                       // T read out: the next item may restage
+    cur = nxt;
+    }  // items
 }
 
 // ------------------------------------------------------------------ 3. serial chunk loop
@@ -769,7 +852,10 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
     if (a.n_tokens > 0) {
-        hipLaunchKernelGGL((gdn_prep<DK, C, TI, FAST>), dim3(static_cast<unsigned>(mc * a.n_heads)),
+        // persistent: as many workgroups as are resident at once, striding over
+        // the (chunk, head) items
+        const long prep_blocks = std::min<long>(mc * a.n_heads, kPrepBlocks);
+        hipLaunchKernelGGL((gdn_prep<DK, C, TI, FAST>), dim3(static_cast<unsigned>(prep_blocks)),
                            dim3(NT), 0, s, static_cast<const T*>(a.k), static_cast<const T*>(a.q),
                            a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, off,
                            static_cast<void*>(Tws));
