@@ -166,6 +166,28 @@ def bench_decode(torch, G, synth, dev, steps, warmup, gdn):
     return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
 
 
+def bench_decode_multi(torch, G, synth, dev, steps, warmup, gdn):
+    """Speculative-decoding verification: 256 requests x 4 draft tokens x 16
+    heads, the state after every position kept in its own slot (1280-slot
+    pool); one read and four writes of each 64 KiB head state per call."""
+    w = synth.decode_multi(seed=6, n_req=256, n_tok=4, n_slots=1280, gdn=gdn)
+    R, J, H, d = w.q.shape
+    q, k, v, a = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha)
+    b = dev(w.beta) if gdn else None
+    pool = dev(w.pool)
+    slots, pos = dev(w.slot_idx), dev(w.extra["pos_slots"])
+    o = torch.empty((R, J, H, d), dtype=torch.bfloat16, device="cuda:0")
+
+    def step(i):
+        if gdn:
+            G.gdn_decode_multi(q, k, v, a, b, pool, slots, pos, o=o)
+        else:
+            G.gla_decode_multi(q, k, v, a, pool, slots, pos, o=o)
+    ms = timed(torch, step, steps, warmup)
+    nbytes = R * H * ((1 + J) * d * d * 4 + J * (4 * d * 2 + (8 if gdn else 4)))
+    return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
+
+
 def bench_mixed(torch, G, synth, dev, steps, warmup):
     import numpy as np
     from gated_deltanet_gla_amd.step import MixedStep
@@ -259,6 +281,10 @@ def main():
         res["gdn_decode"] = bench_decode(torch, G, synth, dev, K, W, gdn=True)
         print(f"# decode {res['gla_decode']['ms']:.3f} / {res['gdn_decode']['ms']:.3f} ms",
               file=sys.stderr, flush=True)
+        res["gla_decode_multi"] = bench_decode_multi(torch, G, synth, dev, K, W, gdn=False)
+        res["gdn_decode_multi"] = bench_decode_multi(torch, G, synth, dev, K, W, gdn=True)
+        print(f"# decode multi {res['gla_decode_multi']['ms']:.3f} / "
+              f"{res['gdn_decode_multi']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("all", "gdn_prefill"):
         res["gdn_prefill"] = bench_gdn_prefill(torch, G, synth, dev, K, W)
         print(f"# gdn prefill {res['gdn_prefill']['ms']:.3f} ms", file=sys.stderr, flush=True)
@@ -303,6 +329,15 @@ def main():
                              "gdn": res["gdn_decode"]["GBps"] / HBM_PEAK_GBPS},
             "ms": {"gla": res["gla_decode"]["ms"], "gdn": res["gdn_decode"]["ms"]},
             "workload": "256 requests x 16 heads, 128x128 fp32 states, 1024-slot pool, in place"}
+    if "gla_decode_multi" in res:
+        out["decode_multi_hbm_GBps"] = {
+            k: res[f"{k}_decode_multi"]["GBps"] for k in ("gla", "gdn")}
+        out["decode_multi_hbm_GBps"].update({
+            "frac_of_peak": {k: res[f"{k}_decode_multi"]["GBps"] / HBM_PEAK_GBPS
+                             for k in ("gla", "gdn")},
+            "ms": {k: res[f"{k}_decode_multi"]["ms"] for k in ("gla", "gdn")},
+            "workload": "256 requests x 4 draft tokens x 16 heads, 128x128 fp32 states, state "
+                        "after every position kept (1280-slot pool)"})
     other = {}
     if "gdn_prefill" in res:
         r = res["gdn_prefill"]

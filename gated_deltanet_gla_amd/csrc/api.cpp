@@ -64,7 +64,7 @@ int check_decode(const void* q, const void* k, const void* v, const float* alpha
 
 extern "C" {
 
-const char* gla_version(void) { return "0.1.0"; }
+const char* gla_version(void) { return "0.2.0"; }
 
 const char* gla_status_string(int status) {
     switch (status) {
@@ -135,7 +135,7 @@ int gla_decode_step(const void* q, const void* k, const void* v, const float* al
                           out_dtype, state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK || n_req == 0) return st;
     gla::DecodeArgs a{q, k, v, alpha, nullptr, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
-                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o};
+                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o, 1, nullptr};
     return hip_status(gla::launch_gla_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -147,8 +147,50 @@ int gdn_decode_step(const void* q, const void* k, const void* v, const float* al
                           state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK || n_req == 0) return st;
     gla::DecodeArgs a{q, k, v, alpha, beta, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
-                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o};
+                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o, 1, nullptr};
     return hip_status(gla::launch_gdn_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int gla_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
+                     int32_t n_req, int32_t n_tok, int32_t n_heads, int32_t dk, int32_t dv,
+                     gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool, int32_t n_slots,
+                     const int32_t* slot_idx, const int32_t* pos_slots, void* o, void* stream) {
+    if (n_tok < 0 || (n_tok > 0 && n_req > 0 && !pos_slots)) return n_tok < 0 ? GLA_ESHAPE : GLA_EPTR;
+    if (static_cast<long>(n_req) * n_tok * n_heads > kMaxWork) return GLA_ESHAPE;
+    int st = check_decode(q, k, v, alpha, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
+                          out_dtype, state_pool, n_slots, slot_idx, o);
+    if (st != GLA_OK || n_req == 0 || n_tok == 0) return st;
+    gla::DecodeArgs a{q, k, v, alpha, nullptr, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
+                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o, n_tok, pos_slots};
+    return hip_status(gla::launch_gla_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* beta, int32_t n_req, int32_t n_tok, int32_t n_heads, int32_t dk,
+                     int32_t dv, gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,
+                     int32_t n_slots, const int32_t* slot_idx, const int32_t* pos_slots, void* o,
+                     void* stream) {
+    if (n_tok < 0 || (n_tok > 0 && n_req > 0 && !pos_slots)) return n_tok < 0 ? GLA_ESHAPE : GLA_EPTR;
+    if (static_cast<long>(n_req) * n_tok * n_heads > kMaxWork) return GLA_ESHAPE;
+    int st = check_decode(q, k, v, alpha, beta, true, n_req, n_heads, dk, dv, in_dtype, out_dtype,
+                          state_pool, n_slots, slot_idx, o);
+    if (st != GLA_OK || n_req == 0 || n_tok == 0) return st;
+    gla::DecodeArgs a{q, k, v, alpha, beta, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
+                      out_dtype == GLA_BF16, state_pool, n_slots, slot_idx, o, n_tok, pos_slots};
+    return hip_status(gla::launch_gdn_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, int32_t dk, int32_t dv,
+                   const int32_t* src_slots, const int32_t* dst_slots, int32_t n_copy,
+                   void* stream) {
+    if (n_copy < 0 || n_heads < 1 || n_slots < 0 || !is_dim(dk) || !is_dim(dv)) return GLA_ESHAPE;
+    if (n_copy == 0) return GLA_OK;
+    if (n_slots < 1) return GLA_ESHAPE;
+    if (!state_pool || !src_slots || !dst_slots) return GLA_EPTR;
+    const long pieces = (static_cast<long>(n_heads) * dk * dv / 4 + 1023) / 1024;
+    if (static_cast<long>(n_copy) * pieces > kMaxWork) return GLA_ESHAPE;
+    gla::CopyArgs a{state_pool, n_slots, n_heads, dk, dv, src_slots, dst_slots, n_copy};
+    return hip_status(gla::launch_state_copy(a, static_cast<hipStream_t>(stream)));
 }
 
 int causal_conv1d_fwd(const void* x, const float* w, const int32_t* cu_seqlens, int32_t n_seqs,

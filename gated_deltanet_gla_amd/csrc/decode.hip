@@ -135,6 +135,163 @@ decode_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __rest
     }
 }
 
+// Several consecutive tokens per request (the draft tokens that one
+// speculative-decoding verification step scores), with the state after
+// every position kept.  Section "Speculative decoding and PD
+// disaggregation": a rejected draft token must not leave its update in the
+// request's state, so each position's state goes to a slot of its own
+// (pos_slots[r * n_tok + j]; negative = not kept) and the request's own slot
+// is only read.  The state is streamed in once, stays in registers across
+// the n_tok steps and is streamed out once per kept position.
+//
+// q/k staging and the reduction buffers are double-buffered by token
+// parity, so each token needs two barriers: one after its q/k land in LDS,
+// one after the partial sums of the reduction are written.
+template <int DK, int DV, class TI, class TO, bool GDN>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
+decode_multi_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __restrict__ k,
+                    const typename TI::T* __restrict__ v, const float* __restrict__ alpha,
+                    const float* __restrict__ beta, float* __restrict__ pool, int n_heads,
+                    int n_tok, int n_slots, const int32_t* __restrict__ slot_idx,
+                    const int32_t* __restrict__ pos_slots, typename TO::T* __restrict__ o) {
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int NT = Sh::NT, CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT;
+    constexpr int NRED = GDN ? 2 : 1;
+
+    const int h = blockIdx.x % n_heads;
+    const int r = blockIdx.x / n_heads;
+    const int t = threadIdx.x;
+    const int cg = t % CG;
+    const int rg = t / CG;
+
+    const int slot = slot_idx[r];
+    if (slot < 0 || slot >= n_slots) return;
+
+    __shared__ float s_q[2][DK];
+    __shared__ float s_k[2][DK];
+    __shared__ f32x4 s_red[2][NRED][RG][CG];
+    __shared__ float s_qk[2][RG];
+
+    const long head_elems = static_cast<long>(DK) * DV;
+    const float* __restrict__ S_in = pool + (static_cast<long>(slot) * n_heads + h) * head_elems;
+
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S_in + row * DV + cg * 4));
+    }
+
+    for (int j = 0; j < n_tok; ++j) {
+        const int par = j & 1;
+        const long tok = (static_cast<long>(r) * n_tok + j) * n_heads + h;
+        for (int i = t; i < DK; i += NT) {
+            s_q[par][i] = TI::load(q, tok * DK + i);
+            s_k[par][i] = TI::load(k, tok * DK + i);
+        }
+        const f32x4 v4 = Vec4<TI>::load(v + tok * DV + cg * 4);
+        const float a = alpha[tok];
+        const int ps = pos_slots[static_cast<long>(r) * n_tok + j];
+        const bool keep = ps >= 0 && ps < n_slots;
+        float* __restrict__ S_out = pool + (static_cast<long>(keep ? ps : 0) * n_heads + h) * head_elems;
+        __syncthreads();
+
+        if constexpr (!GDN) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + RG * i;
+                s[i] = a * s[i] + s_k[par][row] * v4;
+                acc += s_q[par][row] * s[i];
+            }
+            if (keep) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int row = rg + RG * i;
+                    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S_out + row * DV + cg * 4));
+                }
+            }
+            s_red[par][0][rg][cg] = acc;
+            __syncthreads();
+            if (rg == 0) {
+                f32x4 tot = s_red[par][0][0][cg];
+#pragma unroll
+                for (int jj = 1; jj < RG; ++jj) tot += s_red[par][0][jj][cg];
+                Vec4<TO>::store(o + tok * DV + cg * 4, tot);
+            }
+        } else {
+            const float b = beta[tok];
+            f32x4 accq = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
+            float qk = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + RG * i;
+                accq += s_q[par][row] * s[i];
+                acck += s_k[par][row] * s[i];
+                qk += s_q[par][row] * s_k[par][row];
+            }
+            s_red[par][0][rg][cg] = accq;
+            s_red[par][1][rg][cg] = acck;
+            if (cg == 0) s_qk[par][rg] = qk;
+            __syncthreads();
+            f32x4 p = s_red[par][1][0][cg];
+#pragma unroll
+            for (int jj = 1; jj < RG; ++jj) p += s_red[par][1][jj][cg];
+            const f32x4 u = b * (v4 - a * p);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + RG * i;
+                s[i] = a * s[i] + s_k[par][row] * u;
+            }
+            if (keep) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int row = rg + RG * i;
+                    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S_out + row * DV + cg * 4));
+                }
+            }
+            if (rg == 0) {
+                f32x4 qs = s_red[par][0][0][cg];
+                float qkt = s_qk[par][0];
+#pragma unroll
+                for (int jj = 1; jj < RG; ++jj) {
+                    qs += s_red[par][0][jj][cg];
+                    qkt += s_qk[par][jj];
+                }
+                Vec4<TO>::store(o + tok * DV + cg * 4, a * qs + qkt * u);
+            }
+        }
+    }
+}
+
+// Plain copy of whole slots (all heads): dst_slots[i] <- src_slots[i].  One
+// workgroup per (pair, 16 KiB piece); 16-byte loads and stores.  A pair with
+// either slot out of range is skipped.
+__global__ void __launch_bounds__(256)
+state_copy_kernel(float* __restrict__ pool, long slot_vec4, int pieces, int n_slots,
+                  const int32_t* __restrict__ src_slots, const int32_t* __restrict__ dst_slots) {
+    const int pair = blockIdx.x / pieces;
+    const int piece = blockIdx.x % pieces;
+    const int src = src_slots[pair];
+    const int dst = dst_slots[pair];
+    if (src < 0 || src >= n_slots || dst < 0 || dst >= n_slots || src == dst) return;
+    const f32x4* __restrict__ from = reinterpret_cast<const f32x4*>(pool) + src * slot_vec4;
+    f32x4* __restrict__ to = reinterpret_cast<f32x4*>(pool) + dst * slot_vec4;
+    constexpr int kPer = 4;     // 4 vectors per thread: 16 KiB per workgroup
+    const long base = static_cast<long>(piece) * (256 * kPer) + threadIdx.x;
+    f32x4 x[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const long e = base + i * 256;
+        x[i] = e < slot_vec4 ? __builtin_nontemporal_load(from + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const long e = base + i * 256;
+        if (e < slot_vec4) __builtin_nontemporal_store(x[i], to + e);
+    }
+}
+
 template <int DK, int DV, class TI, class TO, bool GDN>
 hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
     using Sh = DecodeShape<DK, DV>;
@@ -146,12 +303,28 @@ hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DK, int DV, class TI, class TO, bool GDN>
+hipError_t launch4_multi(const DecodeArgs& a, hipStream_t s) {
+    using Sh = DecodeShape<DK, DV>;
+    dim3 grid(a.n_heads * a.n_req);
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, TI, TO, GDN>), grid, dim3(Sh::NT), 0, s,
+                       static_cast<const typename TI::T*>(a.q), static_cast<const typename TI::T*>(a.k),
+                       static_cast<const typename TI::T*>(a.v), a.alpha, a.beta, a.pool, a.n_heads,
+                       a.n_tok, a.n_slots, a.slot_idx, a.pos_slots, static_cast<typename TO::T*>(a.o));
+    return hipGetLastError();
+}
+
+template <int DK, int DV, class TI, class TO, bool GDN>
+hipError_t launch_io(const DecodeArgs& a, hipStream_t s) {
+    return a.pos_slots ? launch4_multi<DK, DV, TI, TO, GDN>(a, s) : launch4<DK, DV, TI, TO, GDN>(a, s);
+}
+
 template <int DK, int DV, bool GDN>
 hipError_t launch_dt(const DecodeArgs& a, hipStream_t s) {
     if (a.in_bf16) {
-        return a.out_bf16 ? launch4<DK, DV, BF16, BF16, GDN>(a, s) : launch4<DK, DV, BF16, F32, GDN>(a, s);
+        return a.out_bf16 ? launch_io<DK, DV, BF16, BF16, GDN>(a, s) : launch_io<DK, DV, BF16, F32, GDN>(a, s);
     }
-    return a.out_bf16 ? launch4<DK, DV, F32, BF16, GDN>(a, s) : launch4<DK, DV, F32, F32, GDN>(a, s);
+    return a.out_bf16 ? launch_io<DK, DV, F32, BF16, GDN>(a, s) : launch_io<DK, DV, F32, F32, GDN>(a, s);
 }
 
 template <int DK, bool GDN>
@@ -167,7 +340,7 @@ hipError_t launch_dv(const DecodeArgs& a, hipStream_t s) {
 
 template <bool GDN>
 hipError_t launch(const DecodeArgs& a, hipStream_t s) {
-    if (a.n_req == 0 || a.n_heads == 0) return hipSuccess;
+    if (a.n_req == 0 || a.n_heads == 0 || a.n_tok == 0) return hipSuccess;
     switch (a.dk) {
         case 16: return launch_dv<16, GDN>(a, s);
         case 32: return launch_dv<32, GDN>(a, s);
@@ -181,5 +354,14 @@ hipError_t launch(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s) { return launch<false>(a, s); }
 hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s) { return launch<true>(a, s); }
+
+hipError_t launch_state_copy(const CopyArgs& a, hipStream_t s) {
+    if (a.n_copy == 0) return hipSuccess;
+    const long slot_vec4 = static_cast<long>(a.n_heads) * a.dk * a.dv / 4;
+    const int pieces = static_cast<int>((slot_vec4 + 1023) / 1024);
+    hipLaunchKernelGGL(state_copy_kernel, dim3(a.n_copy * pieces), dim3(256), 0, s, a.pool, slot_vec4,
+                       pieces, a.n_slots, a.src_slots, a.dst_slots);
+    return hipGetLastError();
+}
 
 }  // namespace gla

@@ -20,6 +20,16 @@ struct DecodeArgs {
     int n_slots;
     const int32_t* slot_idx;
     void* o;
+    int n_tok;                    // tokens per request (1 for a single step)
+    const int32_t* pos_slots;     // [n_req, n_tok] slots for per-position states, or NULL
+};
+
+struct CopyArgs {
+    float* pool;
+    int n_slots, n_heads, dk, dv;
+    const int32_t* src_slots;
+    const int32_t* dst_slots;
+    int n_copy;
 };
 
 struct ChunkArgs {
@@ -55,6 +65,7 @@ struct ConvArgs {
 
 hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_state_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s);
 size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
 bool gla_seg_supported(const ChunkArgs& a);

@@ -128,6 +128,64 @@ def gdn_decode_step(q, k, v, alpha, beta, state_pool, slot_idx, *, out_dtype=Non
     return o
 
 
+def _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots, out_dtype, o):
+    for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 4),
+                        (k, "k", (torch.float32, torch.bfloat16), 4),
+                        (v, "v", (torch.float32, torch.bfloat16), 4),
+                        (alpha, "alpha", torch.float32, 3),
+                        (state_pool, "state_pool", torch.float32, 4),
+                        (slot_idx, "slot_idx", torch.int32, 1),
+                        (pos_slots, "pos_slots", torch.int32, 2)]:
+        _check(t, n, d, nd)
+    R, J, H, dk = q.shape
+    dv = v.shape[3]
+    if tuple(pos_slots.shape) != (R, J) or slot_idx.shape[0] != R:
+        raise ValueError("pos_slots must be [n_req, n_tok] and slot_idx [n_req]")
+    out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
+    if o is None:
+        o = torch.empty((R, J, H, dv), dtype=out_dtype, device=q.device)
+    _check(o, "o", out_dtype, 4)
+    return R, J, H, dk, dv, out_dtype, o
+
+
+def gla_decode_multi(q, k, v, alpha, state_pool, slot_idx, pos_slots, *, out_dtype=None, o=None):
+    """n_tok GLA tokens per request from state_pool[slot_idx]; the state after
+    position j goes to state_pool[pos_slots[:, j]] (negative = not kept).
+    q, k [R, n_tok, H, dk]; v [R, n_tok, H, dv]; alpha [R, n_tok, H]. Returns o."""
+    R, J, H, dk, dv, out_dtype, o = _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots,
+                                                  out_dtype, o)
+    _lib.call("gla_decode_multi", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), R, J,
+              H, dk, dv, _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(), state_pool.shape[0],
+              slot_idx.data_ptr(), pos_slots.data_ptr(), o.data_ptr(), _stream(q.device))
+    return o
+
+
+def gdn_decode_multi(q, k, v, alpha, beta, state_pool, slot_idx, pos_slots, *, out_dtype=None,
+                     o=None):
+    """Gated DeltaNet form of gla_decode_multi; beta [R, n_tok, H]."""
+    R, J, H, dk, dv, out_dtype, o = _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots,
+                                                  out_dtype, o)
+    _check(beta, "beta", torch.float32, 3)
+    _lib.call("gdn_decode_multi", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              beta.data_ptr(), R, J, H, dk, dv, _DT[q.dtype], _DT[out_dtype],
+              state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(), pos_slots.data_ptr(),
+              o.data_ptr(), _stream(q.device))
+    return o
+
+
+def gla_state_copy(state_pool, src_slots, dst_slots):
+    """state_pool[dst_slots[i]] <- state_pool[src_slots[i]] (all heads), in place."""
+    _check(state_pool, "state_pool", torch.float32, 4)
+    _check(src_slots, "src_slots", torch.int32, 1)
+    _check(dst_slots, "dst_slots", torch.int32, 1)
+    if src_slots.shape != dst_slots.shape:
+        raise ValueError("src_slots and dst_slots must have the same length")
+    n, H, dk, dv = state_pool.shape
+    _lib.call("gla_state_copy", state_pool.data_ptr(), n, H, dk, dv, src_slots.data_ptr(),
+              dst_slots.data_ptr(), src_slots.shape[0], _stream(state_pool.device))
+    return state_pool
+
+
 def causal_conv1d_fwd(x, w, cu_seqlens, conv_cache, slot_idx, *, zero_init=False, y=None):
     """Depthwise causal conv with per-slot cache (updated in place); returns y."""
     _check(x, "x", (torch.float32, torch.bfloat16), 2)

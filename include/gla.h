@@ -169,6 +169,63 @@ GLA_API int gdn_decode_step(const void* q, const void* k, const void* v, const f
                     void* o, void* stream);
 
 /*
+ * gla_decode_multi -- n_tok consecutive GLA tokens per request with the
+ * state after every position kept, for speculative decoding ("Speculative
+ * decoding and PD disaggregation": verifying draft tokens runs several
+ * recurrence steps, and a rejected token's update must be undone, which for
+ * a recurrent state means keeping the state of every position or replaying).
+ * For request r, starting from S = pool[slot_idx[r]]:
+ *   for j = 0 .. n_tok-1:
+ *     S <- alpha[r,j] S + k[r,j]^T v[r,j];   o[r,j] = q[r,j] S;
+ *     if 0 <= pos_slots[r*n_tok + j] < n_slots:  pool[pos_slots[r*n_tok + j]] <- S
+ * pool[slot_idx[r]] is only read (unless pos_slots names it), so the
+ * request's committed state survives a rejected draft.  After verifying
+ * that a of the n_tok tokens are accepted, the caller makes
+ * pos_slots[r*n_tok + a-1] the request's slot (or copies it back with
+ * gla_state_copy); with a = 0 nothing changes.  A negative pos_slots entry
+ * keeps no state for that position.
+ * q, k [n_req, n_tok, n_heads, dk]; v, o [n_req, n_tok, n_heads, dv];
+ * alpha [n_req, n_tok, n_heads] fp32; slot_idx [n_req]; pos_slots
+ * [n_req, n_tok] int32 in device memory.  All slots named
+ * by pos_slots must be distinct and distinct from the other requests'
+ * slot_idx (a request may name its own slot).  With n_tok = 1 and
+ * pos_slots = slot_idx this is gla_decode_step.
+ */
+GLA_API int gla_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
+                     int32_t n_req, int32_t n_tok, int32_t n_heads, int32_t dk, int32_t dv,
+                     gla_dtype in_dtype, gla_dtype out_dtype,
+                     float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                     const int32_t* pos_slots, void* o, void* stream);
+
+/*
+ * gdn_decode_multi -- the Gated DeltaNet form of gla_decode_multi: per
+ * position p = k S; u = beta (v - alpha p); S <- alpha S + k^T u; o = q S.
+ * beta [n_req, n_tok, n_heads] fp32.
+ */
+GLA_API int gdn_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
+                     const float* beta,
+                     int32_t n_req, int32_t n_tok, int32_t n_heads, int32_t dk, int32_t dv,
+                     gla_dtype in_dtype, gla_dtype out_dtype,
+                     float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                     const int32_t* pos_slots, void* o, void* stream);
+
+/*
+ * gla_state_copy -- pool[dst_slots[i]] <- pool[src_slots[i]] (all heads) for
+ * i < n_copy: commits an accepted speculative position into a fixed slot,
+ * or gives a new request its own copy of a saved prefix state (section
+ * "Prefix caching has to be redone": a state summarises the whole prefix,
+ * so it is reused whole, at the position where it was saved, and each
+ * request that continues from it needs a copy because decoding updates the
+ * state in place).  src/dst_slots [n_copy]
+ * int32, device memory.  A destination must not be the source of another
+ * pair in the same call; pairs with a slot outside [0, n_slots) or with
+ * src == dst are skipped.
+ */
+GLA_API int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, int32_t dk,
+                   int32_t dv, const int32_t* src_slots, const int32_t* dst_slots,
+                   int32_t n_copy, void* stream);
+
+/*
  * causal_conv1d_fwd -- depthwise causal convolution of width W with a
  * per-request cache of the last W-1 inputs ("Two ways to write the same
  * computation", last paragraph; "The real model's ledger": an engine keeps

@@ -24,7 +24,7 @@ Parity status of every function is listed in ``PINS`` below: each entry names
 the pin tests that fix it against something other than itself.
 """
 from .recurrence import (gla_sequence, gdn_sequence, gla_varlen, gdn_varlen,
-                         gla_decode, gdn_decode)
+                         gla_decode, gdn_decode, gla_decode_multi, gdn_decode_multi, state_copy)
 from .conv import causal_conv1d
 from .chunked import gla_chunked, gdn_chunked
 
@@ -36,6 +36,10 @@ PINS = {
     "gla_varlen / gdn_varlen": "per-sequence equality with *_sequence, untouched slots, "
                                "empty sequences",
     "gla_decode / gdn_decode": "one step of *_sequence",
+    "gla_decode_multi / gdn_decode_multi": "each kept state equals the varlen prefill of the "
+                                           "same prefix, closed form of the GLA state after j "
+                                           "tokens, rollback-and-replay, untouched slots",
+    "state_copy": "element values and untouched slots by construction of the pool",
     "causal_conv1d": "numpy.convolve per channel, segmented == one pass == token by token",
     "gla_chunked": "page toy example; equality with the recurrence",
     "gdn_chunked": "equality with the recurrence (the chunked GDN form itself is not on the "

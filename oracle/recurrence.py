@@ -8,7 +8,11 @@ section "Two ways to write the same computation":
     gated variant multiplies in alpha_t as well (read: on the old state);
   - the recurrent algorithm: for each t, update S, then o_t = q_t S.
 Section "Speculative decoding and PD disaggregation": batched decode reads
-and writes each request's state in a pool by slot index.
+and writes each request's state in a pool by slot index; verifying draft
+tokens needs the state of every draft position kept (or a replay), since an
+applied update cannot be taken back.  Section "Prefix caching has to be
+redone": a saved state is reused whole, and each continuation needs its own
+copy.
 
 Shapes (packed, token-major): q, k [T, H, dk]; v [T, H, dv]; alpha, beta
 [T, H]; S [H, dk, dv].  Inputs of any float dtype are upcast to fp64.
@@ -106,3 +110,52 @@ def gdn_decode(q, k, v, alpha, beta, pool, slot_idx):
     R = np.shape(q)[0]
     cu = np.arange(R + 1)
     return gdn_varlen(q, k, v, alpha, beta, cu, pool, slot_idx, zero_init=False)
+
+
+def _decode_multi(step_fn, q, k, v, gates, pool, slot_idx, pos_slots):
+    """n_tok tokens per request r (axis 1 of q), starting from
+    pool[slot_idx[r]]; after token j the state is stored in
+    pool[pos_slots[r, j]] when that index is in range.  The request's own
+    slot is not written unless pos_slots names it.  Returns (o, pool_out)."""
+    q = _f64(q)
+    R, J, H, _ = q.shape
+    dv = np.shape(v)[3]
+    n_slots = np.shape(pool)[0]
+    pool_in = _f64(pool)
+    pool_out = pool_in.copy()
+    o = np.zeros((R, J, H, dv))
+    for r in range(R):
+        S = pool_in[int(slot_idx[r])].copy()
+        for j in range(J):
+            # one recurrence step = the sequence function over one token
+            o1, S = step_fn(q[r, j:j + 1], k[r, j:j + 1], v[r, j:j + 1],
+                            *[g[r, j:j + 1] for g in gates], S0=S)
+            o[r, j] = o1[0]
+            ps = int(pos_slots[r, j])
+            if 0 <= ps < n_slots:
+                pool_out[ps] = S
+    return o, pool_out
+
+
+def gla_decode_multi(q, k, v, alpha, pool, slot_idx, pos_slots):
+    """Several GLA tokens per request with every position's state kept:
+    q, k [R, J, H, dk]; v [R, J, H, dv]; alpha [R, J, H]; pos_slots [R, J]."""
+    return _decode_multi(gla_sequence, q, k, v, [_f64(alpha)], pool, slot_idx, pos_slots)
+
+
+def gdn_decode_multi(q, k, v, alpha, beta, pool, slot_idx, pos_slots):
+    """Gated DeltaNet form of gla_decode_multi; beta [R, J, H]."""
+    return _decode_multi(gdn_sequence, q, k, v, [_f64(alpha), _f64(beta)], pool, slot_idx,
+                         pos_slots)
+
+
+def state_copy(pool, src_slots, dst_slots):
+    """pool[dst[i]] <- pool[src[i]] for every pair with both slots in range
+    (all reads before any write).  Returns the new pool (fp64)."""
+    pool_in = _f64(pool)
+    out = pool_in.copy()
+    n = pool_in.shape[0]
+    for s, d in zip(np.asarray(src_slots).tolist(), np.asarray(dst_slots).tolist()):
+        if 0 <= s < n and 0 <= d < n:
+            out[d] = pool_in[s]
+    return out

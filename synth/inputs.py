@@ -21,7 +21,7 @@ import numpy as np
 __all__ = [
     "bf16_bits", "bf16_to_f32", "round_bf16", "sigmoid",
     "Workload", "page_toy_example", "prefill_gla", "prefill_gdn", "decode",
-    "mixed_varlen", "random_varlen", "loguniform_lengths", "page_toy_workload",
+    "mixed_varlen", "random_varlen", "loguniform_lengths", "page_toy_workload", "decode_multi",
 ]
 
 
@@ -298,3 +298,35 @@ def mixed_varlen(seed: int = 5, n_prefill: int = 48, n_decode: int = 512, H: int
                     chunk=64, extra={"x": x, "w": w, "conv_cache": conv_cache,
                                      "n_prefill": n_prefill, "n_decode": n_decode,
                                      "lengths": lens})
+
+
+def decode_multi(seed: int = 6, n_req: int = 256, n_tok: int = 4, H: int = 16, dk: int = 128,
+                 dv: int = 128, n_slots: int = 2048, gdn: bool = False,
+                 dtype: str = "bf16") -> Workload:
+    """n_tok draft tokens per request (speculative-decoding verification)
+    with a slot for every position's state.  q, k, v [n_req, n_tok, H, d]
+    with the decode value recipe (q = N(0,1)/sqrt(dk), k as q or
+    L2-normalised for GDN, v = N(0,1)); alpha, beta [n_req, n_tok, H] as
+    decode; pool [n_slots, H, dk, dv] ~ N(0, 0.05).  From one permutation
+    of the slots: slot_idx = its first n_req entries, and
+    ``extra['pos_slots']`` [n_req, n_tok] the next n_req * n_tok."""
+    assert n_slots >= n_req * (n_tok + 1)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    M = n_req * n_tok
+    q, k, v = _qkv(rng, M, H, dk, dv, dtype, normalise_k=False)
+    if gdn:
+        k = _l2_normalise(rng.standard_normal((M, H, dk), dtype=np.float32))
+        if dtype == "bf16":
+            k = _bf16(k)
+    alpha, beta = _gates(rng, M, H, True)
+    pool = rng.standard_normal((n_slots, H, dk, dv), dtype=np.float32) * np.float32(0.05)
+    perm = rng.permutation(n_slots).astype(np.int32)
+    slots = perm[:n_req].copy()
+    pos = perm[n_req:n_req + M].reshape(n_req, n_tok).copy()
+    r4 = lambda x: x.reshape(n_req, n_tok, *x.shape[1:]).copy()  # noqa: E731
+    cu = (np.arange(n_req + 1) * n_tok).astype(np.int32)
+    return Workload(name=f"{'gdn' if gdn else 'gla'}-decode-multi-{n_req}req-x{n_tok}-H{H}-"
+                         f"d{dk}x{dv}-pool{n_slots}",
+                    dtype=dtype, q=r4(q), k=r4(k), v=r4(v), alpha=r4(alpha),
+                    beta=r4(beta) if gdn else None, cu_seqlens=cu, pool=pool, slot_idx=slots,
+                    zero_init=False, chunk=1, extra={"pos_slots": pos, "perm": perm})

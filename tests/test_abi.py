@@ -130,3 +130,29 @@ def test_product_path_has_no_oracle_or_fallback():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in src.replace("no oracle", ""), fn
+
+
+def test_decode_multi_and_copy_validation():
+    L = _lib.lib()
+    # q k v alpha R J H dk dv idt odt pool n_slots slots pos o stream
+    base = [FAKE, FAKE, FAKE, FAKE, 8, 4, 16, 128, 128, 1, 1, FAKE, 64, FAKE, FAKE, FAKE, None]
+    for i, bad, st in [(0, None, -1), (14, None, -1), (15, None, -1), (11, None, -1),
+                       (5, -1, -2), (7, 100, -2), (9, 7, -3), (12, 0, -2), (4, -2, -2)]:
+        args = list(base)
+        args[i] = bad
+        assert L.gla_decode_multi(*args) == st, (i, bad)
+    gargs = base[:4] + [None] + base[4:]
+    assert L.gdn_decode_multi(*gargs) == -1
+    # nothing to do: OK without touching pointers
+    assert L.gla_decode_multi(None, None, None, None, 0, 4, 16, 128, 128, 1, 1, None, 4, None,
+                              None, None, None) == 0
+    assert L.gla_decode_multi(FAKE, FAKE, FAKE, FAKE, 8, 0, 16, 128, 128, 1, 1, FAKE, 4, FAKE,
+                              None, FAKE, None) == 0
+    # pool n_slots H dk dv src dst n stream
+    cbase = [FAKE, 64, 16, 128, 128, FAKE, FAKE, 3, None]
+    for i, bad, st in [(0, None, -1), (5, None, -1), (6, None, -1), (3, 48, -2), (7, -1, -2),
+                       (1, 0, -2), (2, 0, -2)]:
+        args = list(cbase)
+        args[i] = bad
+        assert L.gla_state_copy(*args) == st, (i, bad)
+    assert L.gla_state_copy(None, 0, 16, 128, 128, None, None, 0, None) == 0

@@ -229,3 +229,125 @@ def test_conv_segments_and_token_by_token():
         assert np.array_equal(yt[0], y[t])
     assert np.array_equal(c, c1)
     assert np.array_equal(c1[[0, 1]], cache[[0, 1]])
+
+
+# ------------------------------------------------------------------ multi-token decode, state copy
+def _multi_inputs(seed, R=3, J=5, H=2, dk=6, dv=5, n_slots=24):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((R, J, H, dk))
+    k = r.standard_normal((R, J, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((R, J, H, dv))
+    a = 1.0 / (1.0 + np.exp(-(r.standard_normal((R, J, H)) + 2.0)))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal((R, J, H))))
+    pool = r.standard_normal((n_slots, H, dk, dv)) * 0.3
+    perm = r.permutation(n_slots)
+    slots = perm[:R].astype(np.int32)
+    pos = perm[R:R + R * J].reshape(R, J).astype(np.int32)
+    return q, k, v, a, b, pool, slots, pos
+
+
+def test_gla_decode_multi_kept_states_closed_form():
+    """Speculative decoding ("Speculative decoding and PD disaggregation"):
+    the state kept after draft position j is
+        S_j = (prod_{i<=j} a_i) S_0 + sum_{s<=j} (prod_{i=s+1..j} a_i) k_s^T v_s,
+    with the products taken directly, and o_j = q_j S_j."""
+    q, k, v, a, _, pool, slots, pos = _multi_inputs(20)
+    o, out = oracle.gla_decode_multi(q, k, v, a, pool, slots, pos)
+    R, J, H = a.shape
+    worst = 0.0
+    for r in range(R):
+        for j in range(J):
+            for h in range(H):
+                S = np.prod(a[r, :j + 1, h]) * pool[slots[r], h]
+                for s in range(j + 1):
+                    S = S + np.prod(a[r, s + 1:j + 1, h]) * np.outer(k[r, s, h], v[r, s, h])
+                worst = max(worst, np.abs(out[pos[r, j], h] - S).max(),
+                            np.abs(o[r, j, h] - q[r, j, h] @ S).max())
+    assert worst <= pins.TOL
+    # the requests' own slots are only read
+    assert np.array_equal(out[slots], pool[slots])
+
+
+def test_gdn_decode_multi_kept_states_matrix_form():
+    """Gated DeltaNet draft positions: each kept state is the literal
+    a (I - b k^T k) S + b k^T v with d_k x d_k matrices ("Two ways to write
+    the same computation", DeltaNet update with the gate)."""
+    q, k, v, a, b, pool, slots, pos = _multi_inputs(21)
+    o, out = oracle.gdn_decode_multi(q, k, v, a, b, pool, slots, pos)
+    R, J, H, dk = q.shape
+    worst = 0.0
+    for r in range(R):
+        for h in range(H):
+            S = pool[slots[r], h].copy()
+            for j in range(J):
+                kk = k[r, j, h][:, None]
+                S = a[r, j, h] * (np.eye(dk) - b[r, j, h] * kk @ kk.T) @ S \
+                    + b[r, j, h] * kk @ v[r, j, h][None, :]
+                worst = max(worst, np.abs(out[pos[r, j], h] - S).max(),
+                            np.abs(o[r, j, h] - q[r, j, h] @ S).max())
+    assert worst <= pins.TOL
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+def test_decode_multi_rollback_and_prefix_prefill(kind):
+    """Each kept state equals a prefill of the same prefix passing only the
+    state ("Chunked prefill comes for free"), and rolling back to an
+    accepted position then replaying the rejected tokens reproduces the
+    later kept states bitwise."""
+    q, k, v, a, b, pool, slots, pos = _multi_inputs(22)
+    R, J = a.shape[:2]
+    if kind == "gla":
+        o, out = oracle.gla_decode_multi(q, k, v, a, pool, slots, pos)
+    else:
+        o, out = oracle.gdn_decode_multi(q, k, v, a, b, pool, slots, pos)
+    for r in range(R):
+        for j in range(J):
+            if kind == "gla":
+                op, Sp = oracle.gla_sequence(q[r, :j + 1], k[r, :j + 1], v[r, :j + 1],
+                                             a[r, :j + 1], S0=pool[slots[r]])
+            else:
+                op, Sp = oracle.gdn_sequence(q[r, :j + 1], k[r, :j + 1], v[r, :j + 1],
+                                             a[r, :j + 1], b[r, :j + 1], S0=pool[slots[r]])
+            assert np.array_equal(out[pos[r, j]], Sp)
+            assert np.array_equal(o[r, :j + 1], op)
+        # accept 2 tokens, then replay the rest from the kept state
+        acc = 2
+        rest = slice(acc, J)
+        if kind == "gla":
+            _, Sr = oracle.gla_sequence(q[r, rest], k[r, rest], v[r, rest], a[r, rest],
+                                        S0=out[pos[r, acc - 1]])
+        else:
+            _, Sr = oracle.gdn_sequence(q[r, rest], k[r, rest], v[r, rest], a[r, rest],
+                                        b[r, rest], S0=out[pos[r, acc - 1]])
+        assert np.array_equal(Sr, out[pos[r, J - 1]])
+    # untouched slots: neither a request's slot nor a kept position
+    named = set(slots.tolist()) | set(pos.ravel().tolist())
+    for s in range(pool.shape[0]):
+        if s not in named:
+            assert np.array_equal(out[s], pool[s])
+
+
+def test_decode_multi_skips_unkept_positions_and_own_slot():
+    q, k, v, a, _, pool, slots, pos = _multi_inputs(23)
+    pos = pos.copy()
+    pos[:, :-1] = -1                       # keep only the last position
+    pos[0, -1] = slots[0]                  # request 0 commits in place
+    o, out = oracle.gla_decode_multi(q, k, v, a, pool, slots, pos)
+    _, S_last = oracle.gla_sequence(q[0], k[0], v[0], a[0], S0=pool[slots[0]])
+    assert np.array_equal(out[slots[0]], S_last)
+    assert np.array_equal(out[slots[1:]], pool[slots[1:]])
+
+
+def test_state_copy_reads_before_writes():
+    """Prefix reuse ("Prefix caching has to be redone"): a continuation gets
+    its own whole copy of the saved state; slots not named are unchanged."""
+    r = np.random.default_rng(24)
+    pool = r.standard_normal((8, 2, 4, 3))
+    out = oracle.state_copy(pool, np.array([1, 5, 2]), np.array([4, 1, 7]))
+    assert np.array_equal(out[4], pool[1]) and np.array_equal(out[1], pool[5])
+    assert np.array_equal(out[7], pool[2])
+    for s in (0, 2, 3, 5, 6):
+        assert np.array_equal(out[s], pool[s])
+    # out-of-range pairs are skipped
+    assert np.array_equal(oracle.state_copy(pool, np.array([-1, 9]), np.array([0, 0])), pool)
