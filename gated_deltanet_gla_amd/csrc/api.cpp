@@ -45,6 +45,19 @@ int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
     return GLA_OK;
 }
 
+// Checkpoint arguments: an interval that is a positive multiple of the
+// chunk, a non-negative stride, and a slot table whenever the stride is not 0.
+int check_ckpt(int32_t n_seqs, int32_t chunk, int32_t interval, const int32_t* slots,
+               int32_t stride) {
+    if (stride < 0) return GLA_ESHAPE;
+    if (stride == 0) return GLA_OK;
+    if (!is_chunk(chunk)) return GLA_ECHUNK;
+    if (interval < chunk || interval % chunk != 0) return GLA_ECHUNK;
+    if (static_cast<long>(n_seqs) * stride > kMaxWork) return GLA_ESHAPE;
+    if (n_seqs > 0 && !slots) return GLA_EPTR;
+    return GLA_OK;
+}
+
 int check_decode(const void* q, const void* k, const void* v, const float* alpha,
                  const float* beta, bool need_beta, int32_t n_req, int32_t n_heads, int32_t dk,
                  int32_t dv, int in_dtype, int out_dtype, const float* pool, int32_t n_slots,
@@ -93,12 +106,17 @@ size_t gdn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_hea
     return gla::gdn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
 }
 
-int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
-                  int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype,
-                  float* state_pool, int32_t n_slots, const int32_t* slot_idx, uint32_t flags,
-                  void* o, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_chunk(q, k, v, alpha, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads, dk,
+int gla_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* alpha,
+                       const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                       int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype,
+                       gla_dtype out_dtype, float* state_pool, int32_t n_slots,
+                       const int32_t* slot_idx, uint32_t flags, int32_t ckpt_interval,
+                       const int32_t* ckpt_slots, int32_t ckpt_stride, void* o, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    int st = check_ckpt(n_seqs, chunk, ckpt_interval, ckpt_slots, ckpt_stride);
+    if (st != GLA_OK) return st;
+    if (ckpt_stride == 0) ckpt_slots = nullptr;
+    st = check_chunk(q, k, v, alpha, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads, dk,
                          dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (n_seqs == 0) return GLA_OK;
@@ -106,16 +124,22 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
     gla::ChunkArgs a{q, k, v, alpha, nullptr, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                      in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
-                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes};
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes,
+                     ckpt_slots, ckpt_interval, ckpt_stride};
     return hip_status(gla::launch_gla_chunk(a, static_cast<hipStream_t>(stream)));
 }
 
-int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                  const float* beta, const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
-                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype,
-                  gla_dtype out_dtype, float* state_pool, int32_t n_slots, const int32_t* slot_idx,
-                  uint32_t flags, void* o, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_chunk(q, k, v, alpha, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
+int gdn_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const int32_t* cu_seqlens, int32_t n_seqs,
+                       int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                       gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool, int32_t n_slots,
+                       const int32_t* slot_idx, uint32_t flags, int32_t ckpt_interval,
+                       const int32_t* ckpt_slots, int32_t ckpt_stride, void* o, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    int st = check_ckpt(n_seqs, chunk, ckpt_interval, ckpt_slots, ckpt_stride);
+    if (st != GLA_OK) return st;
+    if (ckpt_stride == 0) ckpt_slots = nullptr;
+    st = check_chunk(q, k, v, alpha, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
                          chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (n_seqs == 0) return GLA_OK;
@@ -123,8 +147,29 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
     gla::ChunkArgs a{q, k, v, alpha, beta, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                      in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
-                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes};
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes,
+                     ckpt_slots, ckpt_interval, ckpt_stride};
     return hip_status(gla::launch_gdn_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                  int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx, uint32_t flags,
+                  void* o, void* workspace, size_t workspace_bytes, void* stream) {
+    return gla_chunk_fwd_ckpt(q, k, v, alpha, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
+                              in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, chunk,
+                              nullptr, 0, o, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype,
+                  gla_dtype out_dtype, float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_chunk_fwd_ckpt(q, k, v, alpha, beta, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
+                              chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags,
+                              chunk, nullptr, 0, o, workspace, workspace_bytes, stream);
 }
 
 int gla_decode_step(const void* q, const void* k, const void* v, const float* alpha, int32_t n_req,

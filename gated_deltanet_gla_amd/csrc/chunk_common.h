@@ -232,6 +232,38 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// State checkpoints ("Prefix caching has to be redone": a prefix can be
+// reused only where a whole state was saved, so an engine saves states at
+// block boundaries while it prefills).  Checkpoint j of sequence b is the
+// state after (j + 1) * interval tokens of the sequence in this call and
+// goes to pool slot slots[b * stride + j]; interval is a multiple of the
+// chunk, so every checkpoint falls on the end of a full chunk.
+struct Ckpt {
+    const int32_t* slots;   // [n_seqs, stride] or NULL (no checkpoints)
+    int interval;           // tokens
+    int stride;             // checkpoint entries per sequence
+};
+
+// Pool slot of the checkpoint after `pos` tokens of sequence b, or -1 (no
+// checkpoints, not a checkpoint position, beyond the stride, or a slot
+// outside the pool).  Uniform over the workgroup.
+__device__ __forceinline__ int ckpt_slot(const Ckpt& ck, int b, int pos, int n_slots) {
+    if (ck.slots == nullptr || pos <= 0 || pos % ck.interval != 0) return -1;
+    const int j = pos / ck.interval - 1;
+    if (j >= ck.stride) return -1;
+    const int s = ck.slots[static_cast<long>(b) * ck.stride + j];
+    return (s >= 0 && s < n_slots) ? s : -1;
+}
+
+// An opaque copy of x: code that uses the copy cannot be hoisted above this
+// point.  Checkpoint stores use it for their per-lane offsets, which are
+// otherwise loop-invariant and would be computed once and held in registers
+// across the whole chunk loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // blockIdx -> logical work id, grouping consecutive logical ids on one XCD
 // (blocks are dealt to the 8 XCDs round-robin) so that work sharing inputs
 // through L2 lands on the same XCD.

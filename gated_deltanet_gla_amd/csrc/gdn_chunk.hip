@@ -351,7 +351,7 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                  int n_tokens, int H, float* __restrict__ pool, int n_slots,
                  const int32_t* __restrict__ slot_idx, int zero_init,
                  const int32_t* __restrict__ off, long n_chunks_max, const float* __restrict__ Tws,
-                 typename TO::T* __restrict__ o) {
+                 Ckpt ck, typename TO::T* __restrict__ o) {
     constexpr bool F32 = (TI::bytes == 4);
     using O = Op<F32>;
     using Sm = GdnSmem<DK, BV, C, F32>;
@@ -508,6 +508,21 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                             &sm.udt[LO][nt * 16][0], LT, C);
             }
         }
+        // checkpoint: this wave's tiles of the state after the chunk
+        const int cs = c0 + C <= L ? ckpt_slot(ck, b, c0 + C, n_slots) : -1;
+        if (cs >= 0) {
+            float* Sc = pool + (static_cast<long>(cs) * H + h) * DK * DV +
+                        opaque(ap.row0 * DV + col0 + ap.col);
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                const int t = wave + NW * i;
+                if (t < ST) {
+                    const int mt = t / BT, nt = t % BT;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sc[(mt * 16 + r) * DV + nt * 16] = S[i][r];
+                }
+            }
+        }
     }
 
 #pragma unroll
@@ -573,14 +588,15 @@ struct GdnFastPrefetch {
     int n;
 };
 
-template <int DK, int DV, int C, class TO>
+template <int DK, int DV, int C, class TO, bool CKPT>
 __global__ void __launch_bounds__(FT)
 gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const float* __restrict__ alpha,
                 const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
                 float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
                 int zero_init, const int32_t* __restrict__ off, const int32_t* __restrict__ order,
-                long n_chunks_max, const uint16_t* __restrict__ TP, typename TO::T* __restrict__ o) {
+                long n_chunks_max, const uint16_t* __restrict__ TP, Ckpt ck,
+                typename TO::T* __restrict__ o) {
     using Sm = GdnFastSmem<DK, C>;
     using PF = GdnFastPrefetch<C, DK>;
     using O = Op<false>;
@@ -814,6 +830,14 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 S = mfma_bf16(a, frag_kc_split(&sm.udt[1][0][0], LT, 0, 32 * ks), S);
             }
         }
+        // checkpoint: this wave's state tile after chunk c (block-uniform test)
+        const int cs = CKPT && (c + 1) * C <= L ? ckpt_slot(ck, b, (c + 1) * C, n_slots) : -1;
+        if (CKPT && cs >= 0 && has_tile) {
+            float* Sc = pool + (static_cast<long>(cs) * H + h) * DK * DV +
+                        opaque((wave * 16 + ap.row0) * DV + col0 + ap.col);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sc[r * DV] = S[r];
+        }
         write_state();
         load_tp(tpc, c + 2);
         lds_barrier();
@@ -865,11 +889,18 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     if constexpr (FAST) {
         const long groups = (static_cast<long>(a.n_seqs) * a.n_heads + 7) / 8 * 8;
         const long blocks = groups * (DV / 16);
-        hipLaunchKernelGGL((gdn_fast_kernel<DK, DV, C, TO>), dim3(static_cast<unsigned>(blocks)), dim3(FT),
-                           0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs,
-                           a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, order,
-                           mc, reinterpret_cast<const uint16_t*>(Tws), static_cast<typename TO::T*>(a.o));
+        const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
+        auto serial = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(FT), 0, s,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs,
+                               a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off,
+                               order, mc, reinterpret_cast<const uint16_t*>(Tws), ck,
+                               static_cast<typename TO::T*>(a.o));
+        };
+        // the checkpoint stores are compiled in only where they are asked for
+        if (ck.slots) serial(gdn_fast_kernel<DK, DV, C, TO, true>);
+        else serial(gdn_fast_kernel<DK, DV, C, TO, false>);
         return hipGetLastError();
     } else {
         const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
@@ -877,6 +908,7 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
                            dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens,
                            a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, off, mc, Tws,
+                           Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride},
                            static_cast<typename TO::T*>(a.o));
         return hipGetLastError();
     }

@@ -132,7 +132,7 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                  const typename TI::T* __restrict__ v, const float* __restrict__ alpha,
                  const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
                  float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
-                 int zero_init, typename TO::T* __restrict__ o) {
+                 int zero_init, Ckpt ck, typename TO::T* __restrict__ o) {
     constexpr bool F32 = (TI::bytes == 4);
     using O = Op<F32>;
     using E = typename O::E;
@@ -404,6 +404,21 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                     }
                 }
             }
+            // checkpoint: this wave's tiles of the state after chunk c
+            const int cs = (c + 1) * C <= L ? ckpt_slot(ck, b, (c + 1) * C, n_slots) : -1;
+            if (cs >= 0) {
+                float* Sc = pool + (static_cast<long>(cs) * H + h) * DK * DV +
+                            opaque(ap.row0 * DV + col0 + ap.col);
+#pragma unroll
+                for (int i = 0; i < SMAX; ++i) {
+                    if (i < tcnt) {
+                        const int t = tbeg + i;
+                        const int mt = t / BT, nt = t % BT;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Sc[(mt * 16 + r) * DV + nt * 16] = S[i][r];
+                    }
+                }
+            }
             if (c + 1 < nchunks && NBUF == 2) {
                 stage(buf[(c + 1) % NBUF]);
                 if (c + 2 < nchunks) fetch(c + 2);
@@ -441,6 +456,7 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
                        dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
                        a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init,
+                       Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride},
                        static_cast<typename TO::T*>(a.o));
     return hipGetLastError();
 }

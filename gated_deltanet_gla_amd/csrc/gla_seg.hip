@@ -373,13 +373,13 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
 }
 
 // ------------------------------------------------------------------ pass 2
-template <class TO>
+template <class TO, bool CKPT>
 __global__ void __launch_bounds__(ST)
 gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
             const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
             int H, float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
             int zero_init, int lseg, const float* __restrict__ wstate, const float* __restrict__ wlam,
-            typename TO::T* __restrict__ o) {
+            Ckpt ck, typename TO::T* __restrict__ o) {
     __shared__ int sh[SW + 4];
     SegGeom sg;
     if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
@@ -563,6 +563,18 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         seg_update_mfma_half(S, up, 1);
         seg_stage_gates(buf[(c + 1) & 1], pf);
         seg_fetch(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
+        // checkpoint: this wave's columns of the state after chunk c (the
+        // segment starts sg.g * lseg tokens into its sequence)
+        const int cs = CKPT && n == SC ? ckpt_slot(ck, sg.b, sg.g * lseg + (c + 1) * SC, n_slots) : -1;
+        if (CKPT && cs >= 0) {
+            float* Sc = pool + (static_cast<long>(cs) * H + sg.h) * SD * SD +
+                        opaque(ap.row0 * SD + col + ap.col);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sc[(mt * 16 + r) * SD] = S[mt][r];
+            }
+        }
         lds_barrier();
     }
     if (nch > 0) flush_o(nch - 1);
@@ -614,16 +626,20 @@ hipError_t launch_gla_seg(const ChunkArgs& a, hipStream_t s) {
                        a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
+    auto out_pass = [&](auto kern, auto* o) {
+        hipLaunchKernelGGL(kern, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
+                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
+                           a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
+                           a.zero_init, lseg, wstate, wlam, ck, o);
+    };
+    // the checkpoint stores are compiled in only where they are asked for
     if (a.out_bf16) {
-        hipLaunchKernelGGL((gla_seg_out<BF16>), grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
-                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
-                           a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, wstate, wlam, static_cast<uint16_t*>(a.o));
+        if (ck.slots) out_pass(gla_seg_out<BF16, true>, static_cast<uint16_t*>(a.o));
+        else out_pass(gla_seg_out<BF16, false>, static_cast<uint16_t*>(a.o));
     } else {
-        hipLaunchKernelGGL((gla_seg_out<F32>), grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
-                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
-                           a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, wstate, wlam, static_cast<float*>(a.o));
+        if (ck.slots) out_pass(gla_seg_out<F32, true>, static_cast<float*>(a.o));
+        else out_pass(gla_seg_out<F32, false>, static_cast<float*>(a.o));
     }
     return hipGetLastError();
 }

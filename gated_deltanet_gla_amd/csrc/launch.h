@@ -48,6 +48,9 @@ struct ChunkArgs {
     void* o;
     void* workspace;
     size_t workspace_bytes;
+    const int32_t* ckpt_slots;    // [n_seqs, ckpt_stride] or NULL
+    int ckpt_interval;            // tokens, a multiple of chunk
+    int ckpt_stride;
 };
 
 struct ConvArgs {

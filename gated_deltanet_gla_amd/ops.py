@@ -88,6 +88,55 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, *, chu
     return o
 
 
+def _ckpt_args(ckpt_slots, ckpt_interval, n_seqs):
+    _check(ckpt_slots, "ckpt_slots", torch.int32, 2)
+    if ckpt_slots.shape[0] != n_seqs:
+        raise ValueError("ckpt_slots must be [n_seqs, ckpt_stride]")
+    return int(ckpt_interval), ckpt_slots.data_ptr(), ckpt_slots.shape[1]
+
+
+def gla_chunk_fwd_ckpt(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, ckpt_slots, ckpt_interval,
+                       *, chunk=64, out_dtype=None, zero_init=False, o=None, workspace=None):
+    """gla_chunk_fwd that also writes the state after every ckpt_interval
+    tokens of sequence b to state_pool[ckpt_slots[b, j]] (j-th checkpoint;
+    negative = not saved).  ckpt_slots [n_seqs, stride] int32."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    B = cu_seqlens.shape[0] - 1
+    iv, cp, cs = _ckpt_args(ckpt_slots, ckpt_interval, B)
+    need = _lib.lib().gla_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _lib.call("gla_chunk_fwd_ckpt", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              cu_seqlens.data_ptr(), B, N, H, dk, dv, chunk, _DT[q.dtype], _DT[out_dtype],
+              state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
+              _lib.GLA_ZERO_INIT if zero_init else 0, iv, cp, cs, o.data_ptr(), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream(q.device))
+    return o
+
+
+def gdn_chunk_fwd_ckpt(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, ckpt_slots,
+                       ckpt_interval, *, chunk=64, out_dtype=None, zero_init=False, o=None,
+                       workspace=None):
+    """Gated DeltaNet form of gla_chunk_fwd_ckpt."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    _check(beta, "beta", torch.float32, 2)
+    B = cu_seqlens.shape[0] - 1
+    iv, cp, cs = _ckpt_args(ckpt_slots, ckpt_interval, B)
+    need = _lib.lib().gdn_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _lib.call("gdn_chunk_fwd_ckpt", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              beta.data_ptr(), cu_seqlens.data_ptr(), B, N, H, dk, dv, chunk, _DT[q.dtype],
+              _DT[out_dtype], state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
+              _lib.GLA_ZERO_INIT if zero_init else 0, iv, cp, cs, o.data_ptr(), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream(q.device))
+    return o
+
+
 def workspace_bytes(kind, n_seqs, n_tokens, n_heads, dk, dv, chunk):
     fn = {"gla": "gla_chunk_workspace_bytes", "gdn": "gdn_chunk_workspace_bytes"}[kind]
     return getattr(_lib.lib(), fn)(n_seqs, n_tokens, n_heads, dk, dv, chunk)

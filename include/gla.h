@@ -134,6 +134,42 @@ GLA_API int gdn_chunk_fwd(const void* q, const void* k, const void* v, const flo
                   uint32_t flags, void* o,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gla_chunk_fwd_ckpt / gdn_chunk_fwd_ckpt -- the chunked prefills above,
+ * also saving state checkpoints at block boundaries ("Prefix caching has to
+ * be redone": a linear-attention state summarises its whole prefix, so a
+ * prefix can be reused only at a position where a whole state was saved;
+ * engines save one at every block boundary, or selectively).  Checkpoint j
+ * of sequence b is the state after (j + 1) * ckpt_interval tokens of that
+ * sequence in this call (counted from its first token in the call), written
+ * to pool[ckpt_slots[b * ckpt_stride + j]] for every j < ckpt_stride with
+ * (j + 1) * ckpt_interval <= its length.  ckpt_interval must be a positive
+ * multiple of chunk (GLA_ECHUNK otherwise), so checkpoints fall on chunk
+ * ends.  ckpt_slots [n_seqs, ckpt_stride] int32 in device memory; an entry
+ * outside [0, n_slots) saves nothing.  Checkpoint slots must be distinct
+ * and distinct from every slot_idx entry of the call.  ckpt_stride = 0
+ * (ckpt_slots may then be NULL) is the plain call.  A saved state continues
+ * exactly like the sequence it came from: a later call that starts from
+ * it gives the results of the uncut prompt, up to rounding.
+ */
+GLA_API int gla_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* alpha,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, int32_t ckpt_interval, const int32_t* ckpt_slots,
+                  int32_t ckpt_stride, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+GLA_API int gdn_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, int32_t ckpt_interval, const int32_t* ckpt_slots,
+                  int32_t ckpt_stride, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes the chunked calls need for these sizes (an upper bound
  * that does not depend on the contents of cu_seqlens).  0 = none. */
 GLA_API size_t gla_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,

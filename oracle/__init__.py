@@ -24,7 +24,8 @@ Parity status of every function is listed in ``PINS`` below: each entry names
 the pin tests that fix it against something other than itself.
 """
 from .recurrence import (gla_sequence, gdn_sequence, gla_varlen, gdn_varlen,
-                         gla_decode, gdn_decode, gla_decode_multi, gdn_decode_multi, state_copy)
+                         gla_decode, gdn_decode, gla_decode_multi, gdn_decode_multi, state_copy,
+                         gla_varlen_ckpt, gdn_varlen_ckpt)
 from .conv import causal_conv1d
 from .chunked import gla_chunked, gdn_chunked
 
@@ -40,6 +41,11 @@ PINS = {
                                            "same prefix, closed form of the GLA state after j "
                                            "tokens, rollback-and-replay, untouched slots",
     "state_copy": "element values and untouched slots by construction of the pool",
+    "gla_varlen_ckpt / gdn_varlen_ckpt": "checkpoints against the GLA closed form and the "
+                                         "literal GDN matrix update; continuing from a copy "
+                                         "of a checkpoint equals the uncut run (the page's "
+                                         "prefix-cache demonstration); outputs equal "
+                                         "*_varlen",
     "causal_conv1d": "numpy.convolve per channel, segmented == one pass == token by token",
     "gla_chunked": "page toy example; equality with the recurrence",
     "gdn_chunked": "equality with the recurrence (the chunked GDN form itself is not on the "

@@ -159,3 +159,46 @@ def state_copy(pool, src_slots, dst_slots):
         if 0 <= s < n and 0 <= d < n:
             out[d] = pool_in[s]
     return out
+
+
+def _varlen_ckpt(step_fn, q, k, v, gates, cu_seqlens, pool, slot_idx, ckpt_slots, interval,
+                 zero_init):
+    """Packed varlen recurrence that also saves the state after every
+    ``interval`` tokens of sequence b into pool[ckpt_slots[b, j]] (j-th
+    checkpoint; entries outside the pool save nothing).  Each sequence is
+    run piece by piece, handing only the state on, and the state at the end
+    of each full piece is the checkpoint."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    slots = np.asarray(slot_idx, dtype=np.int64)
+    ck = np.asarray(ckpt_slots, dtype=np.int64)
+    T, H, _ = np.shape(q)
+    dv = np.shape(v)[2]
+    o = np.zeros((T, H, dv))
+    pool_in = _f64(pool)
+    pool_out = pool_in.copy()
+    n_slots = pool_in.shape[0]
+    for b in range(cu.shape[0] - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        S = np.zeros_like(pool_in[slots[b]]) if zero_init else pool_in[slots[b]].copy()
+        for j, p in enumerate(range(s, e, interval)):
+            pe = min(p + interval, e)
+            o[p:pe], S = step_fn(q[p:pe], k[p:pe], v[p:pe], *[g[p:pe] for g in gates], S0=S)
+            if pe - p == interval and j < ck.shape[1] and 0 <= ck[b, j] < n_slots:
+                pool_out[ck[b, j]] = S
+        pool_out[slots[b]] = S
+    return o, pool_out
+
+
+def gla_varlen_ckpt(q, k, v, alpha, cu_seqlens, pool, slot_idx, ckpt_slots, interval,
+                    zero_init=False):
+    """gla_varlen plus state checkpoints every ``interval`` tokens
+    (ckpt_slots [B, stride])."""
+    return _varlen_ckpt(gla_sequence, q, k, v, [_f64(alpha)], cu_seqlens, pool, slot_idx,
+                        ckpt_slots, interval, zero_init)
+
+
+def gdn_varlen_ckpt(q, k, v, alpha, beta, cu_seqlens, pool, slot_idx, ckpt_slots, interval,
+                    zero_init=False):
+    """gdn_varlen plus state checkpoints every ``interval`` tokens."""
+    return _varlen_ckpt(gdn_sequence, q, k, v, [_f64(alpha), _f64(beta)], cu_seqlens, pool,
+                        slot_idx, ckpt_slots, interval, zero_init)

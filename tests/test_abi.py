@@ -156,3 +156,28 @@ def test_decode_multi_and_copy_validation():
         args[i] = bad
         assert L.gla_state_copy(*args) == st, (i, bad)
     assert L.gla_state_copy(None, 0, 16, 128, 128, None, None, 0, None) == 0
+
+
+def test_chunk_ckpt_validation():
+    L = _lib.lib()
+    a = _chunk_args()
+    ws = L.gla_chunk_workspace_bytes(2, 10, 4, 128, 128, 64)
+
+    def gla(interval, slots, stride, C=64):
+        return L.gla_chunk_fwd_ckpt(a["q"], a["k"], a["v"], a["alpha"], a["cu"], a["B"], a["N"],
+                                    a["H"], a["dk"], a["dv"], C, a["idt"], a["odt"], a["pool"],
+                                    a["n_slots"], a["slots"], 0, interval, slots, stride, a["o"],
+                                    FAKE, ws, None)
+    assert gla(64, FAKE, -1) == _lib.GLA_ESHAPE
+    assert gla(96, FAKE, 2) == _lib.GLA_ECHUNK          # not a multiple of the chunk
+    assert gla(32, FAKE, 2) == _lib.GLA_ECHUNK          # shorter than the chunk
+    assert gla(0, FAKE, 2) == _lib.GLA_ECHUNK
+    assert gla(128, None, 2) == _lib.GLA_EPTR
+    assert gla(128, FAKE, 1 << 30) == _lib.GLA_ESHAPE
+    gargs = [a["q"], a["k"], a["v"], a["alpha"], FAKE, a["cu"], a["B"], a["N"], a["H"], a["dk"],
+             a["dv"], 64, a["idt"], a["odt"], a["pool"], a["n_slots"], a["slots"], 0, 100, FAKE, 2,
+             a["o"], FAKE, 1 << 40, None]
+    assert L.gdn_chunk_fwd_ckpt(*gargs) == _lib.GLA_ECHUNK
+    gargs[19] = None
+    gargs[18] = 128
+    assert L.gdn_chunk_fwd_ckpt(*gargs) == _lib.GLA_EPTR

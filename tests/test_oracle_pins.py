@@ -351,3 +351,79 @@ def test_state_copy_reads_before_writes():
         assert np.array_equal(out[s], pool[s])
     # out-of-range pairs are skipped
     assert np.array_equal(oracle.state_copy(pool, np.array([-1, 9]), np.array([0, 0])), pool)
+
+
+# ------------------------------------------------------------------ prefill checkpoints
+def _ckpt_inputs(seed, lengths=(37, 0, 64, 50), H=2, dk=5, dv=4, interval=16, stride=3):
+    r = np.random.default_rng(seed)
+    N = sum(lengths)
+    q = r.standard_normal((N, H, dk))
+    k = r.standard_normal((N, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((N, H, dv))
+    a = 1.0 / (1.0 + np.exp(-(r.standard_normal((N, H)) + 2.0)))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal((N, H))))
+    B = len(lengths)
+    n_slots = B + B * stride + 2
+    pool = r.standard_normal((n_slots, H, dk, dv)) * 0.3
+    perm = r.permutation(n_slots)
+    slots = perm[:B].astype(np.int32)
+    ck = perm[B:B + B * stride].reshape(B, stride).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return q, k, v, a, b, pool, slots, ck, cu, interval
+
+
+def test_gla_ckpt_states_closed_form():
+    """Saved states ("Prefix caching has to be redone": a state can be
+    reused only where it was saved) are the GLA state after that many
+    tokens, here from its closed form with direct products; outputs and
+    final states equal the plain varlen run."""
+    q, k, v, a, _, pool, slots, ck, cu, iv = _ckpt_inputs(25)
+    o, out = oracle.gla_varlen_ckpt(q, k, v, a, cu, pool, slots, ck, iv)
+    o2, out2 = oracle.gla_varlen(q, k, v, a, cu, pool, slots)
+    assert np.array_equal(o, o2) and np.array_equal(out[slots], out2[slots])
+    worst = 0.0
+    n_saved = 0
+    for bi in range(len(slots)):
+        s0, e0 = int(cu[bi]), int(cu[bi + 1])
+        for j in range(ck.shape[1]):
+            p = (j + 1) * iv
+            if p > e0 - s0:
+                assert np.array_equal(out[ck[bi, j]], pool[ck[bi, j]])   # not reached: untouched
+                continue
+            n_saved += 1
+            for h in range(q.shape[1]):
+                S = np.prod(a[s0:s0 + p, h]) * pool[slots[bi], h]
+                for t in range(s0, s0 + p):
+                    S = S + np.prod(a[t + 1:s0 + p, h]) * np.outer(k[t, h], v[t, h])
+                worst = max(worst, np.abs(out[ck[bi, j], h] - S).max())
+    assert n_saved == 2 + 0 + 3 + 3 and worst <= pins.TOL
+
+
+def test_gdn_ckpt_states_matrix_form_and_reuse():
+    """Gated DeltaNet checkpoints against the literal d_k x d_k update, and
+    the page's prefix-cache demonstration: continuing from a copy of a
+    checkpoint gives the same as the uncut prompt (there it printed True for
+    both requests)."""
+    q, k, v, a, b, pool, slots, ck, cu, iv = _ckpt_inputs(26)
+    o, out = oracle.gdn_varlen_ckpt(q, k, v, a, b, cu, pool, slots, ck, iv)
+    dk = q.shape[2]
+    worst = 0.0
+    for bi in range(len(slots)):
+        s0, e0 = int(cu[bi]), int(cu[bi + 1])
+        for h in range(q.shape[1]):
+            S = pool[slots[bi], h].copy()
+            for t in range(s0, e0):
+                kk = k[t, h][:, None]
+                S = a[t, h] * (np.eye(dk) - b[t, h] * kk @ kk.T) @ S + b[t, h] * kk @ v[t, h][None, :]
+                p = t + 1 - s0
+                if p % iv == 0 and p // iv - 1 < ck.shape[1]:
+                    worst = max(worst, np.abs(out[ck[bi, p // iv - 1], h] - S).max())
+        # reuse: continue from the saved state after 16 tokens
+        if e0 - s0 >= iv:
+            cut = s0 + iv
+            o_rest, S_rest = oracle.gdn_sequence(q[cut:e0], k[cut:e0], v[cut:e0], a[cut:e0],
+                                                 b[cut:e0], S0=out[ck[bi, 0]].copy())
+            assert np.array_equal(o_rest, o[cut:e0])
+            assert np.array_equal(S_rest, out[slots[bi]])
+    assert worst <= pins.TOL
