@@ -27,6 +27,7 @@ from .recurrence import (gla_sequence, gdn_sequence, gla_varlen, gdn_varlen,
                          gla_decode, gdn_decode, gla_decode_multi, gdn_decode_multi, state_copy,
                          gla_varlen_ckpt, gdn_varlen_ckpt)
 from .conv import causal_conv1d
+from .linear import phi, lin_attn_sequence, lin_attn_varlen, lin_attn_decode
 from .chunked import gla_chunked, gdn_chunked
 
 PINS = {
@@ -46,6 +47,10 @@ PINS = {
                                          "of a checkpoint equals the uncut run (the page's "
                                          "prefix-cache demonstration); outputs equal "
                                          "*_varlen",
+    "lin_attn_sequence": "the page's parallel kernelised formula (O(T^2) double sum), "
+                         "convex-combination bounds, constant values, phi's closed form",
+    "lin_attn_varlen / lin_attn_decode": "per-sequence equality with lin_attn_sequence, "
+                                         "segmentation through the pool",
     "causal_conv1d": "numpy.convolve per channel, segmented == one pass == token by token",
     "gla_chunked": "page toy example; equality with the recurrence",
     "gdn_chunked": "equality with the recurrence (the chunked GDN form itself is not on the "

@@ -427,3 +427,67 @@ def test_gdn_ckpt_states_matrix_form_and_reuse():
             assert np.array_equal(o_rest, o[cut:e0])
             assert np.array_equal(S_rest, out[slots[bi]])
     assert worst <= pins.TOL
+
+
+# ------------------------------------------------------------------ normalised linear attention
+def _lin_inputs(seed, T=20, H=2, dk=5, dv=4):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((T, H, dk)), r.standard_normal((T, H, dk)),
+            r.standard_normal((T, H, dv)))
+
+
+def test_phi_is_elu_plus_one():
+    """phi(x) = elu(x) + 1 (page "Long context, fast inference, smart
+    decoding, and life beyond attention", listing "Linear attention as a
+    running state"): torch's elu on the CPU, plus one."""
+    import torch
+    x = np.linspace(-30, 30, 2001)
+    ref = torch.nn.functional.elu(torch.from_numpy(x)).numpy() + 1.0
+    assert np.abs(oracle.phi(x) - ref).max() <= 1e-15
+    assert (oracle.phi(x) > 0).all()
+
+
+def test_lin_attn_equals_kernelised_parallel_form():
+    """The recurrence equals the kernelised attention written as a double
+    sum over j <= i (same page, section "Linear attention: removing softmax
+    entirely"), which the listing states it is equivalent to."""
+    q, k, v = _lin_inputs(30)
+    o, S, z = oracle.lin_attn_sequence(q, k, v)
+    T, H, _ = q.shape
+    pq, pk = oracle.phi(q), oracle.phi(k)
+    worst = 0.0
+    for h in range(H):
+        for i in range(T):
+            w = np.array([pq[i, h] @ pk[j, h] for j in range(i + 1)])
+            ref = (w[:, None] * v[:i + 1, h]).sum(0) / (w.sum() + 1e-6)
+            worst = max(worst, np.abs(o[i, h] - ref).max())
+        worst = max(worst, np.abs(S[h] - pk[:, h].T @ v[:, h]).max(),
+                    np.abs(z[h] - pk[:, h].sum(0)).max())
+    assert worst <= pins.TOL
+
+
+def test_lin_attn_convex_combination_and_constants():
+    """Positive weights: each output lies between the smallest and largest
+    value seen so far (up to eps), and constant values are returned as they
+    are (scaled by den / (den + eps))."""
+    q, k, v = _lin_inputs(31, T=40)
+    o, _, _ = oracle.lin_attn_sequence(q, k, v, eps=0.0)
+    lo = np.minimum.accumulate(v, axis=0)
+    hi = np.maximum.accumulate(v, axis=0)
+    assert (o >= lo - 1e-9).all() and (o <= hi + 1e-9).all()
+    vc = np.full_like(v, 2.5)
+    oc, _, _ = oracle.lin_attn_sequence(q, k, vc, eps=0.0)
+    assert np.abs(oc - 2.5).max() <= 1e-12
+
+
+def test_lin_attn_segments_through_pool():
+    """Splitting a sequence and passing (S, z) through the pool gives the
+    same result (state hand-off, "Chunked prefill comes for free")."""
+    q, k, v = _lin_inputs(32, T=30)
+    o, S, z = oracle.lin_attn_sequence(q, k, v)
+    H, dk, dv = 2, 5, 4
+    pool, zpool = np.zeros((3, H, dk, dv)), np.zeros((3, H, dk))
+    o1, pool, zpool = oracle.lin_attn_varlen(q[:11], k[:11], v[:11], [0, 11], pool, zpool, [2])
+    o2, pool, zpool = oracle.lin_attn_varlen(q[11:], k[11:], v[11:], [0, 19], pool, zpool, [2])
+    assert np.array_equal(np.concatenate([o1, o2]), o)
+    assert np.array_equal(pool[2], S) and np.array_equal(zpool[2], z)
