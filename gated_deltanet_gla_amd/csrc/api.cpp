@@ -20,6 +20,12 @@ constexpr long kMaxWork = 1L << 26;
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_EHIP; }
 
+// Stands for the gate argument of the validators when the operation has no
+// gate (normalised linear attention); never dereferenced.
+const float* const kNoGate = reinterpret_cast<const float*>(alignof(float));
+
+bool is_eps(float eps) { return eps >= 0.f && eps <= 3.0e38f; }
+
 int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, bool need_beta, const int32_t* cu_seqlens, int32_t n_seqs,
                 int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
@@ -39,8 +45,9 @@ int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
     }
     if (n_tokens > 0) {
         if (n_seqs < 1) return GLA_ESHAPE;
-        if (!q || !k || !v || !alpha || !o) return GLA_EPTR;
-        if (need_beta && !beta) return GLA_EPTR;
+        if (!q || !k || !v || !o) return GLA_EPTR;
+        if (alpha == kNoGate) return GLA_OK;
+        if (!alpha || (need_beta && !beta)) return GLA_EPTR;
     }
     return GLA_OK;
 }
@@ -68,8 +75,9 @@ int check_decode(const void* q, const void* k, const void* v, const float* alpha
     if (static_cast<long>(n_req) * n_heads > kMaxWork) return GLA_ESHAPE;
     if (n_req == 0) return GLA_OK;
     if (n_slots < 1) return GLA_ESHAPE;
-    if (!q || !k || !v || !alpha || !pool || !slot_idx || !o) return GLA_EPTR;
-    if (need_beta && !beta) return GLA_EPTR;
+    if (!q || !k || !v || !pool || !slot_idx || !o) return GLA_EPTR;
+    if (alpha == kNoGate) return GLA_OK;
+    if (!alpha || (need_beta && !beta)) return GLA_EPTR;
     return GLA_OK;
 }
 
@@ -236,6 +244,38 @@ int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, int32_t 
     if (static_cast<long>(n_copy) * pieces > kMaxWork) return GLA_ESHAPE;
     gla::CopyArgs a{state_pool, n_slots, n_heads, dk, dv, src_slots, dst_slots, n_copy};
     return hip_status(gla::launch_state_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv,
+                       int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,
+                       float* norm_pool, int32_t n_slots, const int32_t* slot_idx, uint32_t flags,
+                       float eps, void* o, void* stream) {
+    int st = check_chunk(q, k, v, kNoGate, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads,
+                         dk, dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
+    if (st != GLA_OK) return st;
+    if (!is_eps(eps)) return GLA_ESHAPE;
+    if (n_seqs == 0) return GLA_OK;
+    if (!norm_pool) return GLA_EPTR;
+    gla::ChunkArgs a{q, k, v, nullptr, nullptr, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
+                     in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, nullptr, 0, nullptr, chunk, 0, norm_pool, eps};
+    return hip_status(gla::launch_lin_attn_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+int lin_attn_decode_step(const void* q, const void* k, const void* v, int32_t n_req,
+                         int32_t n_heads, int32_t dk, int32_t dv, gla_dtype in_dtype,
+                         gla_dtype out_dtype, float* state_pool, float* norm_pool, int32_t n_slots,
+                         const int32_t* slot_idx, float eps, void* o, void* stream) {
+    int st = check_decode(q, k, v, kNoGate, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
+                          out_dtype, state_pool, n_slots, slot_idx, o);
+    if (st != GLA_OK) return st;
+    if (!is_eps(eps)) return GLA_ESHAPE;
+    if (n_req == 0) return GLA_OK;
+    if (!norm_pool) return GLA_EPTR;
+    gla::LinDecodeArgs a{q, k, v, n_req, n_heads, dk, dv, in_dtype == GLA_BF16, out_dtype == GLA_BF16,
+                         state_pool, norm_pool, n_slots, slot_idx, eps, o};
+    return hip_status(gla::launch_lin_attn_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 int causal_conv1d_fwd(const void* x, const float* w, const int32_t* cu_seqlens, int32_t n_seqs,

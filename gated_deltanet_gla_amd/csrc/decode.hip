@@ -264,6 +264,88 @@ decode_multi_kernel(const typename TI::T* __restrict__ q, const typename TI::T* 
     }
 }
 
+// Normalised kernelised linear attention, one token per request (page "Long
+// context, fast inference, smart decoding, and life beyond attention",
+// section "Linear attention: removing softmax entirely", running-state
+// listing), in place on pool[slot] and zpool[slot]:
+//   S <- S + phi(k)^T v;  z <- z + phi(k);  o = phi(q) S / (phi(q) . z + eps)
+// with phi(x) = elu(x) + 1.  Same tiling as decode_kernel; phi(q) . z_new
+// is reduced over d_k with one wave sum per wave.
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+template <int DK, int DV, class TI, class TO>
+__global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
+lin_attn_decode_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __restrict__ k,
+                       const typename TI::T* __restrict__ v, float* __restrict__ pool,
+                       float* __restrict__ zpool, int n_heads, int n_slots,
+                       const int32_t* __restrict__ slot_idx, float eps,
+                       typename TO::T* __restrict__ o) {
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int NT = Sh::NT, CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT;
+    constexpr int NWV = NT / 64;
+
+    const int h = blockIdx.x % n_heads;
+    const int r = blockIdx.x / n_heads;
+    const int t = threadIdx.x;
+    const int cg = t % CG;
+    const int rg = t / CG;
+
+    const int slot = slot_idx[r];
+    if (slot < 0 || slot >= n_slots) return;
+
+    __shared__ float s_q[DK];
+    __shared__ float s_k[DK];
+    __shared__ f32x4 s_red[RG][CG];
+    __shared__ float s_den[NWV];
+
+    const long head = static_cast<long>(slot) * n_heads + h;
+    float* __restrict__ S = pool + head * (DK * DV);
+    float* __restrict__ z = zpool + head * DK;
+
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV + cg * 4));
+    }
+
+    const long tok = static_cast<long>(r) * n_heads + h;
+    float qz = 0.f;
+    for (int i = t; i < DK; i += NT) {
+        const float pq = elu1(TI::load(q, tok * DK + i));
+        const float pk = elu1(TI::load(k, tok * DK + i));
+        s_q[i] = pq;
+        s_k[i] = pk;
+        const float zn = z[i] + pk;
+        z[i] = zn;
+        qz += pq * zn;
+    }
+    qz = wave_sum(qz);
+    if ((t & 63) == 0) s_den[t >> 6] = qz;
+    const f32x4 v4 = Vec4<TI>::load(v + tok * DV + cg * 4);
+    __syncthreads();
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] = s[i] + s_k[row] * v4;
+        acc += s_q[row] * s[i];
+        __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + row * DV + cg * 4));
+    }
+    s_red[rg][cg] = acc;
+    __syncthreads();
+    if (rg == 0) {
+        f32x4 tot = s_red[0][cg];
+#pragma unroll
+        for (int j = 1; j < RG; ++j) tot += s_red[j][cg];
+        float den = eps;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) den += s_den[w];
+        Vec4<TO>::store(o + tok * DV + cg * 4, tot / den);
+    }
+}
+
 // Plain copy of whole slots (all heads): dst_slots[i] <- src_slots[i].  One
 // workgroup per (pair, 16 KiB piece); 16-byte loads and stores.  A pair with
 // either slot out of range is skipped.
@@ -354,6 +436,45 @@ hipError_t launch(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s) { return launch<false>(a, s); }
 hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s) { return launch<true>(a, s); }
+
+template <int DK, int DV, class TI, class TO>
+hipError_t launch_lin4(const LinDecodeArgs& a, hipStream_t s) {
+    using Sh = DecodeShape<DK, DV>;
+    hipLaunchKernelGGL((lin_attn_decode_kernel<DK, DV, TI, TO>), dim3(a.n_heads * a.n_req), dim3(Sh::NT),
+                       0, s, static_cast<const typename TI::T*>(a.q),
+                       static_cast<const typename TI::T*>(a.k), static_cast<const typename TI::T*>(a.v),
+                       a.pool, a.zpool, a.n_heads, a.n_slots, a.slot_idx, a.eps,
+                       static_cast<typename TO::T*>(a.o));
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_lin_dt(const LinDecodeArgs& a, hipStream_t s) {
+    if (a.in_bf16) return a.out_bf16 ? launch_lin4<DK, DV, BF16, BF16>(a, s) : launch_lin4<DK, DV, BF16, F32>(a, s);
+    return a.out_bf16 ? launch_lin4<DK, DV, F32, BF16>(a, s) : launch_lin4<DK, DV, F32, F32>(a, s);
+}
+
+template <int DK>
+hipError_t launch_lin_dv(const LinDecodeArgs& a, hipStream_t s) {
+    switch (a.dv) {
+        case 16: return launch_lin_dt<DK, 16>(a, s);
+        case 32: return launch_lin_dt<DK, 32>(a, s);
+        case 64: return launch_lin_dt<DK, 64>(a, s);
+        case 128: return launch_lin_dt<DK, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s) {
+    if (a.n_req == 0) return hipSuccess;
+    switch (a.dk) {
+        case 16: return launch_lin_dv<16>(a, s);
+        case 32: return launch_lin_dv<32>(a, s);
+        case 64: return launch_lin_dv<64>(a, s);
+        case 128: return launch_lin_dv<128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_state_copy(const CopyArgs& a, hipStream_t s) {
     if (a.n_copy == 0) return hipSuccess;

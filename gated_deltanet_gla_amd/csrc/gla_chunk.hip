@@ -29,6 +29,16 @@
 // q, k, v sit in LDS in their natural token-major layout; contractions over
 // tokens read them with the LDS transpose read.  One LDS-only barrier per
 // chunk (fp32 inputs use a single buffer and two).
+//
+// NORM = true is normalised kernelised linear attention (page "Long
+// context, fast inference, smart decoding, and life beyond attention",
+// section "Linear attention: removing softmax entirely", and its
+// running-state listing): phi(x) = elu(x) + 1 is applied to q and k as they
+// are staged, there is no gate (alpha = 1), and the output is divided by
+// phi(q_i) . z_i + eps with z_i = z_in + sum_{j<=i} phi(k_j).  Inside a chunk
+// that normaliser is the row sum of the masked score tile P (which the
+// output waves hold anyway) plus phi(q_i) . z_in; the state waves carry z
+// from chunk to chunk in a double-buffered LDS vector.
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -99,10 +109,13 @@ struct Prefetch {
     static constexpr int NV = (C * BV / VE + NTS - 1) / NTS;
     u32x4 q[NQ], k[NQ], v[NV];
     float a;   // alpha of row (lane) in every state wave; 1 for rows >= n
+    int n;     // valid rows of the fetched chunk
 
+    template <bool GATED>
     __device__ __forceinline__ void load(int st, const typename TI::T* qg, const typename TI::T* kg,
                                          const typename TI::T* vg, const float* ag, long tstride,
                                          long vstride, long astride, int n) {
+        this->n = n;
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
             const int x = st + u * NTS;
@@ -122,17 +135,35 @@ struct Prefetch {
             if (x < C * BV / VE && row < n) v[u] = *reinterpret_cast<const u32x4*>(vg + row * vstride + vc * VE);
         }
         const int lane = st & 63;
-        a = (lane < n && lane < C) ? ag[lane * astride] : 1.f;
+        a = (GATED && lane < n && lane < C) ? ag[lane * astride] : 1.f;
     }
 };
 
-template <int DK, int DV, int BV, int C, class TI, class TO>
+// phi(x) = elu(x) + 1 on one 16-byte vector of staged elements
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+template <class TI> __device__ __forceinline__ u32x4 phi_vec(u32x4 w);
+template <> __device__ __forceinline__ u32x4 phi_vec<F32>(u32x4 w) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(elu1(__uint_as_float(w[e])));
+    return r;
+}
+template <> __device__ __forceinline__ u32x4 phi_vec<BF16>(u32x4 w) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = pack_bf16x2(elu1(__uint_as_float(w[e] << 16)), elu1(__uint_as_float(w[e] & 0xffff0000u)));
+    return r;
+}
+
+template <int DK, int DV, int BV, int C, class TI, class TO, bool NORM>
 __global__ void __launch_bounds__(NT)
 gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __restrict__ k,
                  const typename TI::T* __restrict__ v, const float* __restrict__ alpha,
                  const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
                  float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
-                 int zero_init, Ckpt ck, typename TO::T* __restrict__ o) {
+                 int zero_init, Ckpt ck, float* __restrict__ zpool, float eps,
+                 typename TO::T* __restrict__ o) {
     constexpr bool F32 = (TI::bytes == 4);
     using O = Op<F32>;
     using E = typename O::E;
@@ -151,6 +182,7 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     static_assert(DV % BV == 0 && BV % 16 == 0 && C % 16 == 0 && C <= 64 && CT <= NO, "tiling");
 
     __shared__ Buf buf[NBUF];
+    __shared__ float zb[NORM ? 2 : 1][NORM ? DK : 1];   // normaliser z, by chunk parity
 
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int vt = work % NVT;
@@ -195,7 +227,7 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     PF pf;
     auto fetch = [&](int c) {
         const long tok0 = s0 + static_cast<long>(c) * C;
-        pf.load(stid, q + tok0 * tstride + h * DK, k + tok0 * tstride + h * DK,
+        pf.template load<!NORM>(stid, q + tok0 * tstride + h * DK, k + tok0 * tstride + h * DK,
                 v + tok0 * vstride + h * DV + col0, alpha + tok0 * H + h, tstride, vstride, H,
                 min(C, L - c * C));
     };
@@ -218,8 +250,16 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
             const int xx = stid + u * PF::NTS;
             if (xx < C * DK / VE) {
                 const int row = xx / (DK / VE), vc = xx % (DK / VE);
-                *reinterpret_cast<u32x4*>(&bb.q[row][vc * VE]) = pf.q[u];
-                *reinterpret_cast<u32x4*>(&bb.k[row][vc * VE]) = pf.k[u];
+                u32x4 qv = pf.q[u], kv = pf.k[u];
+                if constexpr (NORM) {
+                    // rows past the sequence stay zero (phi(0) = 1 would count them)
+                    if (row < pf.n) {
+                        qv = phi_vec<TI>(qv);
+                        kv = phi_vec<TI>(kv);
+                    }
+                }
+                *reinterpret_cast<u32x4*>(&bb.q[row][vc * VE]) = qv;
+                *reinterpret_cast<u32x4*>(&bb.k[row][vc * VE]) = kv;
             }
         }
 #pragma unroll
@@ -254,6 +294,10 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
         fetch(0);
         stage(buf[0]);
         if (nchunks > 1) fetch(1);
+    }
+    const long zoff = (static_cast<long>(slot) * H + h) * DK;
+    if constexpr (NORM) {
+        for (int d = tid; d < DK; d += NT) zb[0][d] = zero_init ? 0.f : zpool[zoff + d];
     }
     lds_barrier();
 
@@ -331,6 +375,27 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                         }
                     }
                 }
+                // ---- normaliser of this wave's rows: row sums of P (rows j are
+                // spread over the 4 lane groups) + phi(q_i) . z_in, then moved
+                // to the output tile layout (lane holds rows row0 .. row0 + 3)
+                float rden[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (NORM) {
+                    float ps = 0.f;
+#pragma unroll
+                    for (int jt = 0; jt < CT; ++jt) {
+                        if (jt <= it) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) ps += pt[jt][r];
+                        }
+                    }
+                    const float* zin = zb[c & 1];
+                    for (int d = lane >> 4; d < DK; d += 4) ps += O::load1(&bb.q[i][d]) * zin[d];
+                    ps += __shfl_xor(ps, 16, 64);
+                    ps += __shfl_xor(ps, 32, 64);
+                    const float den = ps + eps;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) rden[r] = 1.f / __shfl(den, ap.row0 + r, 64);
+                }
                 // ---- O = diag(exp g) Q S + P V
 #pragma unroll
                 for (int nt = 0; nt < BT; ++nt) {
@@ -368,7 +433,7 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = it * 16 + ap.row0 + r;
-                        if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + colg, ov[nt][r]);
+                        if (row < n) TO::store(o, (tok0 + row) * vstride + h * DV + colg, ov[nt][r] * rden[r]);
                     }
                 }
             }
@@ -404,6 +469,14 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                     }
                 }
             }
+            // normaliser after chunk c: z += sum over its rows of phi(k)
+            if constexpr (NORM) {
+                for (int d = stid; d < DK; d += NS * 64) {
+                    float zacc = zb[c & 1][d];
+                    for (int j = 0; j < C; ++j) zacc += O::load1(&bb.k[j][d]);
+                    zb[(c + 1) & 1][d] = zacc;
+                }
+            }
             // checkpoint: this wave's tiles of the state after chunk c
             const int cs = (c + 1) * C <= L ? ckpt_slot(ck, b, (c + 1) * C, n_slots) : -1;
             if (cs >= 0) {
@@ -436,6 +509,11 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
         lds_barrier();
     }
 
+    if constexpr (NORM) {
+        if (vt == 0) {
+            for (int d = tid; d < DK; d += NT) zpool[zoff + d] = zb[nchunks & 1][d];
+        }
+    }
     // ---- final state slice -> pool (zeros for an empty sequence with zero-init)
 #pragma unroll
     for (int i = 0; i < SMAX; ++i) {
@@ -448,48 +526,60 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     }
 }
 
-template <int DK, int DV, int BV, int C, class TI, class TO>
+template <int DK, int DV, int BV, int C, class TI, class TO, bool NORM>
 hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     using T = typename TI::T;
     const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
-    hipLaunchKernelGGL((gla_chunk_kernel<DK, DV, BV, C, TI, TO>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((gla_chunk_kernel<DK, DV, BV, C, TI, TO, NORM>), dim3(static_cast<unsigned>(blocks)),
                        dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
                        a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init,
-                       Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride},
+                       Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.zpool, a.eps,
                        static_cast<typename TO::T*>(a.o));
     return hipGetLastError();
 }
 
-template <int DK, int DV, int C, class TI, class TO>
+template <int DK, int DV, int C, class TI, class TO, bool NORM>
 hipError_t launch_bv(const ChunkArgs& a, hipStream_t s) {
     constexpr int BV = DV >= 32 ? 32 : DV;
-    return launch_inst<DK, DV, BV, C, TI, TO>(a, s);
+    return launch_inst<DK, DV, BV, C, TI, TO, NORM>(a, s);
 }
 
-template <int DK, int DV, class TI, class TO>
+template <int DK, int DV, class TI, class TO, bool NORM>
 hipError_t launch_c(const ChunkArgs& a, hipStream_t s) {
     switch (a.chunk) {
-        case 16: return launch_bv<DK, DV, 16, TI, TO>(a, s);
-        case 32: return launch_bv<DK, DV, 32, TI, TO>(a, s);
-        case 64: return launch_bv<DK, DV, 64, TI, TO>(a, s);
+        case 16: return launch_bv<DK, DV, 16, TI, TO, NORM>(a, s);
+        case 32: return launch_bv<DK, DV, 32, TI, TO, NORM>(a, s);
+        case 64: return launch_bv<DK, DV, 64, TI, TO, NORM>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool NORM>
 hipError_t launch_dt(const ChunkArgs& a, hipStream_t s) {
-    if (a.in_bf16) return a.out_bf16 ? launch_c<DK, DV, BF16, BF16>(a, s) : launch_c<DK, DV, BF16, F32>(a, s);
-    return a.out_bf16 ? launch_c<DK, DV, F32, BF16>(a, s) : launch_c<DK, DV, F32, F32>(a, s);
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_c<DK, DV, BF16, BF16, NORM>(a, s) : launch_c<DK, DV, BF16, F32, NORM>(a, s);
+    return a.out_bf16 ? launch_c<DK, DV, F32, BF16, NORM>(a, s) : launch_c<DK, DV, F32, F32, NORM>(a, s);
 }
 
-template <int DK>
+template <int DK, bool NORM>
 hipError_t launch_dv(const ChunkArgs& a, hipStream_t s) {
     switch (a.dv) {
-        case 16: return launch_dt<DK, 16>(a, s);
-        case 32: return launch_dt<DK, 32>(a, s);
-        case 64: return launch_dt<DK, 64>(a, s);
-        case 128: return launch_dt<DK, 128>(a, s);
+        case 16: return launch_dt<DK, 16, NORM>(a, s);
+        case 32: return launch_dt<DK, 32, NORM>(a, s);
+        case 64: return launch_dt<DK, 64, NORM>(a, s);
+        case 128: return launch_dt<DK, 128, NORM>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool NORM>
+hipError_t launch_dk(const ChunkArgs& a, hipStream_t s) {
+    switch (a.dk) {
+        case 16: return launch_dv<16, NORM>(a, s);
+        case 32: return launch_dv<32, NORM>(a, s);
+        case 64: return launch_dv<64, NORM>(a, s);
+        case 128: return launch_dv<128, NORM>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -506,13 +596,9 @@ size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv
 
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s) {
     if (gla_seg_supported(a)) return launch_gla_seg(a, s);
-    switch (a.dk) {
-        case 16: return launch_dv<16>(a, s);
-        case 32: return launch_dv<32>(a, s);
-        case 64: return launch_dv<64>(a, s);
-        case 128: return launch_dv<128>(a, s);
-    }
-    return hipErrorInvalidValue;
+    return launch_dk<false>(a, s);
 }
+
+hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s) { return launch_dk<true>(a, s); }
 
 }  // namespace gla

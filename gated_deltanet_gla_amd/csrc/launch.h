@@ -24,6 +24,20 @@ struct DecodeArgs {
     const int32_t* pos_slots;     // [n_req, n_tok] slots for per-position states, or NULL
 };
 
+struct LinDecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    int n_req, n_heads, dk, dv;
+    int in_bf16, out_bf16;
+    float* pool;
+    float* zpool;
+    int n_slots;
+    const int32_t* slot_idx;
+    float eps;
+    void* o;
+};
+
 struct CopyArgs {
     float* pool;
     int n_slots, n_heads, dk, dv;
@@ -51,6 +65,8 @@ struct ChunkArgs {
     const int32_t* ckpt_slots;    // [n_seqs, ckpt_stride] or NULL
     int ckpt_interval;            // tokens, a multiple of chunk
     int ckpt_stride;
+    float* zpool;                 // normalised linear attention: [n_slots, n_heads, dk]
+    float eps;
 };
 
 struct ConvArgs {
@@ -69,7 +85,9 @@ struct ConvArgs {
 hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_state_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s);
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s);
 size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
 bool gla_seg_supported(const ChunkArgs& a);
 size_t gla_seg_workspace(int n_seqs, int n_tokens, int n_heads);

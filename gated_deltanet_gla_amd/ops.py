@@ -39,7 +39,8 @@ def _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, out_dtype, o
                         (v, "v", (torch.float32, torch.bfloat16), 3),
                         (alpha, "alpha", torch.float32, 2), (cu_seqlens, "cu_seqlens", torch.int32, 1),
                         (state_pool, "state_pool", torch.float32, 4), (slot_idx, "slot_idx", torch.int32, 1)]:
-        _check(t, n, d, nd)
+        if t is not None or n != "alpha":     # alpha is None for the ungated operation
+            _check(t, n, d, nd)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     N, H, dk = q.shape
@@ -148,7 +149,8 @@ def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o):
                         (v, "v", (torch.float32, torch.bfloat16), 3),
                         (alpha, "alpha", torch.float32, 2),
                         (state_pool, "state_pool", torch.float32, 4), (slot_idx, "slot_idx", torch.int32, 1)]:
-        _check(t, n, d, nd)
+        if t is not None or n != "alpha":     # alpha is None for the ungated operation
+            _check(t, n, d, nd)
     R, H, dk = q.shape
     dv = v.shape[2]
     out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
@@ -233,6 +235,33 @@ def gla_state_copy(state_pool, src_slots, dst_slots):
     _lib.call("gla_state_copy", state_pool.data_ptr(), n, H, dk, dv, src_slots.data_ptr(),
               dst_slots.data_ptr(), src_slots.shape[0], _stream(state_pool.device))
     return state_pool
+
+
+def lin_attn_chunk_fwd(q, k, v, cu_seqlens, state_pool, norm_pool, slot_idx, *, chunk=64,
+                       eps=1e-6, out_dtype=None, zero_init=False, o=None):
+    """Normalised linear attention (phi = elu + 1), chunked; updates
+    state_pool[slot_idx] and norm_pool[slot_idx] ([n_slots, H, dk] fp32) in
+    place, returns o."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, None, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    _check(norm_pool, "norm_pool", torch.float32, 3)
+    _lib.call("lin_attn_chunk_fwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+              cu_seqlens.shape[0] - 1, N, H, dk, dv, chunk, _DT[q.dtype], _DT[out_dtype],
+              state_pool.data_ptr(), norm_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
+              _lib.GLA_ZERO_INIT if zero_init else 0, float(eps), o.data_ptr(), _stream(q.device))
+    return o
+
+
+def lin_attn_decode_step(q, k, v, state_pool, norm_pool, slot_idx, *, eps=1e-6, out_dtype=None,
+                         o=None):
+    """One normalised-linear-attention token per request, in place; returns o."""
+    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, None, state_pool, slot_idx, out_dtype, o)
+    _check(norm_pool, "norm_pool", torch.float32, 3)
+    _lib.call("lin_attn_decode_step", q.data_ptr(), k.data_ptr(), v.data_ptr(), R, H, dk, dv,
+              _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(), norm_pool.data_ptr(),
+              state_pool.shape[0], slot_idx.data_ptr(), float(eps), o.data_ptr(),
+              _stream(q.device))
+    return o
 
 
 def causal_conv1d_fwd(x, w, cu_seqlens, conv_cache, slot_idx, *, zero_init=False, y=None):

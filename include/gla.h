@@ -262,6 +262,40 @@ GLA_API int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, 
                    int32_t n_copy, void* stream);
 
 /*
+ * lin_attn_chunk_fwd -- normalised kernelised linear attention, chunked
+ * prefill (page "Long context, fast inference, smart decoding, and life
+ * beyond attention", section "Linear attention: removing softmax entirely"
+ * and its running-state listing).  With phi(x) = elu(x) + 1 elementwise:
+ *   S_t = S_{t-1} + phi(k_t)^T v_t,   z_t = z_{t-1} + phi(k_t),
+ *   o_t = phi(q_t) S_t / (phi(q_t) . z_t + eps)
+ * (no gate; eps = 1e-6 on the page).  S starts from pool[slot_idx[b]] and
+ * the normaliser z from norm_pool[slot_idx[b]] (both zero with
+ * GLA_ZERO_INIT); both are written back in place.  norm_pool
+ * [n_slots, n_heads, dk] fp32.  Other arguments and the layout as
+ * gla_chunk_fwd (no alpha, no workspace); eps >= 0 and finite
+ * (GLA_ESHAPE otherwise).  For bf16 inputs phi(q) and phi(k) are rounded to
+ * bf16 before the contractions.
+ */
+GLA_API int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, float* norm_pool, int32_t n_slots,
+                  const int32_t* slot_idx, uint32_t flags, float eps, void* o, void* stream);
+
+/*
+ * lin_attn_decode_step -- one token per request of lin_attn_chunk_fwd's
+ * recurrence, in place on pool[slot_idx[r]] and norm_pool[slot_idx[r]]:
+ *   S <- S + phi(k)^T v;  z <- z + phi(k);  o = phi(q) S / (phi(q) . z + eps)
+ * q, k [n_req, n_heads, dk]; v, o [n_req, n_heads, dv].
+ */
+GLA_API int lin_attn_decode_step(const void* q, const void* k, const void* v,
+                  int32_t n_req, int32_t n_heads, int32_t dk, int32_t dv,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, float* norm_pool, int32_t n_slots,
+                  const int32_t* slot_idx, float eps, void* o, void* stream);
+
+/*
  * causal_conv1d_fwd -- depthwise causal convolution of width W with a
  * per-request cache of the last W-1 inputs ("Two ways to write the same
  * computation", last paragraph; "The real model's ledger": an engine keeps

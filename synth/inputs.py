@@ -22,6 +22,7 @@ __all__ = [
     "bf16_bits", "bf16_to_f32", "round_bf16", "sigmoid",
     "Workload", "page_toy_example", "prefill_gla", "prefill_gdn", "decode",
     "mixed_varlen", "random_varlen", "loguniform_lengths", "page_toy_workload", "decode_multi",
+    "lin_attn_varlen",
 ]
 
 
@@ -330,3 +331,31 @@ def decode_multi(seed: int = 6, n_req: int = 256, n_tok: int = 4, H: int = 16, d
                     dtype=dtype, q=r4(q), k=r4(k), v=r4(v), alpha=r4(alpha),
                     beta=r4(beta) if gdn else None, cu_seqlens=cu, pool=pool, slot_idx=slots,
                     zero_init=False, chunk=1, extra={"pos_slots": pos, "perm": perm})
+
+
+def lin_attn_varlen(seed: int, lengths, n_heads: int = 16, dk: int = 128, dv: int = 128, *,
+                    dtype: str = "bf16", n_slots: int | None = None, zero_init: bool = False,
+                    chunk: int = 64, name: str = "lin-attn") -> Workload:
+    """Inputs for normalised kernelised linear attention: q, k, v ~ N(0,1)
+    (unit scale, so the feature map sees both signs over a wide range);
+    states ~ N(0,1) * 4 and normalisers ~ U(16, 48) (positive, like a sum of
+    positive features over an earlier prefix) in a pool of ``n_slots``;
+    slots a random distinct subset.  ``extra['zpool']`` [n_slots, H, dk]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = [int(x) for x in lengths]
+    N, H, B = int(sum(lengths)), n_heads, len(lengths)
+    q = rng.standard_normal((N, H, dk), dtype=np.float32)
+    k = rng.standard_normal((N, H, dk), dtype=np.float32)
+    v = rng.standard_normal((N, H, dv), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    n_slots = n_slots if n_slots is not None else B + 3
+    pool = rng.standard_normal((n_slots, H, dk, dv), dtype=np.float32) * np.float32(4.0)
+    zpool = rng.uniform(16.0, 48.0, size=(n_slots, H, dk)).astype(np.float32)
+    slots = rng.permutation(n_slots)[:B].astype(np.int32)
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return Workload(name=name, dtype=dtype, q=q.astype(np.float32), k=k.astype(np.float32),
+                    v=v.astype(np.float32), alpha=np.ones((N, H), np.float32), cu_seqlens=cu,
+                    pool=pool, slot_idx=slots, zero_init=zero_init, chunk=chunk,
+                    extra={"zpool": zpool})
