@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", default="all",
-                   choices=["all", "gla_prefill", "gdn_prefill", "decode", "mixed"])
+                   choices=["all", "gla_prefill", "gdn_prefill", "decode", "mixed", "lin_attn"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -188,6 +188,57 @@ def bench_decode_multi(torch, G, synth, dev, steps, warmup, gdn):
     return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
 
 
+def bench_gdn_prefill_ckpt(torch, G, synth, dev, steps, warmup):
+    """The Gated DeltaNet prefill saving a state checkpoint every 1024 tokens
+    (8 per sequence, 16 MiB of extra state writes per call)."""
+    import numpy as np
+    w = synth.prefill_gdn()
+    N, H, d = w.n_tokens, w.n_heads, w.dk
+    B, iv = w.n_seqs, 1024
+    stride = int(w.cu_seqlens[1]) // iv
+    n0 = w.pool.shape[0]
+    pool = dev(np.concatenate([w.pool, np.zeros((B * stride,) + w.pool.shape[1:], np.float32)]))
+    ck = dev((n0 + np.arange(B * stride)).reshape(B, stride).astype(np.int32))
+    q, k, v, a, b = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha), dev(w.beta)
+    cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(G.workspace_bytes("gdn", B, N, H, d, d, w.chunk), dtype=torch.uint8,
+                     device="cuda:0")
+    ms = timed(torch, lambda i: G.gdn_chunk_fwd_ckpt(q, k, v, a, b, cu, pool, slots, ck, iv,
+                                                     chunk=w.chunk, o=o, workspace=ws),
+               steps, warmup)
+    return {"workload": w.name + f"-ckpt{iv}", "ms": ms, "tokens_per_s": N / (ms * 1e-3)}
+
+
+def bench_lin_attn(torch, G, synth, dev, steps, warmup):
+    """Normalised linear attention (phi = elu + 1): prefill of 4 x 4096
+    tokens x 16 heads (d = 128, chunk 64, bf16, from pool states), and one
+    decode step of 256 requests x 16 heads."""
+    w = synth.lin_attn_varlen(640, [4096] * 4, 16, 128, 128, dtype="bf16", chunk=64)
+    N, H, d = w.n_tokens, w.n_heads, w.dk
+    q, k, v = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16")
+    pool, zpool = dev(w.pool), dev(w.extra["zpool"])
+    cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+    ms = timed(torch, lambda i: G.lin_attn_chunk_fwd(q, k, v, cu, pool, zpool, slots, chunk=64,
+                                                     o=o), steps, warmup)
+    nbytes = 4 * N * H * d * 2 + 4 * H * (2 * d * d * 4 + 2 * d * 4)
+    R = 256
+    wd = synth.lin_attn_varlen(641, [1] * R, 16, 128, 128, dtype="bf16", n_slots=1024)
+    qd, kd, vd = dev(wd.q, "bf16"), dev(wd.k, "bf16"), dev(wd.v, "bf16")
+    pd, zd, sd = dev(wd.pool), dev(wd.extra["zpool"]), dev(wd.slot_idx)
+    od = torch.empty((R, H, d), dtype=torch.bfloat16, device="cuda:0")
+    msd = timed(torch, lambda i: G.lin_attn_decode_step(qd, kd, vd, pd, zd, sd, o=od), steps,
+                warmup)
+    dbytes = R * H * (2 * d * d * 4 + 2 * d * 4 + 4 * d * 2)
+    return {"prefill": {"workload": "lin-attn-prefill-4x4096-H16-d128-C64-bf16", "ms": ms,
+                        "tokens_per_s": N / (ms * 1e-3),
+                        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+            "decode": {"workload": "lin-attn-decode-256req-H16-d128-pool1024", "ms": msd,
+                       "GBps": dbytes / (msd * 1e-3) / 1e9,
+                       "hbm_frac": dbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
+
+
 def bench_mixed(torch, G, synth, dev, steps, warmup):
     import numpy as np
     from gated_deltanet_gla_amd.step import MixedStep
@@ -288,6 +339,13 @@ def main():
     if args.only in ("all", "gdn_prefill"):
         res["gdn_prefill"] = bench_gdn_prefill(torch, G, synth, dev, K, W)
         print(f"# gdn prefill {res['gdn_prefill']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        res["gdn_prefill_ckpt"] = bench_gdn_prefill_ckpt(torch, G, synth, dev, K, W)
+        print(f"# gdn prefill + checkpoints {res['gdn_prefill_ckpt']['ms']:.3f} ms", file=sys.stderr,
+              flush=True)
+    if args.only in ("all", "lin_attn"):
+        res["lin_attn"] = bench_lin_attn(torch, G, synth, dev, K, W)
+        print(f"# lin attn prefill {res['lin_attn']['prefill']['ms']:.3f} ms, decode "
+              f"{res['lin_attn']['decode']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.only in ("all", "mixed"):
         res["mixed"] = bench_mixed(torch, G, synth, dev, max(3, K // 4), max(1, W // 2))
         print(f"# mixed {res['mixed']['ms']:.3f} ms", file=sys.stderr, flush=True)
@@ -345,6 +403,12 @@ def main():
         other["gdn_prefill"] = {"workload": r["workload"], "tokens_per_s": r["tokens_per_s"],
                                 "ms": r["ms"], "hbm_frac": ach / HBM_PEAK_GBPS,
                                 "mfma_frac": r["flops"] / (r["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    if "gdn_prefill_ckpt" in res:
+        r = res["gdn_prefill_ckpt"]
+        other["gdn_prefill_ckpt"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s")}
+    if "lin_attn" in res:
+        other["lin_attn_prefill"] = res["lin_attn"]["prefill"]
+        other["lin_attn_decode"] = res["lin_attn"]["decode"]
     if "mixed" in res:
         r = res["mixed"]
         other["mixed_gdn_step"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s", "n_tokens",
