@@ -206,3 +206,104 @@ def conv_numpy_convolve(causal_conv1d, seed=11):
         ref = np.convolve(x[:, c], w[c, ::-1])[:N]
         err = max(err, np.abs(y[:, c] - ref).max())
     return max(err, np.abs(cache_out[0] - x[N - (W - 1):]).max())
+
+
+# ---------------------------------------------------------------- normalised linear attention
+def _phi(x):
+    """elu(x) + 1 written out for the pins: x + 1 above zero, e^x below."""
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def lin_parallel_form(lin_attn_sequence, seed=12):
+    """o_i = sum_{j<=i} (phi(q_i).phi(k_j)) v_j / (sum_{j<=i} phi(q_i).phi(k_j) + eps)
+    as a double sum, plus S = phi(K)^T V and z = sum_j phi(k_j)."""
+    r = _rng(seed)
+    T, H, dk, dv = 18, 2, 5, 4
+    q, k, v = r.standard_normal((T, H, dk)), r.standard_normal((T, H, dk)), r.standard_normal((T, H, dv))
+    o, S, z = lin_attn_sequence(q, k, v)
+    pq, pk = _phi(q), _phi(k)
+    worst = 0.0
+    for h in range(H):
+        for i in range(T):
+            w = np.array([pq[i, h] @ pk[j, h] for j in range(i + 1)])
+            ref = (w[:, None] * v[:i + 1, h]).sum(0) / (w.sum() + 1e-6)
+            worst = max(worst, np.abs(o[i, h] - ref).max())
+        worst = max(worst, np.abs(S[h] - pk[:, h].T @ v[:, h]).max(),
+                    np.abs(z[h] - pk[:, h].sum(0)).max())
+    return worst
+
+
+def lin_from_state(lin_attn_sequence, seed=13):
+    """Starting from (S0, z0): o_i = phi(q_i)(S0 + sum phi(k)^T v) / (phi(q_i).(z0 + sum phi(k)) + eps)."""
+    r = _rng(seed)
+    T, H, dk, dv = 9, 2, 4, 3
+    q, k, v = r.standard_normal((T, H, dk)), r.standard_normal((T, H, dk)), r.standard_normal((T, H, dv))
+    S0 = r.standard_normal((H, dk, dv))
+    z0 = r.uniform(1.0, 3.0, (H, dk))
+    o, _, _ = lin_attn_sequence(q, k, v, S0, z0)
+    pq, pk = _phi(q), _phi(k)
+    worst = 0.0
+    for h in range(H):
+        for i in range(T):
+            S = S0[h] + pk[:i + 1, h].T @ v[:i + 1, h]
+            z = z0[h] + pk[:i + 1, h].sum(0)
+            worst = max(worst, np.abs(o[i, h] - pq[i, h] @ S / (pq[i, h] @ z + 1e-6)).max())
+    return worst
+
+
+# ---------------------------------------------------------------- kept states
+def _multi(seed, R=2, J=4, H=2, dk=4, dv=3, n_slots=14):
+    r = _rng(seed)
+    q, k, v = r.standard_normal((R, J, H, dk)), r.standard_normal((R, J, H, dk)), r.standard_normal((R, J, H, dv))
+    a = 1.0 / (1.0 + np.exp(-(r.standard_normal((R, J, H)) + 2.0)))
+    pool = r.standard_normal((n_slots, H, dk, dv))
+    perm = r.permutation(n_slots)
+    return q, k, v, a, pool, perm[:R], perm[R:R + R * J].reshape(R, J)
+
+
+def multi_closed_form(gla_decode_multi, seed=14):
+    """Kept state j of request r = (prod_{i<=j} a_i) S_0 + sum_{s<=j} (prod_{i=s+1..j} a_i) k_s^T v_s;
+    o_j = q_j S_j; the request's own slot unchanged."""
+    q, k, v, a, pool, slots, pos = _multi(seed)
+    o, out = gla_decode_multi(q, k, v, a, pool, slots, pos)
+    worst = float(np.abs(out[slots] - pool[slots]).max())
+    for r in range(q.shape[0]):
+        for j in range(q.shape[1]):
+            for h in range(q.shape[2]):
+                S = np.prod(a[r, :j + 1, h]) * pool[slots[r], h]
+                for s_ in range(j + 1):
+                    S = S + np.prod(a[r, s_ + 1:j + 1, h]) * np.outer(k[r, s_, h], v[r, s_, h])
+                worst = max(worst, np.abs(out[pos[r, j], h] - S).max(),
+                            np.abs(o[r, j, h] - q[r, j, h] @ S).max())
+    return worst
+
+
+def ckpt_closed_form(gla_varlen_ckpt, seed=15):
+    """Checkpoint j of sequence b = the GLA state after (j+1)*interval of its
+    tokens, from its closed form; unreached checkpoint slots untouched."""
+    r = _rng(seed)
+    lengths, H, dk, dv, iv, stride = [13, 8, 3], 2, 3, 3, 4, 3
+    N = sum(lengths)
+    q, k, v = r.standard_normal((N, H, dk)), r.standard_normal((N, H, dk)), r.standard_normal((N, H, dv))
+    a = 1.0 / (1.0 + np.exp(-(r.standard_normal((N, H)) + 2.0)))
+    B = len(lengths)
+    n_slots = B + B * stride
+    pool = r.standard_normal((n_slots, H, dk, dv))
+    perm = r.permutation(n_slots)
+    slots, ck = perm[:B], perm[B:].reshape(B, stride)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    _, out = gla_varlen_ckpt(q, k, v, a, cu, pool, slots, ck, iv)
+    worst = 0.0
+    for b in range(B):
+        s0 = cu[b]
+        for j in range(stride):
+            p = (j + 1) * iv
+            if p > lengths[b]:
+                worst = max(worst, np.abs(out[ck[b, j]] - pool[ck[b, j]]).max())
+                continue
+            for h in range(H):
+                S = np.prod(a[s0:s0 + p, h]) * pool[slots[b], h]
+                for t in range(s0, s0 + p):
+                    S = S + np.prod(a[t + 1:s0 + p, h]) * np.outer(k[t, h], v[t, h])
+                worst = max(worst, np.abs(out[ck[b, j], h] - S).max())
+    return worst

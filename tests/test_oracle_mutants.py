@@ -117,3 +117,90 @@ def test_conv_mutant_caught(kind):
             c[int(slots[0])] = np.roll(c[int(slots[0])], 1, axis=0)
         return y, c
     assert pins.conv_numpy_convolve(f) > 1e-6
+
+
+# ---------------------------------------------------------------- normalised linear attention
+def _lin_mutant(kind):
+    def phi(x):
+        if kind == "phi_without_one":
+            return np.where(x > 0, x, np.exp(np.minimum(x, 0.0)) - 1.0)
+        if kind == "phi_relu":
+            return np.maximum(x, 0.0) + 1.0
+        return oracle.phi(x)
+
+    def f(q, k, v, S0=None, z0=None, eps=1e-6):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        T, H, dk = q.shape
+        S = np.zeros((H, dk, v.shape[2])) if S0 is None else np.array(S0, np.float64)
+        z = np.zeros((H, dk)) if z0 is None else np.array(z0, np.float64)
+        o = np.zeros((T, H, v.shape[2]))
+        for t in range(T):
+            pq, pk = phi(q[t]), phi(k[t])
+            if kind == "read_before_update":
+                o[t] = np.einsum("hd,hde->he", pq, S) / (np.einsum("hd,hd->h", pq, z) + eps)[:, None]
+            S = S + pk[:, :, None] * v[t][:, None, :]
+            if kind != "frozen_normaliser":
+                z = z + pk
+            den = np.einsum("hd,hd->h", pk if kind == "key_in_normaliser" else pq, z) + eps
+            if kind != "read_before_update":
+                o[t] = np.einsum("hd,hde->he", pq, S) / den[:, None]
+        return o, S, z
+    return f
+
+
+LIN_PINS = [pins.lin_parallel_form, pins.lin_from_state]
+
+
+def test_lin_unmutated_copy_passes():
+    assert max(p(_lin_mutant("none")) for p in LIN_PINS) <= pins.TOL
+
+
+@pytest.mark.parametrize("kind", ["phi_without_one", "phi_relu", "read_before_update",
+                                  "frozen_normaliser", "key_in_normaliser"])
+def test_lin_mutant_caught(kind):
+    assert _worst(LIN_PINS, _lin_mutant(kind)) > 1e-6
+
+
+# ---------------------------------------------------------------- kept states
+def _multi_mutant(kind):
+    def f(q, k, v, alpha, pool, slot_idx, pos_slots):
+        pos = np.array(pos_slots)
+        if kind == "position_shift":
+            pos = np.roll(pos, 1, axis=1)
+        o, out = oracle.gla_decode_multi(q, k, v, alpha, pool, slot_idx, pos)
+        if kind == "commits_own_slot":
+            out = out.copy()
+            out[np.asarray(slot_idx)] = out[pos[:, -1]]
+        if kind == "state_before_update":
+            _, prev = oracle.gla_decode_multi(q[:, :-1], k[:, :-1], v[:, :-1], alpha[:, :-1],
+                                              pool, slot_idx, pos[:, 1:])
+            out = out.copy()
+            out[pos[:, 1:]] = prev[pos[:, 1:]]
+            out[pos[:, 0]] = np.asarray(pool)[np.asarray(slot_idx)]
+        return o, out
+    return f
+
+
+@pytest.mark.parametrize("kind", ["position_shift", "commits_own_slot", "state_before_update"])
+def test_multi_mutant_caught(kind):
+    assert pins.multi_closed_form(oracle.gla_decode_multi) <= pins.TOL
+    assert pins.multi_closed_form(_multi_mutant(kind)) > 1e-6
+
+
+def _ckpt_mutant(kind):
+    def f(q, k, v, alpha, cu, pool, slots, ck, interval, zero_init=False):
+        if kind == "interval_plus_one_chunk":
+            return oracle.gla_varlen_ckpt(q, k, v, alpha, cu, pool, slots, ck, interval + 1, zero_init)
+        if kind == "from_zero_state":
+            return oracle.gla_varlen_ckpt(q, k, v, alpha, cu, pool, slots, ck, interval, True)
+        if kind == "shifted_table":
+            return oracle.gla_varlen_ckpt(q, k, v, alpha, cu, pool, slots, np.roll(ck, 1, axis=1),
+                                          interval, zero_init)
+        return oracle.gla_varlen_ckpt(q, k, v, alpha, cu, pool, slots, ck, interval, zero_init)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["interval_plus_one_chunk", "from_zero_state", "shifted_table"])
+def test_ckpt_mutant_caught(kind):
+    assert pins.ckpt_closed_form(_ckpt_mutant("none")) <= pins.TOL
+    assert pins.ckpt_closed_form(_ckpt_mutant(kind)) > 1e-6
