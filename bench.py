@@ -220,8 +220,10 @@ def bench_lin_attn(torch, G, synth, dev, steps, warmup):
     pool, zpool = dev(w.pool), dev(w.extra["zpool"])
     cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(G.workspace_bytes("gla", w.n_seqs, N, H, d, d, 64), dtype=torch.uint8,
+                     device="cuda:0")
     ms = timed(torch, lambda i: G.lin_attn_chunk_fwd(q, k, v, cu, pool, zpool, slots, chunk=64,
-                                                     o=o), steps, warmup)
+                                                     o=o, workspace=ws), steps, warmup)
     nbytes = 4 * N * H * d * 2 + 4 * H * (2 * d * d * 4 + 2 * d * 4)
     R = 256
     wd = synth.lin_attn_varlen(641, [1] * R, 16, 128, 128, dtype="bf16", n_slots=1024)

@@ -41,7 +41,8 @@ SIGNATURES = {
     "gla_state_copy": (ct.c_int, [_F, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "lin_attn_chunk_fwd": (ct.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                       ct.c_int, ct.c_int, _F, _F, _I32, _P, _U32, ct.c_float, _P,
-                                      _P]),
+                                      _P, _SZ, _P]),
+    "lin_attn_chunk_workspace_bytes": (ct.c_size_t, [_I32] * 6),
     "lin_attn_decode_step": (ct.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, ct.c_int, ct.c_int,
                                         _F, _F, _I32, _P, ct.c_float, _P, _P]),
     "causal_conv1d_fwd": (ct.c_int, [_P, _F, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _U32, _P,

@@ -107,6 +107,11 @@ size_t gla_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_hea
     return gla::gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
 }
 
+size_t lin_attn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                                      int32_t dk, int32_t dv, int32_t chunk) {
+    return gla_chunk_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+}
+
 size_t gdn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk,
                                  int32_t dv, int32_t chunk) {
     if (n_seqs < 0 || n_tokens < 0 || n_heads < 1 || !is_dim(dk) || !is_dim(dv) || !is_chunk(chunk))
@@ -250,16 +255,19 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const int32_
                        int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv,
                        int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,
                        float* norm_pool, int32_t n_slots, const int32_t* slot_idx, uint32_t flags,
-                       float eps, void* o, void* stream) {
+                       float eps, void* o, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_chunk(q, k, v, kNoGate, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads,
                          dk, dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (!is_eps(eps)) return GLA_ESHAPE;
     if (n_seqs == 0) return GLA_OK;
     if (!norm_pool) return GLA_EPTR;
+    const size_t need = gla::gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
     gla::ChunkArgs a{q, k, v, nullptr, nullptr, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                      in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
-                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, nullptr, 0, nullptr, chunk, 0, norm_pool, eps};
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes, nullptr, chunk, 0,
+                     norm_pool, eps};
     return hip_status(gla::launch_lin_attn_chunk(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -599,6 +599,10 @@ hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s) {
     return launch_dk<false>(a, s);
 }
 
-hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s) { return launch_dk<true>(a, s); }
+hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s) {
+    // bf16, d_k = d_v = 128, chunk 64 with a workspace: the segmented passes
+    if (gla_seg_supported(a) && a.workspace != nullptr) return launch_lin_attn_seg(a, s);
+    return launch_dk<true>(a, s);
+}
 
 }  // namespace gla

@@ -39,6 +39,14 @@
 // placed next to MFMAs it does not feed (the state update's split before
 // the P V products, the next chunk's LDS writes between the update's
 // products), so the matrix and vector units run side by side.
+// NORM = true runs normalised kernelised linear attention on the same two
+// passes (page "Long context, fast inference, smart decoding, and life
+// beyond attention", section "Linear attention: removing softmax
+// entirely"): phi(x) = elu(x) + 1 is applied to q and k as they are staged,
+// the gate is 1, pass 1 also sums phi(k) over each segment (one MFMA per
+// half chunk against a ones operand: wave w owns rows 16w..16w+15 of the
+// normaliser z) and pass 2 divides each output row by
+// phi(q_i) . z_in + (row sum of P) + eps, carrying z from chunk to chunk.
 // Global accesses go through buffer resources sized to the valid rows, so
 // the loops have no guarded memory instructions; the output pass streams
 // q, k, v with the nontemporal policy (pass 1 reads k, v with the default
@@ -185,8 +193,9 @@ __device__ __forceinline__ void load_state_rowmajor(f32x4 (&S)[8], const float* 
     }
 }
 
-// One chunk's global slices (rows past n read as zero) into registers.
-template <bool WQ>
+// One chunk's global slices (rows past n read as zero) into registers;
+// GATED = false (no gate) loads no alpha.
+template <bool WQ, bool GATED = true>
 __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q, const uint16_t* k,
                                           const uint16_t* v, const float* alpha, long tok0, int n, int h,
                                           int H) {
@@ -197,7 +206,7 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
     // only wave 0 scans the decays: the other waves' alpha loads are out of
     // range (no memory traffic) and read as zero
     const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
-    const BufRsrc ra(alpha + tok0 * H + h, w0 ? rows_extent(n, static_cast<long>(H) * 4, 4) : 0u);
+    const BufRsrc ra(alpha + tok0 * H + h, (GATED && w0) ? rows_extent(n, static_cast<long>(H) * 4, 4) : 0u);
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
@@ -219,29 +228,50 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
     pf.n = n;
 }
 
-// Registers -> LDS: the q, k, v rows.
-template <bool WQ, class Buf>
+// phi(x) = elu(x) + 1 on 8 packed bf16 values
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+__device__ __forceinline__ u32x4 phi8(u32x4 w) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = pack_bf16x2(elu1(__uint_as_float(w[e] << 16)), elu1(__uint_as_float(w[e] & 0xffff0000u)));
+    return r;
+}
+
+// Registers -> LDS: the q, k, v rows (NORM: phi(q), phi(k); rows past the
+// sequence stay zero, since phi(0) = 1 would count them).
+template <bool WQ, bool NORM = false, class Buf>
 __device__ __forceinline__ void seg_stage_rows(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
         const int xx = tid + u * ST;
         const int row = xx / (SD / 8), vc = (xx % (SD / 8)) * 8;
-        if constexpr (WQ) *reinterpret_cast<u32x4*>(&bb.q[row][vc]) = pf.q[u];
-        *reinterpret_cast<u32x4*>(&bb.k[row][vc]) = pf.k[u];
+        u32x4 kv = pf.k[u];
+        if constexpr (NORM) {
+            if (row < pf.n) kv = phi8(kv);
+        }
+        if constexpr (WQ) {
+            u32x4 qv = pf.q[u];
+            if constexpr (NORM) {
+                if (row < pf.n) qv = phi8(qv);
+            }
+            *reinterpret_cast<u32x4*>(&bb.q[row][vc]) = qv;
+        }
+        *reinterpret_cast<u32x4*>(&bb.k[row][vc]) = kv;
         *reinterpret_cast<u32x4*>(&bb.v[row][vc]) = pf.v[u];
     }
 }
 
 // Wave 0 scans log2(alpha), writes the per-token tables and gets the chunk's
 // total log2 decay back (other waves get 0).
-template <bool WQ, class Buf>
+template <bool WQ, bool NORM = false, class Buf>
 __device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>& pf) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     float glast = 0.f;
     if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
-        const float a = lane < pf.n ? pf.a : 1.f;
+        const float a = (!NORM && lane < pf.n) ? pf.a : 1.f;
         const float x = wave_inclusive_sum(__log2f(fmaxf(a, kMinDecay)));
         glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), SC - 1));
         if constexpr (WQ) {
@@ -256,11 +286,21 @@ __device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>&
 
 // Registers -> LDS (rows and gate tables); returns the chunk's total log2
 // decay on wave 0.
-template <bool WQ, class Buf>
+template <bool WQ, bool NORM = false, class Buf>
 __device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
-    const float glast = seg_stage_gates(bb, pf);
-    seg_stage_rows(bb, pf);
+    const float glast = seg_stage_gates<WQ, NORM>(bb, pf);
+    seg_stage_rows<WQ, NORM>(bb, pf);
     return glast;
+}
+
+// z rows 16w..16w+15 (wave w) += sum over the chunk's tokens of phi(k): the
+// k^T fragments of those rows times a ones operand (every column of the
+// accumulator tile holds the same sums).
+template <class Buf>
+__device__ __forceinline__ void seg_z_update(f32x4& z, const Buf& bb, int wave) {
+    const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) z = mfma_bf16(frag_km_split(&bb.k[0][0], LK, wave * 16, 32 * ks), ones, z);
 }
 
 // V^T operand of this wave's 16 columns for the two 32-token halves of the
@@ -324,12 +364,14 @@ __device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, c
 }
 
 // ------------------------------------------------------------------ pass 1
+template <bool NORM>
 __global__ void __launch_bounds__(ST)
 gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
               const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs,
               int n_tokens, int H, const float* __restrict__ pool, int n_slots,
               const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
-              float* __restrict__ wstate, float* __restrict__ wlam) {
+              float* __restrict__ wstate, float* __restrict__ wlam, const float* __restrict__ zpool,
+              float* __restrict__ wz) {
     __shared__ int sh[SW + 4];
     SegGeom sg;
     if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
@@ -345,8 +387,14 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
         if (!zero_init) load_state_rowmajor(S, pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD, col);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
+        if constexpr (NORM) {
+            if (threadIdx.x < SD)
+                wz[sg.ws_slot * SD + threadIdx.x] =
+                    zero_init ? 0.f : zpool[(static_cast<long>(sg.slot) * H + sg.h) * SD + threadIdx.x];
+        }
         return;
     }
+    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
 
     __shared__ KVBuf buf[2];
     const int nch = (sg.t1 - sg.t0 + SC - 1) / SC;
@@ -354,32 +402,40 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * SC; };
     SegPrefetch<false> pf;
     float lam = 0.f;
-    seg_fetch(pf, nullptr, k, v, alpha, tok(0), rows(0), sg.h, H);
-    lam += seg_stage(buf[0], pf);
-    seg_fetch(pf, nullptr, k, v, alpha, tok(1), rows(1), sg.h, H);
+    seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(0), rows(0), sg.h, H);
+    lam += seg_stage<false, NORM>(buf[0], pf);
+    seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(1), rows(1), sg.h, H);
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
         bf16x8 vf[2];
         load_vt(vf, buf[c & 1], col);
         seg_state_update(S, buf[c & 1], vf);
-        const float gl = seg_stage(buf[(c + 1) & 1], pf);
+        if constexpr (NORM) seg_z_update(zacc, buf[c & 1], wave);
+        const float gl = seg_stage<false, NORM>(buf[(c + 1) & 1], pf);
         if (c + 1 < nch) lam += gl;
-        seg_fetch(pf, nullptr, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
+        seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
     if (threadIdx.x == 0) wlam[sg.ws_slot] = lam;
+    if constexpr (NORM) {
+        if (ap.col == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wz[sg.ws_slot * SD + wave * 16 + ap.row0 + r] = zacc[r];
+        }
+    }
 }
 
 // ------------------------------------------------------------------ pass 2
-template <class TO, bool CKPT>
+template <class TO, bool CKPT, bool NORM>
 __global__ void __launch_bounds__(ST)
 gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
             const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
             int H, float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
             int zero_init, int lseg, const float* __restrict__ wstate, const float* __restrict__ wlam,
-            Ckpt ck, typename TO::T* __restrict__ o) {
+            Ckpt ck, float* __restrict__ zpool, const float* __restrict__ wz, float eps,
+            typename TO::T* __restrict__ o) {
     __shared__ int sh[SW + 4];
     SegGeom sg;
     if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
@@ -387,6 +443,10 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     __shared__ uint16_t pbuf[2][SC][SP];           // P = (Q K^T) .* D, hi and lo planes
     // bf16 outputs of the previous chunk, stored to HBM as whole rows
     __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LQ];
+    // NORM: z_in by chunk parity, row sums of the 10 P tiles, phi(q_i) . z_in
+    __shared__ alignas(16) float zb[NORM ? 2 : 1][NORM ? SD : 1];
+    __shared__ float dpart[NORM ? 10 : 1][16];
+    __shared__ float qzb[NORM ? SC : 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,7 +458,9 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     auto rows = [&](int c) { return c < nch ? min(SC, sg.t1 - sg.t0 - c * SC) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * SC; };
     SegPrefetch<true> pf;
-    seg_fetch(pf, q, k, v, alpha, tok(0), rows(0), sg.h, H);     // in flight during the fold
+    seg_fetch<true, !NORM>(pf, q, k, v, alpha, tok(0), rows(0), sg.h, H);     // in flight during the fold
+    const long zoff = (static_cast<long>(sg.slot) * H + sg.h) * SD;
+    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};   // NORM: z rows wave*16 + row0 + r (every column the same)
 
     // ---- entry state of this segment
     f32x4 S[8];
@@ -419,6 +481,17 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
         }
     }
+    if constexpr (NORM) {
+        const int zr = wave * 16 + ap.row0;
+        if (sg.nseg <= 1) {
+            if (!zero_init) zacc = *reinterpret_cast<const f32x4*>(zpool + zoff + zr);
+        } else {
+            zacc = *reinterpret_cast<const f32x4*>(wz + (sg.ws_first + static_cast<long>(sg.nseg - 1) * H) * SD + zr);
+            for (int j = 0; j < sg.g; ++j)
+                zacc += *reinterpret_cast<const f32x4*>(wz + (sg.ws_first + static_cast<long>(j) * H) * SD + zr);
+        }
+        if (ap.col == 0) *reinterpret_cast<f32x4*>(&zb[0][zr]) = zacc;
+    }
     // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
     // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
     for (int idx = tid; idx < 2 * 256; idx += ST) {
@@ -427,8 +500,8 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         pbuf[0][row][cx] = 0;
         pbuf[1][row][cx] = 0;
     }
-    seg_stage(buf[0], pf);
-    seg_fetch(pf, q, k, v, alpha, tok(1), rows(1), sg.h, H);
+    seg_stage<true, NORM>(buf[0], pf);
+    seg_fetch<true, !NORM>(pf, q, k, v, alpha, tok(1), rows(1), sg.h, H);
     lds_barrier();
 
     // P tile t of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3):
@@ -455,6 +528,13 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             pt[r] = (j <= i) ? pt[r] * exp2f(gi - bb.g2[j]) : 0.f;
         }
         Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
+        if constexpr (NORM) {
+            // row i's sum over this tile's 16 keys (spread over the 4 lane groups)
+            float rs = (pt[0] + pt[1]) + (pt[2] + pt[3]);
+            rs += __shfl_xor(rs, 16, 64);
+            rs += __shfl_xor(rs, 32, 64);
+            if ((threadIdx.x & 63) < 16) dpart[t][ap.col] = rs;
+        }
     };
 
     // chunk cc's bf16 outputs: LDS -> HBM, 16 lanes per 256-byte row
@@ -512,6 +592,18 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         }
 #pragma unroll
         for (int it = 0; it < 4; ++it) ot[it] *= bb.eg[it * 16 + ap.col];
+        if constexpr (NORM) {
+            // phi(q_i) . z_in: 8 threads per row, 16 dimensions each
+            const int i = tid >> 3, d0 = (tid & 7) * 16;
+            const float* zin = zb[c & 1];
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc += bf16_bits_to_f32(bb.q[i][d0 + e]) * zin[d0 + e];
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            acc += __shfl_xor(acc, 4, 64);
+            if ((tid & 7) == 0) qzb[i] = acc;
+        }
         lds_barrier();
 
         // ---- phase 2: + V^T P^T (split k order on both operands), outputs,
@@ -543,6 +635,16 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             ot[it] = mfma_bf16(vf[1], pp[it + 2][0], ot[it]);
             ot[it] = mfma_bf16(vf[1], pp[it + 2][1], ot[it]);
         }
+        if constexpr (NORM) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int i = it * 16 + ap.col;
+                float den = qzb[i] + eps;
+#pragma unroll
+                for (int jt = 0; jt <= it; ++jt) den += dpart[it * (it + 1) / 2 + jt][ap.col];
+                ot[it] *= 1.f / den;
+            }
+        }
         // lane: token it*16 + (lane % 16), columns col + 4 (lane / 16) .. +3
         if constexpr (TO::bytes == 2) {
 #pragma unroll
@@ -559,10 +661,14 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         // the next chunk's rows go to LDS between the two halves of the
         // update's MFMAs, the gate scan after them
         seg_update_mfma_half(S, up, 0);
-        seg_stage_rows(buf[(c + 1) & 1], pf);
+        seg_stage_rows<true, NORM>(buf[(c + 1) & 1], pf);
         seg_update_mfma_half(S, up, 1);
-        seg_stage_gates(buf[(c + 1) & 1], pf);
-        seg_fetch(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
+        seg_stage_gates<true, NORM>(buf[(c + 1) & 1], pf);
+        if constexpr (NORM) {
+            seg_z_update(zacc, bb, wave);
+            if (ap.col == 0) *reinterpret_cast<f32x4*>(&zb[(c + 1) & 1][wave * 16 + ap.row0]) = zacc;
+        }
+        seg_fetch<true, !NORM>(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         // checkpoint: this wave's columns of the state after chunk c (the
         // segment starts sg.g * lseg tokens into its sequence)
         const int cs = CKPT && n == SC ? ckpt_slot(ck, sg.b, sg.g * lseg + (c + 1) * SC, n_slots) : -1;
@@ -584,6 +690,9 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * SD + col + ap.col] = S[mt][r];
+        }
+        if constexpr (NORM) {
+            if (ap.col == 0) *reinterpret_cast<f32x4*>(zpool + zoff + wave * 16 + ap.row0) = zacc;
         }
     }
 }
@@ -609,39 +718,55 @@ bool gla_seg_supported(const ChunkArgs& a) {
 }
 
 size_t gla_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
+    // per (segment, head): the log2 decay total, a 64 KiB state slot and (for
+    // normalised linear attention) a 512-byte normaliser slot
     const long maxseg = seg_count_bound(n_seqs, n_tokens, seg_len(n_tokens, n_heads));
     return align256s(sizeof(float) * maxseg * n_heads) +
-           static_cast<size_t>(maxseg) * n_heads * SD * SD * sizeof(float);
+           static_cast<size_t>(maxseg) * n_heads * SD * SD * sizeof(float) +
+           static_cast<size_t>(maxseg) * n_heads * SD * sizeof(float);
 }
 
-hipError_t launch_gla_seg(const ChunkArgs& a, hipStream_t s) {
+namespace {
+
+template <bool NORM>
+hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
     const int lseg = seg_len(a.n_tokens, a.n_heads);
     const long maxseg = seg_count_bound(a.n_seqs, a.n_tokens, lseg);
     char* ws = static_cast<char*>(a.workspace);
     float* wlam = reinterpret_cast<float*>(ws);
     float* wstate = reinterpret_cast<float*>(ws + align256s(sizeof(float) * maxseg * a.n_heads));
+    float* wz = wstate + static_cast<size_t>(maxseg) * a.n_heads * SD * SD;
+    const float* alpha = NORM ? nullptr : a.alpha;
     const dim3 grid(static_cast<unsigned>(maxseg * a.n_heads));
-    hipLaunchKernelGGL(gla_seg_state, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
-                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam);
+    hipLaunchKernelGGL(gla_seg_state<NORM>, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
+                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam,
+                       a.zpool, wz);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
     auto out_pass = [&](auto kern, auto* o) {
         hipLaunchKernelGGL(kern, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
-                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
+                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), alpha,
                            a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, wstate, wlam, ck, o);
+                           a.zero_init, lseg, wstate, wlam, ck, a.zpool, wz, a.eps, o);
     };
     // the checkpoint stores are compiled in only where they are asked for
-    if (a.out_bf16) {
-        if (ck.slots) out_pass(gla_seg_out<BF16, true>, static_cast<uint16_t*>(a.o));
-        else out_pass(gla_seg_out<BF16, false>, static_cast<uint16_t*>(a.o));
-    } else {
-        if (ck.slots) out_pass(gla_seg_out<F32, true>, static_cast<float*>(a.o));
-        else out_pass(gla_seg_out<F32, false>, static_cast<float*>(a.o));
+    if constexpr (!NORM) {
+        if (ck.slots) {
+            if (a.out_bf16) out_pass(gla_seg_out<BF16, true, false>, static_cast<uint16_t*>(a.o));
+            else out_pass(gla_seg_out<F32, true, false>, static_cast<float*>(a.o));
+            return hipGetLastError();
+        }
     }
+    if (a.out_bf16) out_pass(gla_seg_out<BF16, false, NORM>, static_cast<uint16_t*>(a.o));
+    else out_pass(gla_seg_out<F32, false, NORM>, static_cast<float*>(a.o));
     return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_gla_seg(const ChunkArgs& a, hipStream_t s) { return launch_seg<false>(a, s); }
+hipError_t launch_lin_attn_seg(const ChunkArgs& a, hipStream_t s) { return launch_seg<true>(a, s); }
 
 }  // namespace gla

@@ -92,6 +92,7 @@ size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv
 bool gla_seg_supported(const ChunkArgs& a);
 size_t gla_seg_workspace(int n_seqs, int n_tokens, int n_heads);
 hipError_t launch_gla_seg(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_lin_attn_seg(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_gdn_chunk(const ChunkArgs& a, hipStream_t s);
 size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);

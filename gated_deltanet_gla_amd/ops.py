@@ -238,17 +238,23 @@ def gla_state_copy(state_pool, src_slots, dst_slots):
 
 
 def lin_attn_chunk_fwd(q, k, v, cu_seqlens, state_pool, norm_pool, slot_idx, *, chunk=64,
-                       eps=1e-6, out_dtype=None, zero_init=False, o=None):
+                       eps=1e-6, out_dtype=None, zero_init=False, o=None, workspace=None):
     """Normalised linear attention (phi = elu + 1), chunked; updates
     state_pool[slot_idx] and norm_pool[slot_idx] ([n_slots, H, dk] fp32) in
     place, returns o."""
     N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, None, cu_seqlens, state_pool, slot_idx,
                                                out_dtype, o)
     _check(norm_pool, "norm_pool", torch.float32, 3)
+    B = cu_seqlens.shape[0] - 1
+    need = _lib.lib().lin_attn_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _lib.call("lin_attn_chunk_fwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
-              cu_seqlens.shape[0] - 1, N, H, dk, dv, chunk, _DT[q.dtype], _DT[out_dtype],
+              B, N, H, dk, dv, chunk, _DT[q.dtype], _DT[out_dtype],
               state_pool.data_ptr(), norm_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
-              _lib.GLA_ZERO_INIT if zero_init else 0, float(eps), o.data_ptr(), _stream(q.device))
+              _lib.GLA_ZERO_INIT if zero_init else 0, float(eps), o.data_ptr(), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(),
+              _stream(q.device))
     return o
 
 

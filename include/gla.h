@@ -272,16 +272,22 @@ GLA_API int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, 
  * the normaliser z from norm_pool[slot_idx[b]] (both zero with
  * GLA_ZERO_INIT); both are written back in place.  norm_pool
  * [n_slots, n_heads, dk] fp32.  Other arguments and the layout as
- * gla_chunk_fwd (no alpha, no workspace); eps >= 0 and finite
- * (GLA_ESHAPE otherwise).  For bf16 inputs phi(q) and phi(k) are rounded to
- * bf16 before the contractions.
+ * gla_chunk_fwd (no alpha); eps >= 0 and finite (GLA_ESHAPE otherwise).
+ * Requires workspace of lin_attn_chunk_workspace_bytes() bytes (may be 0):
+ * for bf16 inputs with d_k = d_v = 128 and chunk 64 the sequences are cut
+ * into segments as in gla_chunk_fwd, and each segment's sum of phi(k) is
+ * handed on with its state.  For bf16 inputs phi(q) and phi(k) are rounded
+ * to bf16 before the contractions.
  */
 GLA_API int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
                   const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
                   int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
                   gla_dtype in_dtype, gla_dtype out_dtype,
                   float* state_pool, float* norm_pool, int32_t n_slots,
-                  const int32_t* slot_idx, uint32_t flags, float eps, void* o, void* stream);
+                  const int32_t* slot_idx, uint32_t flags, float eps, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+GLA_API size_t lin_attn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                  int32_t dk, int32_t dv, int32_t chunk);
 
 /*
  * lin_attn_decode_step -- one token per request of lin_attn_chunk_fwd's

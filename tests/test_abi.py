@@ -185,15 +185,20 @@ def test_chunk_ckpt_validation():
 
 def test_lin_attn_validation():
     L = _lib.lib()
-    # q k v cu B N H dk dv C idt odt pool zpool n_slots slots flags eps o stream
+    # q k v cu B N H dk dv C idt odt pool zpool n_slots slots flags eps o ws wsb stream
     base = [FAKE, FAKE, FAKE, FAKE, 2, 10, 4, 64, 64, 64, 1, 1, FAKE, FAKE, 4, FAKE, 0, 1e-6, FAKE,
-            None]
+            None, 0, None]
     for i, bad, st in [(0, None, -1), (13, None, -1), (12, None, -1), (3, None, -1),
                        (7, 96, -2), (9, 48, -4), (10, 4, -3), (17, -1.0, -2),
                        (17, float("inf"), -2), (17, float("nan"), -2)]:
         args = list(base)
         args[i] = bad
         assert L.lin_attn_chunk_fwd(*args) == st, (i, bad)
+    need = L.lin_attn_chunk_workspace_bytes(2, 10, 4, 128, 128, 64)
+    assert need == L.gla_chunk_workspace_bytes(2, 10, 4, 128, 128, 64) > 0
+    args = list(base)
+    args[7] = args[8] = 128
+    assert L.lin_attn_chunk_fwd(*args) == _lib.GLA_EWORKSPACE
     # q k v R H dk dv idt odt pool zpool n_slots slots eps o stream
     dbase = [FAKE, FAKE, FAKE, 8, 16, 128, 128, 1, 1, FAKE, FAKE, 32, FAKE, 1e-6, FAKE, None]
     for i, bad, st in [(0, None, -1), (10, None, -1), (14, None, -1), (5, 8, -2), (13, -2.0, -2)]:

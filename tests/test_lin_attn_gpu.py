@@ -71,6 +71,20 @@ def test_lin_attn_chunk_zero_init_and_eps(dtype):
         _check_all(w, o, pool, zpool, _ref(w, eps), dtype)
 
 
+@pytest.mark.parametrize("zero_init", [False, True])
+@pytest.mark.parametrize("lengths,H", [([1000, 77, 0, 640, 300], 2), ([2050, 256, 64], 3),
+                                       ([257, 1], 1)])
+def test_lin_attn_segmented_parity(lengths, H, zero_init):
+    """bf16, d = 128, chunk 64: sequences cut into segments of 256 tokens
+    (several per sequence here), each segment's sum of phi(k) handed on
+    with its state."""
+    note(f"lin_attn segmented lengths={lengths} H={H} zero_init={zero_init}")
+    w = synth.lin_attn_varlen(650 + H + len(lengths), lengths, H, 128, 128, dtype="bf16", chunk=64,
+                              zero_init=zero_init)
+    o, pool, zpool = _chunk(w)
+    _check_all(w, o, pool, zpool, _ref(w), "bf16")
+
+
 def test_lin_attn_bf16_output_is_rne_of_fp32():
     w = synth.lin_attn_varlen(611, [300, 40], 4, 128, 128, dtype="bf16")
     note("lin_attn bf16-out")
