@@ -228,8 +228,9 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<WQ>& pf, const uint16_t* q
     pf.n = n;
 }
 
-// phi(x) = elu(x) + 1 on 8 packed bf16 values
-__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// phi(x) = elu(x) + 1 on 8 packed bf16 values (the hardware exp: the result
+// is rounded to bf16 right after)
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ u32x4 phi8(u32x4 w) {
     u32x4 r;
 #pragma unroll
@@ -460,7 +461,6 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     SegPrefetch<true> pf;
     seg_fetch<true, !NORM>(pf, q, k, v, alpha, tok(0), rows(0), sg.h, H);     // in flight during the fold
     const long zoff = (static_cast<long>(sg.slot) * H + sg.h) * SD;
-    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};   // NORM: z rows wave*16 + row0 + r (every column the same)
 
     // ---- entry state of this segment
     f32x4 S[8];
@@ -482,7 +482,9 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         }
     }
     if constexpr (NORM) {
+        // entry normaliser z_in: rows wave*16 + row0 .. + 3
         const int zr = wave * 16 + ap.row0;
+        f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
         if (sg.nseg <= 1) {
             if (!zero_init) zacc = *reinterpret_cast<const f32x4*>(zpool + zoff + zr);
         } else {
@@ -598,7 +600,15 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             const float* zin = zb[c & 1];
             float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc += bf16_bits_to_f32(bb.q[i][d0 + e]) * zin[d0 + e];
+            for (int h8 = 0; h8 < 2; ++h8) {
+                const u32x4 qw = *reinterpret_cast<const u32x4*>(&bb.q[i][d0 + 8 * h8]);
+                const f32x4 z0 = *reinterpret_cast<const f32x4*>(zin + d0 + 8 * h8);
+                const f32x4 z1 = *reinterpret_cast<const f32x4*>(zin + d0 + 8 * h8 + 4);
+                acc += __uint_as_float(qw.x << 16) * z0.x + __uint_as_float(qw.x & 0xffff0000u) * z0.y;
+                acc += __uint_as_float(qw.y << 16) * z0.z + __uint_as_float(qw.y & 0xffff0000u) * z0.w;
+                acc += __uint_as_float(qw.z << 16) * z1.x + __uint_as_float(qw.z & 0xffff0000u) * z1.y;
+                acc += __uint_as_float(qw.w << 16) * z1.z + __uint_as_float(qw.w & 0xffff0000u) * z1.w;
+            }
             acc += __shfl_xor(acc, 1, 64);
             acc += __shfl_xor(acc, 2, 64);
             acc += __shfl_xor(acc, 4, 64);
@@ -665,8 +675,12 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         seg_update_mfma_half(S, up, 1);
         seg_stage_gates<true, NORM>(buf[(c + 1) & 1], pf);
         if constexpr (NORM) {
-            seg_z_update(zacc, bb, wave);
-            if (ap.col == 0) *reinterpret_cast<f32x4*>(&zb[(c + 1) & 1][wave * 16 + ap.row0]) = zacc;
+            // z_in of the next chunk = z_in + this chunk's sums of phi(k)
+            f32x4 zc = {0.f, 0.f, 0.f, 0.f};
+            seg_z_update(zc, bb, wave);
+            const int zr = wave * 16 + ap.row0;
+            if (ap.col == 0)
+                *reinterpret_cast<f32x4*>(&zb[(c + 1) & 1][zr]) = *reinterpret_cast<const f32x4*>(&zb[c & 1][zr]) + zc;
         }
         seg_fetch<true, !NORM>(pf, q, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         // checkpoint: this wave's columns of the state after chunk c (the
@@ -692,7 +706,8 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * SD + col + ap.col] = S[mt][r];
         }
         if constexpr (NORM) {
-            if (ap.col == 0) *reinterpret_cast<f32x4*>(zpool + zoff + wave * 16 + ap.row0) = zacc;
+            // z after the last chunk (the loop ends with a barrier)
+            if (tid < SD) zpool[zoff + tid] = zb[nch & 1][tid];
         }
     }
 }
