@@ -265,9 +265,9 @@ def bench_mixed(torch, G, synth, dev, steps, warmup):
             "GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 (profiles/traffic.json),
-    or None when the kernel's sources changed since the counters were taken."""
+def _profile_entry(kernel: str):
+    """The rocprofv3 counter entry of a call (profiles/traffic.json), or None
+    when the kernel's sources changed since the counters were taken."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
@@ -277,11 +277,22 @@ def measured_traffic(kernel: str):
         for src in ent["sources"]:
             with open(os.path.join(ROOT, src), "rb") as f:
                 m.update(f.read())
-        if m.hexdigest() != ent["sha256"]:
-            return None
-        return ent["fetch_bytes"] + ent["write_bytes"]
+        return ent if m.hexdigest() == ent["sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per call measured with rocprofv3 (FETCH_SIZE + WRITE_SIZE)."""
+    ent = _profile_entry(kernel)
+    return None if ent is None else ent["fetch_bytes"] + ent["write_bytes"]
+
+
+def measured_mfma(kernel: str):
+    """rocprofv3 MfmaUtil per kernel (% of SIMD cycles with the MFMA unit
+    busy) and the MFMA flops the call executes (SQ_INSTS_VALU_MFMA_MOPS_*)."""
+    ent = _profile_entry(kernel)
+    return None if ent is None else ent.get("mfma")
 
 
 def calib_copy(torch):
@@ -373,7 +384,8 @@ def main():
                          "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic("gla_chunk_fwd"),
                          "kernel": "gla_chunk_fwd (gla_seg_state + gla_seg_out)",
                          "algorithmic_bytes": head["bytes"],
-                         "mfma_frac": head["flops"] / (head["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+                         "mfma_frac": head["flops"] / (head["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "mfma_counters": measured_mfma("gla_chunk_fwd")},
         })
     else:
         out.update({"value": None, "ms_per_step": None, "config": {"workload": args.only}})
@@ -404,7 +416,9 @@ def main():
         ach = r["bytes"] / (r["ms"] * 1e-3) / 1e9
         other["gdn_prefill"] = {"workload": r["workload"], "tokens_per_s": r["tokens_per_s"],
                                 "ms": r["ms"], "hbm_frac": ach / HBM_PEAK_GBPS,
-                                "mfma_frac": r["flops"] / (r["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+                                "mfma_frac": r["flops"] / (r["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                "traffic": measured_traffic("gdn_chunk_fwd"),
+                                "mfma_counters": measured_mfma("gdn_chunk_fwd")}
     if "gdn_prefill_ckpt" in res:
         r = res["gdn_prefill_ckpt"]
         other["gdn_prefill_ckpt"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s")}
