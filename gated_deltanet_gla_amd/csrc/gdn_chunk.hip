@@ -229,8 +229,10 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
                         acc[r] = (j <= i) ? acc[r] * __expf(sm.g[i] - sm.g[j]) : 0.f;
                     }
                 }
-                O::store4(planes + 2 * C * C + i * C + pj * 16 + ap.row0,
-                          planes + 3 * C * C + i * C + pj * 16 + ap.row0, acc);
+                // 32-column blocks wholly above the diagonal are never read
+                if ((pj * 16) / 32 * 32 <= pi * 16 + 15)
+                    O::store4(planes + 2 * C * C + i * C + pj * 16 + ap.row0,
+                              planes + 3 * C * C + i * C + pj * 16 + ap.row0, acc);
             }
         }
     }
@@ -307,9 +309,11 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
             *reinterpret_cast<f32x4*>(dst + r * C + c) = *reinterpret_cast<const f32x4*>(&sm.tri.t[r][c]);
         }
     } else {
-        // T diag(beta) -> planes 0 (hi), 1 (lo)
+        // T diag(beta) -> planes 0 (hi), 1 (lo); 32-column blocks wholly
+        // above the diagonal of a 16-row block are never read
         for (int idx = threadIdx.x; idx < C * C / 4; idx += NT) {
             const int r = (idx * 4) / C, c = (idx * 4) % C;
+            if (c / 32 * 32 > (r / 16) * 16 + 15) continue;
             f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.tri.t[r][c]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) tv[e] *= sm.beta[c + e];
@@ -722,9 +726,14 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) {
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-                dst[pl][ks] = rt.load16(static_cast<uint32_t>(
-                    ((plane0 + pl) * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2));
+            for (int ks = 0; ks < KSC; ++ks) {
+                // columns 32ks.. lie wholly above the diagonal of this row
+                // block: never used, so the offset points past the resource
+                // (reads zero, moves no bytes) and prep does not write them
+                const uint32_t offb = static_cast<uint32_t>(
+                    ((plane0 + pl) * C * C + (it * 16 + (lane & 15)) * C + 32 * ks + (lane >> 4) * 8) * 2);
+                dst[pl][ks] = rt.load16(32 * ks <= it * 16 + 15 ? offb : 0x80000000u);
+            }
         }
     };
 
