@@ -99,6 +99,22 @@ def timed(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps   # ms per call
 
 
+def per_call_ms(torch, fn, n, offset=0):
+    """Each of n calls between its own pair of HIP events on the current
+    stream (after the timed region): median, p10 and p90 in ms."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(offset + i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"p10": float(np.percentile(t, 10)), "median": float(np.median(t)),
+            "p90": float(np.percentile(t, 90)), "calls": n}
+
+
 def bench_gla_prefill(torch, G, synth, dev, steps, warmup):
     w = synth.prefill_gla()
     N, H, d = w.n_tokens, w.n_heads, w.dk
@@ -116,11 +132,12 @@ def bench_gla_prefill(torch, G, synth, dev, steps, warmup):
         G.gla_chunk_fwd(q, k, v, a, cu, pool, slots, chunk=w.chunk, zero_init=True, o=o,
                         workspace=ws)
     ms = timed(torch, step, steps, warmup)
+    dist = per_call_ms(torch, step, max(steps, 20), warmup + steps)
     nbytes = (3 * N * H * d * 2) + N * H * 4 + N * H * d * 2 + w.n_seqs * H * d * d * 4
     flops = N * H * (2 * w.chunk * (2 * d) + 4 * d * d)
     return {"workload": w.name, "ms": ms, "tokens_per_s": N / (ms * 1e-3), "bytes": nbytes,
             "flops": flops, "n_tokens": N, "batch": w.n_seqs, "seq_len": N // w.n_seqs, "heads": H,
-            "d": d, "chunk": w.chunk}
+            "d": d, "chunk": w.chunk, "per_call_ms": dist}
 
 
 def bench_gdn_prefill(torch, G, synth, dev, steps, warmup):
@@ -162,8 +179,10 @@ def bench_decode(torch, G, synth, dev, steps, warmup, gdn):
         else:
             G.gla_decode_step(q, k, v, a, pool, sl, o=o)
     ms = timed(torch, step, steps, warmup)
+    dist = per_call_ms(torch, step, max(steps, 20), warmup + steps)
     nbytes = R * H * (2 * d * d * 4 + 4 * d * 2 + (8 if gdn else 4))
-    return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
+    return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
+            "per_call_ms": dist}
 
 
 def bench_decode_multi(torch, G, synth, dev, steps, warmup, gdn):
@@ -386,6 +405,7 @@ def main():
                          "algorithmic_bytes": head["bytes"],
                          "mfma_frac": head["flops"] / (head["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                          "mfma_counters": measured_mfma("gla_chunk_fwd")},
+            "per_call_ms": head["per_call_ms"],
         })
     else:
         out.update({"value": None, "ms_per_step": None, "config": {"workload": args.only}})
@@ -400,6 +420,8 @@ def main():
             "frac_of_peak": {"gla": res["gla_decode"]["GBps"] / HBM_PEAK_GBPS,
                              "gdn": res["gdn_decode"]["GBps"] / HBM_PEAK_GBPS},
             "ms": {"gla": res["gla_decode"]["ms"], "gdn": res["gdn_decode"]["ms"]},
+            "per_call_ms": {"gla": res["gla_decode"]["per_call_ms"],
+                            "gdn": res["gdn_decode"]["per_call_ms"]},
             "workload": "256 requests x 16 heads, 128x128 fp32 states, 1024-slot pool, in place"}
     if "gla_decode_multi" in res:
         out["decode_multi_hbm_GBps"] = {
