@@ -243,7 +243,9 @@ __device__ __forceinline__ u32x4 phi8(u32x4 w) {
 // sequence stay zero, since phi(0) = 1 would count them).
 template <bool WQ, bool NORM = false, class Buf>
 __device__ __forceinline__ void seg_stage_rows(Buf& bb, const SegPrefetch<WQ>& pf) {
-    const int tid = threadIdx.x;
+    // NORM compares rows with n: keep that row index from being held across
+    // the chunk loop
+    const int tid = NORM ? opaque(static_cast<int>(threadIdx.x)) : static_cast<int>(threadIdx.x);
 #pragma unroll
     for (int u = 0; u < SegPrefetch<WQ>::NV; ++u) {
         const int xx = tid + u * ST;
@@ -300,8 +302,9 @@ __device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
 template <class Buf>
 __device__ __forceinline__ void seg_z_update(f32x4& z, const Buf& bb, int wave) {
     const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    const int m0 = opaque(wave * 16);     // recomputed per chunk, not held across the loop
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) z = mfma_bf16(frag_km_split(&bb.k[0][0], LK, wave * 16, 32 * ks), ones, z);
+    for (int ks = 0; ks < 2; ++ks) z = mfma_bf16(frag_km_split(&bb.k[0][0], LK, m0, 32 * ks), ones, z);
 }
 
 // V^T operand of this wave's 16 columns for the two 32-token halves of the
@@ -535,7 +538,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             float rs = (pt[0] + pt[1]) + (pt[2] + pt[3]);
             rs += __shfl_xor(rs, 16, 64);
             rs += __shfl_xor(rs, 32, 64);
-            if ((threadIdx.x & 63) < 16) dpart[t][ap.col] = rs;
+            if ((threadIdx.x & 63) < 16) dpart[t][opaque(ap.col)] = rs;
         }
     };
 
@@ -595,8 +598,10 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 #pragma unroll
         for (int it = 0; it < 4; ++it) ot[it] *= bb.eg[it * 16 + ap.col];
         if constexpr (NORM) {
-            // phi(q_i) . z_in: 8 threads per row, 16 dimensions each
-            const int i = tid >> 3, d0 = (tid & 7) * 16;
+            // phi(q_i) . z_in: 8 threads per row, 16 dimensions each (the
+            // lane offsets are recomputed each chunk, not held across the loop)
+            const int tq = opaque(tid);
+            const int i = tq >> 3, d0 = (tq & 7) * 16;
             const float* zin = zb[c & 1];
             float acc = 0.f;
 #pragma unroll
@@ -612,7 +617,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             acc += __shfl_xor(acc, 1, 64);
             acc += __shfl_xor(acc, 2, 64);
             acc += __shfl_xor(acc, 4, 64);
-            if ((tid & 7) == 0) qzb[i] = acc;
+            if ((tq & 7) == 0) qzb[i] = acc;
         }
         lds_barrier();
 
@@ -646,12 +651,13 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             ot[it] = mfma_bf16(vf[1], pp[it + 2][1], ot[it]);
         }
         if constexpr (NORM) {
+            const int lc = opaque(ap.col);
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
-                const int i = it * 16 + ap.col;
+                const int i = it * 16 + lc;
                 float den = qzb[i] + eps;
 #pragma unroll
-                for (int jt = 0; jt <= it; ++jt) den += dpart[it * (it + 1) / 2 + jt][ap.col];
+                for (int jt = 0; jt <= it; ++jt) den += dpart[it * (it + 1) / 2 + jt][lc];
                 ot[it] *= 1.f / den;
             }
         }
@@ -678,7 +684,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             // z_in of the next chunk = z_in + this chunk's sums of phi(k)
             f32x4 zc = {0.f, 0.f, 0.f, 0.f};
             seg_z_update(zc, bb, wave);
-            const int zr = wave * 16 + ap.row0;
+            const int zr = opaque(wave * 16 + ap.row0);
             if (ap.col == 0)
                 *reinterpret_cast<f32x4*>(&zb[(c + 1) & 1][zr]) = *reinterpret_cast<const f32x4*>(&zb[c & 1][zr]) + zc;
         }
