@@ -204,7 +204,26 @@ def bench_decode_multi(torch, G, synth, dev, steps, warmup, gdn):
             G.gla_decode_multi(q, k, v, a, pool, slots, pos, o=o)
     ms = timed(torch, step, steps, warmup)
     nbytes = R * H * ((1 + J) * d * d * 4 + J * (4 * d * 2 + (8 if gdn else 4)))
-    return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes}
+    # replay strategy: verify with no state kept, then commit a random
+    # accepted prefix (0..4 tokens) in place by running the draft again
+    import numpy as np
+    none = dev(np.full((R, J), -1, np.int32))
+    acc = np.random.default_rng(7).integers(0, J + 1, size=R)
+    cpos = np.full((R, J), -1, np.int32)
+    for r in range(R):
+        if acc[r] > 0:
+            cpos[r, acc[r] - 1] = w.slot_idx[r]
+    cpos = dev(cpos)
+
+    def replay(i):
+        for pos_ in (none, cpos):
+            if gdn:
+                G.gdn_decode_multi(q, k, v, a, b, pool, slots, pos_, o=o)
+            else:
+                G.gla_decode_multi(q, k, v, a, pool, slots, pos_, o=o)
+    ms_r = timed(torch, replay, steps, warmup)
+    return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
+            "replay_ms": ms_r}
 
 
 def bench_gdn_prefill_ckpt(torch, G, synth, dev, steps, warmup):
@@ -430,6 +449,7 @@ def main():
             "frac_of_peak": {k: res[f"{k}_decode_multi"]["GBps"] / HBM_PEAK_GBPS
                              for k in ("gla", "gdn")},
             "ms": {k: res[f"{k}_decode_multi"]["ms"] for k in ("gla", "gdn")},
+            "replay_strategy_ms": {k: res[f"{k}_decode_multi"]["replay_ms"] for k in ("gla", "gdn")},
             "workload": "256 requests x 4 draft tokens x 16 heads, 128x128 fp32 states, state "
                         "after every position kept (1280-slot pool)"})
     other = {}

@@ -226,6 +226,15 @@ GLA_API int gdn_decode_step(const void* q, const void* k, const void* v, const f
  * by pos_slots must be distinct and distinct from the other requests'
  * slot_idx (a request may name its own slot).  With n_tok = 1 and
  * pos_slots = slot_idx this is gla_decode_step.
+ *
+ * The page's second way to roll back (replay the accepted updates instead
+ * of keeping every position) is the same call twice: verify with every
+ * pos_slots entry negative (the state is read once, nothing is written),
+ * then, once a_r tokens are accepted, call again on those tokens with
+ * pos_slots[r*n_tok + a_r - 1] = slot_idx[r] and every other entry
+ * negative (the state after a_r tokens is written in place; a_r = 0 writes
+ * nothing).  Per head that moves 64 KiB + 128 KiB of state instead of
+ * 64 KiB + n_tok x 64 KiB, at the price of recomputing the accepted steps.
  */
 GLA_API int gla_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
                      int32_t n_req, int32_t n_tok, int32_t n_heads, int32_t dk, int32_t dv,

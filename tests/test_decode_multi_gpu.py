@@ -175,3 +175,57 @@ def test_state_copy_matches_oracle(dk, dv, H):
     torch.cuda.synchronize()
     ref = oracle.state_copy(pool_h, src, dst)
     assert np.array_equal(pool.cpu().numpy(), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
+def test_speculative_replay_strategy(kind):
+    """Verify with no state kept, then commit the accepted prefix by
+    replaying it in place (the page's record-and-replay alternative):
+    verification outputs match the oracle and leave the pool untouched; the
+    committed slot equals the state after the accepted tokens."""
+    import gated_deltanet_gla_amd as G
+    R, J = 16, 4
+    w = synth.decode_multi(seed=44, n_req=R, n_tok=J, H=4, dk=128, dv=128, n_slots=R * (J + 1),
+                           gdn=(kind == "gdn"))
+    q, k, v, a = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha)
+    b = dev(w.beta) if kind == "gdn" else None
+    pool = dev(w.pool)
+    slots = dev(w.slot_idx)
+
+    def run(pos):
+        if kind == "gla":
+            return G.gla_decode_multi(q, k, v, a, pool, slots, dev(pos), out_dtype=torch.float32)
+        return G.gdn_decode_multi(q, k, v, a, b, pool, slots, dev(pos), out_dtype=torch.float32)
+
+    note(f"speculative replay {kind}: verify")
+    none = np.full((R, J), -1, np.int32)
+    o = run(none)
+    torch.cuda.synchronize()
+    if kind == "gla":
+        o_ref, _ = oracle.gla_decode_multi(w.q, w.k, w.v, w.alpha, w.pool, w.slot_idx, none)
+    else:
+        o_ref, _ = oracle.gdn_decode_multi(w.q, w.k, w.v, w.alpha, w.beta, w.pool, w.slot_idx, none)
+    check(host(o), o_ref, "bf16", "verify outputs")
+    assert np.array_equal(pool.cpu().numpy(), w.pool), "verification wrote state"
+
+    acc = np.random.default_rng(45).integers(0, J + 1, size=R)
+    commit = none.copy()
+    for r in range(R):
+        if acc[r] > 0:
+            commit[r, acc[r] - 1] = w.slot_idx[r]
+    note(f"speculative replay {kind}: commit")
+    run(commit)
+    torch.cuda.synchronize()
+    p = host(pool)
+    for r in range(R):
+        n = int(acc[r])
+        S0 = w.pool[w.slot_idx[r]]
+        if n == 0:
+            assert np.array_equal(pool[int(w.slot_idx[r])].cpu().numpy(), S0)
+            continue
+        if kind == "gla":
+            _, S = oracle.gla_sequence(w.q[r, :n], w.k[r, :n], w.v[r, :n], w.alpha[r, :n], S0=S0)
+        else:
+            _, S = oracle.gdn_sequence(w.q[r, :n], w.k[r, :n], w.v[r, :n], w.alpha[r, :n],
+                                       w.beta[r, :n], S0=S0)
+        check(p[w.slot_idx[r]], S, "bf16", f"committed state of request {r} ({n} accepted)")
