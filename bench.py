@@ -258,7 +258,7 @@ def bench_lin_attn(torch, G, synth, dev, steps, warmup):
     pool, zpool = dev(w.pool), dev(w.extra["zpool"])
     cu, slots = dev(w.cu_seqlens), dev(w.slot_idx)
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
-    ws = torch.empty(G.workspace_bytes("gla", w.n_seqs, N, H, d, d, 64), dtype=torch.uint8,
+    ws = torch.empty(G.workspace_bytes("lin", w.n_seqs, N, H, d, d, 64), dtype=torch.uint8,
                      device="cuda:0")
     ms = timed(torch, lambda i: G.lin_attn_chunk_fwd(q, k, v, cu, pool, zpool, slots, chunk=64,
                                                      o=o, workspace=ws), steps, warmup)

@@ -20,13 +20,10 @@ constexpr long kMaxWork = 1L << 26;
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GLA_OK : GLA_EHIP; }
 
-// Stands for the gate argument of the validators when the operation has no
-// gate (normalised linear attention); never dereferenced.
-const float* const kNoGate = reinterpret_cast<const float*>(alignof(float));
-
 bool is_eps(float eps) { return eps >= 0.f && eps <= 3.0e38f; }
 
-int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
+// need_alpha = false for the ungated operation (normalised linear attention).
+int check_chunk(const void* q, const void* k, const void* v, const float* alpha, bool need_alpha,
                 const float* beta, bool need_beta, const int32_t* cu_seqlens, int32_t n_seqs,
                 int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
                 int in_dtype, int out_dtype, const float* pool, int32_t n_slots,
@@ -46,8 +43,7 @@ int check_chunk(const void* q, const void* k, const void* v, const float* alpha,
     if (n_tokens > 0) {
         if (n_seqs < 1) return GLA_ESHAPE;
         if (!q || !k || !v || !o) return GLA_EPTR;
-        if (alpha == kNoGate) return GLA_OK;
-        if (!alpha || (need_beta && !beta)) return GLA_EPTR;
+        if ((need_alpha && !alpha) || (need_beta && !beta)) return GLA_EPTR;
     }
     return GLA_OK;
 }
@@ -66,7 +62,7 @@ int check_ckpt(int32_t n_seqs, int32_t chunk, int32_t interval, const int32_t* s
 }
 
 int check_decode(const void* q, const void* k, const void* v, const float* alpha,
-                 const float* beta, bool need_beta, int32_t n_req, int32_t n_heads, int32_t dk,
+                 bool need_alpha, const float* beta, bool need_beta, int32_t n_req, int32_t n_heads, int32_t dk,
                  int32_t dv, int in_dtype, int out_dtype, const float* pool, int32_t n_slots,
                  const int32_t* slot_idx, const void* o) {
     if (n_req < 0 || n_heads < 1) return GLA_ESHAPE;
@@ -76,8 +72,7 @@ int check_decode(const void* q, const void* k, const void* v, const float* alpha
     if (n_req == 0) return GLA_OK;
     if (n_slots < 1) return GLA_ESHAPE;
     if (!q || !k || !v || !pool || !slot_idx || !o) return GLA_EPTR;
-    if (alpha == kNoGate) return GLA_OK;
-    if (!alpha || (need_beta && !beta)) return GLA_EPTR;
+    if ((need_alpha && !alpha) || (need_beta && !beta)) return GLA_EPTR;
     return GLA_OK;
 }
 
@@ -129,7 +124,7 @@ int gla_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float*
     int st = check_ckpt(n_seqs, chunk, ckpt_interval, ckpt_slots, ckpt_stride);
     if (st != GLA_OK) return st;
     if (ckpt_stride == 0) ckpt_slots = nullptr;
-    st = check_chunk(q, k, v, alpha, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads, dk,
+    st = check_chunk(q, k, v, alpha, true, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads, dk,
                          dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (n_seqs == 0) return GLA_OK;
@@ -152,7 +147,7 @@ int gdn_chunk_fwd_ckpt(const void* q, const void* k, const void* v, const float*
     int st = check_ckpt(n_seqs, chunk, ckpt_interval, ckpt_slots, ckpt_stride);
     if (st != GLA_OK) return st;
     if (ckpt_stride == 0) ckpt_slots = nullptr;
-    st = check_chunk(q, k, v, alpha, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
+    st = check_chunk(q, k, v, alpha, true, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
                          chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (n_seqs == 0) return GLA_OK;
@@ -189,7 +184,7 @@ int gla_decode_step(const void* q, const void* k, const void* v, const float* al
                     int32_t n_heads, int32_t dk, int32_t dv, gla_dtype in_dtype,
                     gla_dtype out_dtype, float* state_pool, int32_t n_slots,
                     const int32_t* slot_idx, void* o, void* stream) {
-    int st = check_decode(q, k, v, alpha, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
+    int st = check_decode(q, k, v, alpha, true, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
                           out_dtype, state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK || n_req == 0) return st;
     gla::DecodeArgs a{q, k, v, alpha, nullptr, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
@@ -201,7 +196,7 @@ int gdn_decode_step(const void* q, const void* k, const void* v, const float* al
                     const float* beta, int32_t n_req, int32_t n_heads, int32_t dk, int32_t dv,
                     gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool, int32_t n_slots,
                     const int32_t* slot_idx, void* o, void* stream) {
-    int st = check_decode(q, k, v, alpha, beta, true, n_req, n_heads, dk, dv, in_dtype, out_dtype,
+    int st = check_decode(q, k, v, alpha, true, beta, true, n_req, n_heads, dk, dv, in_dtype, out_dtype,
                           state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK || n_req == 0) return st;
     gla::DecodeArgs a{q, k, v, alpha, beta, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
@@ -215,7 +210,7 @@ int gla_decode_multi(const void* q, const void* k, const void* v, const float* a
                      const int32_t* slot_idx, const int32_t* pos_slots, void* o, void* stream) {
     if (n_tok < 0 || (n_tok > 0 && n_req > 0 && !pos_slots)) return n_tok < 0 ? GLA_ESHAPE : GLA_EPTR;
     if (static_cast<long>(n_req) * n_tok * n_heads > kMaxWork) return GLA_ESHAPE;
-    int st = check_decode(q, k, v, alpha, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
+    int st = check_decode(q, k, v, alpha, true, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
                           out_dtype, state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK || n_req == 0 || n_tok == 0) return st;
     gla::DecodeArgs a{q, k, v, alpha, nullptr, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
@@ -230,7 +225,7 @@ int gdn_decode_multi(const void* q, const void* k, const void* v, const float* a
                      void* stream) {
     if (n_tok < 0 || (n_tok > 0 && n_req > 0 && !pos_slots)) return n_tok < 0 ? GLA_ESHAPE : GLA_EPTR;
     if (static_cast<long>(n_req) * n_tok * n_heads > kMaxWork) return GLA_ESHAPE;
-    int st = check_decode(q, k, v, alpha, beta, true, n_req, n_heads, dk, dv, in_dtype, out_dtype,
+    int st = check_decode(q, k, v, alpha, true, beta, true, n_req, n_heads, dk, dv, in_dtype, out_dtype,
                           state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK || n_req == 0 || n_tok == 0) return st;
     gla::DecodeArgs a{q, k, v, alpha, beta, n_req, n_heads, dk, dv, in_dtype == GLA_BF16,
@@ -256,7 +251,7 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const int32_
                        int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,
                        float* norm_pool, int32_t n_slots, const int32_t* slot_idx, uint32_t flags,
                        float eps, void* o, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_chunk(q, k, v, kNoGate, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads,
+    int st = check_chunk(q, k, v, nullptr, false, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads,
                          dk, dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
     if (st != GLA_OK) return st;
     if (!is_eps(eps)) return GLA_ESHAPE;
@@ -275,7 +270,7 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v, int32_t n_
                          int32_t n_heads, int32_t dk, int32_t dv, gla_dtype in_dtype,
                          gla_dtype out_dtype, float* state_pool, float* norm_pool, int32_t n_slots,
                          const int32_t* slot_idx, float eps, void* o, void* stream) {
-    int st = check_decode(q, k, v, kNoGate, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
+    int st = check_decode(q, k, v, nullptr, false, nullptr, false, n_req, n_heads, dk, dv, in_dtype,
                           out_dtype, state_pool, n_slots, slot_idx, o);
     if (st != GLA_OK) return st;
     if (!is_eps(eps)) return GLA_ESHAPE;

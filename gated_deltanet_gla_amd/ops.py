@@ -139,7 +139,10 @@ def gdn_chunk_fwd_ckpt(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, c
 
 
 def workspace_bytes(kind, n_seqs, n_tokens, n_heads, dk, dv, chunk):
-    fn = {"gla": "gla_chunk_workspace_bytes", "gdn": "gdn_chunk_workspace_bytes"}[kind]
+    """Workspace bytes of gla_chunk_fwd ("gla"), gdn_chunk_fwd ("gdn") or
+    lin_attn_chunk_fwd ("lin") for these sizes."""
+    fn = {"gla": "gla_chunk_workspace_bytes", "gdn": "gdn_chunk_workspace_bytes",
+          "lin": "lin_attn_chunk_workspace_bytes"}[kind]
     return getattr(_lib.lib(), fn)(n_seqs, n_tokens, n_heads, dk, dv, chunk)
 
 
