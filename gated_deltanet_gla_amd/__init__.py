@@ -5,7 +5,7 @@ The computation runs in the HIP library ``libgla_mi355x.so`` (C ABI in
 include/gla.h); ``ops`` is its thin torch binding.
 """
 from .ops import (gla_chunk_fwd, gdn_chunk_fwd, gla_decode_step, gdn_decode_step,  # noqa: F401
-                  gla_chunk_fwd_ckpt, gdn_chunk_fwd_ckpt, gla_decode_multi, gdn_decode_multi,
+                  gla_chunk_fwd_ckpt, gdn_chunk_fwd_ckpt, gdn_chunk_prep, gdn_chunk_run, gla_decode_multi, gdn_decode_multi,
                   gla_state_copy, lin_attn_chunk_fwd, lin_attn_decode_step, causal_conv1d_fwd,
                   workspace_bytes)
 

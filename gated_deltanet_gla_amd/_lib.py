@@ -28,6 +28,10 @@ SIGNATURES = {
     "gdn_chunk_fwd_ckpt": (ct.c_int, [_P, _P, _P, _F, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                       ct.c_int, ct.c_int, _F, _I32, _P, _U32, _I32, _P, _I32, _P,
                                       _P, _SZ, _P]),
+    "gdn_chunk_prep": (ct.c_int, [_P, _P, _F, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32, ct.c_int,
+                                  _P, _SZ, _P]),
+    "gdn_chunk_run": (ct.c_int, [_P, _P, _P, _F, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                 ct.c_int, ct.c_int, _F, _I32, _P, _U32, _P, _P, _SZ, _P]),
     "gla_chunk_workspace_bytes": (ct.c_size_t, [_I32] * 6),
     "gdn_chunk_workspace_bytes": (ct.c_size_t, [_I32] * 6),
     "gla_decode_step": (ct.c_int, [_P, _P, _P, _F, _I32, _I32, _I32, _I32, ct.c_int, ct.c_int,

@@ -180,6 +180,47 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
                               chunk, nullptr, 0, o, workspace, workspace_bytes, stream);
 }
 
+int gdn_chunk_prep(const void* q, const void* k, const float* alpha, const float* beta,
+                   const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                   int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (n_seqs < 0 || n_tokens < 0 || n_heads < 1) return GLA_ESHAPE;
+    if (!is_dim(dk) || !is_dim(dv)) return GLA_ESHAPE;
+    if (!is_chunk(chunk)) return GLA_ECHUNK;
+    if (!is_dtype(in_dtype)) return GLA_EDTYPE;
+    if (static_cast<long>(n_seqs) * n_heads > kMaxWork) return GLA_ESHAPE;
+    if (static_cast<long>(n_tokens) * n_heads > std::numeric_limits<int32_t>::max() / 128)
+        return GLA_ESHAPE;
+    if (n_tokens > 0 && n_seqs < 1) return GLA_ESHAPE;
+    if (n_seqs == 0) return GLA_OK;
+    if (!cu_seqlens) return GLA_EPTR;
+    if (n_tokens > 0 && (!q || !k || !alpha || !beta)) return GLA_EPTR;
+    const size_t need = gla::gdn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
+    gla::ChunkArgs a{q, k, nullptr, alpha, beta, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv,
+                     chunk, in_dtype == GLA_BF16, 0, nullptr, 0, nullptr, 0, nullptr, workspace,
+                     workspace_bytes, nullptr, chunk, 0, nullptr, 0.f, 1};
+    return hip_status(gla::launch_gdn_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_chunk_run(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype,
+                  gla_dtype out_dtype, float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_chunk(q, k, v, alpha, true, beta, true, cu_seqlens, n_seqs, n_tokens, n_heads,
+                         dk, dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
+    if (st != GLA_OK) return st;
+    if (n_seqs == 0) return GLA_OK;
+    const size_t need = gla::gdn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
+    gla::ChunkArgs a{q, k, v, alpha, beta, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
+                     in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,
+                     (flags & GLA_ZERO_INIT) ? 1 : 0, o, workspace, workspace_bytes, nullptr, chunk,
+                     0, nullptr, 0.f, 2};
+    return hip_status(gla::launch_gdn_chunk(a, static_cast<hipStream_t>(stream)));
+}
+
 int gla_decode_step(const void* q, const void* k, const void* v, const float* alpha, int32_t n_req,
                     int32_t n_heads, int32_t dk, int32_t dv, gla_dtype in_dtype,
                     gla_dtype out_dtype, float* state_pool, int32_t n_slots,

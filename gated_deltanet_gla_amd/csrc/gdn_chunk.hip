@@ -879,11 +879,14 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     int32_t* order = reinterpret_cast<int32_t*>(ws);
     ws += align256(sizeof(int32_t) * a.n_seqs);
     float* Tws = reinterpret_cast<float*>(ws);
+    const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
+    hipError_t e = hipSuccess;
+    // phase 1 (state-independent): chunk offsets, order, inverses / planes
+    if (a.gdn_phases != 2) {
     hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
                        a.n_tokens, C, 0, off, FAST ? order : nullptr);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
     if (a.n_tokens > 0) {
         // persistent: as many workgroups as are resident at once, striding over
         // the (chunk, head) items
@@ -895,6 +898,9 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    }
+    if (a.gdn_phases == 1) return hipSuccess;
+    // phase 2: the serial chunk loop
     if constexpr (FAST) {
         const long groups = (static_cast<long>(a.n_seqs) * a.n_heads + 7) / 8 * 8;
         const long blocks = groups * (DV / 16);

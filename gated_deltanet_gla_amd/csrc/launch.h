@@ -67,6 +67,7 @@ struct ChunkArgs {
     int ckpt_stride;
     float* zpool;                 // normalised linear attention: [n_slots, n_heads, dk]
     float eps;
+    int gdn_phases;               // Gated DeltaNet: 0 = prep then run, 1 = prep only, 2 = run only
 };
 
 struct ConvArgs {

@@ -138,6 +138,38 @@ def gdn_chunk_fwd_ckpt(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, c
     return o
 
 
+def gdn_chunk_prep(q, k, alpha, beta, cu_seqlens, workspace, *, n_dv, chunk=64):
+    """The state-independent part of gdn_chunk_fwd (chunk offsets, inverses,
+    planes) into `workspace`; follow it with gdn_chunk_run on the same
+    inputs and workspace.  n_dv = d_v of the values that run will get."""
+    for t, n in ((q, "q"), (k, "k")):
+        _check(t, n, (torch.float32, torch.bfloat16), 3)
+    _check(alpha, "alpha", torch.float32, 2)
+    _check(beta, "beta", torch.float32, 2)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    N, H, dk = q.shape
+    _lib.call("gdn_chunk_prep", q.data_ptr(), k.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+              cu_seqlens.data_ptr(), cu_seqlens.shape[0] - 1, N, H, dk, n_dv, chunk, _DT[q.dtype],
+              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+              _stream(q.device))
+
+
+def gdn_chunk_run(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, workspace, *, chunk=64,
+                  out_dtype=None, zero_init=False, o=None):
+    """The serial part of gdn_chunk_fwd, after gdn_chunk_prep on the same
+    inputs and workspace; updates state_pool[slot_idx] in place, returns o."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    _check(beta, "beta", torch.float32, 2)
+    _lib.call("gdn_chunk_run", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              beta.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.shape[0] - 1, N, H, dk, dv, chunk,
+              _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(), state_pool.shape[0],
+              slot_idx.data_ptr(), _lib.GLA_ZERO_INIT if zero_init else 0, o.data_ptr(),
+              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+              _stream(q.device))
+    return o
+
+
 def workspace_bytes(kind, n_seqs, n_tokens, n_heads, dk, dv, chunk):
     """Workspace bytes of gla_chunk_fwd ("gla"), gdn_chunk_fwd ("gdn") or
     lin_attn_chunk_fwd ("lin") for these sizes."""

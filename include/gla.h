@@ -170,6 +170,31 @@ GLA_API int gdn_chunk_fwd_ckpt(const void* q, const void* k, const void* v, cons
                   int32_t ckpt_stride, void* o,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gdn_chunk_prep + gdn_chunk_run -- gdn_chunk_fwd in its two parts, for
+ * callers that overlap the state-independent part with other work.
+ * gdn_chunk_prep computes, into the workspace, what does not depend on the
+ * state or on v: the per-sequence chunk offsets and order, and for every
+ * (chunk, head) the inverse T = (I + A)^-1 (with diag(beta) and the decayed
+ * scores P for bf16 inputs).  gdn_chunk_run then runs the serial chunk loop
+ * and must get the same q, k, alpha, beta, cu_seqlens, sizes, in_dtype and
+ * workspace, ordered after gdn_chunk_prep (same stream, or an event); v, the
+ * pool and the outputs are only touched by gdn_chunk_run.  Together they give
+ * exactly gdn_chunk_fwd's results.  Arguments as gdn_chunk_fwd.
+ */
+GLA_API int gdn_chunk_prep(const void* q, const void* k, const float* alpha, const float* beta,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk, gla_dtype in_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+GLA_API int gdn_chunk_run(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                  int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype,
+                  float* state_pool, int32_t n_slots, const int32_t* slot_idx,
+                  uint32_t flags, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes the chunked calls need for these sizes (an upper bound
  * that does not depend on the contents of cu_seqlens).  0 = none. */
 GLA_API size_t gla_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,

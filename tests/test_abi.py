@@ -207,3 +207,23 @@ def test_lin_attn_validation():
         assert L.lin_attn_decode_step(*args) == st, (i, bad)
     assert L.lin_attn_decode_step(None, None, None, 0, 16, 128, 128, 1, 1, None, None, 4, None,
                                   1e-6, None, None) == 0
+
+
+def test_gdn_prep_run_validation():
+    L = _lib.lib()
+    need = L.gdn_chunk_workspace_bytes(2, 10, 4, 128, 128, 64)
+    # q k alpha beta cu B N H dk dv C idt ws wsb stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 4, 128, 128, 64, 1, FAKE, need, None]
+    for i, bad, st in [(0, None, -1), (3, None, -1), (4, None, -1), (12, None, -5), (13, need - 1, -5),
+                       (8, 96, -2), (10, 48, -4), (11, 3, -3), (5, 0, -2)]:
+        args = list(base)
+        args[i] = bad
+        assert L.gdn_chunk_prep(*args) == st, (i, bad)
+    assert L.gdn_chunk_prep(None, None, None, None, None, 0, 0, 4, 128, 128, 64, 1, None, 0, None) == 0
+    a = _chunk_args()
+    rargs = [a["q"], a["k"], a["v"], a["alpha"], FAKE, a["cu"], a["B"], a["N"], a["H"], a["dk"],
+             a["dv"], a["C"], a["idt"], a["odt"], a["pool"], a["n_slots"], a["slots"], 0, a["o"],
+             None, 0, None]
+    assert L.gdn_chunk_run(*rargs) == _lib.GLA_EWORKSPACE
+    rargs[4] = None
+    assert L.gdn_chunk_run(*rargs) == _lib.GLA_EPTR

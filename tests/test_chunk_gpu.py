@@ -250,3 +250,22 @@ def test_degenerate_gates(kind, dtype, d, C):
     else:
         check(host(o), o_ref, dtype, "o")
         check(p, pool_ref[w.slot_idx], dtype, "state")
+
+
+@pytest.mark.parametrize("dtype,dk,C", [("bf16", 128, 64), ("f32", 32, 16)])
+def test_gdn_prep_then_run_equals_fwd(dtype, dk, C):
+    """gdn_chunk_prep followed by gdn_chunk_run gives gdn_chunk_fwd's
+    outputs and states bit for bit."""
+    import gated_deltanet_gla_amd as G
+    w = synth.random_varlen(90 + dk, [300, 1, 0, 129], 2, dk, dk, dtype=dtype, gdn=True, chunk=C)
+    note(f"gdn prep+run {dtype} dk={dk} C={C}")
+    q, k, v = dev(w.q, dtype), dev(w.k, dtype), dev(w.v, dtype)
+    a, b, cu, sl = dev(w.alpha), dev(w.beta), dev(w.cu_seqlens), dev(w.slot_idx)
+    p1, p2 = dev(w.pool), dev(w.pool)
+    ws = torch.empty(max(1, G.workspace_bytes("gdn", w.n_seqs, w.n_tokens, 2, dk, dk, C)),
+                     dtype=torch.uint8, device="cuda:0")
+    o1 = G.gdn_chunk_fwd(q, k, v, a, b, cu, p1, sl, chunk=C, out_dtype=torch.float32)
+    G.gdn_chunk_prep(q, k, a, b, cu, ws, n_dv=dk, chunk=C)
+    o2 = G.gdn_chunk_run(q, k, v, a, b, cu, p2, sl, ws, chunk=C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
