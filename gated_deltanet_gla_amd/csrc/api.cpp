@@ -274,17 +274,26 @@ int gdn_decode_multi(const void* q, const void* k, const void* v, const float* a
     return hip_status(gla::launch_gdn_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+int gla_slot_copy(void* buf, size_t slot_bytes, int32_t n_slots, const int32_t* src_slots,
+                  const int32_t* dst_slots, int32_t n_copy, void* stream) {
+    if (n_copy < 0 || n_slots < 0 || slot_bytes == 0 || slot_bytes % 16 != 0) return GLA_ESHAPE;
+    if (slot_bytes > (static_cast<size_t>(1) << 40)) return GLA_ESHAPE;
+    if (n_copy == 0) return GLA_OK;
+    if (n_slots < 1) return GLA_ESHAPE;
+    if (!buf || !src_slots || !dst_slots) return GLA_EPTR;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return GLA_EPTR;
+    const long pieces = (static_cast<long>(slot_bytes / 16) + 1023) / 1024;
+    if (static_cast<long>(n_copy) * pieces > kMaxWork) return GLA_ESHAPE;
+    gla::CopyArgs a{buf, static_cast<long>(slot_bytes), n_slots, src_slots, dst_slots, n_copy};
+    return hip_status(gla::launch_slot_copy(a, static_cast<hipStream_t>(stream)));
+}
+
 int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, int32_t dk, int32_t dv,
                    const int32_t* src_slots, const int32_t* dst_slots, int32_t n_copy,
                    void* stream) {
     if (n_copy < 0 || n_heads < 1 || n_slots < 0 || !is_dim(dk) || !is_dim(dv)) return GLA_ESHAPE;
-    if (n_copy == 0) return GLA_OK;
-    if (n_slots < 1) return GLA_ESHAPE;
-    if (!state_pool || !src_slots || !dst_slots) return GLA_EPTR;
-    const long pieces = (static_cast<long>(n_heads) * dk * dv / 4 + 1023) / 1024;
-    if (static_cast<long>(n_copy) * pieces > kMaxWork) return GLA_ESHAPE;
-    gla::CopyArgs a{state_pool, n_slots, n_heads, dk, dv, src_slots, dst_slots, n_copy};
-    return hip_status(gla::launch_state_copy(a, static_cast<hipStream_t>(stream)));
+    return gla_slot_copy(state_pool, static_cast<size_t>(n_heads) * dk * dv * sizeof(float),
+                         n_slots, src_slots, dst_slots, n_copy, stream);
 }
 
 int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,

@@ -346,26 +346,27 @@ lin_attn_decode_kernel(const typename TI::T* __restrict__ q, const typename TI::
     }
 }
 
-// Plain copy of whole slots (all heads): dst_slots[i] <- src_slots[i].  One
+// Plain copy of whole slots of a slot-strided buffer (a state pool, a
+// normaliser pool, a conv cache): dst_slots[i] <- src_slots[i].  One
 // workgroup per (pair, 16 KiB piece); 16-byte loads and stores.  A pair with
-// either slot out of range is skipped.
+// either slot out of range, or with src == dst, is skipped.
 __global__ void __launch_bounds__(256)
-state_copy_kernel(float* __restrict__ pool, long slot_vec4, int pieces, int n_slots,
-                  const int32_t* __restrict__ src_slots, const int32_t* __restrict__ dst_slots) {
+slot_copy_kernel(u32x4* __restrict__ buf, long slot_vec4, int pieces, int n_slots,
+                 const int32_t* __restrict__ src_slots, const int32_t* __restrict__ dst_slots) {
     const int pair = blockIdx.x / pieces;
     const int piece = blockIdx.x % pieces;
     const int src = src_slots[pair];
     const int dst = dst_slots[pair];
     if (src < 0 || src >= n_slots || dst < 0 || dst >= n_slots || src == dst) return;
-    const f32x4* __restrict__ from = reinterpret_cast<const f32x4*>(pool) + src * slot_vec4;
-    f32x4* __restrict__ to = reinterpret_cast<f32x4*>(pool) + dst * slot_vec4;
+    const u32x4* __restrict__ from = buf + src * slot_vec4;
+    u32x4* __restrict__ to = buf + dst * slot_vec4;
     constexpr int kPer = 4;     // 4 vectors per thread: 16 KiB per workgroup
     const long base = static_cast<long>(piece) * (256 * kPer) + threadIdx.x;
-    f32x4 x[kPer];
+    u32x4 x[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const long e = base + i * 256;
-        x[i] = e < slot_vec4 ? __builtin_nontemporal_load(from + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+        x[i] = e < slot_vec4 ? __builtin_nontemporal_load(from + e) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -476,12 +477,13 @@ hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_state_copy(const CopyArgs& a, hipStream_t s) {
+hipError_t launch_slot_copy(const CopyArgs& a, hipStream_t s) {
     if (a.n_copy == 0) return hipSuccess;
-    const long slot_vec4 = static_cast<long>(a.n_heads) * a.dk * a.dv / 4;
+    const long slot_vec4 = a.slot_bytes / 16;
     const int pieces = static_cast<int>((slot_vec4 + 1023) / 1024);
-    hipLaunchKernelGGL(state_copy_kernel, dim3(a.n_copy * pieces), dim3(256), 0, s, a.pool, slot_vec4,
-                       pieces, a.n_slots, a.src_slots, a.dst_slots);
+    hipLaunchKernelGGL(slot_copy_kernel, dim3(a.n_copy * pieces), dim3(256), 0, s,
+                       static_cast<u32x4*>(a.buf), slot_vec4, pieces, a.n_slots, a.src_slots,
+                       a.dst_slots);
     return hipGetLastError();
 }
 

@@ -39,8 +39,9 @@ struct LinDecodeArgs {
 };
 
 struct CopyArgs {
-    float* pool;
-    int n_slots, n_heads, dk, dv;
+    void* buf;               // [n_slots, slot_bytes]
+    long slot_bytes;         // a multiple of 16
+    int n_slots;
     const int32_t* src_slots;
     const int32_t* dst_slots;
     int n_copy;
@@ -85,7 +86,7 @@ struct ConvArgs {
 
 hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_state_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_slot_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s);
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s);

@@ -305,6 +305,20 @@ def lin_attn_decode_step(q, k, v, state_pool, norm_pool, slot_idx, *, eps=1e-6, 
     return o
 
 
+def gla_slot_copy(buf, src_slots, dst_slots):
+    """buf[dst_slots[i]] <- buf[src_slots[i]] for a slot-major buffer (a
+    normaliser pool, a conv cache), in place."""
+    _check(buf, "buf")
+    _check(src_slots, "src_slots", torch.int32, 1)
+    _check(dst_slots, "dst_slots", torch.int32, 1)
+    if src_slots.shape != dst_slots.shape:
+        raise ValueError("src_slots and dst_slots must have the same length")
+    slot_bytes = buf[0].numel() * buf.element_size() if buf.shape[0] > 0 else 16
+    _lib.call("gla_slot_copy", buf.data_ptr(), slot_bytes, buf.shape[0], src_slots.data_ptr(),
+              dst_slots.data_ptr(), src_slots.shape[0], _stream(buf.device))
+    return buf
+
+
 def causal_conv1d_fwd(x, w, cu_seqlens, conv_cache, slot_idx, *, zero_init=False, y=None):
     """Depthwise causal conv with per-slot cache (updated in place); returns y."""
     _check(x, "x", (torch.float32, torch.bfloat16), 2)

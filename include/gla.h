@@ -296,6 +296,19 @@ GLA_API int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, 
                    int32_t n_copy, void* stream);
 
 /*
+ * gla_slot_copy -- the same copy for any slot-strided buffer
+ * [n_slots, slot_bytes] (16-byte aligned, slot_bytes a multiple of 16): the
+ * normaliser pool of lin_attn_*, or the conv cache [n_slots, W-1, channels],
+ * which a saved prefix needs together with its state (section "Prefix
+ * caching has to be redone": the checkpoint there holds the states and the
+ * conv cache).  gla_state_copy is gla_slot_copy with slot_bytes =
+ * n_heads * dk * dv * 4.  Same skipping rules.
+ */
+GLA_API int gla_slot_copy(void* buf, size_t slot_bytes, int32_t n_slots,
+                  const int32_t* src_slots, const int32_t* dst_slots, int32_t n_copy,
+                  void* stream);
+
+/*
  * lin_attn_chunk_fwd -- normalised kernelised linear attention, chunked
  * prefill (page "Long context, fast inference, smart decoding, and life
  * beyond attention", section "Linear attention: removing softmax entirely"

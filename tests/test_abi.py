@@ -227,3 +227,15 @@ def test_gdn_prep_run_validation():
     assert L.gdn_chunk_run(*rargs) == _lib.GLA_EWORKSPACE
     rargs[4] = None
     assert L.gdn_chunk_run(*rargs) == _lib.GLA_EPTR
+
+
+def test_slot_copy_validation():
+    L = _lib.lib()
+    # buf slot_bytes n_slots src dst n stream
+    base = [FAKE, 12288, 8, FAKE, FAKE, 3, None]
+    for i, bad, st in [(0, None, -1), (3, None, -1), (4, None, -1), (1, 0, -2), (1, 20, -2),
+                       (2, 0, -2), (5, -1, -2), (0, FAKE + 4, -1)]:
+        args = list(base)
+        args[i] = bad
+        assert L.gla_slot_copy(*args) == st, (i, bad)
+    assert L.gla_slot_copy(None, 16, 0, None, None, 0, None) == 0

@@ -229,3 +229,23 @@ def test_speculative_replay_strategy(kind):
             _, S = oracle.gdn_sequence(w.q[r, :n], w.k[r, :n], w.v[r, :n], w.alpha[r, :n],
                                        w.beta[r, :n], S0=S0)
         check(p[w.slot_idx[r]], S, "bf16", f"committed state of request {r} ({n} accepted)")
+
+
+def test_slot_copy_conv_cache_and_normaliser():
+    """A saved prefix needs the conv cache copied with the state ("Prefix
+    caching has to be redone"): bf16 conv-cache slots [n, 3, 2048] and fp32
+    normaliser slots [n, 16, 128] copied bitwise."""
+    import gated_deltanet_gla_amd as G
+    rng = np.random.default_rng(46)
+    n = 12
+    cache = synth.round_bf16(rng.standard_normal((n, 3, 2048)).astype(np.float32))
+    zpool = rng.standard_normal((n, 16, 128)).astype(np.float32)
+    src = np.array([3, 7, 0, 11], np.int32)
+    dst = np.array([5, 1, 9, 2], np.int32)
+    note("slot copy conv cache + normaliser")
+    c_dev, z_dev = dev(cache, "bf16"), dev(zpool)
+    G.gla_slot_copy(c_dev, dev(src), dev(dst))
+    G.gla_slot_copy(z_dev, dev(src), dev(dst))
+    torch.cuda.synchronize()
+    assert np.array_equal(c_dev.float().cpu().numpy(), oracle.state_copy(cache, src, dst))
+    assert np.array_equal(z_dev.cpu().numpy(), oracle.state_copy(zpool, src, dst))
