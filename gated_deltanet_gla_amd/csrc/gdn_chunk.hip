@@ -43,6 +43,7 @@ namespace {
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr long kPrepBlocks = 768;    // 256 compute units x 3 resident prep workgroups
+constexpr long kWideMin = 1024;      // 16-column serial workgroups above which 32-column ones run
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -559,11 +560,11 @@ gdn_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
 constexpr int FW = 8;                 // waves of the bf16 serial kernel
 constexpr int FT = FW * 64;
 
-template <int DK, int C>
+template <int DK, int C, int BV_>
 struct GdnFastSmem {
-    static constexpr int BV = 16;
-    // rows of the v tile buffer: every thread stages one dword (FT / 8 rows
-    // of 16 values), so the staging has no thread-dependent branch
+    static constexpr int BV = BV_;
+    // rows of the v tile buffer: every thread stages one dword per 16
+    // columns (FT / 8 rows), so the staging has no thread-dependent branch
     static constexpr int VR = FT / 8 > C ? FT / 8 : C;
     static constexpr int LQ = DK + 8;
     static constexpr int LV = BV + 8;
@@ -583,16 +584,16 @@ struct GdnFastSmem {
     alignas(16) uint16_t udt[2][BV][LT];   // (diag(dec) U)^T (hi, lo)
 };
 
-template <int C, int DK>
+template <int C, int DK, int BV>
 struct GdnFastPrefetch {
     static constexpr int NQ = (C * DK / 8 + FT - 1) / FT;
     u32x4 q[NQ], k[NQ];
-    uint32_t v;        // two values of row tid / 8 of the v tile
+    uint32_t v[BV / 16];   // two values of row tid / 8 in each 16-column tile of v
     float a;           // raw gate of token `lane`; only the first n are valid
     int n;
 };
 
-template <int DK, int DV, int C, class TO, bool CKPT>
+template <int DK, int DV, int C, class TO, bool CKPT, int BV_>
 __global__ void __launch_bounds__(FT)
 gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, const float* __restrict__ alpha,
@@ -601,11 +602,12 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 int zero_init, const int32_t* __restrict__ off, const int32_t* __restrict__ order,
                 long n_chunks_max, const uint16_t* __restrict__ TP, Ckpt ck,
                 typename TO::T* __restrict__ o) {
-    using Sm = GdnFastSmem<DK, C>;
-    using PF = GdnFastPrefetch<C, DK>;
+    using Sm = GdnFastSmem<DK, C, BV_>;
+    using PF = GdnFastPrefetch<C, DK, BV_>;
     using O = Op<false>;
     constexpr int BV = Sm::BV, LQ = Sm::LQ, LT = Sm::LT;
     constexpr int NVT = DV / BV;
+    constexpr int NTL = BV / 16;                 // 16-column tiles of this workgroup
     constexpr int CT = C / 16;                   // 16-row blocks per chunk
     constexpr int KSD = DK / 32;                 // k steps over d_k
     constexpr int KSC = C / 32;                  // k steps over the chunk
@@ -649,10 +651,14 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const bool has_tile = wave < KT;
 
     float* Sg = pool + (static_cast<long>(slot) * H + h) * DK * DV;
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    if (has_tile && !zero_init) {
+    f32x4 S[NTL];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[r] = Sg[(wave * 16 + ap.row0 + r) * DV + col0 + ap.col];
+    for (int nt = 0; nt < NTL; ++nt) {
+        S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (has_tile && !zero_init) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[nt][r] = Sg[(wave * 16 + ap.row0 + r) * DV + col0 + nt * 16 + ap.col];
+        }
     }
 
     // rows of chunk c that belong to the sequence (<= 0 past its end)
@@ -675,7 +681,10 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             pf.q[u] = rq.load16_nt(offb);
             pf.k[u] = rk.load16_nt(offb);
         }
-        pf.v = __float_as_uint(rv.loadf_nt(static_cast<uint32_t>(((tid >> 3) * vstride + (tid & 7) * 2) * 2)));
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+            pf.v[j] = __float_as_uint(
+                rv.loadf_nt(static_cast<uint32_t>(((tid >> 3) * vstride + j * 16 + (tid & 7) * 2) * 2)));
         // rows past n get a gate of 1 when staged: a select on the loaded
         // value here would make the wave wait for this load right away
         pf.a = ra.loadf_nt(static_cast<uint32_t>(lane * H * 4));
@@ -704,10 +713,16 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 *reinterpret_cast<u32x4*>(&bb.k[row][vc * 8]) = pf.k[u];
             }
         }
-        *reinterpret_cast<uint32_t*>(&bb.v[tid >> 3][(tid & 7) * 2]) = pf.v;
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) *reinterpret_cast<uint32_t*>(&bb.v[tid >> 3][j * 16 + (tid & 7) * 2]) = pf.v[j];
     };
     auto write_state = [&]() {
-        if (has_tile) O::store4(&sm.st[0][ap.col][wave * 16 + ap.row0], &sm.st[1][ap.col][wave * 16 + ap.row0], S);
+        if (has_tile) {
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt)
+                O::store4(&sm.st[0][nt * 16 + ap.col][wave * 16 + ap.row0],
+                          &sm.st[1][nt * 16 + ap.col][wave * 16 + ap.row0], S[nt]);
+        }
     };
     // This wave's rows of T diag(beta) (x role) or P (q role), hi and lo, for
     // chunk c, as MFMA A operands; zero past the end.  The planes were just
@@ -749,35 +764,49 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         typename Sm::Buf& bb = sm.buf[c & 1];
         const int n = chunk_rows(c);
         const long tok0 = s0 + static_cast<long>(c) * C;
-        f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+        f32x4 qs[NTL];
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) qs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // ---- phase A: X = K S, Y = V - diag(exp g) X (x role); Q S (q role);
         // stage chunk c+1
         if (xrole) {
-            f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+            f32x4 xs[NTL];
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) xs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, 0, 32 * ks);
-                const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, 0, 32 * ks);
                 const bf16x8 kf = frag_kc(&bb.k[0][0], LQ, it * 16, 32 * ks);
-                xs = mfma_bf16(kf, sh, xs);
-                xs = mfma_bf16(kf, sl, xs);
-            }
-            f32x4 y;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = it * 16 + ap.row0 + r;
-                y[r] = bf16_bits_to_f32(bb.v[row][ap.col]) - bb.eg[row] * xs[r];
+                for (int nt = 0; nt < NTL; ++nt) {
+                    const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, nt * 16, 32 * ks);
+                    const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, nt * 16, 32 * ks);
+                    xs[nt] = mfma_bf16(kf, sh, xs[nt]);
+                    xs[nt] = mfma_bf16(kf, sl, xs[nt]);
+                }
             }
-            O::store4(&sm.yt[0][ap.col][it * 16 + ap.row0], &sm.yt[1][ap.col][it * 16 + ap.row0], y);
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                f32x4 y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = it * 16 + ap.row0 + r;
+                    y[r] = bf16_bits_to_f32(bb.v[row][nt * 16 + ap.col]) - bb.eg[row] * xs[nt][r];
+                }
+                O::store4(&sm.yt[0][nt * 16 + ap.col][it * 16 + ap.row0],
+                          &sm.yt[1][nt * 16 + ap.col][it * 16 + ap.row0], y);
+            }
         } else if (qrole) {
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
-                const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, 0, 32 * ks);
-                const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, 0, 32 * ks);
                 const bf16x8 qf = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
-                qs = mfma_bf16(qf, sh, qs);
-                qs = mfma_bf16(qf, sl, qs);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    const bf16x8 sh = frag_kc(&sm.st[0][0][0], LQ, nt * 16, 32 * ks);
+                    const bf16x8 sl = frag_kc(&sm.st[1][0][0], LQ, nt * 16, 32 * ks);
+                    qs[nt] = mfma_bf16(qf, sh, qs[nt]);
+                    qs[nt] = mfma_bf16(qf, sl, qs[nt]);
+                }
             }
         }
         stage(sm.buf[(c + 1) & 1]);
@@ -786,57 +815,69 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
         // ---- phase B: U = T diag(beta) Y (x role)
         if (xrole) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                if (32 * ks <= it * 16 + 15) {
-                    const bf16x8 yh = frag_kc(&sm.yt[0][0][0], LT, 0, 32 * ks);
-                    const bf16x8 yl = frag_kc(&sm.yt[1][0][0], LT, 0, 32 * ks);
-                    u = mfma_bf16(as_bf16x8(tpc[0][ks]), yh, u);
-                    u = mfma_bf16(as_bf16x8(tpc[0][ks]), yl, u);
-                    u = mfma_bf16(as_bf16x8(tpc[1][ks]), yh, u);
+            for (int nt = 0; nt < NTL; ++nt) {
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    if (32 * ks <= it * 16 + 15) {
+                        const bf16x8 yh = frag_kc(&sm.yt[0][0][0], LT, nt * 16, 32 * ks);
+                        const bf16x8 yl = frag_kc(&sm.yt[1][0][0], LT, nt * 16, 32 * ks);
+                        u = mfma_bf16(as_bf16x8(tpc[0][ks]), yh, u);
+                        u = mfma_bf16(as_bf16x8(tpc[0][ks]), yl, u);
+                        u = mfma_bf16(as_bf16x8(tpc[1][ks]), yh, u);
+                    }
                 }
-            }
-            O::store4(&sm.ut[0][ap.col][it * 16 + ap.row0], &sm.ut[1][ap.col][it * 16 + ap.row0], u);
-            f32x4 ud;
+                O::store4(&sm.ut[0][nt * 16 + ap.col][it * 16 + ap.row0],
+                          &sm.ut[1][nt * 16 + ap.col][it * 16 + ap.row0], u);
+                f32x4 ud;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ud[r] = u[r] * bb.dec[it * 16 + ap.row0 + r];
-            O::store4(&sm.udt[0][ap.col][it * 16 + ap.row0], &sm.udt[1][ap.col][it * 16 + ap.row0], ud);
+                for (int r = 0; r < 4; ++r) ud[r] = u[r] * bb.dec[it * 16 + ap.row0 + r];
+                O::store4(&sm.udt[0][nt * 16 + ap.col][it * 16 + ap.row0],
+                          &sm.udt[1][nt * 16 + ap.col][it * 16 + ap.row0], ud);
+            }
         }
         lds_barrier();
 
         // ---- phase C: outputs (q role) and the state hand-off (every wave)
         if (qrole) {
-            f32x4 acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = qs[r] * bb.eg[it * 16 + ap.row0 + r];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                if (32 * ks <= it * 16 + 15) {
-                    const bf16x8 uh = frag_kc(&sm.ut[0][0][0], LT, 0, 32 * ks);
-                    const bf16x8 ul = frag_kc(&sm.ut[1][0][0], LT, 0, 32 * ks);
-                    acc = mfma_bf16(as_bf16x8(tpc[0][ks]), uh, acc);
-                    acc = mfma_bf16(as_bf16x8(tpc[0][ks]), ul, acc);
-                    acc = mfma_bf16(as_bf16x8(tpc[1][ks]), uh, acc);
-                }
-            }
             // rows past the chunk's valid ones fall outside the resource
             const BufRsrc ro(o + tok0 * vstride + h * DV + col0, rows_extent(n, vstride * TO::bytes, BV * TO::bytes));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = it * 16 + ap.row0 + r;
-                const uint32_t offb = static_cast<uint32_t>((row * vstride + ap.col) * TO::bytes);
-                if constexpr (TO::bytes == 2) ro.store_b16(f32_to_bf16_bits(acc[r]), offb);
-                else ro.store_b32(__float_as_uint(acc[r]), offb);
+            for (int nt = 0; nt < NTL; ++nt) {
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = qs[nt][r] * bb.eg[it * 16 + ap.row0 + r];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    if (32 * ks <= it * 16 + 15) {
+                        const bf16x8 uh = frag_kc(&sm.ut[0][0][0], LT, nt * 16, 32 * ks);
+                        const bf16x8 ul = frag_kc(&sm.ut[1][0][0], LT, nt * 16, 32 * ks);
+                        acc = mfma_bf16(as_bf16x8(tpc[0][ks]), uh, acc);
+                        acc = mfma_bf16(as_bf16x8(tpc[0][ks]), ul, acc);
+                        acc = mfma_bf16(as_bf16x8(tpc[1][ks]), uh, acc);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = it * 16 + ap.row0 + r;
+                    const uint32_t offb = static_cast<uint32_t>((row * vstride + nt * 16 + ap.col) * TO::bytes);
+                    if constexpr (TO::bytes == 2) ro.store_b16(f32_to_bf16_bits(acc[r]), offb);
+                    else ro.store_b32(__float_as_uint(acc[r]), offb);
+                }
             }
         }
         if (has_tile) {
-            S *= bb.gamma;
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) S[nt] *= bb.gamma;
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
                 const bf16x8 a = frag_km_split(&bb.k[0][0], LQ, wave * 16, 32 * ks);
-                S = mfma_bf16(a, frag_kc_split(&sm.udt[0][0][0], LT, 0, 32 * ks), S);
-                S = mfma_bf16(a, frag_kc_split(&sm.udt[1][0][0], LT, 0, 32 * ks), S);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) {
+                    S[nt] = mfma_bf16(a, frag_kc_split(&sm.udt[0][0][0], LT, nt * 16, 32 * ks), S[nt]);
+                    S[nt] = mfma_bf16(a, frag_kc_split(&sm.udt[1][0][0], LT, nt * 16, 32 * ks), S[nt]);
+                }
             }
         }
         // checkpoint: this wave's state tile after chunk c (block-uniform test)
@@ -845,7 +886,10 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             float* Sc = pool + (static_cast<long>(cs) * H + h) * DK * DV +
                         opaque((wave * 16 + ap.row0) * DV + col0 + ap.col);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sc[r * DV] = S[r];
+            for (int nt = 0; nt < NTL; ++nt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sc[r * DV + nt * 16] = S[nt][r];
+            }
         }
         write_state();
         load_tp(tpc, c + 2);
@@ -862,7 +906,10 @@ gdn_fast_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     if (has_tile) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sg[(wave * 16 + ap.row0 + r) * DV + col0 + ap.col] = S[r];
+        for (int nt = 0; nt < NTL; ++nt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sg[(wave * 16 + ap.row0 + r) * DV + col0 + nt * 16 + ap.col] = S[nt][r];
+        }
     }
 }
 
@@ -903,7 +950,12 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     // phase 2: the serial chunk loop
     if constexpr (FAST) {
         const long groups = (static_cast<long>(a.n_seqs) * a.n_heads + 7) / 8 * 8;
-        const long blocks = groups * (DV / 16);
+        // 32 state columns per workgroup when there are workgroups to spare
+        // (at least four per compute unit at 16 columns): the per-chunk work
+        // that does not depend on the columns (staging q and k, the T / P
+        // planes, the barriers) is then shared by twice the columns
+        const bool wide = DV % 32 == 0 && groups * (DV / 16) >= kWideMin;
+        const long blocks = groups * (DV / (wide ? 32 : 16));
         const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
         auto serial = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(FT), 0, s,
@@ -914,8 +966,15 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
                                static_cast<typename TO::T*>(a.o));
         };
         // the checkpoint stores are compiled in only where they are asked for
-        if (ck.slots) serial(gdn_fast_kernel<DK, DV, C, TO, true>);
-        else serial(gdn_fast_kernel<DK, DV, C, TO, false>);
+        if constexpr (DV % 32 == 0) {
+            if (wide) {
+                if (ck.slots) serial(gdn_fast_kernel<DK, DV, C, TO, true, 32>);
+                else serial(gdn_fast_kernel<DK, DV, C, TO, false, 32>);
+                return hipGetLastError();
+            }
+        }
+        if (ck.slots) serial(gdn_fast_kernel<DK, DV, C, TO, true, 16>);
+        else serial(gdn_fast_kernel<DK, DV, C, TO, false, 16>);
         return hipGetLastError();
     } else {
         const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);

@@ -269,3 +269,27 @@ def test_gdn_prep_then_run_equals_fwd(dtype, dk, C):
     o2 = G.gdn_chunk_run(q, k, v, a, b, cu, p2, sl, ws, chunk=C, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
+@pytest.mark.parametrize("dk,dv,C,H", [(128, 128, 64, 2), (64, 64, 32, 4), (128, 32, 64, 8)])
+def test_gdn_wide_columns_parity(dk, dv, C, H):
+    """Many (sequence, head) pairs: the bf16 serial kernel runs 32 state
+    columns per workgroup (at least 1024 sixteen-column workgroups' worth of
+    work); varlen batch with empty, one-token and partial-chunk sequences."""
+    import gated_deltanet_gla_amd as G
+    rng = np.random.default_rng(dk + dv + C)
+    B = max(8, 1024 // (H * (dv // 16)))
+    lengths = rng.integers(0, 3 * C + 7, size=B)
+    lengths[:3] = [0, 1, C]
+    w = synth.random_varlen(120 + dk + C, lengths.tolist(), H, dk, dv, dtype="bf16", gdn=True,
+                            chunk=C)
+    note(f"gdn wide dk={dk} dv={dv} C={C} H={H} B={B}")
+    pool = dev(w.pool)
+    o = G.gdn_chunk_fwd(dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha),
+                        dev(w.beta), dev(w.cu_seqlens), pool, dev(w.slot_idx), chunk=C,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, p_ref = oracle.gdn_varlen(w.q, w.k, w.v, w.alpha, w.beta, w.cu_seqlens, w.pool,
+                                     w.slot_idx)
+    check(host(o), o_ref, "bf16", "o")
+    check(host(pool)[w.slot_idx], p_ref[w.slot_idx], "bf16", "state")
