@@ -293,3 +293,29 @@ def test_gdn_wide_columns_parity(dk, dv, C, H):
                                      w.slot_idx)
     check(host(o), o_ref, "bf16", "o")
     check(host(pool)[w.slot_idx], p_ref[w.slot_idx], "bf16", "state")
+
+
+def test_gdn_batch_invariance_across_column_widths():
+    """A sequence prefilled alone (16-column serial workgroups) and inside a
+    batch big enough for 32-column workgroups gets bitwise the same outputs
+    and final state: both widths accumulate every product in the same order."""
+    import gated_deltanet_gla_amd as G
+    H, d = 4, 128
+    lengths = [333] + [70] * 40           # 41 x 4 heads x 8 tiles > 1024: the wide path
+    w = synth.random_varlen(130, lengths, H, d, d, dtype="bf16", gdn=True, n_slots=44)
+    note("gdn batch invariance across widths")
+    q, k, v = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16")
+    a, b = dev(w.alpha), dev(w.beta)
+    pool_all = dev(w.pool)
+    o_all = G.gdn_chunk_fwd(q, k, v, a, b, dev(w.cu_seqlens), pool_all, dev(w.slot_idx),
+                            out_dtype=torch.float32)
+    n0 = lengths[0]
+    pool_one = dev(w.pool)
+    o_one = G.gdn_chunk_fwd(q[:n0].contiguous(), k[:n0].contiguous(), v[:n0].contiguous(),
+                            a[:n0].contiguous(), b[:n0].contiguous(),
+                            dev(np.array([0, n0], np.int32)), pool_one, dev(w.slot_idx[:1]),
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s0 = int(w.slot_idx[0])
+    assert torch.equal(o_all[:n0], o_one)
+    assert torch.equal(pool_all[s0], pool_one[s0])
