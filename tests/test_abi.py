@@ -239,3 +239,31 @@ def test_slot_copy_validation():
         args[i] = bad
         assert L.gla_slot_copy(*args) == st, (i, bad)
     assert L.gla_slot_copy(None, 16, 0, None, None, 0, None) == 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/gla.h compiles as strict C99 and a C program links the library
+    and gets validation results from it (no device is touched)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_gla.c"
+    src.write_text(
+        '#include "gla.h"\n#include <stdio.h>\n'
+        "int main(void) {\n"
+        "  int a = gla_chunk_fwd(0, 0, 0, 0, 0, 0, 0, 16, 128, 128, 64, GLA_BF16, GLA_BF16, 0, 1, 0,"
+        " 0, 0, 0, 0, 0);\n"
+        "  int b = gla_decode_step(0, 0, 0, 0, 4, 16, 128, 128, GLA_BF16, GLA_BF16, 0, 8, 0, 0, 0);\n"
+        "  int c = gla_slot_copy(0, 20, 4, 0, 0, 1, 0);\n"
+        '  printf("%d %d %d %s\\n", a, b, c, gla_version());\n'
+        "  return 0;\n}\n")
+    exe = tmp_path / "use_gla"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lgla_mi355x",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert out[:3] == ["0", str(_lib.GLA_EPTR), str(_lib.GLA_ESHAPE)]
+    assert out[3] == _lib.lib().gla_version().decode()
