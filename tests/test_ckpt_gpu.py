@@ -156,3 +156,21 @@ def test_ckpt_full_size_every_block(kind):
         for b in range(B):
             check(host(pool1[int(ck[b, j])]), host(pool2[int(w.slot_idx[b])]), "bf16",
                   f"checkpoint {j} of sequence {b}")
+
+
+def test_gdn_ckpt_wide_columns():
+    """Checkpoints from the 32-column serial workgroups (a batch with enough
+    (sequence, head) pairs to select them)."""
+    H, d, iv = 2, 128, 128
+    rng = np.random.default_rng(140)
+    lengths = rng.integers(100, 400, size=70).tolist()      # 70 x 2 heads x 8 tiles > 1024
+    note("ckpt gdn wide columns")
+    w = synth.random_varlen(141, lengths, H, d, d, dtype="bf16", gdn=True, chunk=64)
+    stride = 3
+    pool_h, ck = _ckpt_table(w, iv, stride, len(lengths) * stride + 3, seed=142)
+    o, pool = _run("gdn", w, pool_h, ck, iv)
+    o_ref, pool_ref = _oracle("gdn", w, pool_h, ck, iv)
+    check(host(o), o_ref, "bf16", "o")
+    p = host(pool)
+    saved = sorted(set(int(x) for x in ck.ravel() if x >= 0) | set(w.slot_idx.tolist()))
+    check(p[saved], pool_ref[saved], "bf16", "checkpoints and final states")
