@@ -279,6 +279,21 @@ def bench_lin_attn(torch, G, synth, dev, steps, warmup):
                        "hbm_frac": dbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
 
 
+def bench_slot_copy(torch, G, synth, dev, steps, warmup):
+    """Whole-slot copies (prefix-cache copy-on-write, committing a draft
+    position): 256 pairs of 1 MiB state slots (16 heads x 128 x 128 fp32)
+    in a 1024-slot pool; one read and one write of each slot."""
+    import numpy as np
+    pool = torch.randn((1024, 16, 128, 128), device="cuda:0") * 0.05
+    perm = np.random.default_rng(9).permutation(1024).astype(np.int32)
+    pairs = [(dev(perm[512 * r:512 * r + 256].copy()), dev(perm[512 * r + 256:512 * r + 512].copy()))
+             for r in range(2)]
+    ms = timed(torch, lambda i: G.gla_state_copy(pool, *pairs[i % 2]), steps, warmup)
+    nbytes = 2 * 256 * 16 * 128 * 128 * 4
+    return {"workload": "256 slot pairs x 1 MiB, 1024-slot pool", "ms": ms,
+            "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
 def bench_mixed(torch, G, synth, dev, steps, warmup):
     import numpy as np
     from gated_deltanet_gla_amd.step import MixedStep
@@ -383,6 +398,7 @@ def main():
         res["gdn_decode"] = bench_decode(torch, G, synth, dev, K, W, gdn=True)
         print(f"# decode {res['gla_decode']['ms']:.3f} / {res['gdn_decode']['ms']:.3f} ms",
               file=sys.stderr, flush=True)
+        res["slot_copy"] = bench_slot_copy(torch, G, synth, dev, K, W)
         res["gla_decode_multi"] = bench_decode_multi(torch, G, synth, dev, K, W, gdn=False)
         res["gdn_decode_multi"] = bench_decode_multi(torch, G, synth, dev, K, W, gdn=True)
         print(f"# decode multi {res['gla_decode_multi']['ms']:.3f} / "
@@ -442,6 +458,11 @@ def main():
             "per_call_ms": {"gla": res["gla_decode"]["per_call_ms"],
                             "gdn": res["gdn_decode"]["per_call_ms"]},
             "workload": "256 requests x 16 heads, 128x128 fp32 states, 1024-slot pool, in place"}
+    if "slot_copy" in res:
+        r = res["slot_copy"]
+        out["slot_copy_hbm_GBps"] = {"GBps": r["GBps"], "ms": r["ms"],
+                                     "frac_of_peak": r["GBps"] / HBM_PEAK_GBPS,
+                                     "workload": r["workload"]}
     if "gla_decode_multi" in res:
         out["decode_multi_hbm_GBps"] = {
             k: res[f"{k}_decode_multi"]["GBps"] for k in ("gla", "gdn")}
