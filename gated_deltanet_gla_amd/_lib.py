@@ -84,9 +84,15 @@ def status_string(status: int) -> str:
     return lib().gla_status_string(int(status)).decode()
 
 
+_fns: dict = {}
+
+
 def call(name: str, *args) -> int:
     """Call an entry point; raise GlaError on a negative status."""
-    st = getattr(lib(), name)(*args)
+    f = _fns.get(name)
+    if f is None:
+        f = _fns[name] = getattr(lib(), name)
+    st = f(*args)
     if st != GLA_OK:
         raise GlaError(name, st)
     return st
