@@ -51,6 +51,8 @@
 // the loops have no guarded memory instructions; the output pass streams
 // q, k, v with the nontemporal policy (pass 1 reads k, v with the default
 // one, which leaves them in the last-level cache for pass 2).
+#include <algorithm>
+
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -169,6 +171,92 @@ __device__ __forceinline__ bool seg_geometry(SegGeom& sg, const int32_t* cu, int
     sg.t1 = min(sg.t0 + lseg, s1);
     sg.ws_first = static_cast<long>(first) * H + h;
     sg.ws_slot = static_cast<long>(si) * H + h;
+    return true;
+}
+
+// Pass 1 has work only in sequences cut into two or more segments, so its
+// blocks index the segments of those sequences alone (a sequence of one
+// segment counts zero): a batch of short prompts launches no idle blocks.
+// Block s of pass 1 is segment s of the concatenated segment lists of the
+// split sequences; its workspace slot is still that segment's place among
+// all segments of the call (exclusive prefix of max(1, ceil(L_b / lseg))),
+// so both prefix sums are scanned together.  maxseg bounds all segments.
+__device__ __forceinline__ bool split_geometry(SegGeom& sg, const int32_t* cu, int n_seqs, int n_tokens,
+                                               int H, int lseg, const int32_t* slot_idx, int n_slots,
+                                               int maxseg, int* sh) {
+    const int h = blockIdx.x % H;
+    const int si = blockIdx.x / H;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    auto count = [&](int b) {
+        const int s = clampi(cu[b], 0, n_tokens);
+        const int e = clampi(cu[b + 1], s, n_tokens);
+        return max(1, (e - s + lseg - 1) / lseg);
+    };
+    const int per = (n_seqs + ST - 1) / ST;
+    const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
+    int sum_all = 0, sum_split = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int c = count(b);
+        sum_all += c;
+        sum_split += c >= 2 ? c : 0;
+    }
+    int xa = sum_all, xs = sum_split;
+#pragma unroll
+    for (int offs = 1; offs < 64; offs <<= 1) {
+        const int ya = __shfl_up(xa, offs, 64);
+        const int ys = __shfl_up(xs, offs, 64);
+        if (lane >= offs) {
+            xa += ya;
+            xs += ys;
+        }
+    }
+    if (lane == 63) {
+        sh[wave] = xa;
+        sh[SW + wave] = xs;
+    }
+    if (t == 0) sh[2 * SW] = -1;
+    lds_barrier();
+    int run_all = xa - sum_all, run_split = xs - sum_split;
+    for (int w = 0; w < wave; ++w) {
+        run_all += sh[w];
+        run_split += sh[SW + w];
+    }
+    if (sum_split > 0 && run_split <= si && si < run_split + sum_split) {
+        for (int b = b0; b < b1; ++b) {
+            const int c = count(b);
+            const int cs = c >= 2 ? c : 0;
+            if (si < run_split + cs) {
+                sh[2 * SW] = b;
+                sh[2 * SW + 1] = run_all;
+                sh[2 * SW + 2] = c;
+                sh[2 * SW + 3] = si - run_split;
+                break;
+            }
+            run_split += cs;
+            run_all += c;
+        }
+    }
+    lds_barrier();
+    const int b = __builtin_amdgcn_readfirstlane(sh[2 * SW]);
+    if (b < 0) return false;
+    const int first = __builtin_amdgcn_readfirstlane(sh[2 * SW + 1]);
+    const int nseg = __builtin_amdgcn_readfirstlane(sh[2 * SW + 2]);
+    const int g = __builtin_amdgcn_readfirstlane(sh[2 * SW + 3]);
+    // the same guard as the output pass: never past the workspace
+    if (first + nseg > maxseg) return false;
+    const int slot = slot_idx[b];
+    if (slot < 0 || slot >= n_slots) return false;
+    const int s0 = clampi(cu[b], 0, n_tokens);
+    const int s1 = clampi(cu[b + 1], s0, n_tokens);
+    sg.b = b;
+    sg.g = g;
+    sg.nseg = nseg;
+    sg.h = h;
+    sg.slot = slot;
+    sg.t0 = min(s0 + g * lseg, s1);
+    sg.t1 = min(sg.t0 + lseg, s1);
+    sg.ws_first = static_cast<long>(first) * H + h;
+    sg.ws_slot = static_cast<long>(first + g) * H + h;
     return true;
 }
 
@@ -375,10 +463,10 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
               int n_tokens, int H, const float* __restrict__ pool, int n_slots,
               const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
               float* __restrict__ wstate, float* __restrict__ wlam, const float* __restrict__ zpool,
-              float* __restrict__ wz) {
-    __shared__ int sh[SW + 4];
+              float* __restrict__ wz, int maxseg) {
+    __shared__ int sh[2 * SW + 4];
     SegGeom sg;
-    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
+    if (!split_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, maxseg, sh)) return;
     if (sg.nseg <= 1) return;                      // no split: pass 2 reads the pool itself
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const AccPos ap;
@@ -759,12 +847,18 @@ hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
     float* wz = wstate + static_cast<size_t>(maxseg) * a.n_heads * SD * SD;
     const float* alpha = NORM ? nullptr : a.alpha;
     const dim3 grid(static_cast<unsigned>(maxseg * a.n_heads));
-    hipLaunchKernelGGL(gla_seg_state<NORM>, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
-                       a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam,
-                       a.zpool, wz);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // A sequence of k >= 2 segments is longer than (k - 1) * lseg tokens and
+    // k <= 2 (k - 1), so the segments of split sequences number at most
+    // 2 * (n_tokens / lseg); pass 1 launches no more blocks than that.
+    const long nsplit = std::min(maxseg, 2L * (a.n_tokens / lseg));
+    if (nsplit > 0) {
+        hipLaunchKernelGGL(gla_seg_state<NORM>, dim3(static_cast<unsigned>(nsplit * a.n_heads)), dim3(ST), 0,
+                           s, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), alpha,
+                           a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
+                           a.zero_init, lseg, wstate, wlam, a.zpool, wz, static_cast<int>(maxseg));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
     auto out_pass = [&](auto kern, auto* o) {
         hipLaunchKernelGGL(kern, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),

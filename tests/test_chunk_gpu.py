@@ -136,7 +136,9 @@ def test_gla_segmented_many_sequences(zero_init):
     (lengths 0..40, so each thread of a workgroup's segment lookup sums
     several sequences) around three long ones that split into 4, 6 and 7
     segments of 256 tokens (the last one 1 token long): outputs and final
-    states against the recurrence, fp32 and bf16 outputs."""
+    states against the recurrence, fp32 and bf16 outputs.  The first pass
+    indexes only the segments of split sequences, so here its block numbers
+    differ from the segments' workspace slots."""
     rng = np.random.Generator(np.random.PCG64(77))
     short = rng.integers(0, 41, size=600).tolist()
     lens = short[:200] + [1500] + short[200:400] + [1537] + short[400:] + [900]
@@ -152,6 +154,22 @@ def test_gla_segmented_many_sequences(zero_init):
     o16, p16 = run_chunk("gla", w, out_dtype="bf16")
     assert torch.equal(o16.cpu(), rne_bf16(o))
     assert torch.equal(p16, pool)
+
+
+def test_gla_segmented_no_split_sequences():
+    """Many prompts of one segment each (1..256 tokens, under the 320-token
+    segment at this size): the first pass launches blocks, none of which
+    finds a split sequence, and the output pass starts every sequence from
+    its pool slot."""
+    rng = np.random.Generator(np.random.PCG64(78))
+    lens = rng.integers(1, 257, size=300).tolist()
+    lens[::50] = [256] * 6
+    w = synth.random_varlen(17, lens, 2, 128, 128, dtype="bf16")
+    note(f"gla segmented, {len(lens)} one-segment sequences, {sum(lens)} tokens")
+    o, pool = run_chunk("gla", w)
+    o_ref, pool_ref = run_oracle("gla", w)
+    check(host(o), o_ref, "bf16", "o")
+    check(pool.cpu().numpy()[w.slot_idx], pool_ref[w.slot_idx], "bf16", "state")
 
 
 def test_gla_prefill_full_size():
