@@ -44,6 +44,9 @@ def parse():
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
     p.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     p.add_argument("--cpu-sample-seqs", type=int, default=4)
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the benchmark line: GLA / GDN prefill over batch x length mixes "
+                        "and decode over batch sizes, one JSON line per shape")
     return p.parse_args()
 
 
@@ -348,6 +351,72 @@ def measured_mfma(kernel: str):
     return None if ent is None else ent.get("mfma")
 
 
+def run_sweep(torch, G, steps, warmup):
+    """Prefill over batch x length mixes of about the same token count (and
+    two larger ones), decode over batch sizes.  Inputs are drawn on the
+    device with the benchmark's distributions (GLA q, k ~ N(0,1)/sqrt(d);
+    GDN q, k L2-normalised; v ~ N(0,1); alpha = sigmoid(N(0,1)+3); beta =
+    sigmoid(N(0,1))); prefills start from zero states; decode rotates over
+    disjoint slot sets of a 2048-slot pool."""
+    import math
+    H, d, C = 16, 128, 64
+    gen = torch.Generator(device="cuda:0").manual_seed(5)
+
+    def rn(*shape):
+        return torch.randn(*shape, device="cuda:0", generator=gen)
+
+    def qk(n, gdn):
+        if gdn:
+            return torch.nn.functional.normalize(rn(n, H, d), dim=-1).bfloat16()
+        return (rn(n, H, d) / math.sqrt(d)).bfloat16()
+
+    for gdn in (False, True):
+        for B, T in ((1, 16384), (2, 8192), (4, 4096), (16, 1024), (64, 256), (256, 64), (8, 8192),
+                     (1, 65536)):
+            N = B * T
+            sets = [(qk(N, gdn), qk(N, gdn), rn(N, H, d).bfloat16(), torch.sigmoid(rn(N, H) + 3),
+                     torch.sigmoid(rn(N, H))) for _ in range(2)]
+            cu = torch.arange(0, N + 1, T, dtype=torch.int32, device="cuda:0")
+            slots = torch.arange(B, dtype=torch.int32, device="cuda:0")
+            pool = torch.zeros((B, H, d, d), device="cuda:0")
+            o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
+            ws = torch.empty(max(1, G.workspace_bytes("gdn" if gdn else "gla", B, N, H, d, d, C)),
+                             dtype=torch.uint8, device="cuda:0")
+
+            def step(i):
+                q, k, v, a, b = sets[i % 2]
+                if gdn:
+                    G.gdn_chunk_fwd(q, k, v, a, b, cu, pool, slots, chunk=C, zero_init=True, o=o,
+                                    workspace=ws)
+                else:
+                    G.gla_chunk_fwd(q, k, v, a, cu, pool, slots, chunk=C, zero_init=True, o=o,
+                                    workspace=ws)
+            ms = timed(torch, step, steps, warmup)
+            print(json.dumps({"sweep": "gdn_prefill" if gdn else "gla_prefill", "batch": B, "seq_len": T,
+                              "ms": ms, "tokens_per_s": N / (ms * 1e-3)}), flush=True)
+            del sets, o, ws, pool
+    n_slots = 2048
+    pool = rn(n_slots, H, d, d) * 0.05
+    perm = torch.randperm(n_slots, device="cuda:0", generator=gen).to(torch.int32)
+    for gdn in (False, True):
+        for R in (1, 8, 32, 64, 128, 256, 512, 1024):
+            q, k, v = (rn(R, H, d) / math.sqrt(d)).bfloat16(), qk(R, gdn), rn(R, H, d).bfloat16()
+            a, b = torch.sigmoid(rn(R, H) + 3), torch.sigmoid(rn(R, H))
+            nsets = min(8, n_slots // R)
+            sl = [perm[i * R:(i + 1) * R].contiguous() for i in range(nsets)]
+            o = torch.empty((R, H, d), dtype=torch.bfloat16, device="cuda:0")
+
+            def step(i):
+                if gdn:
+                    G.gdn_decode_step(q, k, v, a, b, pool, sl[i % nsets], o=o)
+                else:
+                    G.gla_decode_step(q, k, v, a, pool, sl[i % nsets], o=o)
+            ms = timed(torch, step, steps, warmup)
+            nbytes = R * H * (2 * d * d * 4 + 4 * d * 2 + (8 if gdn else 4))
+            print(json.dumps({"sweep": "gdn_decode" if gdn else "gla_decode", "requests": R, "ms": ms,
+                              "GBps": nbytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def calib_copy(torch):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
@@ -370,7 +439,7 @@ def main():
         sys.exit(2)
 
     cpu = None
-    if not args.no_cpu_baseline and args.only in ("all", "gla_prefill"):
+    if not args.no_cpu_baseline and not args.sweep and args.only in ("all", "gla_prefill"):
         cpu = run_cpu_baseline(args.cpu_sample_seqs)      # before this process touches the GPU
 
     import torch
@@ -378,6 +447,9 @@ def main():
     import synth
     from gated_deltanet_gla_amd import _lib
     _lib.lib()   # fail loudly if the HIP library is missing
+    if args.sweep:
+        run_sweep(torch, G, max(args.steps, 30), args.warmup)
+        return
 
     def dev(x, dtype="f32"):
         import numpy as np
