@@ -17,8 +17,9 @@ architectures", section "Two ways to write the same computation":
   "The real model's ledger" for the width-1 cache).
 
 The definition is the token-by-token recurrence (``recurrence``); the chunked
-forms in ``chunked`` restate the page's chunked algorithm (and a derived
-chunked form for Gated DeltaNet) and exist only to pin the recurrence.
+forms in ``chunked`` evaluate the same recurrence chunk by chunk (GLA from
+direct products of the gates, and a derived chunked form for Gated
+DeltaNet) and exist only to pin the recurrence.
 
 Parity status of every function is listed in ``PINS`` below: each entry names
 the pin tests that fix it against something other than itself.
@@ -36,7 +37,8 @@ PINS = {
     "gdn_sequence": "literal d_k x d_k matrix update, beta=0 closed form, orthogonal-key "
                     "reduction to GLA, retrieval identity, chunked WY form",
     "gla_varlen / gdn_varlen": "per-sequence equality with *_sequence, untouched slots, "
-                               "empty sequences",
+                               "empty sequences; zero_init against the brute-force sum (GLA) and "
+                               "the literal matrix update (GDN) run from zero with a nonzero pool",
     "gla_decode / gdn_decode": "one step of *_sequence",
     "gla_decode_multi / gdn_decode_multi": "each kept state equals the varlen prefill of the "
                                            "same prefix, closed form of the GLA state after j "
@@ -48,10 +50,14 @@ PINS = {
                                          "prefix-cache demonstration); outputs equal "
                                          "*_varlen",
     "lin_attn_sequence": "the page's parallel kernelised formula (O(T^2) double sum), "
-                         "convex-combination bounds, constant values, phi's closed form",
-    "lin_attn_varlen / lin_attn_decode": "per-sequence equality with lin_attn_sequence, "
-                                         "segmentation through the pool",
-    "causal_conv1d": "numpy.convolve per channel, segmented == one pass == token by token",
+                         "the closed form from a given (S0, z0), convex-combination bounds, "
+                         "constant values, phi against torch's elu + 1",
+    "lin_attn_varlen": "segmentation through the pool; zero_init against the double sum from "
+                       "zero with nonzero pools",
+    "lin_attn_decode": "one step's closed form S0 + phi(k)^T v, z0 + phi(k), "
+                       "phi(q)S / (phi(q).z + eps) on each slot; untouched slots",
+    "causal_conv1d": "numpy.convolve per channel, segmented == one pass == token by token; "
+                     "zero_init against numpy.convolve with a nonzero cache",
     "gla_chunked": "page toy example; equality with the recurrence",
     "gdn_chunked": "equality with the recurrence (the chunked GDN form itself is not on the "
                    "page; it is pinned only through the recurrence)",

@@ -3,9 +3,9 @@ infrastructure only).
 
 Source: page "Long context, fast inference, smart decoding, and life beyond
 attention", chapter "Long-context architectures", section "Linear
-attention: removing softmax entirely" (the kernelised formula) and the
-listing "Linear attention as a running state" after it: with the feature
-map
+attention: removing softmax entirely" (the kernelised formula, and its
+statement that the same result can be kept as a running state): with the
+feature map
 phi(x) = elu(x) + 1 (positive, so the normaliser cannot vanish),
     S_i = S_{i-1} + phi(k_i)^T v_i,     z_i = z_{i-1} + phi(k_i),
     o_i = phi(q_i) S_i / (phi(q_i) . z_i + eps),   eps = 1e-6 on the page,
@@ -30,21 +30,35 @@ def phi(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def lin_attn_sequence(q, k, v, S0=None, z0=None, eps=EPS):
-    """One sequence, token by token.  Returns (o [T,H,dv], S_T, z_T)."""
+def lin_attn_sequence(q, k, v, S0=None, z0=None, eps=EPS, block=64):
+    """One sequence.  Returns (o [T,H,dv], S_T, z_T).
+
+    The state and normaliser after token i are prefix sums over the tokens
+    so far, S_i = S_0 + sum_{j<=i} phi(k_j)^T v_j and z_i = z_0 + sum_{j<=i}
+    phi(k_j), taken with a sequential cumulative sum (so cutting the sequence
+    anywhere and carrying (S, z) gives bit-identical results); the output
+    reads them after the token's own write, o_i = phi(q_i) S_i / (phi(q_i) .
+    z_i + eps).  Tokens are taken ``block`` at a time only to bound memory.
+    """
     q, k, v = np.asarray(q, np.float64), np.asarray(k, np.float64), np.asarray(v, np.float64)
     T, H, dk = q.shape
     dv = v.shape[2]
     S = np.zeros((H, dk, dv)) if S0 is None else np.asarray(S0, np.float64).copy()
     z = np.zeros((H, dk)) if z0 is None else np.asarray(z0, np.float64).copy()
-    pq, pk = phi(q), phi(k)
+    fq, fk = phi(q), phi(k)
     o = np.zeros((T, H, dv))
-    for t in range(T):
-        S = S + pk[t][:, :, None] * v[t][:, None, :]
-        z = z + pk[t]
-        num = np.einsum("hd,hde->he", pq[t], S)
-        den = np.einsum("hd,hd->h", pq[t], z) + eps
-        o[t] = num / den[:, None]
+    for s in range(0, T, block):
+        e = min(s + block, T)
+        writes = fk[s:e, :, :, None] * v[s:e, :, None, :]                  # phi(k_j)^T v_j
+        S_run = np.cumsum(np.concatenate([S[None], writes]), axis=0)[1:]    # [n, H, dk, dv]
+        z_run = np.cumsum(np.concatenate([z[None], fk[s:e]]), axis=0)[1:]   # [n, H, dk]
+        num = np.zeros((e - s, H, dv))
+        den = np.full((e - s, H), eps)
+        for d in range(dk):
+            num += fq[s:e, :, d, None] * S_run[:, :, d, :]
+            den += fq[s:e, :, d] * z_run[:, :, d]
+        o[s:e] = num / den[:, :, None]
+        S, z = S_run[-1], z_run[-1]
     return o, S, z
 
 
