@@ -307,3 +307,127 @@ def ckpt_closed_form(gla_varlen_ckpt, seed=15):
                     S = S + np.prod(a[t + 1:s0 + p, h]) * np.outer(k[t, h], v[t, h])
                 worst = max(worst, np.abs(out[ck[b, j], h] - S).max())
     return worst
+
+
+# ---------------------------------------------------------------- decode and zero-init branches
+def lin_decode_closed_form(lin_attn_decode, seed=16):
+    """One token per request r from (S0, z0) = slot r of the pools:
+    S' = S0 + phi(k)^T v, z' = z0 + phi(k), o = phi(q) S' / (phi(q) . z' + eps);
+    slots not named keep their values."""
+    r = _rng(seed)
+    R, H, dk, dv, n_slots = 4, 2, 5, 3, 9
+    q, k, v = r.standard_normal((R, H, dk)), r.standard_normal((R, H, dk)), r.standard_normal((R, H, dv))
+    pool = r.standard_normal((n_slots, H, dk, dv))
+    zpool = r.uniform(1.0, 3.0, (n_slots, H, dk))
+    slots = r.permutation(n_slots)[:R]
+    o, P, Z = lin_attn_decode(q, k, v, pool, zpool, slots)
+    fq, fk = _phi(q), _phi(k)
+    rest = sorted(set(range(n_slots)) - set(slots.tolist()))
+    worst = max(np.abs(P[rest] - pool[rest]).max(), np.abs(Z[rest] - zpool[rest]).max())
+    for i in range(R):
+        for h in range(H):
+            S = pool[slots[i], h] + np.outer(fk[i, h], v[i, h])
+            z = zpool[slots[i], h] + fk[i, h]
+            worst = max(worst, np.abs(P[slots[i], h] - S).max(), np.abs(Z[slots[i], h] - z).max(),
+                        np.abs(o[i, h] - fq[i, h] @ S / (fq[i, h] @ z + 1e-6)).max())
+    return worst
+
+
+def _zero_init_case(seed, lengths=(5, 0, 7), H=2, dk=4, dv=3, n_slots=6):
+    r = _rng(seed)
+    N = sum(lengths)
+    q, k, v = r.standard_normal((N, H, dk)), r.standard_normal((N, H, dk)), r.standard_normal((N, H, dv))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    a = 1.0 / (1.0 + np.exp(-(r.standard_normal((N, H)) + 2.0)))
+    b = 1.0 / (1.0 + np.exp(-r.standard_normal((N, H))))
+    pool = r.standard_normal((n_slots, H, dk, dv)) + 1.0      # nonzero everywhere
+    slots = r.permutation(n_slots)[:len(lengths)]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    return q, k, v, a, b, pool, slots, cu
+
+
+def lin_zero_init(lin_attn_varlen, seed=17):
+    """zero_init: nonzero pool slots are ignored.  Outputs are the kernelised
+    double sum from zero, the slot receives phi(K)^T V and sum phi(k) (zeros
+    for an empty sequence), other slots keep their values."""
+    q, k, v, _, _, pool, slots, cu = _zero_init_case(seed)
+    zpool = np.abs(pool[:, :, :, 0]) + 1.0
+    o, P, Z = lin_attn_varlen(q, k, v, cu, pool, zpool, slots, True)
+    fq, fk = _phi(q), _phi(k)
+    rest = sorted(set(range(pool.shape[0])) - set(slots.tolist()))
+    worst = max(np.abs(P[rest] - pool[rest]).max(), np.abs(Z[rest] - zpool[rest]).max())
+    for b in range(len(slots)):
+        s, e = cu[b], cu[b + 1]
+        for h in range(q.shape[1]):
+            for i in range(s, e):
+                w = np.array([fq[i, h] @ fk[j, h] for j in range(s, i + 1)])
+                ref = (w[:, None] * v[s:i + 1, h]).sum(0) / (w.sum() + 1e-6)
+                worst = max(worst, np.abs(o[i, h] - ref).max())
+            worst = max(worst, np.abs(P[slots[b], h] - fk[s:e, h].T @ v[s:e, h]).max(),
+                        np.abs(Z[slots[b], h] - fk[s:e, h].sum(0)).max())
+    return worst
+
+
+def gla_zero_init(gla_varlen, seed=18):
+    """zero_init: each sequence starts from S = 0 whatever its slot holds:
+    o_t = sum_{s<=t} (prod_{r=s+1..t} alpha_r)(q_t . k_s) v_s with products
+    taken directly; the slot receives the final state (zeros if empty)."""
+    q, k, v, a, _, pool, slots, cu = _zero_init_case(seed)
+    o, P = gla_varlen(q, k, v, a, cu, pool, slots, True)
+    worst = 0.0
+    for b in range(len(slots)):
+        s, e = cu[b], cu[b + 1]
+        for h in range(q.shape[1]):
+            Sref = np.zeros(pool.shape[2:])
+            for t in range(s, e):
+                ref = np.zeros(v.shape[2])
+                for j in range(s, t + 1):
+                    ref = ref + np.prod(a[j + 1:t + 1, h]) * (q[t, h] @ k[j, h]) * v[j, h]
+                worst = max(worst, np.abs(o[t, h] - ref).max())
+                Sref = Sref + np.prod(a[t + 1:e, h]) * np.outer(k[t, h], v[t, h])
+            worst = max(worst, np.abs(P[slots[b], h] - Sref).max())
+    return worst
+
+
+def gdn_zero_init(gdn_varlen, seed=19):
+    """zero_init for Gated DeltaNet: the literal d_k x d_k update
+    alpha (I - beta k^T k) S + beta k^T v run from S = 0."""
+    q, k, v, a, b_, pool, slots, cu = _zero_init_case(seed)
+    o, P = gdn_varlen(q, k, v, a, b_, cu, pool, slots, True)
+    dk = q.shape[2]
+    worst = 0.0
+    for b in range(len(slots)):
+        s, e = cu[b], cu[b + 1]
+        for h in range(q.shape[1]):
+            St = np.zeros(pool.shape[2:])
+            for t in range(s, e):
+                kk = k[t, h][:, None]
+                St = a[t, h] * (np.eye(dk) - b_[t, h] * (kk @ kk.T)) @ St + b_[t, h] * (kk @ v[t, h][None, :])
+                worst = max(worst, np.abs(o[t, h] - q[t, h] @ St).max())
+            worst = max(worst, np.abs(P[slots[b], h] - St).max())
+    return worst
+
+
+def conv_zero_init(causal_conv1d, seed=20):
+    """zero_init: a nonzero cache is read as zeros, so each sequence's output
+    is numpy.convolve of its own inputs (w[c, W-1] on the current input); the
+    cache receives the last W-1 rows of [zeros(W-1); x] (a 2-token sequence
+    leaves one zero row in front of its inputs)."""
+    r = _rng(seed)
+    lengths, Cch, W = [9, 2], 5, 4
+    N = sum(lengths)
+    x = r.standard_normal((N, Cch))
+    w = r.standard_normal((Cch, W))
+    cache = r.standard_normal((4, W - 1, Cch)) + 1.0
+    slots = np.array([3, 1])
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    y, c = causal_conv1d(x, w, cu, cache, slots, True)
+    err = max(np.abs(c[[0, 2]] - cache[[0, 2]]).max(), 0.0)
+    for b in range(2):
+        s, e = cu[b], cu[b + 1]
+        for ch in range(Cch):
+            ref = np.convolve(x[s:e, ch], w[ch, ::-1])[:e - s]
+            err = max(err, np.abs(y[s:e, ch] - ref).max())
+        tail = np.concatenate([np.zeros((W - 1, Cch)), x[s:e]])[-(W - 1):]
+        err = max(err, np.abs(c[slots[b]] - tail).max())
+    return err

@@ -204,3 +204,71 @@ def _ckpt_mutant(kind):
 def test_ckpt_mutant_caught(kind):
     assert pins.ckpt_closed_form(_ckpt_mutant("none")) <= pins.TOL
     assert pins.ckpt_closed_form(_ckpt_mutant(kind)) > 1e-6
+
+
+# ---------------------------------------------------------------- decode and zero-init branches
+def _lin_decode_mutant(kind):
+    def f(q, k, v, pool, zpool, slot_idx, eps=1e-6):
+        slots = np.asarray(slot_idx)
+        if kind == "wrong_slot":
+            slots = np.roll(slots, 1)
+        o, P, Z = oracle.lin_attn_decode(q, k, v, pool, zpool, slots, eps)
+        if kind == "normaliser_not_written":
+            Z = np.asarray(zpool, np.float64).copy()
+        if kind == "output_before_update":
+            fq = oracle.phi(q)
+            S0 = np.asarray(pool, np.float64)[slots]
+            z0 = np.asarray(zpool, np.float64)[slots]
+            o = np.einsum("rhd,rhde->rhe", fq, S0) / (np.einsum("rhd,rhd->rh", fq, z0) + eps)[..., None]
+        return o, P, Z
+    return f
+
+
+@pytest.mark.parametrize("kind", ["wrong_slot", "normaliser_not_written", "output_before_update"])
+def test_lin_decode_mutant_caught(kind):
+    assert pins.lin_decode_closed_form(_lin_decode_mutant("none")) <= pins.TOL
+    assert pins.lin_decode_closed_form(_lin_decode_mutant(kind)) > 1e-6
+
+
+def _zero_init_mutants(kind):
+    """zero-init handled wrongly: ignored altogether, or (normalised linear
+    attention) the state reset but not the normaliser."""
+    def gla(q, k, v, a, cu, pool, slots, zero_init=False):
+        return oracle.gla_varlen(q, k, v, a, cu, pool, slots, zero_init and kind != "ignored")
+
+    def gdn(q, k, v, a, b, cu, pool, slots, zero_init=False):
+        return oracle.gdn_varlen(q, k, v, a, b, cu, pool, slots, zero_init and kind != "ignored")
+
+    def lin(q, k, v, cu, pool, zpool, slots, zero_init=False, eps=1e-6):
+        if kind == "normaliser_kept" and zero_init:
+            P0 = np.asarray(pool, np.float64).copy()
+            P0[np.asarray(slots)] = 0.0
+            return oracle.lin_attn_varlen(q, k, v, cu, P0, zpool, slots, False, eps)
+        return oracle.lin_attn_varlen(q, k, v, cu, pool, zpool, slots, zero_init and kind != "ignored", eps)
+    return gla, gdn, lin
+
+
+@pytest.mark.parametrize("kind", ["ignored", "normaliser_kept"])
+def test_zero_init_mutant_caught(kind):
+    gla, gdn, lin = _zero_init_mutants("none")
+    assert max(pins.gla_zero_init(gla), pins.gdn_zero_init(gdn), pins.lin_zero_init(lin)) <= pins.TOL
+    gla, gdn, lin = _zero_init_mutants(kind)
+    assert pins.lin_zero_init(lin) > 1e-6
+    if kind == "ignored":
+        assert pins.gla_zero_init(gla) > 1e-6 and pins.gdn_zero_init(gdn) > 1e-6
+
+
+@pytest.mark.parametrize("kind", ["ignored", "cache_not_written", "cache_from_old_rows"])
+def test_conv_zero_init_mutant_caught(kind):
+    def f(x, w, cu, cache, slots, zero_init=False):
+        y, c = oracle.causal_conv1d(x, w, cu, cache, slots, zero_init and kind != "ignored")
+        if kind == "cache_not_written":
+            c = c.copy()
+            c[np.asarray(slots)] = np.asarray(cache)[np.asarray(slots)]
+        if kind == "cache_from_old_rows":      # the short sequence keeps old cache rows in front
+            _, c_old = oracle.causal_conv1d(x, w, cu, cache, slots, False)
+            c = c.copy()
+            c[int(slots[1])] = c_old[int(slots[1])]
+        return y, c
+    assert pins.conv_zero_init(oracle.causal_conv1d) <= pins.TOL
+    assert pins.conv_zero_init(f) > 1e-6

@@ -491,3 +491,25 @@ def test_lin_attn_segments_through_pool():
     o2, pool, zpool = oracle.lin_attn_varlen(q[11:], k[11:], v[11:], [0, 19], pool, zpool, [2])
     assert np.array_equal(np.concatenate([o1, o2]), o)
     assert np.array_equal(pool[2], S) and np.array_equal(zpool[2], z)
+
+
+# ------------------------------------------------------------------ decode and zero-init branches
+def test_lin_attn_decode_closed_form():
+    """Normalised linear attention decode: one running-state step per
+    request on its slot of both pools (page "Long context, fast inference,
+    smart decoding, and life beyond attention", section "Linear attention:
+    removing softmax entirely")."""
+    assert pins.lin_decode_closed_form(oracle.lin_attn_decode) <= pins.TOL
+
+
+def test_zero_init_ignores_the_pool():
+    """A fresh request starts from S = 0 whatever its slot holds; the final
+    state still goes to the slot (section "Chunked prefill comes for free":
+    the hand-off is the state alone)."""
+    assert pins.gla_zero_init(oracle.gla_varlen) <= pins.TOL
+    assert pins.gdn_zero_init(oracle.gdn_varlen) <= pins.TOL
+    assert pins.lin_zero_init(oracle.lin_attn_varlen) <= pins.TOL
+
+
+def test_conv_zero_init_ignores_the_cache():
+    assert pins.conv_zero_init(oracle.causal_conv1d) <= pins.TOL
