@@ -45,10 +45,17 @@
  *  - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}.
  *    dtypes: in_dtype, out_dtype in {GLA_F32, GLA_BF16}.  bf16 outputs are
  *    the fp32 result rounded to nearest even.
+ *  - Parity contract: alpha in (0, 1] and finite, as the page states the
+ *    gate ("Two ways to write the same computation"); results then match
+ *    the fp64 recurrence within 1e-5 absolute for fp32 inputs and 3e-3 of
+ *    the largest magnitude for bf16 inputs.  A gate below 2^-126, exactly 0
+ *    (a complete reset) included, is accepted and taken as 2^-126: results
+ *    stay finite, but the chunked form works with log2 alpha, and after such
+ *    a gate inside a chunk fp32 keeps the running log decay (near -126) to
+ *    about 2^-17, so fp32 results then carry up to ~5e-5 absolute error.
  *  - Preconditions (undefined results, not faults, if violated):
- *    alpha in [0, 1] and finite (the chunked form works with log alpha;
- *    alpha = 0, a complete reset, is taken as 2^-126);
- *    beta >= 0 with beta |k|^2 <= 2; q/k/v/o do not overlap the pool.
+ *    alpha in [0, 1] and finite; beta >= 0 with beta |k|^2 <= 2; q/k/v/o
+ *    do not overlap the pool.
  *    Token indices derived from cu_seqlens are clamped to [0, n_tokens),
  *    so a malformed cu_seqlens gives wrong results, never an out-of-bounds
  *    access.
@@ -364,6 +371,24 @@ GLA_API int causal_conv1d_fwd(const void* x, const float* w, const int32_t* cu_s
                       int32_t n_seqs, int32_t n_tokens, int32_t channels, int32_t width,
                       void* conv_cache, int32_t n_slots, const int32_t* slot_idx,
                       uint32_t flags, void* y, gla_dtype dtype, void* stream);
+
+/*
+ * gla_hbm_probe -- measurement helper, not part of the recurrence: the HBM
+ * traffic of one decode step (gla_decode_step / gdn_decode_step at d_k =
+ * d_v = 128) without its arithmetic, to measure the read / write ceiling
+ * that step runs against on the machine at hand.  Item (request r, head h)
+ * is the 64 KiB block state_pool + (slot_idx[r] * n_heads + h) * 16384
+ * floats, accessed with the decode kernel's pattern.  mode 0: read every
+ * block; 1: write zeros over every block (destroys those states); 2: read
+ * each block and write the same bytes back in place (the pool is left as
+ * it was); 3: as 2, with two items per workgroup and both blocks read
+ * before either is written.  sink: 16 bytes of device memory that mode 0
+ * may write (it never does for finite data).  Slots outside [0, n_slots)
+ * are skipped.  dk = dv = 128 only (GLA_ESHAPE otherwise).
+ */
+GLA_API int gla_hbm_probe(int32_t mode, float* state_pool, int32_t n_req, int32_t n_heads,
+                  int32_t dk, int32_t dv, int32_t n_slots, const int32_t* slot_idx,
+                  void* sink, void* stream);
 
 /* Static description of a status code. */
 GLA_API const char* gla_status_string(int status);
