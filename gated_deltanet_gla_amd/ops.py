@@ -30,17 +30,50 @@ def _stream(t):
 
 
 def _check(t, name, dtype=None, dims=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
-        raise ValueError(f"{name} has dtype {t.dtype}")
+    """Layout checks of one tensor (dims, dtype, contiguity); the device is
+    checked by _devices once every shape has been checked."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, has {t.dim()}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
-def _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, out_dtype, o):
+def _shape(t, name, *dims):
+    """t.shape must equal dims (None: any size)."""
+    if t.dim() != len(dims) or any(d is not None and s != d for s, d in zip(t.shape, dims)):
+        want = "[" + ", ".join("*" if d is None else str(d) for d in dims) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _devices(*named):
+    """Every tensor given (None entries skipped) is a device tensor, all on
+    the device of the first."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
+def _ws_check(workspace):
+    if workspace is not None:
+        _check(workspace, "workspace")
+
+
+def _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, out_dtype, o, beta=None,
+                  workspace=None, extra=()):
+    """Checks of the chunked entry points: q, k [N, H, dk]; v, o [N, H, dv];
+    alpha (and beta) [N, H]; cu_seqlens [B + 1]; state_pool
+    [n_slots, H, dk, dv]; slot_idx [B]; everything on one device."""
     for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 3),
                         (k, "k", (torch.float32, torch.bfloat16), 3),
                         (v, "v", (torch.float32, torch.bfloat16), 3),
@@ -52,10 +85,28 @@ def _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, out_dtype, o
         raise ValueError("q, k, v must share a dtype")
     N, H, dk = q.shape
     dv = v.shape[2]
+    _shape(k, "k", N, H, dk)
+    _shape(v, "v", N, H, dv)
+    if alpha is not None:
+        _shape(alpha, "alpha", N, H)
+    if beta is not None:
+        _check(beta, "beta", torch.float32, 2)
+        _shape(beta, "beta", N, H)
+    if cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must hold n_seqs + 1 entries")
+    B = cu_seqlens.shape[0] - 1
+    _shape(slot_idx, "slot_idx", B)
+    _shape(state_pool, "state_pool", None, H, dk, dv)
+    _ws_check(workspace)
     out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
+    if o is not None:
+        _check(o, "o", out_dtype, 3)
+        _shape(o, "o", N, H, dv)
+    _devices(("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("cu_seqlens", cu_seqlens),
+             ("state_pool", state_pool), ("slot_idx", slot_idx), ("o", o), ("workspace", workspace),
+             *extra)
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
-    _check(o, "o", out_dtype, 3)
     return N, H, dk, dv, out_dtype, o
 
 
@@ -63,7 +114,7 @@ def gla_chunk_fwd(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, *, chunk=64,
                   zero_init=False, o=None, workspace=None):
     """Chunked GLA prefill; updates state_pool[slot_idx] in place, returns o."""
     N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
-                                               out_dtype, o)
+                                               out_dtype, o, workspace=workspace)
     B = cu_seqlens.shape[0] - 1
     need = _lib.lib().gla_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
     if need and workspace is None:
@@ -81,8 +132,7 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, *, chu
                   out_dtype=None, zero_init=False, o=None, workspace=None):
     """Chunked Gated DeltaNet prefill; updates state_pool[slot_idx] in place, returns o."""
     N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
-                                               out_dtype, o)
-    _check(beta, "beta", torch.float32, 2)
+                                               out_dtype, o, beta=beta, workspace=workspace)
     B = cu_seqlens.shape[0] - 1
     need = _lib.lib().gdn_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
     if need and workspace is None:
@@ -97,7 +147,6 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, *, chu
 
 
 def _ckpt_args(ckpt_slots, ckpt_interval, n_seqs):
-    _check(ckpt_slots, "ckpt_slots", torch.int32, 2)
     if ckpt_slots.shape[0] != n_seqs:
         raise ValueError("ckpt_slots must be [n_seqs, ckpt_stride]")
     return int(ckpt_interval), ckpt_slots.data_ptr(), ckpt_slots.shape[1]
@@ -108,8 +157,10 @@ def gla_chunk_fwd_ckpt(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, ckpt_sl
     """gla_chunk_fwd that also writes the state after every ckpt_interval
     tokens of sequence b to state_pool[ckpt_slots[b, j]] (j-th checkpoint;
     negative = not saved).  ckpt_slots [n_seqs, stride] int32."""
+    _check(ckpt_slots, "ckpt_slots", torch.int32, 2)
     N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
-                                               out_dtype, o)
+                                               out_dtype, o, workspace=workspace,
+                                               extra=(("ckpt_slots", ckpt_slots),))
     B = cu_seqlens.shape[0] - 1
     iv, cp, cs = _ckpt_args(ckpt_slots, ckpt_interval, B)
     need = _lib.lib().gla_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
@@ -128,9 +179,10 @@ def gdn_chunk_fwd_ckpt(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, c
                        ckpt_interval, *, chunk=64, out_dtype=None, zero_init=False, o=None,
                        workspace=None):
     """Gated DeltaNet form of gla_chunk_fwd_ckpt."""
+    _check(ckpt_slots, "ckpt_slots", torch.int32, 2)
     N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
-                                               out_dtype, o)
-    _check(beta, "beta", torch.float32, 2)
+                                               out_dtype, o, beta=beta, workspace=workspace,
+                                               extra=(("ckpt_slots", ckpt_slots),))
     B = cu_seqlens.shape[0] - 1
     iv, cp, cs = _ckpt_args(ckpt_slots, ckpt_interval, B)
     need = _lib.lib().gdn_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
@@ -154,7 +206,17 @@ def gdn_chunk_prep(q, k, alpha, beta, cu_seqlens, workspace, *, n_dv, chunk=64):
     _check(alpha, "alpha", torch.float32, 2)
     _check(beta, "beta", torch.float32, 2)
     _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _check(workspace, "workspace")
+    if q.dtype != k.dtype:
+        raise ValueError("q, k must share a dtype")
     N, H, dk = q.shape
+    _shape(k, "k", N, H, dk)
+    _shape(alpha, "alpha", N, H)
+    _shape(beta, "beta", N, H)
+    if cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must hold n_seqs + 1 entries")
+    _devices(("q", q), ("k", k), ("alpha", alpha), ("beta", beta), ("cu_seqlens", cu_seqlens),
+             ("workspace", workspace))
     _lib.call("gdn_chunk_prep", q.data_ptr(), k.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
               cu_seqlens.data_ptr(), cu_seqlens.shape[0] - 1, N, H, dk, n_dv, chunk, _DT[q.dtype],
               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -165,9 +227,9 @@ def gdn_chunk_run(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, worksp
                   out_dtype=None, zero_init=False, o=None):
     """The serial part of gdn_chunk_fwd, after gdn_chunk_prep on the same
     inputs and workspace; updates state_pool[slot_idx] in place, returns o."""
+    _check(workspace, "workspace")
     N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
-                                               out_dtype, o)
-    _check(beta, "beta", torch.float32, 2)
+                                               out_dtype, o, beta=beta, workspace=workspace)
     _lib.call("gdn_chunk_run", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
               beta.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.shape[0] - 1, N, H, dk, dv, chunk,
               _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(), state_pool.shape[0],
@@ -185,7 +247,10 @@ def workspace_bytes(kind, n_seqs, n_tokens, n_heads, dk, dv, chunk):
     return getattr(_lib.lib(), fn)(n_seqs, n_tokens, n_heads, dk, dv, chunk)
 
 
-def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o):
+def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o, beta=None, extra=()):
+    """Checks of the one-token decode entry points: q, k [R, H, dk]; v, o
+    [R, H, dv]; alpha (and beta) [R, H]; state_pool [n_slots, H, dk, dv];
+    slot_idx [R]; everything on one device."""
     for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 3),
                         (k, "k", (torch.float32, torch.bfloat16), 3),
                         (v, "v", (torch.float32, torch.bfloat16), 3),
@@ -193,12 +258,27 @@ def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o):
                         (state_pool, "state_pool", torch.float32, 4), (slot_idx, "slot_idx", torch.int32, 1)]:
         if t is not None or n != "alpha":     # alpha is None for the ungated operation
             _check(t, n, d, nd)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
     R, H, dk = q.shape
     dv = v.shape[2]
+    _shape(k, "k", R, H, dk)
+    _shape(v, "v", R, H, dv)
+    if alpha is not None:
+        _shape(alpha, "alpha", R, H)
+    if beta is not None:
+        _check(beta, "beta", torch.float32, 2)
+        _shape(beta, "beta", R, H)
+    _shape(slot_idx, "slot_idx", R)
+    _shape(state_pool, "state_pool", None, H, dk, dv)
     out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
+    if o is not None:
+        _check(o, "o", out_dtype, 3)
+        _shape(o, "o", R, H, dv)
+    _devices(("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("state_pool", state_pool),
+             ("slot_idx", slot_idx), ("o", o), *extra)
     if o is None:
         o = torch.empty((R, H, dv), dtype=out_dtype, device=q.device)
-    _check(o, "o", out_dtype, 3)
     return R, H, dk, dv, out_dtype, o
 
 
@@ -213,15 +293,18 @@ def gla_decode_step(q, k, v, alpha, state_pool, slot_idx, *, out_dtype=None, o=N
 
 def gdn_decode_step(q, k, v, alpha, beta, state_pool, slot_idx, *, out_dtype=None, o=None):
     """One Gated DeltaNet decode token per request, in place; returns o."""
-    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o)
-    _check(beta, "beta", torch.float32, 2)
+    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o,
+                                                beta=beta)
     _lib.call("gdn_decode_step", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
               beta.data_ptr(), R, H, dk, dv, _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(),
               state_pool.shape[0], slot_idx.data_ptr(), o.data_ptr(), _stream(q))
     return o
 
 
-def _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots, out_dtype, o):
+def _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots, out_dtype, o, beta=None):
+    """Checks of the multi-token decode: q, k [R, J, H, dk]; v, o
+    [R, J, H, dv]; alpha (and beta) [R, J, H]; state_pool [n_slots, H, dk, dv];
+    slot_idx [R]; pos_slots [R, J]; everything on one device."""
     for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 4),
                         (k, "k", (torch.float32, torch.bfloat16), 4),
                         (v, "v", (torch.float32, torch.bfloat16), 4),
@@ -230,14 +313,27 @@ def _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots, out_dtype, o)
                         (slot_idx, "slot_idx", torch.int32, 1),
                         (pos_slots, "pos_slots", torch.int32, 2)]:
         _check(t, n, d, nd)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
     R, J, H, dk = q.shape
     dv = v.shape[3]
+    _shape(k, "k", R, J, H, dk)
+    _shape(v, "v", R, J, H, dv)
+    _shape(alpha, "alpha", R, J, H)
+    if beta is not None:
+        _check(beta, "beta", torch.float32, 3)
+        _shape(beta, "beta", R, J, H)
     if tuple(pos_slots.shape) != (R, J) or slot_idx.shape[0] != R:
         raise ValueError("pos_slots must be [n_req, n_tok] and slot_idx [n_req]")
+    _shape(state_pool, "state_pool", None, H, dk, dv)
     out_dtype = out_dtype or (o.dtype if o is not None else q.dtype)
+    if o is not None:
+        _check(o, "o", out_dtype, 4)
+        _shape(o, "o", R, J, H, dv)
+    _devices(("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("state_pool", state_pool),
+             ("slot_idx", slot_idx), ("pos_slots", pos_slots), ("o", o))
     if o is None:
         o = torch.empty((R, J, H, dv), dtype=out_dtype, device=q.device)
-    _check(o, "o", out_dtype, 4)
     return R, J, H, dk, dv, out_dtype, o
 
 
@@ -257,8 +353,7 @@ def gdn_decode_multi(q, k, v, alpha, beta, state_pool, slot_idx, pos_slots, *, o
                      o=None):
     """Gated DeltaNet form of gla_decode_multi; beta [R, n_tok, H]."""
     R, J, H, dk, dv, out_dtype, o = _multi_common(q, k, v, alpha, state_pool, slot_idx, pos_slots,
-                                                  out_dtype, o)
-    _check(beta, "beta", torch.float32, 3)
+                                                  out_dtype, o, beta=beta)
     _lib.call("gdn_decode_multi", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
               beta.data_ptr(), R, J, H, dk, dv, _DT[q.dtype], _DT[out_dtype],
               state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(), pos_slots.data_ptr(),
@@ -273,6 +368,7 @@ def gla_state_copy(state_pool, src_slots, dst_slots):
     _check(dst_slots, "dst_slots", torch.int32, 1)
     if src_slots.shape != dst_slots.shape:
         raise ValueError("src_slots and dst_slots must have the same length")
+    _devices(("state_pool", state_pool), ("src_slots", src_slots), ("dst_slots", dst_slots))
     n, H, dk, dv = state_pool.shape
     _lib.call("gla_state_copy", state_pool.data_ptr(), n, H, dk, dv, src_slots.data_ptr(),
               dst_slots.data_ptr(), src_slots.shape[0], _stream(state_pool))
@@ -284,9 +380,12 @@ def lin_attn_chunk_fwd(q, k, v, cu_seqlens, state_pool, norm_pool, slot_idx, *, 
     """Normalised linear attention (phi = elu + 1), chunked; updates
     state_pool[slot_idx] and norm_pool[slot_idx] ([n_slots, H, dk] fp32) in
     place, returns o."""
-    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, None, cu_seqlens, state_pool, slot_idx,
-                                               out_dtype, o)
     _check(norm_pool, "norm_pool", torch.float32, 3)
+    _shape(norm_pool, "norm_pool", state_pool.shape[0] if state_pool.dim() == 4 else None,
+           q.shape[1] if q.dim() == 3 else None, q.shape[2] if q.dim() == 3 else None)
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, None, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o, workspace=workspace,
+                                               extra=(("norm_pool", norm_pool),))
     B = cu_seqlens.shape[0] - 1
     need = _lib.lib().lin_attn_chunk_workspace_bytes(B, N, H, dk, dv, chunk)
     if need and workspace is None:
@@ -303,8 +402,11 @@ def lin_attn_chunk_fwd(q, k, v, cu_seqlens, state_pool, norm_pool, slot_idx, *, 
 def lin_attn_decode_step(q, k, v, state_pool, norm_pool, slot_idx, *, eps=1e-6, out_dtype=None,
                          o=None):
     """One normalised-linear-attention token per request, in place; returns o."""
-    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, None, state_pool, slot_idx, out_dtype, o)
     _check(norm_pool, "norm_pool", torch.float32, 3)
+    _shape(norm_pool, "norm_pool", state_pool.shape[0] if state_pool.dim() == 4 else None,
+           q.shape[1] if q.dim() == 3 else None, q.shape[2] if q.dim() == 3 else None)
+    R, H, dk, dv, out_dtype, o = _decode_common(q, k, v, None, state_pool, slot_idx, out_dtype, o,
+                                                extra=(("norm_pool", norm_pool),))
     _lib.call("lin_attn_decode_step", q.data_ptr(), k.data_ptr(), v.data_ptr(), R, H, dk, dv,
               _DT[q.dtype], _DT[out_dtype], state_pool.data_ptr(), norm_pool.data_ptr(),
               state_pool.shape[0], slot_idx.data_ptr(), float(eps), o.data_ptr(),
@@ -320,6 +422,7 @@ def gla_slot_copy(buf, src_slots, dst_slots):
     _check(dst_slots, "dst_slots", torch.int32, 1)
     if src_slots.shape != dst_slots.shape:
         raise ValueError("src_slots and dst_slots must have the same length")
+    _devices(("buf", buf), ("src_slots", src_slots), ("dst_slots", dst_slots))
     slot_bytes = buf[0].numel() * buf.element_size() if buf.shape[0] > 0 else 16
     _lib.call("gla_slot_copy", buf.data_ptr(), slot_bytes, buf.shape[0], src_slots.data_ptr(),
               dst_slots.data_ptr(), src_slots.shape[0], _stream(buf))
@@ -335,11 +438,34 @@ def causal_conv1d_fwd(x, w, cu_seqlens, conv_cache, slot_idx, *, zero_init=False
     _check(slot_idx, "slot_idx", torch.int32, 1)
     N, C = x.shape
     W = w.shape[1]
+    _shape(w, "w", C, W)
+    if cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must hold n_seqs + 1 entries")
+    _shape(slot_idx, "slot_idx", cu_seqlens.shape[0] - 1)
+    _shape(conv_cache, "conv_cache", None, W - 1, C)
+    if y is not None:
+        _check(y, "y", x.dtype, 2)
+        _shape(y, "y", N, C)
+    _devices(("x", x), ("w", w), ("cu_seqlens", cu_seqlens), ("conv_cache", conv_cache),
+             ("slot_idx", slot_idx), ("y", y))
     if y is None:
         y = torch.empty_like(x)
-    _check(y, "y", x.dtype, 2)
     _lib.call("causal_conv1d_fwd", x.data_ptr(), w.data_ptr(), cu_seqlens.data_ptr(),
               cu_seqlens.shape[0] - 1, N, C, W, conv_cache.data_ptr(), conv_cache.shape[0],
               slot_idx.data_ptr(), _lib.GLA_ZERO_INIT if zero_init else 0, y.data_ptr(),
               _DT[x.dtype], _stream(x))
     return y
+
+
+def gla_hbm_probe(mode, state_pool, slot_idx, sink=None):
+    """Measurement helper: the decode step's HBM traffic on state_pool at
+    slot_idx without its arithmetic (mode 0 read, 1 write zeros, 2 read and
+    write back in place, 3 as 2 with two heads per workgroup)."""
+    _check(state_pool, "state_pool", torch.float32, 4)
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    if sink is None:
+        sink = torch.empty(4, dtype=torch.int32, device=state_pool.device)
+    _devices(("state_pool", state_pool), ("slot_idx", slot_idx), ("sink", sink))
+    n, H, dk, dv = state_pool.shape
+    _lib.call("gla_hbm_probe", int(mode), state_pool.data_ptr(), slot_idx.shape[0], H, dk, dv, n,
+              slot_idx.data_ptr(), sink.data_ptr(), _stream(state_pool))
