@@ -43,7 +43,6 @@ def parse():
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
     p.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
-    p.add_argument("--cpu-sample-seqs", type=int, default=4)
     p.add_argument("--sweep", action="store_true",
                    help="instead of the benchmark line: GLA / GDN prefill over batch x length mixes "
                         "and decode over batch sizes, one JSON line per shape")
@@ -51,36 +50,97 @@ def parse():
 
 
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline_child(n_seqs: int, min_seconds: float = 10.0, max_reps: int = 3):
-    """The fp64 oracle, single-threaded on one core, on a bounded sample of
-    the headline workload: its first n_seqs sequences (4096 tokens x 16
-    heads each), repeated until min_seconds have passed (at most max_reps)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_child():
+    """The fp64 oracle, single-threaded on one pinned core, timed on each
+    workload: the toy example, the GLA prefill (all 4 x 4096 tokens x 16
+    heads), one GLA and one Gated DeltaNet decode step (256 requests x 16
+    heads; the pool passed holds just the 256 slots the step touches, so
+    the oracle does not copy the 768 others), the Gated DeltaNet prefill
+    (all 2 x 8192 tokens x 16 heads) and the mixed step on heads 0 and 7 of
+    every request (conv over those heads' channels, then the recurrence),
+    scaled by 16 / 2 since heads are independent."""
+    host = {"os_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": _cpu_model()}
     os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
-    import numpy as np  # noqa: F401  (threads pinned by the parent's env)
+    import numpy as np
     import oracle
     import synth
-    w = synth.prefill_gla()
-    T = int(w.cu_seqlens[1])
-    n = T * n_seqs
-    reps, dt = 0, 0.0
-    while reps < max_reps and (reps == 0 or dt < min_seconds):
+
+    def clock(fn):
         t0 = time.perf_counter()
-        oracle.gla_varlen(w.q[:n], w.k[:n], w.v[:n], w.alpha[:n], w.cu_seqlens[: n_seqs + 1],
-                          w.pool, w.slot_idx[:n_seqs], True)
-        dt += time.perf_counter() - t0
-        reps += 1
-    print(json.dumps({"value": reps * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                      "seconds": dt,
-                      "sample": f"{n_seqs} of 4 sequences (4096 tokens x 16 heads each) x {reps} "
-                                f"repetitions, fp64 token-by-token recurrence, numpy, 1 pinned core"}))
+        fn()
+        return time.perf_counter() - t0
+
+    cfg = {}
+    w = synth.page_toy_workload()
+    dt = clock(lambda: oracle.gla_varlen(w.q, w.k, w.v, w.alpha, w.cu_seqlens, w.pool, w.slot_idx, True))
+    cfg["toy"] = {"tokens_per_s": 64 / dt, "seconds": dt, "sample": "whole workload (T=64, d=16, 1 head)"}
+    w = synth.prefill_gla()
+    N = w.n_tokens
+    dt = clock(lambda: oracle.gla_varlen(w.q, w.k, w.v, w.alpha, w.cu_seqlens, w.pool, w.slot_idx, True))
+    cfg["gla_prefill"] = {"tokens_per_s": N / dt, "seconds": dt,
+                          "sample": "whole workload (4 x 4096 tokens x 16 heads)"}
+    for gdn in (False, True):
+        w = synth.decode(seed=3, gdn=gdn)
+        R = w.q.shape[0]
+        sub = w.pool[w.slot_idx]
+        ident = np.arange(R, dtype=np.int32)
+        if gdn:
+            f = lambda: oracle.gdn_decode(w.q, w.k, w.v, w.alpha, w.beta, sub, ident)  # noqa: E731
+        else:
+            f = lambda: oracle.gla_decode(w.q, w.k, w.v, w.alpha, sub, ident)  # noqa: E731
+        dt = clock(f)
+        nbytes = R * w.q.shape[1] * (2 * 128 * 128 * 4 + 4 * 128 * 2 + (8 if gdn else 4))
+        cfg["gdn_decode" if gdn else "gla_decode"] = {
+            "ms_per_step": dt * 1e3, "GBps": nbytes / dt / 1e9, "seconds": dt,
+            "sample": "whole step (256 requests x 16 heads)"}
+    w = synth.prefill_gdn()
+    N = w.n_tokens
+    dt = clock(lambda: oracle.gdn_varlen(w.q, w.k, w.v, w.alpha, w.beta, w.cu_seqlens, w.pool,
+                                         w.slot_idx))
+    cfg["gdn_prefill"] = {"tokens_per_s": N / dt, "seconds": dt,
+                          "sample": "whole workload (2 x 8192 tokens x 16 heads)"}
+    w = synth.mixed_varlen()
+    heads, d = [0, 7], 128
+    ch = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
+    N = w.n_tokens
+
+    def mixed():
+        y, _ = oracle.causal_conv1d(w.extra["x"][:, ch], w.extra["w"][ch], w.cu_seqlens,
+                                    w.extra["conv_cache"][:, :, ch], w.slot_idx)
+        v = synth.round_bf16(y.astype(np.float32)).reshape(-1, len(heads), d)
+        sl = w.slot_idx
+        oracle.gdn_varlen(w.q[:, heads], w.k[:, heads], v, w.alpha[:, heads], w.beta[:, heads],
+                          w.cu_seqlens, w.pool[sl][:, heads], np.arange(len(sl), dtype=np.int32))
+    dt = clock(mixed)
+    cfg["mixed_gdn_step"] = {"tokens_per_s": N / (dt * 16 / len(heads)), "seconds": dt,
+                             "sample": f"heads 0 and 7 of all {N} tokens (conv over their 256 "
+                                       f"channels, then the recurrence), time scaled by 8"}
+    head = cfg["gla_prefill"]
+    print(json.dumps({"value": head["tokens_per_s"], "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                      "sample": "GLA prefill, whole workload (4 x 4096 tokens x 16 heads), fp64 "
+                                "token-by-token recurrence in numpy on 1 pinned core",
+                      "seconds": sum(c["seconds"] for c in cfg.values()),
+                      "host": host, "configs": cfg}))
 
 
-def run_cpu_baseline(n_seqs: int):
+def run_cpu_baseline():
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
                NUMEXPR_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
-    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
-                          "--cpu-sample-seqs", str(n_seqs)], env=env, capture_output=True, text=True,
-                         timeout=600)
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child"],
+                         env=env, capture_output=True, text=True, timeout=900)
     if res.returncode != 0:
         raise RuntimeError(f"cpu baseline failed: {res.stderr[-2000:]}")
     return json.loads(res.stdout.strip().splitlines()[-1])
@@ -158,11 +218,12 @@ def bench_gdn_prefill(torch, G, synth, dev, steps, warmup):
         q, k, v, a, b = sets[i % 2]
         G.gdn_chunk_fwd(q, k, v, a, b, cu, pool, slots, chunk=w.chunk, o=o, workspace=ws)
     ms = timed(torch, step, steps, warmup)
+    dist = per_call_ms(torch, step, max(steps, 20), warmup + steps)
     nbytes = 3 * N * H * d * 2 + 2 * N * H * 4 + N * H * d * 2 + 2 * w.n_seqs * H * d * d * 4
     C = w.chunk
     flops = N * H * (2 * C * (3 * d + 2 * d) + C * C // 3 + 6 * d * d)
     return {"workload": w.name, "ms": ms, "tokens_per_s": N / (ms * 1e-3), "bytes": nbytes,
-            "flops": flops}
+            "flops": flops, "per_call_ms": dist}
 
 
 def bench_decode(torch, G, synth, dev, steps, warmup, gdn):
@@ -206,6 +267,7 @@ def bench_decode_multi(torch, G, synth, dev, steps, warmup, gdn):
         else:
             G.gla_decode_multi(q, k, v, a, pool, slots, pos, o=o)
     ms = timed(torch, step, steps, warmup)
+    dist = per_call_ms(torch, step, max(steps, 20), warmup + steps)
     nbytes = R * H * ((1 + J) * d * d * 4 + J * (4 * d * 2 + (8 if gdn else 4)))
     # replay strategy: verify with no state kept, then commit a random
     # accepted prefix (0..4 tokens) in place by running the draft again
@@ -226,7 +288,7 @@ def bench_decode_multi(torch, G, synth, dev, steps, warmup, gdn):
                 G.gla_decode_multi(q, k, v, a, pool, slots, pos_, o=o)
     ms_r = timed(torch, replay, steps, warmup)
     return {"workload": w.name, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
-            "replay_ms": ms_r}
+            "replay_ms": ms_r, "per_call_ms": dist}
 
 
 def bench_gdn_prefill_ckpt(torch, G, synth, dev, steps, warmup):
@@ -245,10 +307,12 @@ def bench_gdn_prefill_ckpt(torch, G, synth, dev, steps, warmup):
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
     ws = torch.empty(G.workspace_bytes("gdn", B, N, H, d, d, w.chunk), dtype=torch.uint8,
                      device="cuda:0")
-    ms = timed(torch, lambda i: G.gdn_chunk_fwd_ckpt(q, k, v, a, b, cu, pool, slots, ck, iv,
-                                                     chunk=w.chunk, o=o, workspace=ws),
-               steps, warmup)
-    return {"workload": w.name + f"-ckpt{iv}", "ms": ms, "tokens_per_s": N / (ms * 1e-3)}
+    def step(i):
+        G.gdn_chunk_fwd_ckpt(q, k, v, a, b, cu, pool, slots, ck, iv, chunk=w.chunk, o=o, workspace=ws)
+    ms = timed(torch, step, steps, warmup)
+    dist = per_call_ms(torch, step, max(steps, 20), warmup + steps)
+    return {"workload": w.name + f"-ckpt{iv}", "ms": ms, "tokens_per_s": N / (ms * 1e-3),
+            "per_call_ms": dist}
 
 
 def bench_lin_attn(torch, G, synth, dev, steps, warmup):
@@ -263,23 +327,27 @@ def bench_lin_attn(torch, G, synth, dev, steps, warmup):
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda:0")
     ws = torch.empty(G.workspace_bytes("lin", w.n_seqs, N, H, d, d, 64), dtype=torch.uint8,
                      device="cuda:0")
-    ms = timed(torch, lambda i: G.lin_attn_chunk_fwd(q, k, v, cu, pool, zpool, slots, chunk=64,
-                                                     o=o, workspace=ws), steps, warmup)
+    def pstep(i):
+        G.lin_attn_chunk_fwd(q, k, v, cu, pool, zpool, slots, chunk=64, o=o, workspace=ws)
+    ms = timed(torch, pstep, steps, warmup)
+    pdist = per_call_ms(torch, pstep, max(steps, 20), warmup + steps)
     nbytes = 4 * N * H * d * 2 + 4 * H * (2 * d * d * 4 + 2 * d * 4)
     R = 256
     wd = synth.lin_attn_varlen(641, [1] * R, 16, 128, 128, dtype="bf16", n_slots=1024)
     qd, kd, vd = dev(wd.q, "bf16"), dev(wd.k, "bf16"), dev(wd.v, "bf16")
     pd, zd, sd = dev(wd.pool), dev(wd.extra["zpool"]), dev(wd.slot_idx)
     od = torch.empty((R, H, d), dtype=torch.bfloat16, device="cuda:0")
-    msd = timed(torch, lambda i: G.lin_attn_decode_step(qd, kd, vd, pd, zd, sd, o=od), steps,
-                warmup)
+    def dstep(i):
+        G.lin_attn_decode_step(qd, kd, vd, pd, zd, sd, o=od)
+    msd = timed(torch, dstep, steps, warmup)
+    ddist = per_call_ms(torch, dstep, max(steps, 20), warmup + steps)
     dbytes = R * H * (2 * d * d * 4 + 2 * d * 4 + 4 * d * 2)
     return {"prefill": {"workload": "lin-attn-prefill-4x4096-H16-d128-C64-bf16", "ms": ms,
                         "tokens_per_s": N / (ms * 1e-3),
-                        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "per_call_ms": pdist},
             "decode": {"workload": "lin-attn-decode-256req-H16-d128-pool1024", "ms": msd,
                        "GBps": dbytes / (msd * 1e-3) / 1e9,
-                       "hbm_frac": dbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
+                       "hbm_frac": dbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBPS, "per_call_ms": ddist}}
 
 
 def bench_slot_copy(torch, G, synth, dev, steps, warmup):
@@ -291,10 +359,38 @@ def bench_slot_copy(torch, G, synth, dev, steps, warmup):
     perm = np.random.default_rng(9).permutation(1024).astype(np.int32)
     pairs = [(dev(perm[512 * r:512 * r + 256].copy()), dev(perm[512 * r + 256:512 * r + 512].copy()))
              for r in range(2)]
-    ms = timed(torch, lambda i: G.gla_state_copy(pool, *pairs[i % 2]), steps, warmup)
+    def step(i):
+        G.gla_state_copy(pool, *pairs[i % 2])
+    ms = timed(torch, step, steps, warmup)
+    dist = per_call_ms(torch, step, max(steps, 20), warmup + steps)
     nbytes = 2 * 256 * 16 * 128 * 128 * 4
     return {"workload": "256 slot pairs x 1 MiB, 1024-slot pool", "ms": ms,
-            "GBps": nbytes / (ms * 1e-3) / 1e9}
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "per_call_ms": dist}
+
+
+def bench_hbm_ceiling(torch, G, synth, dev, steps, warmup):
+    """The decode step's HBM footprint without its arithmetic
+    (gla_hbm_probe): 256 requests x 16 heads of 64 KiB state blocks in a
+    1024-slot pool, the 4 disjoint slot quarters rotated as in the decode
+    leg; read only, write only, read + write back in place, and read +
+    write with two heads per workgroup."""
+    w = synth.decode(seed=3, gdn=False)
+    R, H, d = w.q.shape
+    pool = dev(w.pool)
+    perm = w.extra["perm"]
+    quarters = [dev(perm[i * R:(i + 1) * R].copy()) for i in range(len(perm) // R)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    block = R * H * d * d * 4
+    out = {"workload": "256 requests x 16 heads x 64 KiB, 1024-slot pool, slot quarters rotated",
+           "bytes_read_per_call": block}
+    for mode, name, nb in ((0, "read", block), (1, "write", block), (2, "read_write", 2 * block),
+                           (3, "read_write_2heads_per_wg", 2 * block)):
+        def step(i, mode=mode):
+            G.gla_hbm_probe(mode, pool, quarters[i % len(quarters)], sink)
+        ms = timed(torch, step, steps, warmup)
+        out[name] = {"GBps": nb / (ms * 1e-3) / 1e9, "ms": ms,
+                     "per_call_ms": per_call_ms(torch, step, max(steps, 20), warmup + steps)}
+    return out
 
 
 def bench_mixed(torch, G, synth, dev, steps, warmup):
@@ -311,6 +407,7 @@ def bench_mixed(torch, G, synth, dev, steps, warmup):
                          dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.alpha), dev(w.beta),
                          dev(w.cu_seqlens), dev(cu_p), dev(w.pool), dev(w.slot_idx), P, NP)
     ms = timed(torch, lambda i: step_obj(), steps, warmup)
+    dist = per_call_ms(torch, lambda i: step_obj(), max(steps, 5), warmup + steps)
     nbytes = (N * H * d * 2 * 3 + N * H * 8            # q, k, o; alpha, beta
               + N * H * d * 2 * 2                       # conv x in, y out (= v)
               + N * H * d * 2                           # v read by the recurrence
@@ -318,7 +415,7 @@ def bench_mixed(torch, G, synth, dev, steps, warmup):
               + len(lens) * 3 * H * d * 2 * 2)          # conv cache read + write
     return {"workload": w.name, "ms": ms, "tokens_per_s": N / (ms * 1e-3), "n_tokens": N,
             "prefill_tokens": NP, "longest_prompt": int(lens[:P].max()), "bytes": nbytes,
-            "GBps": nbytes / (ms * 1e-3) / 1e9}
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "per_call_ms": dist}
 
 
 def _profile_entry(kernel: str):
@@ -447,7 +544,7 @@ def calib_copy(torch):
 def main():
     args = parse()
     if args.cpu_baseline_child:
-        cpu_baseline_child(args.cpu_sample_seqs)
+        cpu_baseline_child()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -457,7 +554,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and not args.sweep and args.only in ("all", "gla_prefill"):
-        cpu = run_cpu_baseline(args.cpu_sample_seqs)      # before this process touches the GPU
+        cpu = run_cpu_baseline()      # before this process touches the GPU
 
     import torch
     import gated_deltanet_gla_amd as G
@@ -488,6 +585,10 @@ def main():
         print(f"# decode {res['gla_decode']['ms']:.3f} / {res['gdn_decode']['ms']:.3f} ms",
               file=sys.stderr, flush=True)
         res["slot_copy"] = bench_slot_copy(torch, G, synth, dev, K, W)
+        res["hbm_ceiling"] = bench_hbm_ceiling(torch, G, synth, dev, K, W)
+        print(f"# ceiling read {res['hbm_ceiling']['read']['GBps']:.0f} write "
+              f"{res['hbm_ceiling']['write']['GBps']:.0f} read+write "
+              f"{res['hbm_ceiling']['read_write']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
         res["gla_decode_multi"] = bench_decode_multi(torch, G, synth, dev, K, W, gdn=False)
         res["gdn_decode_multi"] = bench_decode_multi(torch, G, synth, dev, K, W, gdn=True)
         print(f"# decode multi {res['gla_decode_multi']['ms']:.3f} / "
@@ -539,6 +640,17 @@ def main():
                                   "unit": "GB/s", "frac": r["GBps"] / HBM_PEAK_GBPS,
                                   "traffic": measured_traffic("decode_kernel_gla"),
                                   "kernel": "decode_kernel (GLA)", "algorithmic_bytes": r["bytes"]}
+        if "hbm_ceiling" in res:
+            c = res["hbm_ceiling"]
+            best = max(c["read_write"]["GBps"], c["read_write_2heads_per_wg"]["GBps"])
+            out["roofline_decode"]["measured_ceiling"] = {
+                "read_GBps": c["read"]["GBps"], "write_GBps": c["write"]["GBps"],
+                "read_write_GBps": c["read_write"]["GBps"],
+                "read_write_2heads_per_wg_GBps": c["read_write_2heads_per_wg"]["GBps"],
+                "frac_of_read_write": r["GBps"] / best,
+                "workload": c["workload"], "per_call_ms": {k: c[k]["per_call_ms"] for k in
+                                                           ("read", "write", "read_write",
+                                                            "read_write_2heads_per_wg")}}
         out["decode_hbm_GBps"] = {
             "gla": res["gla_decode"]["GBps"], "gdn": res["gdn_decode"]["GBps"],
             "frac_of_peak": {"gla": res["gla_decode"]["GBps"] / HBM_PEAK_GBPS,
@@ -551,7 +663,7 @@ def main():
         r = res["slot_copy"]
         out["slot_copy_hbm_GBps"] = {"GBps": r["GBps"], "ms": r["ms"],
                                      "frac_of_peak": r["GBps"] / HBM_PEAK_GBPS,
-                                     "workload": r["workload"]}
+                                     "workload": r["workload"], "per_call_ms": r["per_call_ms"]}
     if "gla_decode_multi" in res:
         out["decode_multi_hbm_GBps"] = {
             k: res[f"{k}_decode_multi"]["GBps"] for k in ("gla", "gdn")}
@@ -560,6 +672,7 @@ def main():
                              for k in ("gla", "gdn")},
             "ms": {k: res[f"{k}_decode_multi"]["ms"] for k in ("gla", "gdn")},
             "replay_strategy_ms": {k: res[f"{k}_decode_multi"]["replay_ms"] for k in ("gla", "gdn")},
+            "per_call_ms": {k: res[f"{k}_decode_multi"]["per_call_ms"] for k in ("gla", "gdn")},
             "workload": "256 requests x 4 draft tokens x 16 heads, 128x128 fp32 states, state "
                         "after every position kept (1280-slot pool)"})
     other = {}
@@ -570,17 +683,19 @@ def main():
                                 "ms": r["ms"], "hbm_frac": ach / HBM_PEAK_GBPS,
                                 "mfma_frac": r["flops"] / (r["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                 "traffic": measured_traffic("gdn_chunk_fwd"),
-                                "mfma_counters": measured_mfma("gdn_chunk_fwd")}
+                                "mfma_counters": measured_mfma("gdn_chunk_fwd"),
+                                "per_call_ms": r["per_call_ms"]}
     if "gdn_prefill_ckpt" in res:
         r = res["gdn_prefill_ckpt"]
-        other["gdn_prefill_ckpt"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s")}
+        other["gdn_prefill_ckpt"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s", "per_call_ms")}
     if "lin_attn" in res:
         other["lin_attn_prefill"] = res["lin_attn"]["prefill"]
         other["lin_attn_decode"] = res["lin_attn"]["decode"]
     if "mixed" in res:
         r = res["mixed"]
         other["mixed_gdn_step"] = {k: r[k] for k in ("workload", "ms", "tokens_per_s", "n_tokens",
-                                                     "prefill_tokens", "longest_prompt", "GBps")}
+                                                     "prefill_tokens", "longest_prompt", "GBps",
+                                                     "per_call_ms")}
         other["mixed_gdn_step"]["hbm_frac"] = r["GBps"] / HBM_PEAK_GBPS
     if other:
         out["other_workloads"] = other

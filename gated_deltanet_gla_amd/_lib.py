@@ -44,6 +44,7 @@ SIGNATURES = {
                                     ct.c_int, _F, _I32, _P, _P, _P, _P]),
     "gla_state_copy": (ct.c_int, [_F, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "gla_slot_copy": (ct.c_int, [_P, _SZ, _I32, _P, _P, _I32, _P]),
+    "gla_hbm_probe": (ct.c_int, [ct.c_int32, _F, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "lin_attn_chunk_fwd": (ct.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                       ct.c_int, ct.c_int, _F, _F, _I32, _P, _U32, ct.c_float, _P,
                                       _P, _SZ, _P]),

@@ -296,6 +296,18 @@ int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, int32_t 
                          n_slots, src_slots, dst_slots, n_copy, stream);
 }
 
+int gla_hbm_probe(int32_t mode, float* state_pool, int32_t n_req, int32_t n_heads, int32_t dk,
+                  int32_t dv, int32_t n_slots, const int32_t* slot_idx, void* sink, void* stream) {
+    if (mode < 0 || mode > 3 || n_req < 0 || n_heads < 1 || n_slots < 0) return GLA_ESHAPE;
+    if (dk != 128 || dv != 128) return GLA_ESHAPE;
+    if (static_cast<long>(n_req) * n_heads > kMaxWork) return GLA_ESHAPE;
+    if (n_req == 0) return GLA_OK;
+    if (n_slots < 1) return GLA_ESHAPE;
+    if (!state_pool || !slot_idx || !sink) return GLA_EPTR;
+    return hip_status(gla::launch_hbm_probe(mode, state_pool, n_req, n_heads, n_slots, slot_idx, sink,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                        int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv,
                        int32_t chunk, gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,

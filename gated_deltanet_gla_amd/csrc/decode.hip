@@ -375,6 +375,58 @@ slot_copy_kernel(u32x4* __restrict__ buf, long slot_vec4, int pieces, int n_slot
     }
 }
 
+// Measurement helper: the decode step's HBM footprint without its
+// arithmetic.  Item (request r, head h) is the 64 KiB block at
+// pool + (slot_idx[r] * n_heads + h) * 64 KiB, accessed like decode_kernel
+// does (256 threads, 16 independent 16-byte nontemporal accesses each,
+// thread t touching vectors t + 256 i).  MODE 0 reads every block; 1 writes
+// zeros to it; 2 reads it and writes the same bytes back in place; 3 does 2
+// for two items per workgroup, both blocks read before either is written.
+// The value read is folded into a test that never holds for finite data,
+// so the loads cannot be dropped.
+template <int MODE>
+__global__ void __launch_bounds__(256)
+hbm_probe_kernel(u32x4* __restrict__ pool, int n_heads, int n_items, int n_slots,
+                 const int32_t* __restrict__ slot_idx, uint32_t salt, u32x4* __restrict__ sink) {
+    constexpr int PER = MODE == 3 ? 2 : 1;
+    constexpr int NV = 16;
+    const int t = threadIdx.x;
+    u32x4* base[PER];
+    bool ok[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int wi = blockIdx.x * PER + p;
+        const int h = wi % n_heads, r = wi / n_heads;
+        const int slot = wi < n_items ? slot_idx[r] : -1;
+        ok[p] = slot >= 0 && slot < n_slots;
+        base[p] = pool + (static_cast<long>(ok[p] ? slot : 0) * n_heads + h) * (256 * NV);
+    }
+    u32x4 x[PER][NV];
+    if constexpr (MODE != 1) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                x[p][i] = ok[p] ? __builtin_nontemporal_load(base[p] + t + 256 * i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (MODE == 0) {
+        u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc &= x[0][i];
+        if ((acc.x & acc.y & acc.z & acc.w) == 0xffffffffu) sink[0] = acc;   // NaN bit patterns only
+    } else {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            if (!ok[p]) continue;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const u32x4 y = MODE == 1 ? u32x4{salt, salt, salt, salt} : (x[p][i] ^ salt);
+                __builtin_nontemporal_store(y, base[p] + t + 256 * i);
+            }
+        }
+    }
+}
+
 template <int DK, int DV, class TI, class TO, bool GDN>
 hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
     using Sh = DecodeShape<DK, DV>;
@@ -475,6 +527,22 @@ hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s) {
         case 128: return launch_lin_dv<128>(a, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_hbm_probe(int mode, float* pool, int n_req, int n_heads, int n_slots,
+                            const int32_t* slot_idx, void* sink, hipStream_t s) {
+    const int items = n_req * n_heads;
+    if (items == 0) return hipSuccess;
+    u32x4* p = reinterpret_cast<u32x4*>(pool);
+    u32x4* sk = static_cast<u32x4*>(sink);
+    switch (mode) {
+        case 0: hipLaunchKernelGGL(hbm_probe_kernel<0>, dim3(items), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
+        case 1: hipLaunchKernelGGL(hbm_probe_kernel<1>, dim3(items), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
+        case 2: hipLaunchKernelGGL(hbm_probe_kernel<2>, dim3(items), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
+        case 3: hipLaunchKernelGGL(hbm_probe_kernel<3>, dim3((items + 1) / 2), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_slot_copy(const CopyArgs& a, hipStream_t s) {

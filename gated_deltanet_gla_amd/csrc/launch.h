@@ -87,6 +87,8 @@ struct ConvArgs {
 hipError_t launch_gla_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_slot_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_hbm_probe(int mode, float* pool, int n_req, int n_heads, int n_slots,
+                            const int32_t* slot_idx, void* sink, hipStream_t s);
 hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s);
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s);
