@@ -298,7 +298,7 @@ int gla_state_copy(float* state_pool, int32_t n_slots, int32_t n_heads, int32_t 
 
 int gla_hbm_probe(int32_t mode, float* state_pool, int32_t n_req, int32_t n_heads, int32_t dk,
                   int32_t dv, int32_t n_slots, const int32_t* slot_idx, void* sink, void* stream) {
-    if (mode < 0 || mode > 3 || n_req < 0 || n_heads < 1 || n_slots < 0) return GLA_ESHAPE;
+    if (mode < 0 || mode > 15 || n_req < 0 || n_heads < 1 || n_slots < 0) return GLA_ESHAPE;
     if (dk != 128 || dv != 128) return GLA_ESHAPE;
     if (static_cast<long>(n_req) * n_heads > kMaxWork) return GLA_ESHAPE;
     if (n_req == 0) return GLA_OK;

@@ -378,17 +378,18 @@ slot_copy_kernel(u32x4* __restrict__ buf, long slot_vec4, int pieces, int n_slot
 // Measurement helper: the decode step's HBM footprint without its
 // arithmetic.  Item (request r, head h) is the 64 KiB block at
 // pool + (slot_idx[r] * n_heads + h) * 64 KiB, accessed like decode_kernel
-// does (256 threads, 16 independent 16-byte nontemporal accesses each,
-// thread t touching vectors t + 256 i).  MODE 0 reads every block; 1 writes
-// zeros to it; 2 reads it and writes the same bytes back in place; 3 does 2
-// for two items per workgroup, both blocks read before either is written.
-// The value read is folded into a test that never holds for finite data,
-// so the loads cannot be dropped.
-template <int MODE>
+// does (256 threads, 16 independent 16-byte accesses each, thread t
+// touching vectors t + 256 i).  OP 0 reads every block; 1 writes zeros to
+// it; 2 reads it and writes the same bytes back in place; 3 does 2 for two
+// items per workgroup, both blocks read before either is written.  Loads
+// and stores use the nontemporal policy unless LDEF / SDEF ask for the
+// default one.  The values read are folded into a test that holds only if
+// every word read is all ones (a NaN pattern), so the loads stay.
+template <int OP, bool LDEF, bool SDEF>
 __global__ void __launch_bounds__(256)
 hbm_probe_kernel(u32x4* __restrict__ pool, int n_heads, int n_items, int n_slots,
                  const int32_t* __restrict__ slot_idx, uint32_t salt, u32x4* __restrict__ sink) {
-    constexpr int PER = MODE == 3 ? 2 : 1;
+    constexpr int PER = OP == 3 ? 2 : 1;
     constexpr int NV = 16;
     const int t = threadIdx.x;
     u32x4* base[PER];
@@ -402,26 +403,31 @@ hbm_probe_kernel(u32x4* __restrict__ pool, int n_heads, int n_items, int n_slots
         base[p] = pool + (static_cast<long>(ok[p] ? slot : 0) * n_heads + h) * (256 * NV);
     }
     u32x4 x[PER][NV];
-    if constexpr (MODE != 1) {
+    if constexpr (OP != 1) {
 #pragma unroll
         for (int p = 0; p < PER; ++p)
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                x[p][i] = ok[p] ? __builtin_nontemporal_load(base[p] + t + 256 * i) : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < NV; ++i) {
+                const u32x4* src = base[p] + t + 256 * i;
+                x[p][i] = !ok[p] ? u32x4{0u, 0u, 0u, 0u}
+                                 : (LDEF ? *src : __builtin_nontemporal_load(src));
+            }
     }
-    if constexpr (MODE == 0) {
-        u32x4 acc = {0u, 0u, 0u, 0u};
+    if constexpr (OP == 0) {
+        u32x4 acc = {~0u, ~0u, ~0u, ~0u};
 #pragma unroll
         for (int i = 0; i < NV; ++i) acc &= x[0][i];
-        if ((acc.x & acc.y & acc.z & acc.w) == 0xffffffffu) sink[0] = acc;   // NaN bit patterns only
+        if ((acc.x & acc.y & acc.z & acc.w) == 0xffffffffu) sink[0] = acc;
     } else {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             if (!ok[p]) continue;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const u32x4 y = MODE == 1 ? u32x4{salt, salt, salt, salt} : (x[p][i] ^ salt);
-                __builtin_nontemporal_store(y, base[p] + t + 256 * i);
+                const u32x4 y = OP == 1 ? u32x4{salt, salt, salt, salt} : (x[p][i] ^ salt);
+                u32x4* dst = base[p] + t + 256 * i;
+                if constexpr (SDEF) *dst = y;
+                else __builtin_nontemporal_store(y, dst);
             }
         }
     }
@@ -529,18 +535,40 @@ hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+template <int OP, bool LDEF, bool SDEF>
+void probe_launch(int items, u32x4* p, int n_heads, int n_slots, const int32_t* slot_idx, u32x4* sk,
+                  hipStream_t s) {
+    const int blocks = OP == 3 ? (items + 1) / 2 : items;
+    hipLaunchKernelGGL((hbm_probe_kernel<OP, LDEF, SDEF>), dim3(blocks), dim3(256), 0, s, p, n_heads, items,
+                       n_slots, slot_idx, 0u, sk);
+}
+
+template <int OP>
+void probe_policy(int policy, int items, u32x4* p, int n_heads, int n_slots, const int32_t* slot_idx,
+                  u32x4* sk, hipStream_t s) {
+    switch (policy) {
+        case 0: probe_launch<OP, false, false>(items, p, n_heads, n_slots, slot_idx, sk, s); break;
+        case 1: probe_launch<OP, true, false>(items, p, n_heads, n_slots, slot_idx, sk, s); break;
+        case 2: probe_launch<OP, false, true>(items, p, n_heads, n_slots, slot_idx, sk, s); break;
+        default: probe_launch<OP, true, true>(items, p, n_heads, n_slots, slot_idx, sk, s); break;
+    }
+}
+
+// mode: bits 0-1 the operation (read, write, read + write, read + write
+// with two items per workgroup); bit 2 default-policy loads; bit 3
+// default-policy stores.
 hipError_t launch_hbm_probe(int mode, float* pool, int n_req, int n_heads, int n_slots,
                             const int32_t* slot_idx, void* sink, hipStream_t s) {
     const int items = n_req * n_heads;
     if (items == 0) return hipSuccess;
     u32x4* p = reinterpret_cast<u32x4*>(pool);
     u32x4* sk = static_cast<u32x4*>(sink);
-    switch (mode) {
-        case 0: hipLaunchKernelGGL(hbm_probe_kernel<0>, dim3(items), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
-        case 1: hipLaunchKernelGGL(hbm_probe_kernel<1>, dim3(items), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
-        case 2: hipLaunchKernelGGL(hbm_probe_kernel<2>, dim3(items), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
-        case 3: hipLaunchKernelGGL(hbm_probe_kernel<3>, dim3((items + 1) / 2), dim3(256), 0, s, p, n_heads, items, n_slots, slot_idx, 0u, sk); break;
-        default: return hipErrorInvalidValue;
+    const int policy = (mode >> 2) & 3;
+    switch (mode & 3) {
+        case 0: probe_policy<0>(policy, items, p, n_heads, n_slots, slot_idx, sk, s); break;
+        case 1: probe_policy<1>(policy, items, p, n_heads, n_slots, slot_idx, sk, s); break;
+        case 2: probe_policy<2>(policy, items, p, n_heads, n_slots, slot_idx, sk, s); break;
+        default: probe_policy<3>(policy, items, p, n_heads, n_slots, slot_idx, sk, s); break;
     }
     return hipGetLastError();
 }

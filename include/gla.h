@@ -378,11 +378,13 @@ GLA_API int causal_conv1d_fwd(const void* x, const float* w, const int32_t* cu_s
  * d_v = 128) without its arithmetic, to measure the read / write ceiling
  * that step runs against on the machine at hand.  Item (request r, head h)
  * is the 64 KiB block state_pool + (slot_idx[r] * n_heads + h) * 16384
- * floats, accessed with the decode kernel's pattern.  mode 0: read every
- * block; 1: write zeros over every block (destroys those states); 2: read
- * each block and write the same bytes back in place (the pool is left as
- * it was); 3: as 2, with two items per workgroup and both blocks read
- * before either is written.  sink: 16 bytes of device memory that mode 0
+ * floats, accessed with the decode kernel's pattern.  mode & 3 = 0: read
+ * every block; 1: write zeros over every block (destroys those states); 2:
+ * read each block and write the same bytes back in place (the pool is left
+ * as it was); 3: as 2, with two items per workgroup and both blocks read
+ * before either is written.  Loads and stores are nontemporal, unless bit 2
+ * (loads) or bit 3 (stores) of mode asks for the default cache policy.
+ * sink: 16 bytes of device memory that a read
  * may write (it never does for finite data).  Slots outside [0, n_slots)
  * are skipped.  dk = dv = 128 only (GLA_ESHAPE otherwise).
  */
