@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgla_mi35
 
 GLA_F32, GLA_BF16 = 0, 1
 GLA_OK, GLA_EPTR, GLA_ESHAPE, GLA_EDTYPE, GLA_ECHUNK, GLA_EWORKSPACE, GLA_EHIP = 0, -1, -2, -3, -4, -5, -6
+GLA_ESCRATCH = -7
+GLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 GLA_ZERO_INIT = 1
 
 # name -> (restype, argtypes); mirrors include/gla.h
@@ -20,6 +22,8 @@ _P, _F, _I32, _U32, _SZ = ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_uint32, ct.
 SIGNATURES = {
     "gla_chunk_fwd": (ct.c_int, [_P, _P, _P, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  ct.c_int, ct.c_int, _F, _I32, _P, _U32, _P, _P, _SZ, _P]),
+    "gla_chunk_fwd_noalloc": (ct.c_int, [_P, _P, _P, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                         ct.c_int, ct.c_int, _F, _I32, _P, _U32, _P, _P]),
     "gdn_chunk_fwd": (ct.c_int, [_P, _P, _P, _F, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  ct.c_int, ct.c_int, _F, _I32, _P, _U32, _P, _P, _SZ, _P]),
     "gla_chunk_fwd_ckpt": (ct.c_int, [_P, _P, _P, _F, _P, _I32, _I32, _I32, _I32, _I32, _I32,

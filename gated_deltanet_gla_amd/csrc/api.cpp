@@ -2,9 +2,11 @@
 // (nothing is enqueued when it fails) and dispatch to the kernel launchers.
 #include "gla.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <limits>
+#include <mutex>
 
 #include "launch.h"
 
@@ -76,6 +78,37 @@ int check_decode(const void* q, const void* k, const void* v, const float* alpha
     return GLA_OK;
 }
 
+// Scratch of gla_chunk_fwd_noalloc: a fixed array in each GPU's memory, so
+// that entry point allocates nothing.  In host code the name `scratch` is
+// only a stand-in for the symbol; its device address (one per GPU) comes
+// from hipGetSymbolAddress and is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[GLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_init;
+
+// The scratch array's address on the current device, looked up on the
+// first call made with that device current and kept.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GLA_EHIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_init);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();     // leave no sticky error for the caller's next call
+                return GLA_EHIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,6 +124,7 @@ const char* gla_status_string(int status) {
         case GLA_ECHUNK: return "unsupported chunk size";
         case GLA_EWORKSPACE: return "workspace missing or too small";
         case GLA_EHIP: return "HIP launch failed";
+        case GLA_ESCRATCH: return "the call needs more scratch than gla_chunk_fwd_noalloc's fixed array";
     }
     return "unknown status";
 }
@@ -168,6 +202,26 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
     return gla_chunk_fwd_ckpt(q, k, v, alpha, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                               in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, chunk,
                               nullptr, 0, o, workspace, workspace_bytes, stream);
+}
+
+int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
+                          int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                          gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,
+                          int32_t n_slots, const int32_t* slot_idx, uint32_t flags, void* o,
+                          void* stream) {
+    int st = check_chunk(q, k, v, alpha, true, nullptr, false, cu_seqlens, n_seqs, n_tokens, n_heads,
+                         dk, dv, chunk, in_dtype, out_dtype, state_pool, n_slots, slot_idx, flags, o);
+    if (st != GLA_OK) return st;
+    if (n_seqs == 0) return GLA_OK;
+    const size_t need = gla::gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (need > GLA_NOALLOC_SCRATCH_BYTES) return GLA_ESCRATCH;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != GLA_OK) return st;
+    return gla_chunk_fwd(q, k, v, alpha, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk, in_dtype,
+                         out_dtype, state_pool, n_slots, slot_idx, flags, o, ws,
+                         GLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,

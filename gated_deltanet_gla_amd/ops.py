@@ -128,6 +128,21 @@ def gla_chunk_fwd(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, *, chunk=64,
     return o
 
 
+def gla_chunk_fwd_noalloc(q, k, v, alpha, cu_seqlens, state_pool, slot_idx, *, chunk=64,
+                          out_dtype=None, zero_init=False, o=None):
+    """gla_chunk_fwd without a workspace: the library's fixed per-GPU scratch
+    array is used instead, so the C call allocates nothing (pass ``o`` to
+    allocate nothing here either).  Calls that overlap on one GPU race."""
+    N, H, dk, dv, out_dtype, o = _chunk_common(q, k, v, alpha, cu_seqlens, state_pool, slot_idx,
+                                               out_dtype, o)
+    B = cu_seqlens.shape[0] - 1
+    _lib.call("gla_chunk_fwd_noalloc", q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+              cu_seqlens.data_ptr(), B, N, H, dk, dv, chunk, _DT[q.dtype], _DT[out_dtype],
+              state_pool.data_ptr(), state_pool.shape[0], slot_idx.data_ptr(),
+              _lib.GLA_ZERO_INIT if zero_init else 0, o.data_ptr(), _stream(q))
+    return o
+
+
 def gdn_chunk_fwd(q, k, v, alpha, beta, cu_seqlens, state_pool, slot_idx, *, chunk=64,
                   out_dtype=None, zero_init=False, o=None, workspace=None):
     """Chunked Gated DeltaNet prefill; updates state_pool[slot_idx] in place, returns o."""

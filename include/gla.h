@@ -85,7 +85,8 @@ enum {
     GLA_EDTYPE = -3,     /* unsupported dtype                                 */
     GLA_ECHUNK = -4,     /* unsupported chunk size                            */
     GLA_EWORKSPACE = -5, /* workspace missing or smaller than required        */
-    GLA_EHIP = -6        /* the HIP launch failed                             */
+    GLA_EHIP = -6,       /* the HIP launch failed                             */
+    GLA_ESCRATCH = -7    /* needs more than gla_chunk_fwd_noalloc's fixed scratch */
 };
 
 /* flags */
@@ -118,6 +119,30 @@ GLA_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const flo
                   float* state_pool, int32_t n_slots, const int32_t* slot_idx,
                   uint32_t flags, void* o,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gla_chunk_fwd_noalloc -- gla_chunk_fwd for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments, results and
+ * errors without the workspace.  The per-segment states go to a fixed
+ * array of GLA_NOALLOC_SCRATCH_BYTES in each GPU's memory, owned by the
+ * library and held until the process ends; the call allocates nothing.  A
+ * call whose gla_chunk_workspace_bytes() exceeds that size returns
+ * GLA_ESCRATCH with nothing enqueued (at 16 heads, d = 128, chunk 64 the
+ * bound is 64 KiB + 516 B per (segment, head) with about n_tokens / 1024 +
+ * n_seqs segments, so e.g. 40 sequences totalling 16384 tokens fit).  All
+ * calls on one GPU share that array: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and give wrong results;
+ * calls ordered on one stream do not.  The array's address on a device is
+ * looked up the first time the call runs with that device current.
+ */
+#define GLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+GLA_API int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                  const float* alpha, const int32_t* cu_seqlens, int32_t n_seqs,
+                  int32_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int32_t chunk,
+                  gla_dtype in_dtype, gla_dtype out_dtype, float* state_pool,
+                  int32_t n_slots, const int32_t* slot_idx, uint32_t flags, void* o,
+                  void* stream);
 
 /*
  * gdn_chunk_fwd -- Gated DeltaNet prefill, chunked.  Same contract as
