@@ -391,6 +391,16 @@ struct BufRsrc {
     __device__ __forceinline__ float loadf_nt(uint32_t off) const {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNT));
     }
+    // with a wave-uniform byte offset soff added to the per-lane one
+    __device__ __forceinline__ u32x4 load16(uint32_t off, uint32_t soff) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+    }
+    __device__ __forceinline__ u32x4 load16_nt(uint32_t off, uint32_t soff) const {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kNT));
+    }
+    __device__ __forceinline__ float loadf_nt(uint32_t off, uint32_t soff) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kNT));
+    }
     __device__ __forceinline__ void store_b16_nt(uint16_t v, uint32_t off) const {
         __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kNT);
     }
@@ -458,15 +468,15 @@ __device__ __forceinline__ int wave_inclusive_sum_i(int v) {
 // count in LDS); larger batches keep their own order.
 constexpr int kOrderMax = 1024;
 
-// Exclusive scan of max(min_count, ceil(L_b / span)) over the sequences (L_b
-// from the clamped cu_seqlens): off[b] = first span index of sequence b,
-// off[n_seqs] = total.  One workgroup of 1024 threads; each thread sums a
+// Exclusive scan of max(min_count, ceil(L_b / span) - sub) over the
+// sequences (L_b from the clamped cu_seqlens): off[b] = first span index of
+// sequence b, off[n_seqs] = total.  One workgroup of 1024 threads; each thread sums a
 // contiguous range of sequences, then wave scans and a scan of the 16 wave
 // totals.  With order != nullptr also writes the sequences by decreasing
 // length (ties by index): order[r] = sequence of rank r.
 __global__ void __launch_bounds__(1024)
 span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span, int min_count,
-             int32_t* __restrict__ off, int32_t* __restrict__ order) {
+             int sub, int32_t* __restrict__ off, int32_t* __restrict__ order) {
     __shared__ int wsum[16];
     __shared__ int lens[kOrderMax];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -474,7 +484,7 @@ span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span,
         const int s = clampi(cu[b], 0, n_tokens);
         return clampi(cu[b + 1], s, n_tokens) - s;
     };
-    auto count = [&](int b) { return max(min_count, (length(b) + span - 1) / span); };
+    auto count = [&](int b) { return max(min_count, (length(b) + span - 1) / span - sub); };
     const int per = (n_seqs + 1023) / 1024;
     const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
     int sum = 0;

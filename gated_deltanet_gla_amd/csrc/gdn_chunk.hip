@@ -96,20 +96,23 @@ struct PrepPrefetch {
     float a;           // gate (wave 0) / beta (wave 1) of token `lane`, raw
 };
 
-// TP = false: write T (fp32, C x C) per (chunk, head).
-// TP = true (bf16 inputs): write four bf16 C x C planes per (chunk, head):
+// PL = 0: write T (fp32, C x C) per (chunk, head).
+// PL = 4 (bf16 inputs): write four bf16 C x C planes per (chunk, head):
 //   T diag(beta) hi, lo, and P = (Q K^T) .* D (lower, decayed) hi, lo.
-template <int DK, int C, class TI, bool TP>
+// PL = 2 (bf16 inputs): T diag(beta) hi, lo only.
+template <int DK, int C, class TI, int PL>
 __global__ void __launch_bounds__(NT, 3)       // three resident workgroups per compute unit
 gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict__ q,
          const float* __restrict__ alpha, const float* __restrict__ beta,
          const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
          const int32_t* __restrict__ off, void* __restrict__ Tws) {
     constexpr bool F32 = (TI::bytes == 4);
+    constexpr bool TP = PL > 0;          // bf16 planes
+    constexpr bool WP = PL == 4;         // ... including P
     static_assert(!(TP && F32), "planes are bf16");
     using O = Op<F32>;
-    using Sm = PrepSmem<DK, C, F32, TP>;
-    using PF = PrepPrefetch<TI, C, DK, TP>;
+    using Sm = PrepSmem<DK, C, F32, WP>;
+    using PF = PrepPrefetch<TI, C, DK, WP>;
     constexpr int LQ = Sm::LQ;
     constexpr int NB = C / 16;
     constexpr int TPW = (NB * NB + NW - 1) / NW;   // 16x16 tiles per wave
@@ -147,13 +150,13 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
     auto fetch = [&](PF& pf, const PrepItem& it) {
         const uint32_t ext = rows_extent(it.n, tstride * TI::bytes, DK * TI::bytes);
         const BufRsrc rk(k + it.tok0 * tstride + it.h * DK, ext);
-        const BufRsrc rq(q + it.tok0 * tstride + it.h * DK, TP ? ext : 0u);
+        const BufRsrc rq(q + it.tok0 * tstride + it.h * DK, WP ? ext : 0u);
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int x = threadIdx.x + u * NT;
             const uint32_t offb = static_cast<uint32_t>(((x / VPR) * tstride + (x % VPR) * VE) * TI::bytes);
             pf.k[u] = rk.load16_nt(offb);
-            if constexpr (TP) pf.q[u] = rq.load16_nt(offb);
+            if constexpr (WP) pf.q[u] = rq.load16_nt(offb);
         }
         const float* gsrc = wave == 0 ? alpha : beta;
         const BufRsrc rg(gsrc + it.tok0 * H + it.h, wave < 2 ? rows_extent(it.n, static_cast<long>(H) * 4, 4) : 0u);
@@ -166,7 +169,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
             if (C * DK / VE == PF::NV * NT || x < C * DK / VE) {
                 const int row = x / VPR, vc = x % VPR;
                 *reinterpret_cast<u32x4*>(&sm.in.k[row][vc * VE]) = pf.k[u];
-                if constexpr (TP) *reinterpret_cast<u32x4*>(&sm.in.q[row][vc * VE]) = pf.q[u];
+                if constexpr (WP) *reinterpret_cast<u32x4*>(&sm.in.q[row][vc * VE]) = pf.q[u];
             }
         }
         if (wave == 0) {
@@ -198,7 +201,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
     const int n = cur.n;
     (void)n;
     const AccPos ap;
-    uint16_t* planes = static_cast<uint16_t*>(Tws) + (static_cast<long>(ci) * H + h) * 4 * C * C;
+    uint16_t* planes = static_cast<uint16_t*>(Tws) + (static_cast<long>(ci) * H + h) * (TP ? PL : 1) * C * C;
     // A = strictly-lower(diag(beta) (K K^T .* D)), fp32, held in registers
     // until k (and q) are no longer read; P = (Q K^T) .* D as P^T tiles (lane:
     // 4 consecutive j of row i) straight to planes 2, 3
@@ -218,7 +221,7 @@ gdn_prep(const typename TI::T* __restrict__ k, const typename TI::T* __restrict_
                     areg[m][r] = (j < i) ? sm.beta[i] * __expf(sm.g[i] - sm.g[j]) * areg[m][r] : 0.f;
                 }
             }
-            if constexpr (TP) {
+            if constexpr (WP) {
                 const int pj = t / NB, pi = t % NB;
                 const int i = pi * 16 + ap.col;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -918,7 +921,10 @@ template <int DK, int DV, int C, class TI, class TO>
 hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     using T = typename TI::T;
     constexpr bool F32 = (TI::bytes == 4);
-    constexpr bool FAST = !F32 && C >= 32 && DK >= 32;
+    // bf16, d_k = d_v = 128, 64-token chunks: the segmented path (gdn_seg.hip)
+    constexpr bool SEG = !F32 && DK == 128 && DV == 128 && C == 64;
+    constexpr bool FAST = !F32 && !SEG && C >= 32 && DK >= 32;
+    constexpr int PL = SEG ? 2 : (FAST ? 4 : 0);   // planes per (chunk, head); 0: fp32 T
     constexpr int BV = F32 ? 16 : (DV >= 32 ? 32 : DV);
     char* ws = static_cast<char*>(a.workspace);
     int32_t* off = reinterpret_cast<int32_t*>(ws);
@@ -927,18 +933,23 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     ws += align256(sizeof(int32_t) * a.n_seqs);
     float* Tws = reinterpret_cast<float*>(ws);
     const long mc = max_chunks(a.n_seqs, a.n_tokens, C);
+    ws += static_cast<size_t>(mc) * a.n_heads * C * C * 8;        // T / planes (8 C^2 bytes each)
     hipError_t e = hipSuccess;
     // phase 1 (state-independent): chunk offsets, order, inverses / planes
     if (a.gdn_phases != 2) {
     hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
-                       a.n_tokens, C, 0, off, FAST ? order : nullptr);
+                       a.n_tokens, C, 0, 0, off, FAST ? order : nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.n_tokens > 0) {
+    if (a.n_tokens > 0 && SEG) {
+        // one wave per (chunk, head) item (gdn_seg.hip)
+        e = launch_gdn_seg_prep(a, off, reinterpret_cast<uint16_t*>(Tws), mc, s);
+        if (e != hipSuccess) return e;
+    } else if (a.n_tokens > 0) {
         // persistent: as many workgroups as are resident at once, striding over
         // the (chunk, head) items
         const long prep_blocks = std::min<long>(mc * a.n_heads, kPrepBlocks);
-        hipLaunchKernelGGL((gdn_prep<DK, C, TI, FAST>), dim3(static_cast<unsigned>(prep_blocks)),
+        hipLaunchKernelGGL((gdn_prep<DK, C, TI, PL>), dim3(static_cast<unsigned>(prep_blocks)),
                            dim3(NT), 0, s, static_cast<const T*>(a.k), static_cast<const T*>(a.q),
                            a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, off,
                            static_cast<void*>(Tws));
@@ -948,7 +959,9 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     }
     if (a.gdn_phases == 1) return hipSuccess;
     // phase 2: the serial chunk loop
-    if constexpr (FAST) {
+    if constexpr (SEG) {
+        return launch_gdn_seg(a, off, reinterpret_cast<const uint16_t*>(Tws), mc, ws, s);
+    } else if constexpr (FAST) {
         const long groups = (static_cast<long>(a.n_seqs) * a.n_heads + 7) / 8 * 8;
         // 32 state columns per workgroup when there are workgroups to spare
         // (at least four per compute unit at 16 columns): the per-chunk work
@@ -1017,11 +1030,13 @@ hipError_t launch_dv(const ChunkArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int, int, int chunk) {
+size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk) {
     // per (chunk, head): T in fp32 (generic path) or four bf16 planes (bf16 path): 8 C^2 bytes
     // plus chunk offsets and the longest-first sequence order
+    // (and, for the segmented path at d_k = d_v = 128 and chunk 64, its segment bookkeeping and states)
+    const size_t seg = (dk == 128 && dv == 128 && chunk == 64) ? gdn_seg_workspace(n_seqs, n_tokens, n_heads) : 0;
     return align256(sizeof(int32_t) * (n_seqs + 1)) + align256(sizeof(int32_t) * n_seqs) +
-           static_cast<size_t>(max_chunks(n_seqs, n_tokens, chunk)) * n_heads * chunk * chunk * 8;
+           static_cast<size_t>(max_chunks(n_seqs, n_tokens, chunk)) * n_heads * chunk * chunk * 8 + seg;
 }
 
 hipError_t launch_gdn_chunk(const ChunkArgs& a, hipStream_t s) {

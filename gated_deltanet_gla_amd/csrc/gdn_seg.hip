@@ -1,0 +1,980 @@
+// Chunked Gated DeltaNet prefill for bf16 inputs with d_k = d_v = 128 and
+// 64-token chunks: one workgroup per (segment, head) covering all 128 state
+// columns, long sequences cut into segments.
+//
+// "Inference for linear attention and hybrid architectures", section "Two
+// ways to write the same computation": DeltaNet's update
+// (I - b_t k_t^T k_t) S + b_t k_t^T v_t with a decay gate multiplied in, and
+// the remark that the in-chunk corrections must first be written in matrix
+// form.  The matrix form used here (derived; the page poses it as an
+// exercise): inside a chunk entered with state S, with g the running log
+// decay, T = (I + A)^-1 for A_tj = b_t exp(g_t - g_j) (k_t . k_j), j < t,
+//   X = K S,  Y = V - diag(exp g) X,  U = T diag(b) Y,
+//   O = diag(exp g) Q S + ((Q K^T) .* D) U,
+//   S <- exp(g_last) S + K^T diag(exp(g_last - g)) U.
+// T diag(b) does not depend on S; gdn_prep computes it for every chunk
+// beforehand and leaves it in the workspace as bf16 hi / lo planes.
+//
+// Layout of the work.  Each of the 8 waves owns 16 columns of the 128 x 128
+// fp32 state, all rows, as MFMA accumulator tiles.  For the 16x16x32 MFMA a
+// pair of those tiles (rows 32s .. 32s + 31) is, as it stands, the B operand
+// of X = K S and the A operand of O^T = S^T Q^T, with the contraction index
+// in the "split" order {4g .. 4g + 3} u {16 + 4g .. 16 + 4g + 3} per lane
+// group g.  Y and U come out of their products in the same accumulator
+// layout, so they are in turn the B operand of U = T diag(b) Y and of the
+// state update, and (transposed) the A operand of O^T += U^T P^T.  The whole
+// chain is therefore local to a wave: only q, k, v, T diag(b) and
+// P = (Q K^T) .* D are shared, through LDS.  P is formed once per chunk by
+// all waves (10 lower-triangle tiles).  Outputs come out transposed, lane =
+// token, 4 consecutive columns each, and go through LDS to whole-row stores.
+//
+// Operand format: every MFMA takes fp16 operands (v_mfma_f32_16x16x32_f16,
+// fp32 accumulation).  q and k are converted to fp16 as they are staged
+// (exact for bf16 values below 2^15 in magnitude); v stays bf16 (it only
+// enters Y on the vector unit).  The fp32-derived operands S, Y and U are
+// rounded to fp16 after scaling each wave's slice by a power of two that
+// keeps its largest magnitude below 2^15, undone exactly on the fp32
+// results; gdn_seg_prep does the same for T diag(b), per (chunk, head).
+// P needs |q_i| |k_j| < 2^15 (always true for L2-normalised q and k).
+// A bf16 hi + lo pair would keep about 16 significant bits per operand at
+// two MFMAs per product; fp16 keeps 11 at one, which puts the result about
+// 5e-4 from the exact one on L2-normalised inputs (a simulation of this
+// chunked form in numpy), against 1e-5 for hi + lo.  The scan multiplies
+// the transitions with hi + lo pairs: it runs once per segment.
+//
+// Segments ("Chunked prefill comes for free": a prompt cut into pieces is
+// processed the same way when only the state is handed on; here the pieces
+// of one prompt run side by side).  The update is affine in the state that
+// enters a segment: S_out = M S_in + dS, where dS is the segment's state
+// from S_in = 0 and M (d_k x d_k) its transition, the product of the chunks'
+// exp(g_last) I - K^T diag(exp(g_last - g)) T diag(b) diag(exp g) K.  So:
+//   pass 1 (gdn_seg_state): for every segment but the last of a sequence cut
+//     into several, dS and M, by running the state update alone on [S | M]
+//     from [0 | I] (M takes no values: its Y is -diag(exp g) K M);
+//   scan (gdn_seg_scan): per (sequence, head), S_in(0) = the pool state and
+//     S_in(j + 1) = M_j S_in(j) + dS_j, written over dS_j (S_in(0) over M_0);
+//   pass 2 (gdn_seg_out): every segment from its S_in, outputs included; the
+//     last one writes the final state to the pool.
+// A sequence of one segment is handled by pass 2 alone, reading and writing
+// the pool.  State slots in the workspace hold each lane's 32 accumulator
+// values contiguously (16-byte accesses).
+#include <algorithm>
+
+#include "chunk_common.h"
+#include "launch.h"
+
+namespace gla {
+namespace {
+
+constexpr int NWV = 8;             // waves
+constexpr int NTH = NWV * 64;      // threads
+constexpr int D = 128;             // d_k = d_v
+constexpr int CH = 64;             // chunk
+constexpr int LQ = D + 8;          // LDS row stride of q (read along rows)
+constexpr int LK = D + 16;         // k, v read with the transpose read and k's 16-byte row reads
+constexpr int LX = D + 8;          // k read in the split order of X = K S (8-byte reads)
+constexpr int LP = CH + 8;         // P and T diag(beta)
+constexpr int LM = D + 8;          // the transition in the scan (read transposed)
+constexpr int kTargetBlocks = 256; // about one workgroup per compute unit
+constexpr int kPlaneElems = CH * CH;       // T diag(beta) (fp16) per (chunk, head)
+
+// One chunk of the global inputs in registers: 2 x 16 bytes per thread of
+// each 64 x 128 bf16 tile, 16 bytes of the 8 KiB fp16 T diag(beta) plane,
+// and the gate of token `lane` (wave 0).
+template <bool WQ, bool WV>
+struct GPrefetch {
+    u32x4 q[WQ ? 2 : 1], k[2], v[2], t;
+    float a;
+    float tinv;        // the inverse scale of this chunk's T diag(beta)
+    int n;
+};
+
+// Buffer resources over one segment's rows of q, k, v, alpha and its T
+// planes, built once; chunk c is then reached through a scalar offset.
+// Rows past the segment read as zero, and so does a chunk past its last
+// one (its offset is the resource's size).
+struct SegSrc {
+    BufRsrc q, k, v, a, t;
+    uint32_t q_end, a_end, t_end;
+    uint32_t q_step, a_step, t_step;     // bytes per chunk
+    const float* tinv;
+    long ti0;                            // tinv index of chunk 0
+    int nch, H;
+};
+
+template <bool WQ, bool WV>
+__device__ __forceinline__ SegSrc seg_src(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                                          const uint16_t* planes, const float* tinv, long t0, int rows, long ci0,
+                                          int nch, int h, int H) {
+    const long stride = static_cast<long>(H) * D;
+    const uint32_t ext = rows_extent(rows, stride * 2, D * 2);
+    const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+    const uint32_t aext = rows_extent(rows, static_cast<long>(H) * 4, 4);
+    const uint32_t text = static_cast<uint32_t>(nch > 0 ? ((nch - 1) * static_cast<long>(H) + 1) * kPlaneElems * 2 : 0);
+    SegSrc r{BufRsrc(q + t0 * stride + h * D, WQ ? ext : 0u), BufRsrc(k + t0 * stride + h * D, ext),
+             BufRsrc(v + t0 * stride + h * D, WV ? ext : 0u), BufRsrc(alpha + t0 * H + h, w0 ? aext : 0u),
+             BufRsrc(planes + (ci0 * H + h) * kPlaneElems, text),
+             ext, aext, text,
+             static_cast<uint32_t>(CH * stride * 2), static_cast<uint32_t>(CH * H * 4),
+             static_cast<uint32_t>(static_cast<long>(H) * kPlaneElems * 2),
+             tinv, ci0 * H + h, nch, H};
+    return r;
+}
+
+// Global -> registers for chunk c of the segment.
+template <bool WQ, bool WV>
+__device__ __forceinline__ void g_fetch(GPrefetch<WQ, WV>& pf, const SegSrc& sr, int c, int n) {
+    const bool in = c < sr.nch;
+    const uint32_t so = in ? c * sr.q_step : sr.q_end;
+    const uint32_t sa = in ? c * sr.a_step : sr.a_end;
+    const uint32_t st = in ? c * sr.t_step : sr.t_end;
+    const int tid = threadIdx.x;
+    const long stride = static_cast<long>(sr.H) * D;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int x = tid + u * NTH;
+        const uint32_t offb = static_cast<uint32_t>(((x / (D / 8)) * stride + (x % (D / 8)) * 8) * 2);
+        pf.k[u] = sr.k.load16_nt(offb, so);
+        if constexpr (WV) pf.v[u] = sr.v.load16_nt(offb, so);
+        if constexpr (WQ) pf.q[u] = sr.q.load16_nt(offb, so);
+    }
+    // T plane: vector tid of 512 (row tid / 8, 8 columns (tid % 8) * 8);
+    // rows 0..31 x columns 32..63 are never used
+    pf.t = sr.t.load16((tid >> 3) < 32 && (tid & 7) >= 4 ? sr.t_end : static_cast<uint32_t>(tid * 16), st);
+    pf.tinv = in ? sr.tinv[sr.ti0 + static_cast<long>(c) * sr.H] : 0.f;
+    pf.a = sr.a.loadf_nt(static_cast<uint32_t>((tid & 63) * sr.H * 4), sa);
+    pf.n = n;
+}
+
+// Gate tables of a chunk from wave 0's prefetched gates (rows past n:
+// alpha = 1): running log2 decay, 2^g2, 2^(g2_last - g2), 2^g2_last.
+template <class PF>
+__device__ __forceinline__ void g_stage_gates(float* g2, float* eg, float* dec, float* gamma, const PF& pf) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
+        const float a = lane < pf.n ? pf.a : 1.f;
+        const float x = wave_inclusive_sum(__log2f(fmaxf(a, kMinDecay)));
+        const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
+        if (g2) g2[lane] = x;
+        if (eg) eg[lane] = exp2f(x);
+        dec[lane] = exp2f(glast - x);
+        if (lane == 0) *gamma = exp2f(glast);
+    }
+}
+
+// fp16 operands: two fp32 values -> packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 hv = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, hv);
+}
+// 8 bf16 values (one 16-byte vector) -> 8 fp16 values
+__device__ __forceinline__ u32x4 bf16x8_to_f16(u32x4 w) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = pk_f16(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xffff0000u));
+    return r;
+}
+__device__ __forceinline__ f32x4 mfma_f16(const bf16x8& a, const bf16x8& b, f32x4 c) {
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+}
+// A pair of accumulator tiles times s as one fp16 operand fragment (split k order).
+__device__ __forceinline__ bf16x8 f16_pair(const f32x4& a, const f32x4& b, float sc) {
+    return as_bf16x8(u32x4{pk_f16(a.x * sc, a.y * sc), pk_f16(a.z * sc, a.w * sc), pk_f16(b.x * sc, b.y * sc),
+                           pk_f16(b.z * sc, b.w * sc)});
+}
+// Range guard: a power of two s with (largest |x| of the wave) * s < 2^15,
+// and 1 / s (both exact; s is capped at 2^126 for tiny or zero slices).
+struct Scale {
+    float s, inv;
+};
+__device__ __forceinline__ Scale range_scale(float local_max) {
+    float m = local_max;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const int eb = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu);   // m < 2^(eb - 126)
+    const int sf = clampi(268 - eb, 1, 253);                               // s = 2^(141 - eb)
+    return {__uint_as_float(static_cast<uint32_t>(sf) << 23), __uint_as_float(static_cast<uint32_t>(254 - sf) << 23)};
+}
+__device__ __forceinline__ float absmax4(const f32x4& v, float m) {
+    return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// Registers -> LDS: a 64 x 128 tile, as it is (bf16) or converted to fp16.
+template <bool TO_F16>
+__device__ __forceinline__ void g_stage_tile(uint16_t* dst, int ld, const u32x4 (&w)[2], uint16_t* dst2 = nullptr,
+                                             int ld2 = 0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int x = threadIdx.x + u * NTH;
+        const u32x4 val = TO_F16 ? bf16x8_to_f16(w[u]) : w[u];
+        *reinterpret_cast<u32x4*>(dst + (x / (D / 8)) * ld + (x % (D / 8)) * 8) = val;
+        if (dst2) *reinterpret_cast<u32x4*>(dst2 + (x / (D / 8)) * ld2 + (x % (D / 8)) * 8) = val;
+    }
+}
+__device__ __forceinline__ void g_stage_plane(uint16_t (*t)[LP], const u32x4& w) {
+    *reinterpret_cast<u32x4*>(&t[threadIdx.x >> 3][(threadIdx.x & 7) * 8]) = w;
+}
+
+// A state slot of the workspace: lane l of wave w keeps its 8 tiles x 4
+// values at ((w * 64 + l) * 32).
+__device__ __forceinline__ float* g_slot(float* ws, long slot) { return ws + slot * D * D + threadIdx.x * 32; }
+__device__ __forceinline__ void g_slot_load(f32x4 (&S)[8], const float* p) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(p + mt * 4);
+}
+__device__ __forceinline__ void g_slot_store(float* p, const f32x4 (&S)[8]) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(p + mt * 4) = S[mt];
+}
+// This wave's 8 tiles of a row-major [d][n] state (columns col .. col + 15).
+__device__ __forceinline__ void g_rowmajor_load(f32x4 (&S)[8], const float* src, int col) {
+    const AccPos ap;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[mt][r] = src[(mt * 16 + ap.row0 + r) * D + col + ap.col];
+}
+
+// Split a pair of accumulator tiles into bf16 hi / lo operand fragments
+// (the scan's products).
+__device__ __forceinline__ void split_pair(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+    s16x4 h0, l0, h1, l1;
+    split4(a, h0, l0);
+    split4(b, h1, l1);
+    hi = cat8(h0, h1);
+    lo = cat8(l0, l1);
+}
+
+// The fp16 operand fragments of this wave's state slice (tiles 2s, 2s + 1
+// for the d_k block s) and the scale they carry.
+__device__ __forceinline__ Scale state_operand(bf16x8 (&sf)[4], const f32x4 (&S)[8]) {
+    float m = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) m = absmax4(S[mt], m);
+    const Scale sc = range_scale(m);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sf[s] = f16_pair(S[2 * s], S[2 * s + 1], sc.s);
+    return sc;
+}
+
+// Y = V - diag(eg) X xinv for this wave's columns (V^T fragments vf hold
+// tokens 32ks + 4g + {0..3} (first half) and 32ks + 16 + 4g + {0..3}; xinv
+// undoes the state operand's scale), as fp16 operand fragments by 32-token
+// half; returns their scale.  NEG_ONLY: Y = -diag(eg) X xinv.
+template <bool NEG_ONLY>
+__device__ __forceinline__ Scale form_y(bf16x8 (&yf)[2], const f32x4 (&X)[4], const bf16x8 (&vf)[2], const float* eg,
+                                        float xinv) {
+    const int g4 = ((threadIdx.x & 63) >> 4) * 4;
+    f32x4 y[4];
+    float m = 0.f;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const f32x4 e = *reinterpret_cast<const f32x4*>(eg + it * 16 + g4) * xinv;
+        if constexpr (NEG_ONLY) {
+            y[it] = -(e * X[it]);
+        } else {
+            const u32x4 vw = __builtin_bit_cast(u32x4, vf[it >> 1]);
+            const uint32_t w0 = (it & 1) ? vw.z : vw.x, w1 = (it & 1) ? vw.w : vw.y;
+            const f32x4 vv = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
+                              __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
+            y[it] = vv - e * X[it];
+        }
+        m = absmax4(y[it], m);
+    }
+    const Scale sc = range_scale(m);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) yf[ks] = f16_pair(y[2 * ks], y[2 * ks + 1], sc.s);
+    return sc;
+}
+
+// U = T diag(beta) Y (lower triangular: row block it uses token halves
+// ks <= it / 2; uinv undoes the scales of T diag(beta) and Y), then
+// diag(dec) U and (WANT_U) U as fp16 operand fragments under one scale,
+// which is returned.
+template <bool WANT_U = true>
+__device__ __forceinline__ Scale form_u(bf16x8 (&uf)[2], bf16x8 (&df)[2], const bf16x8 (&yf)[2], const uint16_t (*t)[LP],
+                                        const float* dec, float uinv) {
+    f32x4 U[4];
+    float m = 0.f;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        U[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks <= (it >> 1); ++ks) U[it] = mfma_f16(frag_kc_split(&t[0][0], LP, it * 16, 32 * ks), yf[ks], U[it]);
+        m = absmax4(U[it], m);
+    }
+    // the scale is taken on the true U = uinv U[it]; dec <= 1, so the same
+    // scale serves diag(dec) U
+    Scale sc = range_scale(m * uinv);
+    const float f = uinv * sc.s;
+    const int g4 = ((threadIdx.x & 63) >> 4) * 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const f32x4 u0 = U[2 * ks] * f, u1 = U[2 * ks + 1] * f;
+        if constexpr (WANT_U) uf[ks] = f16_pair(u0, u1, 1.f);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dec + 32 * ks + g4);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dec + 32 * ks + 16 + g4);
+        df[ks] = f16_pair(u0 * d0, u1 * d1, 1.f);
+    }
+    return sc;
+}
+
+// S (this wave's columns) <- gamma S + K^T diag(dec) U (df carries dinv).
+__device__ __forceinline__ void state_update(f32x4 (&S)[8], const uint16_t* kbase, float gam, const bf16x8 (&df)[2],
+                                             float dinv) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc = mfma_f16(frag_km_split(kbase, LK, mt * 16, 32 * ks), df[ks], acc);
+        S[mt] = gam * S[mt] + dinv * acc;
+    }
+}
+
+// X = K S (rows of the chunk x this wave's columns, times the state
+// operand's scale); O^T = S^T Q^T (same scale) too when WQ.
+template <bool WQ>
+__device__ __forceinline__ void k_times_s(f32x4 (&X)[4], f32x4* ot, const bf16x8 (&sf)[4], const uint16_t* kbase,
+                                          const uint16_t* qbase) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        X[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (WQ) ot[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            X[it] = mfma_f16(frag_kc_split(kbase, LX, it * 16, 32 * s), sf[s], X[it]);
+            if constexpr (WQ) ot[it] = mfma_f16(sf[s], frag_kc_split(qbase, LQ, it * 16, 32 * s), ot[it]);
+        }
+    }
+}
+
+// Pass 1's two products with K, for the state columns S and the transition
+// columns M of this wave at once, so each K fragment is read once.
+__device__ __forceinline__ void k_times_sm(f32x4 (&XS)[4], f32x4 (&XM)[4], const bf16x8 (&sf)[4], const bf16x8 (&mf)[4],
+                                           const uint16_t* kbase) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) XS[it] = XM[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const bf16x8 kf = frag_kc_split(kbase, LX, it * 16, 32 * s);
+            XS[it] = mfma_f16(kf, sf[s], XS[it]);
+            XM[it] = mfma_f16(kf, mf[s], XM[it]);
+        }
+    }
+}
+__device__ __forceinline__ void state_update_sm(f32x4 (&S)[8], f32x4 (&M)[8], const uint16_t* kbase, float gam,
+                                                const bf16x8 (&sdf)[2], float sinv, const bf16x8 (&mdf)[2], float minv) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        f32x4 as = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 kt = frag_km_split(kbase, LK, mt * 16, 32 * ks);
+            as = mfma_f16(kt, sdf[ks], as);
+            am = mfma_f16(kt, mdf[ks], am);
+        }
+        S[mt] = gam * S[mt] + sinv * as;
+        M[mt] = gam * M[mt] + minv * am;
+    }
+}
+
+// Which sequence, segment and slot a block works on.
+struct GSeg {
+    int b, g, nseg, slot, t0, t1;
+    long ci0;          // global chunk index of the segment's first chunk
+    long jsplit;       // index of the sequence's first split segment
+};
+
+// false (for the whole block) if the slot is invalid, or if a malformed
+// cu_seqlens gives the sequence split segments beyond the workspace's
+// nsplit_max.
+__device__ __forceinline__ bool seg_bounds(GSeg& sg, int b, int g, int nseg, const int32_t* cu, int n_tokens,
+                                           const int32_t* coff, const int32_t* soff, const int32_t* slot_idx,
+                                           int n_slots, int lseg, long nsplit_max) {
+    const int slot = slot_idx[b];
+    if (slot < 0 || slot >= n_slots) return false;
+    if (nseg > 1 && static_cast<long>(soff[b]) + nseg - 1 > nsplit_max) return false;
+    const int s0 = clampi(cu[b], 0, n_tokens);
+    const int s1 = clampi(cu[b + 1], s0, n_tokens);
+    sg.b = b;
+    sg.g = g;
+    sg.nseg = nseg;
+    sg.slot = slot;
+    sg.t0 = min(s0 + g * lseg, s1);
+    sg.t1 = min(sg.t0 + lseg, s1);
+    sg.ci0 = static_cast<long>(coff[b]) + static_cast<long>(g) * (lseg / CH);
+    sg.jsplit = soff[b];
+    return true;
+}
+
+// ------------------------------------------------------------------ prep
+// T diag(beta) for every (chunk, head), one wave per item, the items strided
+// over a persistent grid.  A = strictly-lower(diag(beta) (K K^T .* D)) comes
+// from the MFMA on K fragments loaded straight from HBM; T = (I + A)^-1 by
+// forward substitution with one lane per column of T (lane j keeps column
+// j in registers and reads row r of A from LDS as a broadcast:
+// x_r = [r == j] - sum_{m < r} A_rm x_m); then column j is scaled by beta_j,
+// the item by a power of two (range guard; its inverse goes to tinv), and
+// written as one fp16 plane, one 128-byte row per store instruction.  Rows
+// 0..31 x columns 32..63 are zero and never read: not written.
+constexpr int PW = 4;              // waves per prep workgroup
+constexpr int LA = CH + 4;         // fp32 row stride of A in LDS
+constexpr int kPrepGroups = 512;   // 2 resident workgroups per compute unit
+
+__global__ void __launch_bounds__(PW * 64, 2)
+gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, const float* __restrict__ beta,
+             const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H, const int32_t* __restrict__ coff,
+             uint16_t* __restrict__ planes, float* __restrict__ tinv) {
+    __shared__ alignas(16) float As[PW][CH][LA];
+    __shared__ alignas(16) float gs[PW][CH];
+    __shared__ alignas(16) float bs[PW][CH];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const AccPos ap;
+    const long n_items = static_cast<long>(coff[n_seqs]) * H;
+    const long stride = static_cast<long>(H) * D;
+    auto wave_sync = []() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+    for (long item = static_cast<long>(blockIdx.x) * PW + wave; item < n_items;
+         item += static_cast<long>(gridDim.x) * PW) {
+        const int h = static_cast<int>(item % H);
+        const int ci = static_cast<int>(item / H);
+        const int b = find_span_owner(coff, n_seqs, ci);
+        const int s0 = clampi(cu[b], 0, n_tokens);
+        const int s1 = clampi(cu[b + 1], s0, n_tokens);
+        const int c0 = (ci - coff[b]) * CH;
+        const int n = max(0, min(CH, s1 - s0 - c0));
+        const long tok0 = s0 + max(c0, 0);
+
+        const BufRsrc rk(k + tok0 * stride + h * D, rows_extent(n, stride * 2, D * 2));
+        u32x4 kf[4][4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kf[tt][ks] = rk.load16_nt(static_cast<uint32_t>(
+                    ((tt * 16 + (lane & 15)) * stride + 32 * ks + (lane >> 4) * 8) * 2));
+        const uint32_t gext = rows_extent(n, static_cast<long>(H) * 4, 4);
+        const float a = BufRsrc(alpha + tok0 * H + h, gext).loadf_nt(static_cast<uint32_t>(lane * H * 4));
+        const float bt = BufRsrc(beta + tok0 * H + h, gext).loadf_nt(static_cast<uint32_t>(lane * H * 4));
+        gs[wave][lane] = wave_inclusive_sum(__log2f(fmaxf(lane < n ? a : 1.f, kMinDecay)));
+        bs[wave][lane] = lane < n ? bt : 0.f;
+        wave_sync();
+        // A, the 10 tiles on and below the diagonal (entries j >= i are 0)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int jt = 0; jt <= tt; ++jt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16(as_bf16x8(kf[tt][ks]), as_bf16x8(kf[jt][ks]), acc);
+                const int j = jt * 16 + ap.col;
+                const float gj = gs[wave][j];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = tt * 16 + ap.row0 + r;
+                    As[wave][i][j] = (j < i) ? bs[wave][i] * exp2f(gs[wave][i] - gj) * acc[r] : 0.f;
+                }
+            }
+        }
+        wave_sync();
+        // T = (I + A)^-1, column `me` (the lane index, recomputed per item so
+        // the 64 selects below are not hoisted out of the item loop)
+        const int me = opaque(lane);
+        float x[CH];
+#pragma unroll
+        for (int r = 0; r < CH; ++r) x[r] = 0.f;
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            float acc = (r == me) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < r; m += 4) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&As[wave][r][m]);
+                acc -= a4.x * x[m];
+                if (m + 1 < r) acc -= a4.y * x[m + 1];
+                if (m + 2 < r) acc -= a4.z * x[m + 2];
+                if (m + 3 < r) acc -= a4.w * x[m + 3];
+            }
+            x[r] = acc;
+            // keep the next rows' LDS reads from being hoisted (and held in
+            // registers) across this one
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // T diag(beta) -> an fp16 plane scaled by a power of two (its
+        // inverse kept per item), row r per store instruction
+        const float bj = bs[wave][lane];
+        float mloc = 0.f;
+#pragma unroll
+        for (int r = 0; r < CH; ++r) mloc = fmaxf(mloc, fabsf(x[r] * bj));
+        const Scale sc = range_scale(mloc);
+        if (lane == 0) tinv[item] = sc.inv;
+        const BufRsrc rp(planes + item * kPlaneElems, kPlaneElems * 2u);
+#pragma unroll
+        for (int r = 0; r < CH; r += 2) {
+            // rows r and r + 1 of column `me`: two 2-byte stores
+            const uint32_t hv = pk_f16(x[r] * bj * sc.s, x[r + 1] * bj * sc.s);
+            const bool skip = r < 32 && me >= 32;
+            rp.store_b16(static_cast<uint16_t>(hv & 0xffffu),
+                         skip ? 0x80000000u : static_cast<uint32_t>((r * CH + me) * 2));
+            rp.store_b16(static_cast<uint16_t>(hv >> 16),
+                         skip ? 0x80000000u : static_cast<uint32_t>(((r + 1) * CH + me) * 2));
+        }
+        wave_sync();       // this wave's A and gate tables are rewritten by its next item
+    }
+}
+
+// ------------------------------------------------------------------ pass 1
+struct StateBuf {
+    alignas(16) uint16_t k[CH][LK];      // fp16
+    alignas(16) uint16_t kx[CH][LX];     // fp16, the same rows at the stride of X's reads
+    alignas(16) uint16_t v[CH][LK];      // bf16
+    alignas(16) uint16_t t[CH][LP];      // T diag(beta), fp16, scaled
+    alignas(16) float eg[CH];
+    alignas(16) float dec[CH];
+    float gamma;
+    float tinv;
+};
+
+__global__ void __launch_bounds__(NTH)
+gdn_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+              const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H, int n_slots,
+              const int32_t* __restrict__ slot_idx, int lseg, const int32_t* __restrict__ coff,
+              const int32_t* __restrict__ seg_off, const int32_t* __restrict__ split_off,
+              const uint16_t* __restrict__ planes, const float* __restrict__ tinv, long n_chunks_max,
+              long nsplit_max, float* __restrict__ wsS, float* __restrict__ wsM) {
+    const int h = blockIdx.x % H;
+    const int j = blockIdx.x / H;
+    if (j >= split_off[n_seqs]) return;
+    const int b = find_span_owner(split_off, n_seqs, j);
+    const int g = j - split_off[b];
+    GSeg sg;
+    if (!seg_bounds(sg, b, g, seg_off[b + 1] - seg_off[b], cu, n_tokens, coff, split_off, slot_idx, n_slots, lseg,
+                    nsplit_max))
+        return;
+    const int nch = (sg.t1 - sg.t0 + CH - 1) / CH;
+    if (sg.ci0 < 0 || sg.ci0 + nch > n_chunks_max) return;     // malformed cu_seqlens only
+
+    __shared__ StateBuf buf[2];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const AccPos ap;
+    const int col = wave * 16;
+
+    // [S | M] from [0 | I]: this wave's columns of both
+    f32x4 S[8], M[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[mt][r] = (mt * 16 + ap.row0 + r == col + ap.col) ? 1.f : 0.f;
+    }
+
+    auto rows = [&](int c) { return c < nch ? min(CH, sg.t1 - sg.t0 - c * CH) : 0; };
+    auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * CH; };
+    GPrefetch<false, true> pf;
+    const SegSrc src = seg_src<false, true>(nullptr, k, v, alpha, planes, tinv, sg.t0, sg.t1 - sg.t0, sg.ci0, nch, h, H);
+    auto fetch = [&](int c) { g_fetch(pf, src, c, rows(c)); };
+    auto stage = [&](StateBuf& bb) {
+        g_stage_gates(nullptr, bb.eg, bb.dec, &bb.gamma, pf);
+        g_stage_tile<true>(&bb.k[0][0], LK, pf.k, &bb.kx[0][0], LX);
+        g_stage_tile<false>(&bb.v[0][0], LK, pf.v);
+        g_stage_plane(bb.t, pf.t);
+        if (threadIdx.x == 0) bb.tinv = pf.tinv;
+    };
+    fetch(0);
+    stage(buf[0]);
+    fetch(1);
+    lds_barrier();
+    for (int c = 0; c < nch; ++c) {
+        const StateBuf& bb = buf[c & 1];
+        bf16x8 vf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&bb.v[0][0], LK, col, 32 * ks);
+        // the segment's own state contribution S (with values) and its
+        // transition M (no values: Y = -diag(eg) K M)
+        bf16x8 sf[4], mf[4];
+        const Scale ss = state_operand(sf, S);
+        const Scale sm = state_operand(mf, M);
+        f32x4 XS[4], XM[4];
+        k_times_sm(XS, XM, sf, mf, &bb.kx[0][0]);
+        bf16x8 yf[2], un[2], sdf[2], mdf[2];
+        const Scale sy = form_y<false>(yf, XS, vf, bb.eg, ss.inv);
+        const Scale su = form_u<false>(un, sdf, yf, bb.t, bb.dec, bb.tinv * sy.inv);
+        const Scale my = form_y<true>(yf, XM, vf, bb.eg, sm.inv);
+        const Scale mu = form_u<false>(un, mdf, yf, bb.t, bb.dec, bb.tinv * my.inv);
+        state_update_sm(S, M, &bb.k[0][0], bb.gamma, sdf, su.inv, mdf, mu.inv);
+        stage(buf[(c + 1) & 1]);
+        fetch(c + 2);
+        lds_barrier();
+    }
+    const long slot = (sg.jsplit + g) * H + h;
+    g_slot_store(g_slot(wsS, slot), S);
+    g_slot_store(g_slot(wsM, slot), M);
+}
+
+// ------------------------------------------------------------------ scan
+// Per (split sequence, head): S_in(0) = pool state (or 0) goes to M slot 0
+// once M_0 has been read; then S_in(j + 1) = M_j S_in(j) + dS_j goes over
+// dS slot j.  M_j is staged into LDS transposed, as bf16 hi / lo, and read
+// as the A operand with the transpose read.
+__global__ void __launch_bounds__(NTH)
+gdn_seg_scan(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H, const float* __restrict__ pool,
+             int n_slots, const int32_t* __restrict__ slot_idx, int zero_init,
+             const int32_t* __restrict__ split_off, long nsplit_max, float* __restrict__ wsS,
+             float* __restrict__ wsM) {
+    const int h = blockIdx.x % H;
+    const int j = blockIdx.x / H;
+    if (j >= split_off[n_seqs]) return;
+    const int b = find_span_owner(split_off, n_seqs, j);
+    if (j != split_off[b]) return;                  // one block per split sequence
+    const int nsplit = split_off[b + 1] - split_off[b];
+    if (static_cast<long>(j) + nsplit > nsplit_max) return;      // malformed cu_seqlens only
+    const int slot = slot_idx[b];
+    if (slot < 0 || slot >= n_slots) return;
+    (void)cu;
+    (void)n_tokens;
+
+    __shared__ uint16_t mt_s[2][D][LM];              // M^T (row = input index), hi and lo
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const AccPos ap;
+    const int col = wave * 16;
+    f32x4 S[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!zero_init) g_rowmajor_load(S, pool + (static_cast<long>(slot) * H + h) * D * D, col);
+
+    f32x4 Mn[8], dSn[8];
+    g_slot_load(Mn, g_slot(wsM, static_cast<long>(j) * H + h));
+    g_slot_load(dSn, g_slot(wsS, static_cast<long>(j) * H + h));
+    for (int step = 0; step < nsplit; ++step) {
+        const long sl = static_cast<long>(j + step) * H + h;
+        f32x4 Mc[8], dS[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            Mc[mt] = Mn[mt];
+            dS[mt] = dSn[mt];
+        }
+        if (step + 1 < nsplit) {
+            g_slot_load(Mn, g_slot(wsM, sl + H));
+            g_slot_load(dSn, g_slot(wsS, sl + H));
+        }
+        // M_j -> LDS as M^T: lane holds M[16 mt + row0 + r][col + lane % 16]
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint32_t h0, l0, h1, l1;
+            split_bf16x2(Mc[mt][0], Mc[mt][1], h0, l0);
+            split_bf16x2(Mc[mt][2], Mc[mt][3], h1, l1);
+            *reinterpret_cast<u32x2*>(&mt_s[0][col + ap.col][mt * 16 + ap.row0]) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(&mt_s[1][col + ap.col][mt * 16 + ap.row0]) = u32x2{l0, l1};
+        }
+        // S_in(0) over M_0's slot: the values stored above used every word
+        // this lane read from it
+        if (step == 0) g_slot_store(g_slot(wsM, sl), S);
+        lds_barrier();
+        bf16x8 sh[4], slo[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) split_pair(S[2 * s], S[2 * s + 1], sh[s], slo[s]);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            f32x4 acc = dS[mt];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 ah = frag_km_split(&mt_s[0][0][0], LM, mt * 16, 32 * s);
+                const bf16x8 al = frag_km_split(&mt_s[1][0][0], LM, mt * 16, 32 * s);
+                acc = mfma_bf16(ah, sh[s], acc);
+                acc = mfma_bf16(ah, slo[s], acc);
+                acc = mfma_bf16(al, sh[s], acc);
+            }
+            S[mt] = acc;
+        }
+        g_slot_store(g_slot(wsS, sl), S);                        // S_in(step + 1)
+        lds_barrier();
+    }
+}
+
+// ------------------------------------------------------------------ pass 2
+struct KGate {
+    alignas(16) uint16_t k[CH][LK];      // fp16
+    alignas(16) uint16_t kx[CH][LX];     // fp16, the same rows at the stride of X's reads
+    alignas(16) float g2[CH];
+    alignas(16) float eg[CH];
+    alignas(16) float dec[CH];
+    float gamma;
+    float tinv;
+};
+
+template <class TO, bool CKPT>
+__global__ void __launch_bounds__(NTH)
+gdn_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+            const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
+            float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
+            const int32_t* __restrict__ coff, const int32_t* __restrict__ seg_off,
+            const int32_t* __restrict__ split_off, const uint16_t* __restrict__ planes,
+            const float* __restrict__ tinv, long n_chunks_max, long nsplit_max, const float* __restrict__ wsS,
+            const float* __restrict__ wsM, Ckpt ck,
+            typename TO::T* __restrict__ o) {
+    const int h = blockIdx.x % H;
+    const int si = blockIdx.x / H;
+    if (si >= seg_off[n_seqs]) return;
+    const int b = find_span_owner(seg_off, n_seqs, si);
+    const int g = si - seg_off[b];
+    GSeg sg;
+    if (!seg_bounds(sg, b, g, seg_off[b + 1] - seg_off[b], cu, n_tokens, coff, split_off, slot_idx, n_slots, lseg,
+                    nsplit_max))
+        return;
+    const int nch = (sg.t1 - sg.t0 + CH - 1) / CH;
+    if (sg.ci0 < 0 || sg.ci0 + nch > n_chunks_max) return;     // malformed cu_seqlens only
+
+    __shared__ KGate kb[2];
+    __shared__ alignas(16) uint16_t sq[CH][LQ];      // fp16
+    __shared__ alignas(16) uint16_t sv[CH][LK];      // bf16
+    __shared__ alignas(16) uint16_t st[CH][LP];      // T diag(beta), fp16, scaled
+    __shared__ alignas(16) uint16_t sp[CH][LP];      // P, fp16
+    __shared__ alignas(16) uint16_t obuf[TO::bytes == 2 ? CH : 1][LQ];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const AccPos ap;
+    const int col = wave * 16;
+    const long stride = static_cast<long>(H) * D;
+
+    auto rows = [&](int c) { return c < nch ? min(CH, sg.t1 - sg.t0 - c * CH) : 0; };
+    auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * CH; };
+    GPrefetch<true, true> pf;
+    const SegSrc src = seg_src<true, true>(q, k, v, alpha, planes, tinv, sg.t0, sg.t1 - sg.t0, sg.ci0, nch, h, H);
+    auto fetch = [&](int c) { g_fetch(pf, src, c, rows(c)); };
+    fetch(0);
+
+    // entry state
+    f32x4 S[8];
+    float* Sg = pool + (static_cast<long>(sg.slot) * H + h) * D * D;
+    if (sg.nseg <= 1) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!zero_init) g_rowmajor_load(S, Sg, col);
+    } else {
+        const float* src = g == 0 ? g_slot(const_cast<float*>(wsM), sg.jsplit * H + h)
+                                  : g_slot(const_cast<float*>(wsS), (sg.jsplit + g - 1) * H + h);
+        g_slot_load(S, src);
+    }
+    // P tiles above the diagonal that the products still read (rows 0-15 x
+    // columns 16-31, rows 32-47 x columns 48-63) stay zero
+    for (int idx = tid; idx < 2 * 256; idx += NTH) {
+        const int t = idx >> 8, e = idx & 255;
+        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+        sp[row][cx] = 0;
+    }
+    auto stage = [&](KGate& kk) {
+        g_stage_gates(kk.g2, kk.eg, kk.dec, &kk.gamma, pf);
+        g_stage_tile<true>(&kk.k[0][0], LK, pf.k, &kk.kx[0][0], LX);
+        g_stage_tile<true>(&sq[0][0], LQ, pf.q);
+        g_stage_tile<false>(&sv[0][0], LK, pf.v);
+        g_stage_plane(st, pf.t);
+        if (threadIdx.x == 0) kk.tinv = pf.tinv;
+    };
+    stage(kb[0]);
+    fetch(1);
+    lds_barrier();
+
+    // P tile t of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+    auto p_tile = [&](const KGate& kk, int t) {
+        const int it = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+        const int jt = t - it * (it + 1) / 2;
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            pt = mfma_f16(frag_kc(&kk.k[0][0], LK, jt * 16, 32 * ks), frag_kc(&sq[0][0], LQ, it * 16, 32 * ks), pt);
+        const int i = it * 16 + ap.col;
+        const float gi = kk.g2[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = jt * 16 + ap.row0 + r;
+            pt[r] = (jj <= i) ? pt[r] * exp2f(gi - kk.g2[jj]) : 0.f;
+        }
+        *reinterpret_cast<u32x2*>(&sp[i][jt * 16 + ap.row0]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
+    };
+    // chunk cc's bf16 outputs: LDS -> HBM, 16 lanes per 256-byte row
+    auto flush_o = [&](int cc) {
+        if constexpr (TO::bytes == 2) {
+            const BufRsrc ro(o + tok(cc) * stride + h * D, rows_extent(rows(cc), stride * 2, D * 2));
+#pragma unroll
+            for (int u = 0; u < CH * D / 8 / NTH; ++u) {
+                const int x = tid + u * NTH, row = x / (D / 8), vc = (x % (D / 8)) * 8;
+                ro.store_b128(*reinterpret_cast<const u32x4*>(&obuf[row][vc]),
+                              static_cast<uint32_t>((row * stride + vc) * 2));
+            }
+        }
+    };
+
+    for (int c = 0; c < nch; ++c) {
+        const KGate& kk = kb[c & 1];
+        const int n = rows(c);
+        const long tok0 = tok(c);
+        if (c > 0) flush_o(c - 1);
+
+        // ---- phase 1: P tiles -> LDS; X = K S, O^T = S^T Q^T; Y; U
+        p_tile(kk, wave);
+        if (wave + NWV < 10) p_tile(kk, wave + NWV);
+        bf16x8 sf[4];
+        const Scale ss = state_operand(sf, S);
+        f32x4 X[4], ot[4];
+        k_times_s<true>(X, ot, sf, &kk.kx[0][0], &sq[0][0]);
+        bf16x8 vf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&sv[0][0], LK, col, 32 * ks);
+        bf16x8 yf[2], uf[2], df[2];
+        const Scale sy = form_y<false>(yf, X, vf, kk.eg, ss.inv);
+        const Scale su = form_u(uf, df, yf, st, kk.dec, kk.tinv * sy.inv);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) ot[it] *= kk.eg[it * 16 + ap.col] * ss.inv;
+        lds_barrier();
+
+        // ---- phase 2: O^T += U^T P^T; outputs; state update; next chunk
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks <= (it >> 1); ++ks) pu = mfma_f16(uf[ks], frag_kc_split(&sp[0][0], LP, it * 16, 32 * ks), pu);
+            ot[it] += su.inv * pu;
+        }
+        // lane: token it*16 + (lane % 16), columns col + 4 (lane / 16) .. +3
+        if constexpr (TO::bytes == 2) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                *reinterpret_cast<u32x2*>(&obuf[it * 16 + ap.col][col + ap.row0]) =
+                    u32x2{pack_bf16x2(ot[it][0], ot[it][1]), pack_bf16x2(ot[it][2], ot[it][3])};
+        } else {
+            const BufRsrc ro(o + tok0 * stride + h * D, rows_extent(n, stride * 4, D * 4));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
+                              static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
+        }
+        state_update(S, &kk.k[0][0], kk.gamma, df, su.inv);
+        stage(kb[(c + 1) & 1]);
+        fetch(c + 2);
+        // checkpoint: this wave's columns of the state after chunk c
+        const int cs = CKPT && n == CH ? ckpt_slot(ck, sg.b, sg.g * lseg + (c + 1) * CH, n_slots) : -1;
+        if (CKPT && cs >= 0) {
+            float* Sc = pool + (static_cast<long>(cs) * H + h) * D * D + opaque(ap.row0 * D + col + ap.col);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sc[(mt * 16 + r) * D] = S[mt][r];
+            }
+        }
+        lds_barrier();
+    }
+    if (nch > 0) flush_o(nch - 1);
+
+    if (sg.g == sg.nseg - 1) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * D + col + ap.col] = S[mt][r];
+        }
+    }
+}
+
+// Segment length: whole chunks, at least 4 of them, such that the call
+// has about kTargetBlocks (segment, head) workgroups when it is long enough.
+int g_seg_len(int n_tokens, int n_heads) {
+    const long target = n_heads >= kTargetBlocks ? 1 : kTargetBlocks / n_heads;
+    long L = (n_tokens + target - 1) / target;
+    L = ((L + CH - 1) / CH) * CH;
+    return static_cast<int>(L < 4 * CH ? 4 * CH : L);
+}
+
+__host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+// Workspace of the segmented path beyond the chunk offsets and T planes:
+// segment offsets, split-segment offsets, and two 64 KiB state slots per
+// (split segment, head).  A sequence of s >= 2 segments is longer than
+// (s - 1) * lseg tokens, so split segments number at most n_tokens / lseg.
+size_t gdn_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
+    const long nsplit = n_tokens / g_seg_len(n_tokens, n_heads);
+    return 2 * al256(sizeof(int32_t) * (n_seqs + 1)) +
+           2 * static_cast<size_t>(nsplit) * n_heads * D * D * sizeof(float);
+}
+
+// The fp16 T planes take the first n_chunks_max * H * 8 KiB of the plane
+// region; their inverse scales (one float per (chunk, head)) follow.
+float* plane_scales(const uint16_t* planes, long n_chunks_max, int H) {
+    return const_cast<float*>(reinterpret_cast<const float*>(planes + n_chunks_max * H * kPlaneElems));
+}
+
+hipError_t launch_gdn_seg_prep(const ChunkArgs& a, const int32_t* coff, uint16_t* planes, long n_chunks_max,
+                               hipStream_t s) {
+    const long groups = std::min<long>((n_chunks_max * a.n_heads + PW - 1) / PW, kPrepGroups);
+    if (groups <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gdn_seg_prep, dim3(static_cast<unsigned>(groups)), dim3(PW * 64), 0, s,
+                       static_cast<const uint16_t*>(a.k), a.alpha, a.beta, a.cu_seqlens, a.n_seqs, a.n_tokens,
+                       a.n_heads, coff, planes, plane_scales(planes, n_chunks_max, a.n_heads));
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_t* planes, long n_chunks_max,
+                          void* seg_ws, hipStream_t s) {
+    const int lseg = g_seg_len(a.n_tokens, a.n_heads);
+    const long nsplit = a.n_tokens / lseg;
+    const long maxseg = nsplit + a.n_seqs;
+    char* ws = static_cast<char*>(seg_ws);
+    int32_t* seg_off = reinterpret_cast<int32_t*>(ws);
+    ws += al256(sizeof(int32_t) * (a.n_seqs + 1));
+    int32_t* split_off = reinterpret_cast<int32_t*>(ws);
+    ws += al256(sizeof(int32_t) * (a.n_seqs + 1));
+    float* wsS = reinterpret_cast<float*>(ws);
+    float* wsM = wsS + static_cast<size_t>(nsplit) * a.n_heads * D * D;
+    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 1, 0,
+                       seg_off, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (nsplit > 0) {
+        hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 0,
+                           1, split_off, nullptr);
+        const dim3 grid1(static_cast<unsigned>(nsplit * a.n_heads));
+        hipLaunchKernelGGL(gdn_seg_state, grid1, dim3(NTH), 0, s, static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
+                           a.n_heads, a.n_slots, a.slot_idx, lseg, coff, seg_off, split_off, planes,
+                           plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM);
+        hipLaunchKernelGGL(gdn_seg_scan, grid1, dim3(NTH), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads,
+                           a.pool, a.n_slots, a.slot_idx, a.zero_init, split_off, nsplit, wsS, wsM);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 0,
+                           1, split_off, nullptr);
+    }
+    const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
+    const dim3 grid2(static_cast<unsigned>(maxseg * a.n_heads));
+    auto out_pass = [&](auto kern, auto* o) {
+        hipLaunchKernelGGL(kern, grid2, dim3(NTH), 0, s, static_cast<const uint16_t*>(a.q),
+                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
+                           a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
+                           a.zero_init, lseg, coff, seg_off, split_off, planes,
+                           plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM, ck, o);
+    };
+    if (ck.slots) {
+        if (a.out_bf16) out_pass(gdn_seg_out<BF16, true>, static_cast<uint16_t*>(a.o));
+        else out_pass(gdn_seg_out<F32, true>, static_cast<float*>(a.o));
+    } else {
+        if (a.out_bf16) out_pass(gdn_seg_out<BF16, false>, static_cast<uint16_t*>(a.o));
+        else out_pass(gdn_seg_out<F32, false>, static_cast<float*>(a.o));
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gla

@@ -156,6 +156,18 @@ GLA_API int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  * solved as U = T diag(b) V - (T diag(b exp g) K) S with T = (I + A)^-1,
  * followed by the GLA chunk formulas with U in place of V.
  * Requires workspace of gdn_chunk_workspace_bytes() bytes (may be 0).
+ * For bf16 inputs with d_k = d_v = 128 and C = 64, each (sequence segment,
+ * head) is one workgroup over all 128 state columns, and a sequence longer
+ * than the segment length (about n_tokens * n_heads / 256 tokens, at least
+ * 256) is cut into segments that run side by side: a first pass computes
+ * each segment's state contribution and its d_k x d_k transition, a scan
+ * over the segments forms every segment's entry state, and the second pass
+ * produces the outputs (the state hand-off of "Chunked prefill comes for
+ * free", used inside one call).  That path multiplies fp16 operands with
+ * fp32 accumulation, each fp32-derived operand scaled by a power of two
+ * into fp16's range; it needs |q_i| |k_j| < 2^15 and |q|, |k| entries
+ * below 2^15 (true for L2-normalised q and k) and gives results about 5e-4
+ * (relative to the largest) from the exact ones on such inputs.
  */
 GLA_API int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                   const float* beta,
