@@ -535,6 +535,31 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
     }
 }
 
+// ------------------------------------------------------------------ passes
+// Arguments shared by the two passes.
+struct SegArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* alpha;
+    const int32_t* cu;
+    int n_seqs, n_tokens, H;
+    float* pool;
+    int n_slots;
+    const int32_t* slot_idx;
+    int zero_init, lseg;
+    const int32_t* coff;          // first global chunk of every sequence
+    const int32_t* seg_off;       // first segment of every sequence
+    const int32_t* split_off;     // first split segment (every segment but the last of a split sequence)
+    const uint16_t* planes;       // T diag(beta) per (chunk, head), fp16
+    const float* tinv;            // their inverse scales
+    long n_chunks_max, nsplit_max;
+    float* wsS;                   // per (split segment, head): dS, then the entry state of the next segment
+    float* wsM;                   // per (split segment, head): M; slot 0 of a sequence then its S_in(0)
+    Ckpt ck;
+    void* o;
+};
+
 // ------------------------------------------------------------------ pass 1
 struct StateBuf {
     alignas(16) uint16_t k[CH][LK];      // fp16
@@ -547,26 +572,21 @@ struct StateBuf {
     float tinv;
 };
 
-__global__ void __launch_bounds__(NTH)
-gdn_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ alpha,
-              const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H, int n_slots,
-              const int32_t* __restrict__ slot_idx, int lseg, const int32_t* __restrict__ coff,
-              const int32_t* __restrict__ seg_off, const int32_t* __restrict__ split_off,
-              const uint16_t* __restrict__ planes, const float* __restrict__ tinv, long n_chunks_max,
-              long nsplit_max, float* __restrict__ wsS, float* __restrict__ wsM) {
-    const int h = blockIdx.x % H;
-    const int j = blockIdx.x / H;
-    if (j >= split_off[n_seqs]) return;
-    const int b = find_span_owner(split_off, n_seqs, j);
-    const int g = j - split_off[b];
+// Pass 1 for split segment j of head h (block work item bid = j * H + h).
+__device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, const SegArgs& a) {
+    const int H = a.H;
+    const int h = bid % H;
+    const int j = bid / H;
+    if (j >= a.split_off[a.n_seqs]) return;
+    const int b = find_span_owner(a.split_off, a.n_seqs, j);
+    const int g = j - a.split_off[b];
     GSeg sg;
-    if (!seg_bounds(sg, b, g, seg_off[b + 1] - seg_off[b], cu, n_tokens, coff, split_off, slot_idx, n_slots, lseg,
-                    nsplit_max))
+    if (!seg_bounds(sg, b, g, a.seg_off[b + 1] - a.seg_off[b], a.cu, a.n_tokens, a.coff, a.split_off, a.slot_idx,
+                    a.n_slots, a.lseg, a.nsplit_max))
         return;
     const int nch = (sg.t1 - sg.t0 + CH - 1) / CH;
-    if (sg.ci0 < 0 || sg.ci0 + nch > n_chunks_max) return;     // malformed cu_seqlens only
+    if (sg.ci0 < 0 || sg.ci0 + nch > a.n_chunks_max) return;     // malformed cu_seqlens only
 
-    __shared__ StateBuf buf[2];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const AccPos ap;
     const int col = wave * 16;
@@ -583,7 +603,8 @@ gdn_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, co
     auto rows = [&](int c) { return c < nch ? min(CH, sg.t1 - sg.t0 - c * CH) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * CH; };
     GPrefetch<false, true> pf;
-    const SegSrc src = seg_src<false, true>(nullptr, k, v, alpha, planes, tinv, sg.t0, sg.t1 - sg.t0, sg.ci0, nch, h, H);
+    const SegSrc src = seg_src<false, true>(nullptr, a.k, a.v, a.alpha, a.planes, a.tinv, sg.t0, sg.t1 - sg.t0, sg.ci0,
+                                            nch, h, H);
     auto fetch = [&](int c) { g_fetch(pf, src, c, rows(c)); };
     auto stage = [&](StateBuf& bb) {
         g_stage_gates(nullptr, bb.eg, bb.dec, &bb.gamma, pf);
@@ -619,8 +640,8 @@ gdn_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, co
         lds_barrier();
     }
     const long slot = (sg.jsplit + g) * H + h;
-    g_slot_store(g_slot(wsS, slot), S);
-    g_slot_store(g_slot(wsM, slot), M);
+    g_slot_store(g_slot(a.wsS, slot), S);
+    g_slot_store(g_slot(a.wsM, slot), M);
 }
 
 // ------------------------------------------------------------------ scan
@@ -714,34 +735,44 @@ struct KGate {
     float tinv;
 };
 
-template <class TO, bool CKPT>
-__global__ void __launch_bounds__(NTH)
-gdn_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-            const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
-            float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
-            const int32_t* __restrict__ coff, const int32_t* __restrict__ seg_off,
-            const int32_t* __restrict__ split_off, const uint16_t* __restrict__ planes,
-            const float* __restrict__ tinv, long n_chunks_max, long nsplit_max, const float* __restrict__ wsS,
-            const float* __restrict__ wsM, Ckpt ck,
-            typename TO::T* __restrict__ o) {
-    const int h = blockIdx.x % H;
-    const int si = blockIdx.x / H;
-    if (si >= seg_off[n_seqs]) return;
-    const int b = find_span_owner(seg_off, n_seqs, si);
-    const int g = si - seg_off[b];
+struct OutSmem {
+    KGate kb[2];
+    alignas(16) uint16_t sq[CH][LQ];      // fp16
+    alignas(16) uint16_t sv[CH][LK];      // bf16
+    alignas(16) uint16_t st[CH][LP];      // T diag(beta), fp16, scaled
+    alignas(16) uint16_t sp[CH][LP];      // P, fp16
+    alignas(16) uint16_t obuf[CH][LQ];    // bf16 outputs of the previous chunk
+};
+
+// Pass 2 for segment si of head h (bid = si * H + h); SPLIT selects the
+// segments of sequences cut into several (true) or of those that are not.
+template <class TO, bool CKPT, bool SPLIT>
+__device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs& a) {
+    const int H = a.H;
+    const int h = bid % H;
+    const int si = bid / H;
+    if (si >= a.seg_off[a.n_seqs]) return;
+    const int b = find_span_owner(a.seg_off, a.n_seqs, si);
+    const int g = si - a.seg_off[b];
+    const int nseg = a.seg_off[b + 1] - a.seg_off[b];
+    if ((nseg > 1) != SPLIT) return;
     GSeg sg;
-    if (!seg_bounds(sg, b, g, seg_off[b + 1] - seg_off[b], cu, n_tokens, coff, split_off, slot_idx, n_slots, lseg,
-                    nsplit_max))
+    if (!seg_bounds(sg, b, g, nseg, a.cu, a.n_tokens, a.coff, a.split_off, a.slot_idx, a.n_slots, a.lseg,
+                    a.nsplit_max))
         return;
     const int nch = (sg.t1 - sg.t0 + CH - 1) / CH;
-    if (sg.ci0 < 0 || sg.ci0 + nch > n_chunks_max) return;     // malformed cu_seqlens only
-
-    __shared__ KGate kb[2];
-    __shared__ alignas(16) uint16_t sq[CH][LQ];      // fp16
-    __shared__ alignas(16) uint16_t sv[CH][LK];      // bf16
-    __shared__ alignas(16) uint16_t st[CH][LP];      // T diag(beta), fp16, scaled
-    __shared__ alignas(16) uint16_t sp[CH][LP];      // P, fp16
-    __shared__ alignas(16) uint16_t obuf[TO::bytes == 2 ? CH : 1][LQ];
+    if (sg.ci0 < 0 || sg.ci0 + nch > a.n_chunks_max) return;     // malformed cu_seqlens only
+    const int lseg = a.lseg;
+    const int n_slots = a.n_slots;
+    const Ckpt ck = a.ck;
+    float* pool = a.pool;
+    typename TO::T* o = static_cast<typename TO::T*>(a.o);
+    KGate (&kb)[2] = sm.kb;
+    uint16_t (&sq)[CH][LQ] = sm.sq;
+    uint16_t (&sv)[CH][LK] = sm.sv;
+    uint16_t (&st)[CH][LP] = sm.st;
+    uint16_t (&sp)[CH][LP] = sm.sp;
+    uint16_t (&obuf)[CH][LQ] = sm.obuf;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -752,7 +783,8 @@ gdn_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     auto rows = [&](int c) { return c < nch ? min(CH, sg.t1 - sg.t0 - c * CH) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * CH; };
     GPrefetch<true, true> pf;
-    const SegSrc src = seg_src<true, true>(q, k, v, alpha, planes, tinv, sg.t0, sg.t1 - sg.t0, sg.ci0, nch, h, H);
+    const SegSrc src = seg_src<true, true>(a.q, a.k, a.v, a.alpha, a.planes, a.tinv, sg.t0, sg.t1 - sg.t0, sg.ci0,
+                                           nch, h, H);
     auto fetch = [&](int c) { g_fetch(pf, src, c, rows(c)); };
     fetch(0);
 
@@ -762,10 +794,9 @@ gdn_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     if (sg.nseg <= 1) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (!zero_init) g_rowmajor_load(S, Sg, col);
+        if (!a.zero_init) g_rowmajor_load(S, Sg, col);
     } else {
-        const float* src = g == 0 ? g_slot(const_cast<float*>(wsM), sg.jsplit * H + h)
-                                  : g_slot(const_cast<float*>(wsS), (sg.jsplit + g - 1) * H + h);
+        const float* src = g == 0 ? g_slot(a.wsM, sg.jsplit * H + h) : g_slot(a.wsS, (sg.jsplit + g - 1) * H + h);
         g_slot_load(S, src);
     }
     // P tiles above the diagonal that the products still read (rows 0-15 x
@@ -887,10 +918,39 @@ gdn_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     }
 }
 
+union SegSmem {
+    StateBuf st[2];
+    OutSmem out;
+};
+
+// Phase A: pass 1 for the split segments (blocks [0, n1)), which the scan
+// waits for, and next to it pass 2 for sequences that are not split, which
+// depend on nothing else (blocks [n1, ...)).
+template <class TO, bool CKPT>
+__global__ void __launch_bounds__(NTH)
+gdn_seg_a(SegArgs a, int n1) {
+    __shared__ SegSmem sm;
+    if (static_cast<int>(blockIdx.x) < n1) seg_state_body(sm.st, blockIdx.x, a);
+    else seg_out_body<TO, CKPT, false>(sm.out, blockIdx.x - n1, a);
+}
+
+// Phase B (after the scan): pass 2 for the segments of split sequences.
+template <class TO, bool CKPT>
+__global__ void __launch_bounds__(NTH)
+gdn_seg_b(SegArgs a) {
+    __shared__ SegSmem sm;
+    seg_out_body<TO, CKPT, true>(sm.out, blockIdx.x, a);
+}
+
 // Segment length: whole chunks, at least 4 of them, such that the call
 // has about kTargetBlocks (segment, head) workgroups when it is long enough.
-int g_seg_len(int n_tokens, int n_heads) {
-    const long target = n_heads >= kTargetBlocks ? 1 : kTargetBlocks / n_heads;
+// With many (sequence, head) pairs the batch fills the GPU without cutting,
+// and segments only bound the longest chain: pass 1 of a split segment and
+// pass 2 after the scan run one after the other, so the segments are made
+// half as long (about 2 kTargetBlocks of them) to keep that path short.
+int g_seg_len(int n_seqs, int n_tokens, int n_heads) {
+    const long blocks = static_cast<long>(n_seqs) * n_heads >= 2 * kTargetBlocks ? 2 * kTargetBlocks : kTargetBlocks;
+    const long target = n_heads >= blocks ? 1 : blocks / n_heads;
     long L = (n_tokens + target - 1) / target;
     L = ((L + CH - 1) / CH) * CH;
     return static_cast<int>(L < 4 * CH ? 4 * CH : L);
@@ -905,7 +965,7 @@ __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_
 // (split segment, head).  A sequence of s >= 2 segments is longer than
 // (s - 1) * lseg tokens, so split segments number at most n_tokens / lseg.
 size_t gdn_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
-    const long nsplit = n_tokens / g_seg_len(n_tokens, n_heads);
+    const long nsplit = n_tokens / g_seg_len(n_seqs, n_tokens, n_heads);
     return 2 * al256(sizeof(int32_t) * (n_seqs + 1)) +
            2 * static_cast<size_t>(nsplit) * n_heads * D * D * sizeof(float);
 }
@@ -928,7 +988,7 @@ hipError_t launch_gdn_seg_prep(const ChunkArgs& a, const int32_t* coff, uint16_t
 
 hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_t* planes, long n_chunks_max,
                           void* seg_ws, hipStream_t s) {
-    const int lseg = g_seg_len(a.n_tokens, a.n_heads);
+    const int lseg = g_seg_len(a.n_seqs, a.n_tokens, a.n_heads);
     const long nsplit = a.n_tokens / lseg;
     const long maxseg = nsplit + a.n_seqs;
     char* ws = static_cast<char*>(seg_ws);
@@ -940,39 +1000,33 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
     float* wsM = wsS + static_cast<size_t>(nsplit) * a.n_heads * D * D;
     hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 1, 0,
                        seg_off, nullptr);
+    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 0, 1,
+                       split_off, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (nsplit > 0) {
-        hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 0,
-                           1, split_off, nullptr);
-        const dim3 grid1(static_cast<unsigned>(nsplit * a.n_heads));
-        hipLaunchKernelGGL(gdn_seg_state, grid1, dim3(NTH), 0, s, static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
-                           a.n_heads, a.n_slots, a.slot_idx, lseg, coff, seg_off, split_off, planes,
-                           plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM);
-        hipLaunchKernelGGL(gdn_seg_scan, grid1, dim3(NTH), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads,
-                           a.pool, a.n_slots, a.slot_idx, a.zero_init, split_off, nsplit, wsS, wsM);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    } else {
-        hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 0,
-                           1, split_off, nullptr);
-    }
-    const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
-    const dim3 grid2(static_cast<unsigned>(maxseg * a.n_heads));
-    auto out_pass = [&](auto kern, auto* o) {
-        hipLaunchKernelGGL(kern, grid2, dim3(NTH), 0, s, static_cast<const uint16_t*>(a.q),
-                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha,
-                           a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, coff, seg_off, split_off, planes,
-                           plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM, ck, o);
+    const SegArgs sa{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads,
+                     a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, coff, seg_off, split_off, planes,
+                     plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM,
+                     Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.o};
+    const int n1 = static_cast<int>(nsplit * a.n_heads);
+    const dim3 grid_a(static_cast<unsigned>(n1 + maxseg * a.n_heads));
+    const dim3 grid_b(static_cast<unsigned>(maxseg * a.n_heads));
+    auto passes = [&](auto ka, auto kb) {
+        hipLaunchKernelGGL(ka, grid_a, dim3(NTH), 0, s, sa, n1);
+        if (nsplit > 0) {
+            hipLaunchKernelGGL(gdn_seg_scan, dim3(static_cast<unsigned>(n1)), dim3(NTH), 0, s, a.cu_seqlens,
+                               a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init,
+                               split_off, nsplit, wsS, wsM);
+            hipLaunchKernelGGL(kb, grid_b, dim3(NTH), 0, s, sa);
+        }
     };
-    if (ck.slots) {
-        if (a.out_bf16) out_pass(gdn_seg_out<BF16, true>, static_cast<uint16_t*>(a.o));
-        else out_pass(gdn_seg_out<F32, true>, static_cast<float*>(a.o));
+    if (sa.ck.slots) {
+        if (a.out_bf16) passes(gdn_seg_a<BF16, true>, gdn_seg_b<BF16, true>);
+        else passes(gdn_seg_a<F32, true>, gdn_seg_b<F32, true>);
     } else {
-        if (a.out_bf16) out_pass(gdn_seg_out<BF16, false>, static_cast<uint16_t*>(a.o));
-        else out_pass(gdn_seg_out<F32, false>, static_cast<float*>(a.o));
+        if (a.out_bf16) passes(gdn_seg_a<BF16, false>, gdn_seg_b<BF16, false>);
+        else passes(gdn_seg_a<F32, false>, gdn_seg_b<F32, false>);
     }
     return hipGetLastError();
 }
