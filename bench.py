@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="instead of the benchmark line: GLA / GDN prefill over batch x length mixes "
                         "and decode over batch sizes, one JSON line per shape")
+    p.add_argument("--sweep-kind", default="all", choices=["all", "gla", "gdn", "decode"],
+                   help="with --sweep: only the GLA prefills, the GDN prefills or the decodes")
     return p.parse_args()
 
 
@@ -463,7 +465,7 @@ def measured_mfma(kernel: str):
     return None if ent is None else ent.get("mfma")
 
 
-def run_sweep(torch, G, steps, warmup):
+def run_sweep(torch, G, steps, warmup, kind="all"):
     """Prefill over batch x length mixes of about the same token count (and
     two larger ones), decode over batch sizes.  Inputs are drawn on the
     device with the benchmark's distributions (GLA q, k ~ N(0,1)/sqrt(d);
@@ -482,7 +484,7 @@ def run_sweep(torch, G, steps, warmup):
             return torch.nn.functional.normalize(rn(n, H, d), dim=-1).bfloat16()
         return (rn(n, H, d) / math.sqrt(d)).bfloat16()
 
-    for gdn in (False, True):
+    for gdn in [g for g, name in ((False, "gla"), (True, "gdn")) if kind in ("all", name)]:
         for B, T in ((1, 16384), (2, 8192), (4, 4096), (16, 1024), (64, 256), (256, 64), (8, 8192),
                      (1, 65536)):
             N = B * T
@@ -507,6 +509,8 @@ def run_sweep(torch, G, steps, warmup):
             print(json.dumps({"sweep": "gdn_prefill" if gdn else "gla_prefill", "batch": B, "seq_len": T,
                               "ms": ms, "tokens_per_s": N / (ms * 1e-3)}), flush=True)
             del sets, o, ws, pool
+    if kind not in ("all", "decode"):
+        return
     n_slots = 2048
     pool = rn(n_slots, H, d, d) * 0.05
     perm = torch.randperm(n_slots, device="cuda:0", generator=gen).to(torch.int32)
@@ -577,7 +581,7 @@ def main():
     from gated_deltanet_gla_amd import _lib
     _lib.lib()   # fail loudly if the HIP library is missing
     if args.sweep:
-        run_sweep(torch, G, max(args.steps, 30), args.warmup)
+        run_sweep(torch, G, max(args.steps, 30), args.warmup, args.sweep_kind)
         return
 
     def dev(x, dtype="f32"):

@@ -474,11 +474,9 @@ constexpr int kOrderMax = 1024;
 // contiguous range of sequences, then wave scans and a scan of the 16 wave
 // totals.  With order != nullptr also writes the sequences by decreasing
 // length (ties by index): order[r] = sequence of rank r.
-__global__ void __launch_bounds__(1024)
-span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span, int min_count,
-             int sub, int32_t* __restrict__ off, int32_t* __restrict__ order) {
-    __shared__ int wsum[16];
-    __shared__ int lens[kOrderMax];
+__device__ __forceinline__ void span_offsets_body(const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
+                                                  int span, int min_count, int sub, int32_t* __restrict__ off,
+                                                  int32_t* __restrict__ order, int* wsum, int* lens) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     auto length = [&](int b) {
         const int s = clampi(cu[b], 0, n_tokens);
@@ -516,6 +514,30 @@ span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span,
     } else {
         for (int b = t; b < n_seqs; b += 1024) order[b] = b;
     }
+}
+
+__global__ void __launch_bounds__(1024)
+span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span, int min_count,
+             int sub, int32_t* __restrict__ off, int32_t* __restrict__ order) {
+    __shared__ int wsum[16];
+    __shared__ int lens[kOrderMax];
+    span_offsets_body(cu, n_seqs, n_tokens, span, min_count, sub, off, order, wsum, lens);
+}
+
+// Several such scans over the same sequences in one launch, workgroup i
+// doing scan i (no order).
+struct SpanScan {
+    int span, min_count, sub;
+    int32_t* off;
+};
+struct SpanScans {
+    SpanScan s[3];
+};
+__global__ void __launch_bounds__(1024)
+span_offsets_multi(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, SpanScans sc) {
+    __shared__ int wsum[16];
+    const SpanScan& x = sc.s[blockIdx.x];
+    span_offsets_body(cu, n_seqs, n_tokens, x.span, x.min_count, x.sub, x.off, nullptr, wsum, nullptr);
 }
 
 // Largest b in [0, n_seqs) with off[b] <= idx (off non-decreasing).

@@ -937,9 +937,13 @@ hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     hipError_t e = hipSuccess;
     // phase 1 (state-independent): chunk offsets, order, inverses / planes
     if (a.gdn_phases != 2) {
-    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
-                       a.n_tokens, C, 0, 0, off, FAST ? order : nullptr);
-    e = hipGetLastError();
+    if constexpr (SEG) {
+        e = launch_gdn_seg_offsets(a, off, ws, s);
+    } else {
+        hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs,
+                           a.n_tokens, C, 0, 0, off, FAST ? order : nullptr);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     if (a.n_tokens > 0 && SEG) {
         // one wave per (chunk, head) item (gdn_seg.hip)

@@ -52,12 +52,14 @@
 //     into several, dS and M, by running the state update alone on [S | M]
 //     from [0 | I] (M takes no values: its Y is -diag(exp g) K M);
 //   scan (gdn_seg_scan): per (sequence, head), S_in(0) = the pool state and
-//     S_in(j + 1) = M_j S_in(j) + dS_j, written over dS_j (S_in(0) over M_0);
+//     S_in(j + 1) = M_j S_in(j) + dS_j, written over dS_j (S_in(0) to a slot
+//     of its own);
 //   pass 2 (gdn_seg_out): every segment from its S_in, outputs included; the
 //     last one writes the final state to the pool.
 // A sequence of one segment is handled by pass 2 alone, reading and writing
-// the pool.  State slots in the workspace hold each lane's 32 accumulator
-// values contiguously (16-byte accesses).
+// the pool.  State slots in the workspace are tile-major (a wave reads or
+// writes one accumulator tile as one contiguous 1 KiB); M is stored as the
+// scan's A operand fragments.
 #include <algorithm>
 
 #include "chunk_common.h"
@@ -74,7 +76,6 @@ constexpr int LQ = D + 8;          // LDS row stride of q (read along rows)
 constexpr int LK = D + 16;         // k, v read with the transpose read and k's 16-byte row reads
 constexpr int LX = D + 8;          // k read in the split order of X = K S (8-byte reads)
 constexpr int LP = CH + 8;         // P and T diag(beta)
-constexpr int LM = D + 8;          // the transition in the scan (read transposed)
 constexpr int kTargetBlocks = 256; // about one workgroup per compute unit
 constexpr int kPlaneElems = CH * CH;       // T diag(beta) (fp16) per (chunk, head)
 
@@ -219,17 +220,27 @@ __device__ __forceinline__ void g_stage_plane(uint16_t (*t)[LP], const u32x4& w)
     *reinterpret_cast<u32x4*>(&t[threadIdx.x >> 3][(threadIdx.x & 7) * 8]) = w;
 }
 
-// A state slot of the workspace: lane l of wave w keeps its 8 tiles x 4
-// values at ((w * 64 + l) * 32).
-__device__ __forceinline__ float* g_slot(float* ws, long slot) { return ws + slot * D * D + threadIdx.x * 32; }
+// A state slot of the workspace, tile-major: accumulator tile (row block mt,
+// column block cb) is 1 KiB, lane l's 4 values at ((cb * 8 + mt) * 64 + l) * 4,
+// so every access of a wave to one tile is one contiguous 1 KiB.
+__device__ __forceinline__ long g_tile(int cb, int mt, int lane) { return ((cb * 8 + mt) * 64 + lane) * 4; }
+// this wave's column block (8 tiles) of a slot
+__device__ __forceinline__ float* g_slot(float* ws, long slot) {
+    return ws + slot * D * D + g_tile(threadIdx.x >> 6, 0, threadIdx.x & 63);
+}
 __device__ __forceinline__ void g_slot_load(f32x4 (&S)[8], const float* p) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(p + mt * 4);
+    for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(p + mt * 256);
 }
 __device__ __forceinline__ void g_slot_store(float* p, const f32x4 (&S)[8]) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(p + mt * 4) = S[mt];
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(p + mt * 256) = S[mt];
 }
+// M in the layout the scan reads it in: the A operand fragments of row
+// block rb, 32-deep block s and half h2 (columns 32 s + 16 h2 .. + 15), lane
+// l holding M[16 rb + l % 16][32 s + 16 h2 + 4 (l / 16) + e], e = 0..3, at
+// (((rb * 4 + s) * 2 + h2) * 64 + l) * 4; each fragment is 1 KiB.
+__device__ __forceinline__ long g_mfrag(int rb, int s, int h2, int lane) { return (((rb * 4 + s) * 2 + h2) * 64 + lane) * 4; }
 // This wave's 8 tiles of a row-major [d][n] state (columns col .. col + 15).
 __device__ __forceinline__ void g_rowmajor_load(f32x4 (&S)[8], const float* src, int col) {
     const AccPos ap;
@@ -555,7 +566,8 @@ struct SegArgs {
     const float* tinv;            // their inverse scales
     long n_chunks_max, nsplit_max;
     float* wsS;                   // per (split segment, head): dS, then the entry state of the next segment
-    float* wsM;                   // per (split segment, head): M; slot 0 of a sequence then its S_in(0)
+    float* wsM;                   // per (split segment, head): M, as the scan's operand fragments
+    float* wsI;                   // per split sequence (at its first split segment) and head: S_in(0)
     Ckpt ck;
     void* o;
 };
@@ -641,87 +653,141 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
     }
     const long slot = (sg.jsplit + g) * H + h;
     g_slot_store(g_slot(a.wsS, slot), S);
-    g_slot_store(g_slot(a.wsM, slot), M);
+    // M[16 mt + row0 + r][col + ap.col] -> row block mt, column k = col + ap.col
+    // (s = wave / 2, h2 = wave % 2), fragment lane row0 + r + 16 (ap.col / 4)
+    float* mfr = a.wsM + slot * D * D;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            mfr[g_mfrag(mt, wave >> 1, wave & 1, ap.row0 + r + 16 * (ap.col >> 2)) + (ap.col & 3)] = M[mt][r];
 }
 
 // ------------------------------------------------------------------ scan
-// Per (split sequence, head): S_in(0) = pool state (or 0) goes to M slot 0
-// once M_0 has been read; then S_in(j + 1) = M_j S_in(j) + dS_j goes over
-// dS slot j.  M_j is staged into LDS transposed, as bf16 hi / lo, and read
-// as the A operand with the transpose read.
+// Per (split sequence, head): S_in(0) = the pool state (or 0), then
+// S_in(j + 1) = M_j S_in(j) + dS_j.  The state's columns are independent, so
+// kScanGroups workgroups share a (sequence, head), each with kScanCols
+// 16-column blocks, at equal blockIdx % 8 (one XCD, so M_j is fetched into
+// one L2).  Wave w forms rows 16 w .. 16 w + 15 of its workgroup's blocks:
+// its A operand, rows of M_j, is read from the fragment-major slot into
+// registers two steps ahead and serves every block; the B operands, the
+// blocks' S_in(j), go round through LDS, one barrier a step.  Every
+// workgroup reads all of M_j each step: wider workgroups move fewer bytes
+// from L2 and lengthen each step's LDS reads and MFMA chains.
+// The products take bf16 hi + lo pairs (three MFMAs per 32-deep block).
+// S_in(j + 1) overwrites dS_j (each word by the lane that read it) and
+// S_in(0) goes to the sequence's slot in wsI.
+// kScanCols: 16-column blocks per workgroup (1 or 2, the latter when there
+// are many (sequence, head) pairs; kScanGroups = 8 / kScanCols workgroups
+// per pair).
+template <int kScanCols>
 __global__ void __launch_bounds__(NTH)
-gdn_seg_scan(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H, const float* __restrict__ pool,
-             int n_slots, const int32_t* __restrict__ slot_idx, int zero_init,
-             const int32_t* __restrict__ split_off, long nsplit_max, float* __restrict__ wsS,
-             float* __restrict__ wsM) {
-    const int h = blockIdx.x % H;
-    const int j = blockIdx.x / H;
+gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
+             int zero_init, const int32_t* __restrict__ split_off, long nsplit_max, float* __restrict__ wsS,
+             const float* __restrict__ wsM, float* __restrict__ wsI) {
+    constexpr int kScanGroups = 8 / kScanCols;
+    const int x = blockIdx.x;
+    const int part = (x >> 3) % kScanGroups;         // which kScanCols column blocks
+    const long grp = static_cast<long>(x / (8 * kScanGroups)) * 8 + (x & 7);   // split segment * H + head
+    if (grp >= nsplit_max * H) return;
+    const int h = static_cast<int>(grp % H);
+    const int j = static_cast<int>(grp / H);
     if (j >= split_off[n_seqs]) return;
     const int b = find_span_owner(split_off, n_seqs, j);
-    if (j != split_off[b]) return;                  // one block per split sequence
+    if (j != split_off[b]) return;                  // the first split segment stands for the sequence
     const int nsplit = split_off[b + 1] - split_off[b];
     if (static_cast<long>(j) + nsplit > nsplit_max) return;      // malformed cu_seqlens only
     const int slot = slot_idx[b];
     if (slot < 0 || slot >= n_slots) return;
-    (void)cu;
-    (void)n_tokens;
 
-    __shared__ uint16_t mt_s[2][D][LM];              // M^T (row = input index), hi and lo
+    __shared__ f32x4 xs[2][kScanCols][NWV][64];      // S_in by column block and row block
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const AccPos ap;
-    const int col = wave * 16;
-    f32x4 S[8];
+    // this lane's words of a state slot in column block c of the workgroup
+    auto lofs = [&](int c) { return g_tile(part * kScanCols + c, wave, lane); };
+    f32x4 S[kScanCols];
+    const float* src = pool + (static_cast<long>(slot) * H + h) * D * D;
+    float* s0 = wsI + (static_cast<long>(j) * H + h) * D * D;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!zero_init) g_rowmajor_load(S, pool + (static_cast<long>(slot) * H + h) * D * D, col);
-
-    f32x4 Mn[8], dSn[8];
-    g_slot_load(Mn, g_slot(wsM, static_cast<long>(j) * H + h));
-    g_slot_load(dSn, g_slot(wsS, static_cast<long>(j) * H + h));
-    for (int step = 0; step < nsplit; ++step) {
-        const long sl = static_cast<long>(j + step) * H + h;
-        f32x4 Mc[8], dS[8];
+    for (int c = 0; c < kScanCols; ++c) {
+        S[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!zero_init) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            Mc[mt] = Mn[mt];
-            dS[mt] = dSn[mt];
+            for (int r = 0; r < 4; ++r)
+                S[c][r] = src[(wave * 16 + ap.row0 + r) * D + (part * kScanCols + c) * 16 + ap.col];
         }
-        if (step + 1 < nsplit) {
-            g_slot_load(Mn, g_slot(wsM, sl + H));
-            g_slot_load(dSn, g_slot(wsS, sl + H));
-        }
-        // M_j -> LDS as M^T: lane holds M[16 mt + row0 + r][col + lane % 16]
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            uint32_t h0, l0, h1, l1;
-            split_bf16x2(Mc[mt][0], Mc[mt][1], h0, l0);
-            split_bf16x2(Mc[mt][2], Mc[mt][3], h1, l1);
-            *reinterpret_cast<u32x2*>(&mt_s[0][col + ap.col][mt * 16 + ap.row0]) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(&mt_s[1][col + ap.col][mt * 16 + ap.row0]) = u32x2{l0, l1};
-        }
-        // S_in(0) over M_0's slot: the values stored above used every word
-        // this lane read from it
-        if (step == 0) g_slot_store(g_slot(wsM, sl), S);
-        lds_barrier();
-        bf16x8 sh[4], slo[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) split_pair(S[2 * s], S[2 * s + 1], sh[s], slo[s]);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            f32x4 acc = dS[mt];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 ah = frag_km_split(&mt_s[0][0][0], LM, mt * 16, 32 * s);
-                const bf16x8 al = frag_km_split(&mt_s[1][0][0], LM, mt * 16, 32 * s);
-                acc = mfma_bf16(ah, sh[s], acc);
-                acc = mfma_bf16(ah, slo[s], acc);
-                acc = mfma_bf16(al, sh[s], acc);
-            }
-            S[mt] = acc;
-        }
-        g_slot_store(g_slot(wsS, sl), S);                        // S_in(step + 1)
-        lds_barrier();
+        *reinterpret_cast<f32x4*>(s0 + lofs(c)) = S[c];
     }
+
+    // M_j row 16 wave + lane % 16 at columns 32 s + 4 g + (0..3) and
+    // 32 s + 16 + 4 g + (0..3): the split order of the B operand's tile pairs
+    struct Pf {
+        f32x4 m[8];
+        f32x4 d[kScanCols];
+    };
+    auto load = [&](Pf& p, int step) {
+        const long sl = (static_cast<long>(j) + step) * H + h;
+        const float* mp = wsM + sl * D * D;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            p.m[2 * s] = *reinterpret_cast<const f32x4*>(mp + g_mfrag(wave, s, 0, lane));
+            p.m[2 * s + 1] = *reinterpret_cast<const f32x4*>(mp + g_mfrag(wave, s, 1, lane));
+        }
+#pragma unroll
+        for (int c = 0; c < kScanCols; ++c) p.d[c] = *reinterpret_cast<const f32x4*>(wsS + sl * D * D + lofs(c));
+        __builtin_amdgcn_sched_barrier(0);     // sets complete in the order they were issued
+    };
+    auto run = [&](const Pf& p, int step) {
+        // fences keep the scheduler from converting a later step's M early,
+        // which would wait for the loads issued for that step
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = step & 1;       // LDS buffers alternate, so one barrier a step suffices
+#pragma unroll
+        for (int c = 0; c < kScanCols; ++c) xs[buf][c][wave][lane] = S[c];
+        lds_barrier();
+        f32x4 acc[kScanCols];
+#pragma unroll
+        for (int c = 0; c < kScanCols; ++c) acc[c] = p.d[c];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 ah, al;
+            split_pair(p.m[2 * s], p.m[2 * s + 1], ah, al);
+#pragma unroll
+            for (int c = 0; c < kScanCols; ++c) {
+                bf16x8 bh, bl;
+                split_pair(xs[buf][c][2 * s][lane], xs[buf][c][2 * s + 1][lane], bh, bl);
+                acc[c] = mfma_bf16(ah, bh, acc[c]);
+                acc[c] = mfma_bf16(ah, bl, acc[c]);
+                acc[c] = mfma_bf16(al, bh, acc[c]);
+            }
+        }
+        float* dst = wsS + ((static_cast<long>(j) + step) * H + h) * D * D;
+#pragma unroll
+        for (int c = 0; c < kScanCols; ++c) {
+            S[c] = acc[c];
+            *reinterpret_cast<f32x4*>(dst + lofs(c)) = S[c];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // three register sets, each reloaded right after use (a clamped step
+    // instead of a branch past the end); the loop body has a single path,
+    // so the load-counter wait before each step covers only that step's set
+    Pf pa, pb, pc;
+    load(pa, 0);
+    load(pb, min(1, nsplit - 1));
+    load(pc, min(2, nsplit - 1));
+    int step = 0;
+    for (; step + 2 < nsplit; step += 3) {
+        run(pa, step);
+        load(pa, min(step + 3, nsplit - 1));
+        run(pb, step + 1);
+        load(pb, min(step + 4, nsplit - 1));
+        run(pc, step + 2);
+        load(pc, min(step + 5, nsplit - 1));
+    }
+    if (step < nsplit) run(pa, step);
+    if (step + 1 < nsplit) run(pb, step + 1);
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -796,7 +862,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
         for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!a.zero_init) g_rowmajor_load(S, Sg, col);
     } else {
-        const float* src = g == 0 ? g_slot(a.wsM, sg.jsplit * H + h) : g_slot(a.wsS, (sg.jsplit + g - 1) * H + h);
+        const float* src = g == 0 ? g_slot(a.wsI, sg.jsplit * H + h) : g_slot(a.wsS, (sg.jsplit + g - 1) * H + h);
         g_slot_load(S, src);
     }
     // P tiles above the diagonal that the products still read (rows 0-15 x
@@ -961,19 +1027,31 @@ __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_
 }  // namespace
 
 // Workspace of the segmented path beyond the chunk offsets and T planes:
-// segment offsets, split-segment offsets, and two 64 KiB state slots per
-// (split segment, head).  A sequence of s >= 2 segments is longer than
+// segment offsets, split-segment offsets, and three 64 KiB state slots per
+// (split segment, head): dS, M and (at a sequence's first) S_in(0).  A sequence of s >= 2 segments is longer than
 // (s - 1) * lseg tokens, so split segments number at most n_tokens / lseg.
 size_t gdn_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
     const long nsplit = n_tokens / g_seg_len(n_seqs, n_tokens, n_heads);
     return 2 * al256(sizeof(int32_t) * (n_seqs + 1)) +
-           2 * static_cast<size_t>(nsplit) * n_heads * D * D * sizeof(float);
+           3 * static_cast<size_t>(nsplit) * n_heads * D * D * sizeof(float);
 }
 
 // The fp16 T planes take the first n_chunks_max * H * 8 KiB of the plane
 // region; their inverse scales (one float per (chunk, head)) follow.
 float* plane_scales(const uint16_t* planes, long n_chunks_max, int H) {
     return const_cast<float*>(reinterpret_cast<const float*>(planes + n_chunks_max * H * kPlaneElems));
+}
+
+// The chunk offsets (coff, ahead of gdn_seg_prep) and the segment and
+// split-segment offsets of launch_gdn_seg, in one launch.
+hipError_t launch_gdn_seg_offsets(const ChunkArgs& a, int32_t* coff, void* seg_ws, hipStream_t s) {
+    const int lseg = g_seg_len(a.n_seqs, a.n_tokens, a.n_heads);
+    char* ws = static_cast<char*>(seg_ws);
+    int32_t* seg_off = reinterpret_cast<int32_t*>(ws);
+    int32_t* split_off = reinterpret_cast<int32_t*>(ws + al256(sizeof(int32_t) * (a.n_seqs + 1)));
+    const SpanScans sc{{SpanScan{CH, 0, 0, coff}, SpanScan{lseg, 1, 0, seg_off}, SpanScan{lseg, 0, 1, split_off}}};
+    hipLaunchKernelGGL(span_offsets_multi, dim3(3), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, sc);
+    return hipGetLastError();
 }
 
 hipError_t launch_gdn_seg_prep(const ChunkArgs& a, const int32_t* coff, uint16_t* planes, long n_chunks_max,
@@ -998,16 +1076,11 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
     ws += al256(sizeof(int32_t) * (a.n_seqs + 1));
     float* wsS = reinterpret_cast<float*>(ws);
     float* wsM = wsS + static_cast<size_t>(nsplit) * a.n_heads * D * D;
-    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 1, 0,
-                       seg_off, nullptr);
-    hipLaunchKernelGGL(span_offsets, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, lseg, 0, 1,
-                       split_off, nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    float* wsI = wsM + static_cast<size_t>(nsplit) * a.n_heads * D * D;
     const SegArgs sa{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads,
                      a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, coff, seg_off, split_off, planes,
-                     plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM,
+                     plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM, wsI,
                      Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.o};
     const int n1 = static_cast<int>(nsplit * a.n_heads);
     const dim3 grid_a(static_cast<unsigned>(n1 + maxseg * a.n_heads));
@@ -1015,9 +1088,15 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
     auto passes = [&](auto ka, auto kb) {
         hipLaunchKernelGGL(ka, grid_a, dim3(NTH), 0, s, sa, n1);
         if (nsplit > 0) {
-            hipLaunchKernelGGL(gdn_seg_scan, dim3(static_cast<unsigned>(n1)), dim3(NTH), 0, s, a.cu_seqlens,
-                               a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init,
-                               split_off, nsplit, wsS, wsM);
+            // one column block per scan workgroup while that leaves the GPU
+            // mostly idle, two once there are many (sequence, head) pairs
+            auto scan = [&](auto kern, int groups) {
+                hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((n1 + 7) / 8 * 8 * groups)), dim3(NTH), 0, s,
+                                   a.n_seqs, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, split_off,
+                                   nsplit, wsS, wsM, wsI);
+            };
+            if (static_cast<long>(a.n_seqs) * a.n_heads <= 32) scan(gdn_seg_scan<1>, 8);
+            else scan(gdn_seg_scan<2>, 4);
             hipLaunchKernelGGL(kb, grid_b, dim3(NTH), 0, s, sa);
         }
     };

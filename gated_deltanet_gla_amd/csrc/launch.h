@@ -100,6 +100,7 @@ hipError_t launch_lin_attn_seg(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_gdn_chunk(const ChunkArgs& a, hipStream_t s);
 size_t gdn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
 size_t gdn_seg_workspace(int n_seqs, int n_tokens, int n_heads);
+hipError_t launch_gdn_seg_offsets(const ChunkArgs& a, int32_t* coff, void* seg_ws, hipStream_t s);
 hipError_t launch_gdn_seg_prep(const ChunkArgs& a, const int32_t* chunk_off, uint16_t* planes, long n_chunks_max,
                                hipStream_t s);
 hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* chunk_off, const uint16_t* planes, long n_chunks_max,
