@@ -192,16 +192,34 @@ __device__ __forceinline__ bf16x8 f16_pair(const f32x4& a, const f32x4& b, float
 struct Scale {
     float s, inv;
 };
+// Maximum of a non-negative float over the wave, as a wave-uniform value:
+// integer maxima of the bit patterns (the same order for x >= 0) within each
+// row of 16 lanes by DPP, then over the four rows' lanes 0, 16, 32, 48.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    int v = __float_as_int(x);
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false));    // quad_perm [1,0,3,2]
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false));    // quad_perm [2,3,0,1]
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false));   // row_ror:4
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false));   // row_ror:8
+    const int r = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                      max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+    return __int_as_float(r);
+}
 __device__ __forceinline__ Scale range_scale(float local_max) {
-    float m = local_max;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float m = wave_max_nonneg(local_max);
     const int eb = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu);   // m < 2^(eb - 126)
     const int sf = clampi(268 - eb, 1, 253);                               // s = 2^(141 - eb)
     return {__uint_as_float(static_cast<uint32_t>(sf) << 23), __uint_as_float(static_cast<uint32_t>(254 - sf) << 23)};
 }
+// max(m, |a|, |b|) as two medians against +inf (v_med3_f32 with the
+// absolute values as source modifiers): fmaxf would first quiet each |x|
+// against signalling NaN, one more instruction per value
+__device__ __forceinline__ float absmax3(float m, float a, float b) {
+    constexpr float inf = __builtin_inff();
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(fabsf(a), fabsf(b), inf), m, inf);
+}
 __device__ __forceinline__ float absmax4(const f32x4& v, float m) {
-    return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+    return absmax3(absmax3(m, v.x, v.y), v.z, v.w);
 }
 
 // Registers -> LDS: a 64 x 128 tile, as it is (bf16) or converted to fp16.
