@@ -79,6 +79,10 @@ constexpr int LP = CH + 8;         // P and T diag(beta)
 constexpr int kTargetBlocks = 256; // about one workgroup per compute unit
 constexpr int kPlaneElems = CH * CH;       // T diag(beta) (fp16) per (chunk, head)
 
+// 2^x by the hardware instruction alone (exp2f adds a rescaling for results
+// below 2^-126, which here are decay factors as good as zero).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // One chunk of the global inputs in registers: 2 x 16 bytes per thread of
 // each 64 x 128 bf16 tile, 16 bytes of the 8 KiB fp16 T diag(beta) plane,
 // and the gate of token `lane` (wave 0).
@@ -158,9 +162,9 @@ __device__ __forceinline__ void g_stage_gates(float* g2, float* eg, float* dec, 
         const float x = wave_inclusive_sum(__log2f(fmaxf(a, kMinDecay)));
         const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), CH - 1));
         if (g2) g2[lane] = x;
-        if (eg) eg[lane] = exp2f(x);
-        dec[lane] = exp2f(glast - x);
-        if (lane == 0) *gamma = exp2f(glast);
+        if (eg) eg[lane] = hw_exp2(x);
+        dec[lane] = hw_exp2(glast - x);
+        if (lane == 0) *gamma = hw_exp2(glast);
     }
 }
 
@@ -514,7 +518,7 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = tt * 16 + ap.row0 + r;
-                    As[wave][i][j] = (j < i) ? bs[wave][i] * exp2f(gs[wave][i] - gj) * acc[r] : 0.f;
+                    As[wave][i][j] = (j < i) ? bs[wave][i] * hw_exp2(gs[wave][i] - gj) * acc[r] : 0.f;
                 }
             }
         }
@@ -915,7 +919,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = jt * 16 + ap.row0 + r;
-            pt[r] = (jj <= i) ? pt[r] * exp2f(gi - kk.g2[jj]) : 0.f;
+            pt[r] = (jj <= i) ? pt[r] * hw_exp2(gi - kk.g2[jj]) : 0.f;
         }
         *reinterpret_cast<u32x2*>(&sp[i][jt * 16 + ap.row0]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
     };
