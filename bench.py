@@ -717,6 +717,7 @@ def main():
                                                      "prefill_tokens", "longest_prompt", "GBps",
                                                      "per_call_ms")}
         other["mixed_gdn_step"]["hbm_frac"] = r["GBps"] / HBM_PEAK_GBPS
+        other["mixed_gdn_step"]["traffic"] = measured_traffic("mixed_gdn_step")
     if other:
         out["other_workloads"] = other
     if "copy" in res:

@@ -36,7 +36,7 @@ def _check(t, name, dtype=None, dims=None):
         raise ValueError(f"{name} must be a tensor")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, has {t.dim()}")
-    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+    if dtype is not None and t.dtype is not dtype and (type(dtype) is not tuple or t.dtype not in dtype):
         raise ValueError(f"{name} has dtype {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -44,9 +44,13 @@ def _check(t, name, dtype=None, dims=None):
 
 def _shape(t, name, *dims):
     """t.shape must equal dims (None: any size)."""
-    if t.dim() != len(dims) or any(d is not None and s != d for s, d in zip(t.shape, dims)):
-        want = "[" + ", ".join("*" if d is None else str(d) for d in dims) + "]"
-        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    s = t.shape
+    if s == dims:
+        return
+    if len(s) == len(dims) and all(d is None or a == d for a, d in zip(s, dims)):
+        return
+    want = "[" + ", ".join("*" if d is None else str(d) for d in dims) + "]"
+    raise ValueError(f"{name} has shape {list(s)}, expected {want}")
 
 
 def _devices(*named):
@@ -56,12 +60,13 @@ def _devices(*named):
     for name, t in named:
         if t is None:
             continue
-        if not t.is_cuda:
+        g = t.get_device()
+        if g < 0:
             raise ValueError(f"{name} must be a device tensor")
         if dev is None:
-            dev = t.device
-        elif t.device != dev:
-            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+            dev = g
+        elif g != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on device {dev}")
 
 
 def _ws_check(workspace):
@@ -262,10 +267,48 @@ def workspace_bytes(kind, n_seqs, n_tokens, n_heads, dk, dv, chunk):
     return getattr(_lib.lib(), fn)(n_seqs, n_tokens, n_heads, dk, dv, chunk)
 
 
+def _decode_fast_ok(q, k, v, alpha, state_pool, slot_idx, out_dtype, o, beta):
+    """The common case of a decode call in one pass of cheap tests: every
+    tensor given, contiguous, of the expected dtype and shape, all on one
+    device.  False sends the call through the per-tensor checks, which name
+    what is wrong."""
+    try:
+        if o is None or alpha is None or (out_dtype is not None and out_dtype is not o.dtype):
+            return False
+        dt = q.dtype
+        if dt is not torch.bfloat16 and dt is not torch.float32:
+            return False
+        qs = q.shape
+        if len(qs) != 3 or k.shape != qs or k.dtype is not dt or v.dtype is not dt:
+            return False
+        R, H, dk = qs
+        vs = v.shape
+        if len(vs) != 3 or vs[0] != R or vs[1] != H or o.shape != vs:
+            return False
+        ps = state_pool.shape
+        if len(ps) != 4 or ps[1] != H or ps[2] != dk or ps[3] != vs[2]:
+            return False
+        if (alpha.shape != (R, H) or alpha.dtype is not torch.float32 or state_pool.dtype is not torch.float32
+                or slot_idx.shape != (R,) or slot_idx.dtype is not torch.int32):
+            return False
+        ts = (q, k, v, alpha, state_pool, slot_idx, o)
+        if beta is not None:
+            if beta.shape != (R, H) or beta.dtype is not torch.float32:
+                return False
+            ts += (beta,)
+        g = q.get_device()
+        return g >= 0 and all(t.is_contiguous() and t.get_device() == g for t in ts)
+    except AttributeError:          # something that is not a tensor
+        return False
+
+
 def _decode_common(q, k, v, alpha, state_pool, slot_idx, out_dtype, o, beta=None, extra=()):
     """Checks of the one-token decode entry points: q, k [R, H, dk]; v, o
     [R, H, dv]; alpha (and beta) [R, H]; state_pool [n_slots, H, dk, dv];
     slot_idx [R]; everything on one device."""
+    if _decode_fast_ok(q, k, v, alpha, state_pool, slot_idx, out_dtype, o, beta) and not extra:
+        R, H, dk = q.shape
+        return R, H, dk, v.shape[2], o.dtype, o
     for t, n, d, nd in [(q, "q", (torch.float32, torch.bfloat16), 3),
                         (k, "k", (torch.float32, torch.bfloat16), 3),
                         (v, "v", (torch.float32, torch.bfloat16), 3),

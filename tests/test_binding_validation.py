@@ -102,6 +102,59 @@ def test_decode_shape_mismatch_refused(case):
     assert "device tensor" not in str(e.value)
 
 
+class _OnDevice0(torch.Tensor):
+    """A CPU tensor that reports device index 0, so the decode fast path's
+    shape and dtype tests can be exercised without a GPU."""
+
+    def get_device(self):
+        return 0
+
+
+def _dev0(t):
+    return torch.Tensor._make_subclass(_OnDevice0, t)
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_decode_fast_path_accepts_only_valid_calls(gdn):
+    """The one-pass test that lets a valid decode call skip the per-tensor
+    checks accepts the valid call and nothing else: every mismatch of the
+    table above, a wrong dtype, a non-contiguous tensor, a missing output
+    and a tensor on another device send the call to the detailed checks."""
+    from gated_deltanet_gla_amd import ops
+
+    def args(**over):
+        a = decode_args(**over)
+        a = {n: _dev0(t) for n, t in a.items()}
+        a["o"] = _dev0(over.get("o", torch.zeros(B, H, D, dtype=bf)))
+        a["beta"] = _dev0(over.get("beta", torch.ones(B, H))) if gdn else None
+        return a
+
+    def ok(a, out_dtype=None):
+        return ops._decode_fast_ok(a["q"], a["k"], a["v"], a["alpha"], a["state_pool"], a["slot_idx"],
+                                   out_dtype, a["o"], a["beta"])
+
+    assert ok(args())
+    assert ok(args(), out_dtype=bf)
+    assert not ok(args(), out_dtype=f32)
+    for case, over in DECODE_BAD.items():
+        assert not ok(args(**over)), case
+    assert not ok(args(k=torch.zeros(B, H, D, dtype=f32)))
+    assert not ok(args(q=torch.zeros(B, H, D, dtype=torch.float16), k=torch.zeros(B, H, D, dtype=torch.float16),
+                       v=torch.zeros(B, H, D, dtype=torch.float16)))
+    assert not ok(args(alpha=torch.ones(B, H, dtype=torch.float64)))
+    assert not ok(args(slot_idx=torch.tensor([0, 3], dtype=torch.int64)))
+    assert not ok(args(o=torch.zeros(B, H, D + 16, dtype=bf)))
+    assert not ok(args(v=torch.zeros(B, D, H, dtype=bf).transpose(1, 2)))
+    if gdn:
+        assert not ok(args(beta=torch.ones(B, H + 1)))
+    a = args()
+    a["o"] = None
+    assert not ok(a)
+    a = args()
+    a["state_pool"] = torch.zeros(NS, H, D, D)          # reports no device
+    assert not ok(a)
+
+
 def test_multi_and_norm_pool_and_conv_shapes_refused():
     J = 3
     q = torch.zeros(B, J, H, D, dtype=bf)
