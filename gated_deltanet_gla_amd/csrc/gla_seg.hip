@@ -71,6 +71,8 @@ constexpr int LQ = SD + 8;         // 68 dwords
 constexpr int LK = SD + 16;        // 72 dwords
 constexpr int SP = SC + 8;         // LDS line of a P row (36 dwords)
 constexpr int kSegBlocks = 256;    // one workgroup on each of the 256 compute units
+constexpr int kShortChunks = 4;    // batches of sequences this short (mean chunks) ...
+constexpr int kMaxItems = 16;      // ... put up to this many heads in one output-pass block
 
 struct KVBuf {                     // pass 1 staging
     alignas(16) uint16_t k[SC][LK];
@@ -104,17 +106,16 @@ struct SegGeom {
     long ws_first;     // slot of the sequence's first segment
 };
 
-// Which (sequence, segment, head) this block works on; false (for the whole
-// block) if none.  Segment s of the call belongs to the sequence b whose
+// Which (sequence, segment, head) work item bid = segment * H + head is;
+// false (for the whole block) if none.  Segment s of the call belongs to the sequence b whose
 // exclusive prefix sum of max(1, ceil(L_b / lseg)) covers s; the block
 // computes that prefix sum itself (threads sum contiguous ranges of
 // sequences, then a wave scan and a scan of the wave totals).
 __device__ __forceinline__ bool seg_geometry(SegGeom& sg, const int32_t* cu, int n_seqs, int n_tokens,
                                              int H, int lseg, const int32_t* slot_idx, int n_slots,
-                                             int* sh) {
-    const int h = blockIdx.x % H;
-    const int si = blockIdx.x / H;
-    const int maxseg = gridDim.x / H;
+                                             int* sh, int bid, int maxseg) {
+    const int h = bid % H;
+    const int si = bid / H;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     auto count = [&](int b) {
         const int s = clampi(cu[b], 0, n_tokens);
@@ -530,7 +531,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             typename TO::T* __restrict__ o) {
     __shared__ int sh[SW + 4];
     SegGeom sg;
-    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh)) return;
+    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh, blockIdx.x, gridDim.x / H)) return;
     __shared__ QKVBuf buf[2];
     __shared__ uint16_t pbuf[2][SC][SP];           // P = (Q K^T) .* D, hi and lo planes
     // bf16 outputs of the previous chunk, stored to HBM as whole rows
@@ -806,6 +807,288 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     }
 }
 
+// The output pass for batches of short prompts (plain GLA, no checkpoints):
+// a block takes `items` work items, heads h0 .. h0 + items - 1 of one
+// segment (items divides H).  Their chunks form one stream, item after
+// item, so the next item's first loads are in flight while the current
+// item's last chunk runs, and a batch of short prompts does not pay a
+// block's start-up and drain per (sequence, head).  Between items the
+// final state of one goes out and the entry state of the next comes in;
+// entry states of split sequences are folded from the workspace there.
+template <class TO>
+__global__ void __launch_bounds__(ST)
+gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                  const uint16_t* __restrict__ v, const float* __restrict__ alpha, const int32_t* __restrict__ cu,
+                  int n_seqs, int n_tokens, int H, float* __restrict__ pool, int n_slots,
+                  const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
+                  const float* __restrict__ wstate, const float* __restrict__ wlam, int items,
+                  typename TO::T* __restrict__ o) {
+    __shared__ int sh[SW + 4];
+    SegGeom sg;
+    if (!seg_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, sh, blockIdx.x * items,
+                      gridDim.x * items / H))
+        return;
+    __shared__ QKVBuf buf[2];
+    __shared__ uint16_t pbuf[2][SC][SP];           // P = (Q K^T) .* D, hi and lo planes
+    // bf16 outputs of the previous chunk, stored to HBM as whole rows
+    __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LQ];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const AccPos ap;
+    const int col = wave * 16;
+    const long stride = static_cast<long>(H) * SD;
+    const bool last_seg = sg.g == sg.nseg - 1;
+
+    const int nch = (sg.t1 - sg.t0 + SC - 1) / SC;
+    auto rows = [&](int c) { return c < nch ? min(SC, sg.t1 - sg.t0 - c * SC) : 0; };
+    auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * SC; };
+    // the loads of chunk c of item it (nothing past the last item)
+    SegPrefetch<true> pf;
+    auto fetch = [&](int c, int it) {
+        seg_fetch<true, true>(pf, q, k, v, alpha, tok(c), it < items ? rows(c) : 0, sg.h + min(it, items - 1), H);
+    };
+    // the position `ahead` chunks after chunk c of item it (past the last
+    // item when the segment has no chunks: the stream is empty)
+    auto step = [&](int c, int it, int ahead, int& c2, int& it2) {
+        c2 = c + ahead;
+        it2 = it;
+        if (nch <= 0) {
+            c2 = 0;
+            it2 = items;
+            return;
+        }
+        while (c2 >= nch) {
+            c2 -= nch;
+            ++it2;
+        }
+    };
+    fetch(0, 0);     // in flight during the fold
+
+    // ---- entry state of item it
+    f32x4 S[8];
+    // a pool state through a buffer resource: the lane's offset in one
+    // register, each of its 32 rows a scalar offset (no per-row addresses)
+    const uint32_t lane_off = static_cast<uint32_t>((ap.row0 * SD + col + ap.col) * 4);
+    auto pool_state = [&](int it) {
+        return BufRsrc(pool + (static_cast<long>(sg.slot) * H + sg.h + it) * SD * SD, SD * SD * 4);
+    };
+    auto entry = [&](int it) {
+        if (sg.nseg <= 1) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!zero_init) {
+                const BufRsrc rs = pool_state(it);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (mt * 16 + r) * SD * 4);
+            }
+        } else {
+            const float* s0 = frag_slot(wstate, sg.ws_first + it + static_cast<long>(sg.nseg - 1) * H);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
+            for (int j = 0; j < sg.g; ++j) {
+                const long sj = sg.ws_first + it + static_cast<long>(j) * H;
+                const float dcy = exp2f(wlam[sj]);
+                const float* dS = frag_slot(wstate, sj);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
+            }
+        }
+    };
+    // the final state of item it (this wave's columns), last segment only
+    auto final_state = [&](int it) {
+        const BufRsrc rs = pool_state(it);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (mt * 16 + r) * SD * 4);
+    };
+    entry(0);
+    // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
+    // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
+    for (int idx = tid; idx < 2 * 256; idx += ST) {
+        const int t = idx >> 8, e = idx & 255;
+        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+        pbuf[0][row][cx] = 0;
+        pbuf[1][row][cx] = 0;
+    }
+    seg_stage<true, false>(buf[0], pf);
+    {
+        int c1, i1;
+        step(0, 0, 1, c1, i1);
+        fetch(c1, i1);
+    }
+    lds_barrier();
+
+    // P tile t of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3):
+    // operand reads, then the MFMAs and the decay / mask / split epilogue
+    auto tile_it = [](int t) { return t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3)); };
+    auto p_load = [&](const QKVBuf& bb, int t, bf16x8 (&pa)[4], bf16x8 (&pb)[4]) {
+        const int it = tile_it(t), jt = t - it * (it + 1) / 2;
+#pragma unroll
+        for (int ks = 0; ks < SD / 32; ++ks) {
+            pa[ks] = frag_kc(&bb.k[0][0], LK, jt * 16, 32 * ks);
+            pb[ks] = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * ks);
+        }
+    };
+    auto p_finish = [&](const QKVBuf& bb, int t, const bf16x8 (&pa)[4], const bf16x8 (&pb)[4]) {
+        const int it = tile_it(t), jt = t - it * (it + 1) / 2;
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < SD / 32; ++ks) pt = mfma_bf16(pa[ks], pb[ks], pt);
+        const int i = it * 16 + ap.col;
+        const float gi = bb.g2[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = jt * 16 + ap.row0 + r;
+            pt[r] = (j <= i) ? pt[r] * exp2f(gi - bb.g2[j]) : 0.f;
+        }
+        Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
+    };
+
+    // bf16 outputs of chunk cc of item it: LDS -> HBM, 16 lanes per 256-byte row
+    auto flush_o = [&](int cc, int it) {
+        if constexpr (TO::bytes == 2) {
+            const BufRsrc ro(o + tok(cc) * stride + (sg.h + it) * SD, rows_extent(rows(cc), stride * 2, SD * 2));
+#pragma unroll
+            for (int u = 0; u < SC * SD / 8 / ST; ++u) {
+                const int x = tid + u * ST, row = x / (SD / 8), vc = (x % (SD / 8)) * 8;
+                ro.store_b128(*reinterpret_cast<const u32x4*>(&obuf[row][vc]),
+                              static_cast<uint32_t>((row * stride + vc) * 2));
+            }
+        }
+    };
+
+    const int total = items * nch;
+    int c = 0, item = 0;             // chunk and item of stream position vc
+    int pc = 0, pitem = 0;           // those of the position before
+    for (int vc = 0; vc < total; ++vc) {
+        const QKVBuf& bb = buf[vc & 1];
+        const int n = rows(c);
+        const long tok0 = tok(c);
+        const int hk = sg.h + item;
+        if (vc > 0) flush_o(pc, pitem);
+
+        // ---- phase 1: P tiles (split over the waves) -> LDS, and
+        // O^T = S^T Q^T for this wave's columns (the state accumulator tiles
+        // serve as the A operand directly: rows = columns of S)
+        bf16x8 pa[4], pb[4], qf[4][4];
+        p_load(bb, wave, pa, pb);
+#pragma unroll
+        for (int s = 0; s < SD / 32; ++s)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) qf[s][it] = frag_kc_split(&bb.q[0][0], LQ, it * 16, 32 * s);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 sh8[4], sl8[4];
+#pragma unroll
+        for (int s = 0; s < SD / 32; ++s) {
+            s16x4 h0, l0, h1, l1;
+            split4(S[2 * s], h0, l0);
+            split4(S[2 * s + 1], h1, l1);
+            sh8[s] = cat8(h0, h1);
+            sl8[s] = cat8(l0, l1);
+        }
+        f32x4 ot[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) ot[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < SD / 32; ++s)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                ot[it] = mfma_bf16(sh8[s], qf[s][it], ot[it]);
+                ot[it] = mfma_bf16(sl8[s], qf[s][it], ot[it]);
+            }
+        p_finish(bb, wave, pa, pb);
+        if (wave + SW < 10) {
+            p_load(bb, wave + SW, pa, pb);
+            p_finish(bb, wave + SW, pa, pb);
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) ot[it] *= bb.eg[it * 16 + ap.col];
+        lds_barrier();
+
+        // ---- phase 2: + V^T P^T (split k order on both operands), outputs,
+        // state update, next chunk
+        bf16x8 vf[2], pp[6][2];
+        load_vt(vf, bb, col);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            pp[it][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 0);
+            pp[it][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 0);
+        }
+#pragma unroll
+        for (int it = 2; it < 4; ++it) {
+            pp[it + 2][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 32);
+            pp[it + 2][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 32);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the state update's operand reads and VALU work go ahead of the
+        // P V MFMAs, which do not depend on them, so they can overlap
+        SegUpd up;
+        seg_update_prep(up, S, bb, vf);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
+            ot[it] = mfma_bf16(vf[0], pp[it][1], ot[it]);
+        }
+#pragma unroll
+        for (int it = 2; it < 4; ++it) {
+            ot[it] = mfma_bf16(vf[1], pp[it + 2][0], ot[it]);
+            ot[it] = mfma_bf16(vf[1], pp[it + 2][1], ot[it]);
+        }
+        // lane: token it*16 + (lane % 16), columns col + 4 (lane / 16) .. +3
+        if constexpr (TO::bytes == 2) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                *reinterpret_cast<u32x2*>(&obuf[it * 16 + ap.col][col + ap.row0]) =
+                    u32x2{pack_bf16x2(ot[it][0], ot[it][1]), pack_bf16x2(ot[it][2], ot[it][3])};
+        } else {
+            const BufRsrc ro(o + tok0 * stride + hk * SD, rows_extent(n, stride * 4, SD * 4));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
+                              static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
+        }
+        // the next chunk's rows go to LDS between the two halves of the
+        // update's MFMAs, the gate scan after them
+        seg_update_mfma_half(S, up, 0);
+        seg_stage_rows<true, false>(buf[(vc + 1) & 1], pf);
+        seg_update_mfma_half(S, up, 1);
+        seg_stage_gates<true, false>(buf[(vc + 1) & 1], pf);
+        const bool item_end = c == nch - 1;
+        {
+            int c2, i2;
+            step(c, item, 2, c2, i2);
+            fetch(c2, i2);
+        }
+        if (item_end) {
+            if (last_seg) final_state(item);
+            if (item + 1 < items) entry(item + 1);
+        }
+        pc = c;
+        pitem = item;
+        if (item_end) {
+            c = 0;
+            ++item;
+        } else {
+            ++c;
+        }
+        lds_barrier();
+    }
+    if (nch > 0) flush_o(pc, pitem);
+    if (nch == 0) {
+        // empty sequence: every item's state goes back as it came in (after
+        // the loop, which does not run: placed before it, this code made
+        // the loop's register allocation spill)
+        for (int it = 0; it < items; ++it) {
+            if (it > 0) entry(it);
+            if (last_seg) final_state(it);
+        }
+    }
+}
+
 // Every sequence gets at least one segment (an empty one still writes its
 // state back).  Segment length: whole chunks, at least 4 of them, about
 // kSegBlocks workgroups in total.
@@ -819,6 +1102,18 @@ int seg_len(int n_tokens, int n_heads) {
 __host__ __device__ constexpr size_t align256s(size_t x) { return (x + 255) & ~size_t(255); }
 
 long seg_count_bound(int n_seqs, int n_tokens, int lseg) { return n_tokens / lseg + n_seqs; }
+
+// Work items (heads of one segment) per output-pass block: 1 unless the
+// batch is short sequences (at most kShortChunks chunks on average); then
+// the largest divisor of H up to kMaxItems that still launches at least
+// kSegBlocks blocks, one per compute unit.
+int seg_items(int n_seqs, int n_tokens, int n_heads, long maxseg) {
+    if (n_seqs <= 0 || static_cast<long>(n_tokens) > static_cast<long>(n_seqs) * kShortChunks * SC) return 1;
+    int best = 1;
+    for (int k = 2; k <= kMaxItems && k <= n_heads; ++k)
+        if (n_heads % k == 0 && maxseg * n_heads / k >= kSegBlocks) best = k;
+    return best;
+}
 
 }  // namespace
 
@@ -860,6 +1155,23 @@ hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
+    // several heads per block for batches of short prompts (plain GLA; the
+    // checkpoint and normalised variants keep one)
+    if constexpr (!NORM) {
+        const int items = ck.slots ? 1 : seg_items(a.n_seqs, a.n_tokens, a.n_heads, maxseg);
+        if (items > 1) {
+            auto multi = [&](auto kern, auto* o) {
+                hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(maxseg * a.n_heads / items)), dim3(ST), 0, s,
+                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                                   static_cast<const uint16_t*>(a.v), alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
+                                   a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam,
+                                   items, o);
+            };
+            if (a.out_bf16) multi(gla_seg_out_multi<BF16>, static_cast<uint16_t*>(a.o));
+            else multi(gla_seg_out_multi<F32>, static_cast<float*>(a.o));
+            return hipGetLastError();
+        }
+    }
     auto out_pass = [&](auto kern, auto* o) {
         hipLaunchKernelGGL(kern, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), alpha,
