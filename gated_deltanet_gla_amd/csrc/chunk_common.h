@@ -407,6 +407,9 @@ struct BufRsrc {
     __device__ __forceinline__ void storef(float v, uint32_t off, uint32_t soff) const {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, soff, 0);
     }
+    __device__ __forceinline__ void store_b128(u32x4 v, uint32_t off, uint32_t soff) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, 0);
+    }
     __device__ __forceinline__ void store_b16_nt(uint16_t v, uint32_t off) const {
         __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kNT);
     }

@@ -815,12 +815,12 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 // block's start-up and drain per (sequence, head).  Between items the
 // final state of one goes out and the entry state of the next comes in;
 // entry states of split sequences are folded from the workspace there.
-template <class TO>
+template <class TO, bool ZERO>
 __global__ void __launch_bounds__(ST)
 gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ alpha, const int32_t* __restrict__ cu,
                   int n_seqs, int n_tokens, int H, float* __restrict__ pool, int n_slots,
-                  const int32_t* __restrict__ slot_idx, int zero_init, int lseg,
+                  const int32_t* __restrict__ slot_idx, int lseg,
                   const float* __restrict__ wstate, const float* __restrict__ wlam, int items,
                   typename TO::T* __restrict__ o) {
     __shared__ int sh[SW + 4];
@@ -877,7 +877,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         if (sg.nseg <= 1) {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!zero_init) {
+            if constexpr (!ZERO) {
                 const BufRsrc rs = pool_state(it);
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt)
@@ -897,6 +897,16 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             }
         }
     };
+    // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
+    // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
+    auto zero_p_upper = [&]() {
+        for (int idx = tid; idx < 2 * 256; idx += ST) {
+            const int t = idx >> 8, e = idx & 255;
+            const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+            pbuf[0][row][cx] = 0;
+            pbuf[1][row][cx] = 0;
+        }
+    };
     // the final state of item it (this wave's columns), last segment only
     auto final_state = [&](int it) {
         const BufRsrc rs = pool_state(it);
@@ -905,15 +915,59 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
             for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (mt * 16 + r) * SD * 4);
     };
+    // Between item it and item it + 1 (all threads, after a barrier that
+    // ends every read of the free chunk buffer fb and of pbuf; ends with the
+    // P tiles that must stay zero zeroed again, which the next chunk's P V
+    // reads after its own barrier).  The final state of item it (last
+    // segment only) goes through LDS into rows (rows 0-95 over fb, 96-127
+    // over pbuf, kRow floats a row) and out as whole 512-byte rows, 16 bytes
+    // a lane, instead of 32 scattered 4-byte stores per lane.  The next
+    // item's entry state is loaded into S before those stores are issued,
+    // and S is used (an empty asm) after them: the load-counter wait for it
+    // then leaves the stores in flight, and none is needed at the top of
+    // the chunk loop, where it would wait for them.  With ZERO (zero_init)
+    // a one-segment entry state is zeros: no loads, no wait.
+    constexpr int kRow = SD + 4;
+    static_assert(96 * kRow * 4 <= sizeof(QKVBuf) && 32 * kRow * 4 <= sizeof(pbuf), "state staging");
+    auto next_item = [&](int it, QKVBuf& fb) {
+        float* lo = reinterpret_cast<float*>(&fb);
+        float* hi = reinterpret_cast<float*>(&pbuf[0][0][0]);
+        // lane offsets recomputed here (opaque), not held across the chunk loop
+        if (last_seg) {
+            const int wo = opaque(ap.row0 * kRow + col + ap.col);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                float* base = (mt < 6 ? lo + mt * 16 * kRow : hi + (mt - 6) * 16 * kRow) + wo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) base[r * kRow] = S[mt][r];
+            }
+        }
+        if (it + 1 < items) entry(it + 1);
+        lds_barrier();
+        {
+            // issued on every path (an empty range when this is not the
+            // last segment), for the same reason as the output flush
+            const BufRsrc rs(pool + (static_cast<long>(sg.slot) * H + sg.h + it) * SD * SD,
+                             last_seg ? SD * SD * 4 : 0u);
+            const int t = opaque(tid);
+            const int ro = (t >> 5) * kRow + (t & 31) * 4;
+            const uint32_t go = static_cast<uint32_t>(((t >> 5) * SD + (t & 31) * 4) * 4);
+#pragma unroll
+            for (int u = 0; u < SD / (ST / 32); ++u) {
+                const float* src = (u < 6 ? lo + u * 16 * kRow : hi + (u - 6) * 16 * kRow) + ro;
+                rs.store_b128(*reinterpret_cast<const u32x4*>(src), go, static_cast<uint32_t>(u * 16 * SD * 4));
+            }
+        }
+        if constexpr (!ZERO) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                asm volatile("" ::"v"(S[mt][0]), "v"(S[mt][1]), "v"(S[mt][2]), "v"(S[mt][3]));
+        }
+        lds_barrier();
+        zero_p_upper();
+    };
     entry(0);
-    // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
-    // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
-    for (int idx = tid; idx < 2 * 256; idx += ST) {
-        const int t = idx >> 8, e = idx & 255;
-        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
-        pbuf[0][row][cx] = 0;
-        pbuf[1][row][cx] = 0;
-    }
+    zero_p_upper();
     seg_stage<true, false>(buf[0], pf);
     {
         int c1, i1;
@@ -948,10 +1002,15 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
     };
 
-    // bf16 outputs of chunk cc of item it: LDS -> HBM, 16 lanes per 256-byte row
-    auto flush_o = [&](int cc, int it) {
+    // bf16 outputs of chunk cc of item it: LDS -> HBM, 16 lanes per 256-byte
+    // row.  Issued every chunk, before the first with nothing to write (an
+    // empty range: no memory traffic), so that every path through the loop
+    // has the same vector-memory operations and the load-counter waits for
+    // the prefetched rows can leave younger stores in flight.
+    auto flush_o = [&](int cc, int it, bool live) {
         if constexpr (TO::bytes == 2) {
-            const BufRsrc ro(o + tok(cc) * stride + (sg.h + it) * SD, rows_extent(rows(cc), stride * 2, SD * 2));
+            const BufRsrc ro(o + tok(cc) * stride + (sg.h + it) * SD,
+                             live ? rows_extent(rows(cc), stride * 2, SD * 2) : 0u);
 #pragma unroll
             for (int u = 0; u < SC * SD / 8 / ST; ++u) {
                 const int x = tid + u * ST, row = x / (SD / 8), vc = (x % (SD / 8)) * 8;
@@ -969,7 +1028,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         const int n = rows(c);
         const long tok0 = tok(c);
         const int hk = sg.h + item;
-        if (vc > 0) flush_o(pc, pitem);
+        flush_o(pc, pitem, vc > 0);
 
         // ---- phase 1: P tiles (split over the waves) -> LDS, and
         // O^T = S^T Q^T for this wave's columns (the state accumulator tiles
@@ -1063,10 +1122,8 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             step(c, item, 2, c2, i2);
             fetch(c2, i2);
         }
-        if (item_end) {
-            if (last_seg) final_state(item);
-            if (item + 1 < items) entry(item + 1);
-        }
+        lds_barrier();
+        if (item_end) next_item(item, buf[vc & 1]);
         pc = c;
         pitem = item;
         if (item_end) {
@@ -1075,9 +1132,8 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         } else {
             ++c;
         }
-        lds_barrier();
     }
-    if (nch > 0) flush_o(pc, pitem);
+    if (nch > 0) flush_o(pc, pitem, true);
     if (nch == 0) {
         // empty sequence: every item's state goes back as it came in (after
         // the loop, which does not run: placed before it, this code made
@@ -1164,11 +1220,15 @@ hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
                 hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(maxseg * a.n_heads / items)), dim3(ST), 0, s,
                                    static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                    static_cast<const uint16_t*>(a.v), alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
-                                   a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, wstate, wlam,
-                                   items, o);
+                                   a.n_heads, a.pool, a.n_slots, a.slot_idx, lseg, wstate, wlam, items, o);
             };
-            if (a.out_bf16) multi(gla_seg_out_multi<BF16>, static_cast<uint16_t*>(a.o));
-            else multi(gla_seg_out_multi<F32>, static_cast<float*>(a.o));
+            if (a.zero_init) {
+                if (a.out_bf16) multi(gla_seg_out_multi<BF16, true>, static_cast<uint16_t*>(a.o));
+                else multi(gla_seg_out_multi<F32, true>, static_cast<float*>(a.o));
+            } else {
+                if (a.out_bf16) multi(gla_seg_out_multi<BF16, false>, static_cast<uint16_t*>(a.o));
+                else multi(gla_seg_out_multi<F32, false>, static_cast<float*>(a.o));
+            }
             return hipGetLastError();
         }
     }
