@@ -138,7 +138,9 @@ size_t gla_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_hea
 
 size_t lin_attn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
                                       int32_t dk, int32_t dv, int32_t chunk) {
-    return gla_chunk_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    if (n_seqs < 0 || n_tokens < 0 || n_heads < 1 || !is_dim(dk) || !is_dim(dv) || !is_chunk(chunk))
+        return 0;
+    return gla::lin_attn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
 }
 
 size_t gdn_chunk_workspace_bytes(int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t dk,
@@ -373,7 +375,7 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const int32_
     if (!is_eps(eps)) return GLA_ESHAPE;
     if (n_seqs == 0) return GLA_OK;
     if (!norm_pool) return GLA_EPTR;
-    const size_t need = gla::gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
+    const size_t need = gla::lin_attn_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GLA_EWORKSPACE;
     gla::ChunkArgs a{q, k, v, nullptr, nullptr, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, chunk,
                      in_dtype == GLA_BF16, out_dtype == GLA_BF16, state_pool, n_slots, slot_idx,

@@ -226,6 +226,10 @@ __device__ __forceinline__ void log_decay_scan(const float* alpha, long astride,
 // global memory, which makes every wave drain its outstanding global loads
 // (the next chunk's prefetch) and stores at each barrier; the chunk loops
 // exchange data between waves through LDS alone.
+// 2^x by the hardware instruction alone (exp2f adds a rescaling for results
+// below 2^-126; the decay factors formed here are as good as zero there).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();

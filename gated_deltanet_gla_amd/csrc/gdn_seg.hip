@@ -79,10 +79,6 @@ constexpr int LP = CH + 8;         // P and T diag(beta)
 constexpr int kTargetBlocks = 256; // about one workgroup per compute unit
 constexpr int kPlaneElems = CH * CH;       // T diag(beta) (fp16) per (chunk, head)
 
-// 2^x by the hardware instruction alone (exp2f adds a rescaling for results
-// below 2^-126, which here are decay factors as good as zero).
-__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // One chunk of the global inputs in registers: 2 x 16 bytes per thread of
 // each 64 x 128 bf16 tile, 16 bytes of the 8 KiB fp16 T diag(beta) plane,
 // and the gate of token `lane` (wave 0).

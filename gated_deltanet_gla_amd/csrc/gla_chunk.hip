@@ -39,6 +39,8 @@
 // that normaliser is the row sum of the masked score tile P (which the
 // output waves hold anyway) plus phi(q_i) . z_in; the state waves carry z
 // from chunk to chunk in a double-buffered LDS vector.
+#include <algorithm>
+
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -162,8 +164,8 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
                  const typename TI::T* __restrict__ v, const float* __restrict__ alpha,
                  const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H,
                  float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
-                 int zero_init, Ckpt ck, float* __restrict__ zpool, float eps,
-                 typename TO::T* __restrict__ o) {
+                 int zero_init, Ckpt ck, float* __restrict__ zpool, const float* __restrict__ zsnap,
+                 float eps, typename TO::T* __restrict__ o) {
     constexpr bool F32 = (TI::bytes == 4);
     using O = Op<F32>;
     using E = typename O::E;
@@ -297,7 +299,11 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     }
     const long zoff = (static_cast<long>(slot) * H + h) * DK;
     if constexpr (NORM) {
-        for (int d = tid; d < DK; d += NT) zb[0][d] = zero_init ? 0.f : zpool[zoff + d];
+        // with several d_v tiles per head, the entry z comes from a copy
+        // taken before the launch: tile 0 writes the final z to norm_pool,
+        // possibly before another tile of the same head has started
+        const float* zsrc = zsnap ? zsnap + (static_cast<long>(b) * H + h) * DK : zpool + zoff;
+        for (int d = tid; d < DK; d += NT) zb[0][d] = zero_init ? 0.f : zsrc[d];
     }
     lds_barrier();
 
@@ -526,15 +532,38 @@ gla_chunk_kernel(const typename TI::T* __restrict__ q, const typename TI::T* __r
     }
 }
 
+// Copy of every sequence's entry normaliser z (norm_pool[slot_idx[b]], all
+// heads) into snap[b][h][:], for the chunk kernel's d_v tiles to read.
+__global__ void __launch_bounds__(256)
+z_snapshot(const float* __restrict__ zpool, int n_slots, const int32_t* __restrict__ slot_idx, int n_seqs,
+           int H, int dk, float* __restrict__ snap) {
+    const long n = static_cast<long>(n_seqs) * H * dk;
+    for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += gridDim.x * 256L) {
+        const long bh = i / dk;
+        const int b = static_cast<int>(bh / H);
+        const int slot = slot_idx[b];
+        snap[i] = (slot >= 0 && slot < n_slots) ? zpool[(static_cast<long>(slot) * H + bh % H) * dk + i % dk] : 0.f;
+    }
+}
+
 template <int DK, int DV, int BV, int C, class TI, class TO, bool NORM>
 hipError_t launch_inst(const ChunkArgs& a, hipStream_t s) {
     using T = typename TI::T;
     const long blocks = static_cast<long>(a.n_seqs) * a.n_heads * (DV / BV);
+    const float* zsnap = nullptr;
+    if (NORM && DV / BV > 1 && !a.zero_init) {
+        // the workspace holds the entry z of every (sequence, head)
+        float* snap = static_cast<float*>(a.workspace);
+        const long n = static_cast<long>(a.n_seqs) * a.n_heads * DK;
+        hipLaunchKernelGGL(z_snapshot, dim3(static_cast<unsigned>(std::min<long>((n + 255) / 256, 1024))),
+                           dim3(256), 0, s, a.zpool, a.n_slots, a.slot_idx, a.n_seqs, a.n_heads, DK, snap);
+        zsnap = snap;
+    }
     hipLaunchKernelGGL((gla_chunk_kernel<DK, DV, BV, C, TI, TO, NORM>), dim3(static_cast<unsigned>(blocks)),
                        dim3(NT), 0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens,
                        a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init,
-                       Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.zpool, a.eps,
+                       Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.zpool, zsnap, a.eps,
                        static_cast<typename TO::T*>(a.o));
     return hipGetLastError();
 }
@@ -597,6 +626,13 @@ size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s) {
     if (gla_seg_supported(a)) return launch_gla_seg(a, s);
     return launch_dk<false>(a, s);
+}
+
+// The generic path splits d_v into 32-column tiles; with more than one per
+// head it needs the entry normalisers copied to the workspace first.
+size_t lin_attn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk) {
+    const size_t snap = dv > 32 ? static_cast<size_t>(n_seqs) * n_heads * dk * sizeof(float) : 0;
+    return std::max(snap, gla_chunk_workspace(n_seqs, n_tokens, n_heads, dk, dv, chunk));
 }
 
 hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s) {

@@ -368,10 +368,10 @@ __device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>&
         glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), SC - 1));
         if constexpr (WQ) {
             bb.g2[lane] = x;
-            bb.eg[lane] = exp2f(x);
+            bb.eg[lane] = hw_exp2(x);
         }
-        bb.dec[lane] = exp2f(glast - x);
-        if (lane == 0) bb.gamma = exp2f(glast);
+        bb.dec[lane] = hw_exp2(glast - x);
+        if (lane == 0) bb.gamma = hw_exp2(glast);
     }
     return glast;
 }
@@ -567,7 +567,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
         for (int j = 0; j < sg.g; ++j) {
             const long sj = sg.ws_first + static_cast<long>(j) * H;
-            const float dcy = exp2f(wlam[sj]);
+            const float dcy = hw_exp2(wlam[sj]);
             const float* dS = frag_slot(wstate, sj);
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
@@ -619,7 +619,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = jt * 16 + ap.row0 + r;
-            pt[r] = (j <= i) ? pt[r] * exp2f(gi - bb.g2[j]) : 0.f;
+            pt[r] = (j <= i) ? pt[r] * hw_exp2(gi - bb.g2[j]) : 0.f;
         }
         Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
         if constexpr (NORM) {
@@ -890,7 +890,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
             for (int j = 0; j < sg.g; ++j) {
                 const long sj = sg.ws_first + it + static_cast<long>(j) * H;
-                const float dcy = exp2f(wlam[sj]);
+                const float dcy = hw_exp2(wlam[sj]);
                 const float* dS = frag_slot(wstate, sj);
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
@@ -997,7 +997,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = jt * 16 + ap.row0 + r;
-            pt[r] = (j <= i) ? pt[r] * exp2f(gi - bb.g2[j]) : 0.f;
+            pt[r] = (j <= i) ? pt[r] * hw_exp2(gi - bb.g2[j]) : 0.f;
         }
         Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
     };

@@ -91,6 +91,7 @@ hipError_t launch_hbm_probe(int mode, float* pool, int n_req, int n_heads, int n
                             const int32_t* slot_idx, void* sink, hipStream_t s);
 hipError_t launch_lin_attn_decode(const LinDecodeArgs& a, hipStream_t s);
 hipError_t launch_gla_chunk(const ChunkArgs& a, hipStream_t s);
+size_t lin_attn_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
 hipError_t launch_lin_attn_chunk(const ChunkArgs& a, hipStream_t s);
 size_t gla_chunk_workspace(int n_seqs, int n_tokens, int n_heads, int dk, int dv, int chunk);
 bool gla_seg_supported(const ChunkArgs& a);

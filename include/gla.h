@@ -367,8 +367,11 @@ GLA_API int gla_slot_copy(void* buf, size_t slot_bytes, int32_t n_slots,
  * Requires workspace of lin_attn_chunk_workspace_bytes() bytes (may be 0):
  * for bf16 inputs with d_k = d_v = 128 and chunk 64 the sequences are cut
  * into segments as in gla_chunk_fwd, and each segment's sum of phi(k) is
- * handed on with its state.  For bf16 inputs phi(q) and phi(k) are rounded
- * to bf16 before the contractions.
+ * handed on with its state; otherwise, for d_v > 32 (several 32-column
+ * d_v tiles per head), it holds a copy of the entry normalisers taken
+ * before the kernel runs, so that no tile reads a z another tile has
+ * already replaced.  For bf16 inputs phi(q) and phi(k) are rounded to bf16
+ * before the contractions.
  */
 GLA_API int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
                   const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,

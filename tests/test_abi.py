@@ -196,6 +196,13 @@ def test_lin_attn_validation():
         assert L.lin_attn_chunk_fwd(*args) == st, (i, bad)
     need = L.lin_attn_chunk_workspace_bytes(2, 10, 4, 128, 128, 64)
     assert need == L.gla_chunk_workspace_bytes(2, 10, 4, 128, 128, 64) > 0
+    # the generic path with several d_v tiles per head keeps a copy of the
+    # entry normalisers (2 sequences x 4 heads x dk floats); one tile needs none
+    assert L.lin_attn_chunk_workspace_bytes(2, 10, 4, 32, 64, 32) == 2 * 4 * 32 * 4
+    assert L.lin_attn_chunk_workspace_bytes(2, 10, 4, 64, 32, 32) == 0
+    args = list(base)
+    args[9] = 32
+    assert L.lin_attn_chunk_fwd(*args) == _lib.GLA_EWORKSPACE
     args = list(base)
     args[7] = args[8] = 128
     assert L.lin_attn_chunk_fwd(*args) == _lib.GLA_EWORKSPACE
