@@ -489,13 +489,17 @@ constexpr int kOrderMax = 1024;
 // length (ties by index): order[r] = sequence of rank r.
 __device__ __forceinline__ void span_offsets_body(const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
                                                   int span, int min_count, int sub, int32_t* __restrict__ off,
-                                                  int32_t* __restrict__ order, int* wsum, int* lens) {
+                                                  int32_t* __restrict__ order, int* wsum, int* lens,
+                                                  int min_keep = 0) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     auto length = [&](int b) {
         const int s = clampi(cu[b], 0, n_tokens);
         return clampi(cu[b + 1], s, n_tokens) - s;
     };
-    auto count = [&](int b) { return max(min_count, (length(b) + span - 1) / span - sub); };
+    auto count = [&](int b) {
+        const int c = max(min_count, (length(b) + span - 1) / span - sub);
+        return c < min_keep ? 0 : c;
+    };
     const int per = (n_seqs + 1023) / 1024;
     const int b0 = min(t * per, n_seqs), b1 = min(b0 + per, n_seqs);
     int sum = 0;
@@ -538,19 +542,19 @@ span_offsets(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int span,
 }
 
 // Several such scans over the same sequences in one launch, workgroup i
-// doing scan i (no order).
+// doing scan i (no order); a count below min_keep counts as 0.
 struct SpanScan {
-    int span, min_count, sub;
+    int span, min_count, sub, min_keep;
     int32_t* off;
 };
 struct SpanScans {
-    SpanScan s[3];
+    SpanScan s[4];
 };
 __global__ void __launch_bounds__(1024)
 span_offsets_multi(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, SpanScans sc) {
     __shared__ int wsum[16];
     const SpanScan& x = sc.s[blockIdx.x];
-    span_offsets_body(cu, n_seqs, n_tokens, x.span, x.min_count, x.sub, x.off, nullptr, wsum, nullptr);
+    span_offsets_body(cu, n_seqs, n_tokens, x.span, x.min_count, x.sub, x.off, nullptr, wsum, nullptr, x.min_keep);
 }
 
 // Largest b in [0, n_seqs) with off[b] <= idx (off non-decreasing).

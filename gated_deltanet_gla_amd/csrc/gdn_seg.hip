@@ -580,6 +580,7 @@ struct SegArgs {
     const int32_t* coff;          // first global chunk of every sequence
     const int32_t* seg_off;       // first segment of every sequence
     const int32_t* split_off;     // first split segment (every segment but the last of a split sequence)
+    const int32_t* splitseg_off;  // first segment among those of split sequences (all their segments)
     const uint16_t* planes;       // T diag(beta) per (chunk, head), fp16
     const float* tinv;            // their inverse scales
     long n_chunks_max, nsplit_max;
@@ -1018,12 +1019,19 @@ gdn_seg_a(SegArgs a, int n1) {
     else seg_out_body<TO, CKPT, false>(sm.out, blockIdx.x - n1, a);
 }
 
-// Phase B (after the scan): pass 2 for the segments of split sequences.
+// Phase B (after the scan): pass 2 for the segments of split sequences,
+// block j being segment j / H of their concatenated segment lists (a batch
+// of short prompts launches no idle blocks here).
 template <class TO, bool CKPT>
 __global__ void __launch_bounds__(NTH)
 gdn_seg_b(SegArgs a) {
     __shared__ SegSmem sm;
-    seg_out_body<TO, CKPT, true>(sm.out, blockIdx.x, a);
+    const int h = blockIdx.x % a.H;
+    const int jj = blockIdx.x / a.H;
+    if (jj >= a.splitseg_off[a.n_seqs]) return;
+    const int b = find_span_owner(a.splitseg_off, a.n_seqs, jj);
+    const int si = a.seg_off[b] + (jj - a.splitseg_off[b]);
+    seg_out_body<TO, CKPT, true>(sm.out, si * a.H + h, a);
 }
 
 // Segment length: whole chunks, at least 4 of them, such that the call
@@ -1045,12 +1053,13 @@ __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_
 }  // namespace
 
 // Workspace of the segmented path beyond the chunk offsets and T planes:
-// segment offsets, split-segment offsets, and three 64 KiB state slots per
+// segment offsets, split-segment offsets, offsets among the segments of
+// split sequences, and three 64 KiB state slots per
 // (split segment, head): dS, M and (at a sequence's first) S_in(0).  A sequence of s >= 2 segments is longer than
 // (s - 1) * lseg tokens, so split segments number at most n_tokens / lseg.
 size_t gdn_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
     const long nsplit = n_tokens / g_seg_len(n_seqs, n_tokens, n_heads);
-    return 2 * al256(sizeof(int32_t) * (n_seqs + 1)) +
+    return 3 * al256(sizeof(int32_t) * (n_seqs + 1)) +
            3 * static_cast<size_t>(nsplit) * n_heads * D * D * sizeof(float);
 }
 
@@ -1060,15 +1069,19 @@ float* plane_scales(const uint16_t* planes, long n_chunks_max, int H) {
     return const_cast<float*>(reinterpret_cast<const float*>(planes + n_chunks_max * H * kPlaneElems));
 }
 
-// The chunk offsets (coff, ahead of gdn_seg_prep) and the segment and
-// split-segment offsets of launch_gdn_seg, in one launch.
+// The chunk offsets (coff, ahead of gdn_seg_prep) and the segment,
+// split-segment and split-sequence-segment offsets of launch_gdn_seg, in
+// one launch.
 hipError_t launch_gdn_seg_offsets(const ChunkArgs& a, int32_t* coff, void* seg_ws, hipStream_t s) {
     const int lseg = g_seg_len(a.n_seqs, a.n_tokens, a.n_heads);
     char* ws = static_cast<char*>(seg_ws);
+    const size_t oa = al256(sizeof(int32_t) * (a.n_seqs + 1));
     int32_t* seg_off = reinterpret_cast<int32_t*>(ws);
-    int32_t* split_off = reinterpret_cast<int32_t*>(ws + al256(sizeof(int32_t) * (a.n_seqs + 1)));
-    const SpanScans sc{{SpanScan{CH, 0, 0, coff}, SpanScan{lseg, 1, 0, seg_off}, SpanScan{lseg, 0, 1, split_off}}};
-    hipLaunchKernelGGL(span_offsets_multi, dim3(3), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, sc);
+    int32_t* split_off = reinterpret_cast<int32_t*>(ws + oa);
+    int32_t* splitseg_off = reinterpret_cast<int32_t*>(ws + 2 * oa);
+    const SpanScans sc{{SpanScan{CH, 0, 0, 0, coff}, SpanScan{lseg, 1, 0, 0, seg_off},
+                        SpanScan{lseg, 0, 1, 0, split_off}, SpanScan{lseg, 0, 0, 2, splitseg_off}}};
+    hipLaunchKernelGGL(span_offsets_multi, dim3(4), dim3(1024), 0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, sc);
     return hipGetLastError();
 }
 
@@ -1092,17 +1105,21 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
     ws += al256(sizeof(int32_t) * (a.n_seqs + 1));
     int32_t* split_off = reinterpret_cast<int32_t*>(ws);
     ws += al256(sizeof(int32_t) * (a.n_seqs + 1));
+    int32_t* splitseg_off = reinterpret_cast<int32_t*>(ws);
+    ws += al256(sizeof(int32_t) * (a.n_seqs + 1));
     float* wsS = reinterpret_cast<float*>(ws);
     float* wsM = wsS + static_cast<size_t>(nsplit) * a.n_heads * D * D;
     float* wsI = wsM + static_cast<size_t>(nsplit) * a.n_heads * D * D;
     const SegArgs sa{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads,
-                     a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, coff, seg_off, split_off, planes,
-                     plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM, wsI,
+                     a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, coff, seg_off, split_off, splitseg_off,
+                     planes, plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM, wsI,
                      Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.o};
     const int n1 = static_cast<int>(nsplit * a.n_heads);
     const dim3 grid_a(static_cast<unsigned>(n1 + maxseg * a.n_heads));
-    const dim3 grid_b(static_cast<unsigned>(maxseg * a.n_heads));
+    // a sequence of k >= 2 segments is longer than (k - 1) lseg tokens and
+    // k <= 2 (k - 1): the segments of split sequences number at most 2 nsplit
+    const dim3 grid_b(static_cast<unsigned>(std::min(maxseg, 2 * nsplit) * a.n_heads));
     auto passes = [&](auto ka, auto kb) {
         hipLaunchKernelGGL(ka, grid_a, dim3(NTH), 0, s, sa, n1);
         if (nsplit > 0) {
