@@ -1003,6 +1003,237 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
     }
 }
 
+// Pass 2 for batches of short prompts: `items` heads h0 .. h0 + items - 1
+// (items divides H) of one unsplit sequence's segment (bid0 = segment * H +
+// h0), their chunks one stream, item after item, so the next head's loads
+// are in flight while the current head's last chunk runs.  Between heads
+// the final state of one goes to the pool through buffer stores with scalar
+// row offsets.  The output flush and the state stores are issued on every
+// path (empty ranges where there is nothing to write), so that the loop's
+// load-counter waits for the prefetched rows leave younger stores in flight.
+template <class TO, bool ZERO>
+__device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, const SegArgs& a) {
+    const int H = a.H;
+    const int h0 = bid0 % H;
+    const int si = bid0 / H;
+    if (si >= a.seg_off[a.n_seqs]) return;
+    const int b = find_span_owner(a.seg_off, a.n_seqs, si);
+    const int g = si - a.seg_off[b];
+    const int nseg = a.seg_off[b + 1] - a.seg_off[b];
+    if (nseg > 1) return;
+    GSeg sg;
+    if (!seg_bounds(sg, b, g, nseg, a.cu, a.n_tokens, a.coff, a.split_off, a.slot_idx, a.n_slots, a.lseg,
+                    a.nsplit_max))
+        return;
+    const int nch = (sg.t1 - sg.t0 + CH - 1) / CH;
+    if (sg.ci0 < 0 || sg.ci0 + nch > a.n_chunks_max) return;     // malformed cu_seqlens only
+    float* pool = a.pool;
+    typename TO::T* o = static_cast<typename TO::T*>(a.o);
+    KGate (&kb)[2] = sm.kb;
+    uint16_t (&sq)[CH][LQ] = sm.sq;
+    uint16_t (&sv)[CH][LK] = sm.sv;
+    uint16_t (&st)[CH][LP] = sm.st;
+    uint16_t (&sp)[CH][LP] = sm.sp;
+    uint16_t (&obuf)[CH][LQ] = sm.obuf;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const AccPos ap;
+    const int col = wave * 16;
+    const long stride = static_cast<long>(H) * D;
+
+    auto rows = [&](int c) { return c < nch ? min(CH, sg.t1 - sg.t0 - c * CH) : 0; };
+    auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * CH; };
+    GPrefetch<true, true> pf;
+    // chunk c of item it (nothing past the last item: a chunk past the end)
+    auto fetch = [&](int c, int it) {
+        const SegSrc src = seg_src<true, true>(a.q, a.k, a.v, a.alpha, a.planes, a.tinv, sg.t0, sg.t1 - sg.t0,
+                                               sg.ci0, nch, h0 + min(it, items - 1), H);
+        const int cc = it < items ? c : nch;
+        g_fetch(pf, src, cc, rows(cc));
+    };
+    // the position `ahead` chunks after chunk c of item it
+    auto step = [&](int c, int it, int ahead, int& c2, int& it2) {
+        c2 = c + ahead;
+        it2 = it;
+        if (nch <= 0) {
+            c2 = 0;
+            it2 = items;
+            return;
+        }
+        while (c2 >= nch) {
+            c2 -= nch;
+            ++it2;
+        }
+    };
+    fetch(0, 0);
+
+    // pool states through buffer resources: the lane's offset in one
+    // register, each of its 32 rows a scalar offset
+    const uint32_t lane_off = static_cast<uint32_t>((ap.row0 * D + col + ap.col) * 4);
+    auto pool_state = [&](int it, bool live) {
+        return BufRsrc(pool + (static_cast<long>(sg.slot) * H + h0 + it) * D * D, live ? D * D * 4 : 0u);
+    };
+    f32x4 S[8];
+    auto entry = [&](int it) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!ZERO) {
+            const BufRsrc rs = pool_state(it, true);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (mt * 16 + r) * D * 4);
+        }
+    };
+    auto final_state = [&](int it, bool live) {
+        const BufRsrc rs = pool_state(it, live);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (mt * 16 + r) * D * 4);
+    };
+    entry(0);
+    if (nch == 0) {
+        // empty sequence: every head's state goes back as it came in
+        for (int it = 0; it < items; ++it) {
+            if (it > 0) entry(it);
+            final_state(it, true);
+        }
+        return;
+    }
+    // P tiles above the diagonal that the products still read (rows 0-15 x
+    // columns 16-31, rows 32-47 x columns 48-63) stay zero
+    for (int idx = tid; idx < 2 * 256; idx += NTH) {
+        const int t = idx >> 8, e = idx & 255;
+        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+        sp[row][cx] = 0;
+    }
+    auto stage = [&](KGate& kk) {
+        g_stage_gates(kk.g2, kk.eg, kk.dec, &kk.gamma, pf);
+        g_stage_tile<true>(&kk.k[0][0], LK, pf.k, &kk.kx[0][0], LX);
+        g_stage_tile<true>(&sq[0][0], LQ, pf.q);
+        g_stage_tile<false>(&sv[0][0], LK, pf.v);
+        g_stage_plane(st, pf.t);
+        if (threadIdx.x == 0) kk.tinv = pf.tinv;
+    };
+    stage(kb[0]);
+    {
+        int c1, i1;
+        step(0, 0, 1, c1, i1);
+        fetch(c1, i1);
+    }
+    lds_barrier();
+
+    auto p_tile = [&](const KGate& kk, int t) {
+        const int it = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+        const int jt = t - it * (it + 1) / 2;
+        f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            pt = mfma_f16(frag_kc(&kk.k[0][0], LK, jt * 16, 32 * ks), frag_kc(&sq[0][0], LQ, it * 16, 32 * ks), pt);
+        const int i = it * 16 + ap.col;
+        const float gi = kk.g2[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = jt * 16 + ap.row0 + r;
+            pt[r] = (jj <= i) ? pt[r] * hw_exp2(gi - kk.g2[jj]) : 0.f;
+        }
+        *reinterpret_cast<u32x2*>(&sp[i][jt * 16 + ap.row0]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
+    };
+    // bf16 outputs of chunk cc of item it: LDS -> HBM, 16 lanes per 256-byte row
+    auto flush_o = [&](int cc, int it, bool live) {
+        if constexpr (TO::bytes == 2) {
+            const BufRsrc ro(o + tok(cc) * stride + (h0 + it) * D,
+                             live ? rows_extent(rows(cc), stride * 2, D * 2) : 0u);
+#pragma unroll
+            for (int u = 0; u < CH * D / 8 / NTH; ++u) {
+                const int x = tid + u * NTH, row = x / (D / 8), vc = (x % (D / 8)) * 8;
+                ro.store_b128(*reinterpret_cast<const u32x4*>(&obuf[row][vc]),
+                              static_cast<uint32_t>((row * stride + vc) * 2));
+            }
+        }
+    };
+
+    const int total = items * nch;
+    int c = 0, item = 0;              // chunk and item of stream position vc
+    int pc = 0, pitem = 0;            // those of the position before
+    for (int vc = 0; vc < total; ++vc) {
+        const KGate& kk = kb[vc & 1];
+        const int n = rows(c);
+        const long tok0 = tok(c);
+        const int hk = h0 + item;
+        flush_o(pc, pitem, vc > 0);
+
+        // ---- phase 1: P tiles -> LDS; X = K S, O^T = S^T Q^T; Y; U
+        p_tile(kk, wave);
+        if (wave + NWV < 10) p_tile(kk, wave + NWV);
+        bf16x8 sf[4];
+        const Scale ss = state_operand(sf, S);
+        f32x4 X[4], ot[4];
+        k_times_s<true>(X, ot, sf, &kk.kx[0][0], &sq[0][0]);
+        bf16x8 vf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&sv[0][0], LK, col, 32 * ks);
+        bf16x8 yf[2], uf[2], df[2];
+        const Scale sy = form_y<false>(yf, X, vf, kk.eg, ss.inv);
+        const Scale su = form_u(uf, df, yf, st, kk.dec, kk.tinv * sy.inv);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) ot[it] *= kk.eg[it * 16 + ap.col] * ss.inv;
+        lds_barrier();
+
+        // ---- phase 2: O^T += U^T P^T; outputs; state update; next chunk
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks <= (it >> 1); ++ks) pu = mfma_f16(uf[ks], frag_kc_split(&sp[0][0], LP, it * 16, 32 * ks), pu);
+            ot[it] += su.inv * pu;
+        }
+        if constexpr (TO::bytes == 2) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                *reinterpret_cast<u32x2*>(&obuf[it * 16 + ap.col][col + ap.row0]) =
+                    u32x2{pack_bf16x2(ot[it][0], ot[it][1]), pack_bf16x2(ot[it][2], ot[it][3])};
+        } else {
+            const BufRsrc ro(o + tok0 * stride + hk * D, rows_extent(n, stride * 4, D * 4));
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
+                              static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
+        }
+        state_update(S, &kk.k[0][0], kk.gamma, df, su.inv);
+        stage(kb[(vc + 1) & 1]);
+        {
+            int c2, i2;
+            step(c, item, 2, c2, i2);
+            fetch(c2, i2);
+        }
+        // between heads: this head's final state out, the next head's entry
+        // state in (zeros with ZERO, which then waits for nothing; loaded
+        // otherwise, and used here so that the wait for it falls in this
+        // chunk, not at the top of the loop)
+        const bool item_end = c == nch - 1;
+        final_state(item, item_end);
+        if (item_end && item + 1 < items) entry(item + 1);
+        if constexpr (!ZERO) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                asm volatile("" ::"v"(S[mt][0]), "v"(S[mt][1]), "v"(S[mt][2]), "v"(S[mt][3]));
+        }
+        pc = c;
+        pitem = item;
+        if (item_end) {
+            c = 0;
+            ++item;
+        } else {
+            ++c;
+        }
+        lds_barrier();
+    }
+    flush_o(pc, pitem, true);
+}
+
 union SegSmem {
     StateBuf st[2];
     OutSmem out;
@@ -1017,6 +1248,16 @@ gdn_seg_a(SegArgs a, int n1) {
     __shared__ SegSmem sm;
     if (static_cast<int>(blockIdx.x) < n1) seg_state_body(sm.st, blockIdx.x, a);
     else seg_out_body<TO, CKPT, false>(sm.out, blockIdx.x - n1, a);
+}
+
+// Phase A for batches of short prompts: pass 1 as above, and pass 2 for
+// unsplit sequences with `items` heads per block.
+template <class TO, bool ZERO>
+__global__ void __launch_bounds__(NTH)
+gdn_seg_a_multi(SegArgs a, int n1, int items) {
+    __shared__ SegSmem sm;
+    if (static_cast<int>(blockIdx.x) < n1) seg_state_body(sm.st, blockIdx.x, a);
+    else seg_out_multi<TO, ZERO>(sm.out, (blockIdx.x - n1) * items, items, a);
 }
 
 // Phase B (after the scan): pass 2 for the segments of split sequences,
@@ -1046,6 +1287,17 @@ int g_seg_len(int n_seqs, int n_tokens, int n_heads) {
     long L = (n_tokens + target - 1) / target;
     L = ((L + CH - 1) / CH) * CH;
     return static_cast<int>(L < 4 * CH ? 4 * CH : L);
+}
+
+// Heads of one segment per phase-A pass-2 block: 1 unless the batch is
+// short sequences (at most 4 chunks on average); then the largest divisor
+// of H up to 16 that still launches at least kTargetBlocks such blocks.
+int g_seg_items(int n_seqs, int n_tokens, int n_heads, long maxseg) {
+    if (n_seqs <= 0 || static_cast<long>(n_tokens) > static_cast<long>(n_seqs) * 4 * CH) return 1;
+    int best = 1;
+    for (int k = 2; k <= 16 && k <= n_heads; ++k)
+        if (n_heads % k == 0 && maxseg * n_heads / k >= kTargetBlocks) best = k;
+    return best;
 }
 
 __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1120,8 +1372,22 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
     // a sequence of k >= 2 segments is longer than (k - 1) lseg tokens and
     // k <= 2 (k - 1): the segments of split sequences number at most 2 nsplit
     const dim3 grid_b(static_cast<unsigned>(std::min(maxseg, 2 * nsplit) * a.n_heads));
+    // several heads per block for batches of short prompts (no checkpoints)
+    const int items = sa.ck.slots ? 1 : g_seg_items(a.n_seqs, a.n_tokens, a.n_heads, maxseg);
     auto passes = [&](auto ka, auto kb) {
-        hipLaunchKernelGGL(ka, grid_a, dim3(NTH), 0, s, sa, n1);
+        if (items > 1) {
+            const dim3 grid_m(static_cast<unsigned>(n1 + maxseg * a.n_heads / items));
+            auto multi = [&](auto kern) { hipLaunchKernelGGL(kern, grid_m, dim3(NTH), 0, s, sa, n1, items); };
+            if (a.zero_init) {
+                if (a.out_bf16) multi(gdn_seg_a_multi<BF16, true>);
+                else multi(gdn_seg_a_multi<F32, true>);
+            } else {
+                if (a.out_bf16) multi(gdn_seg_a_multi<BF16, false>);
+                else multi(gdn_seg_a_multi<F32, false>);
+            }
+        } else {
+            hipLaunchKernelGGL(ka, grid_a, dim3(NTH), 0, s, sa, n1);
+        }
         if (nsplit > 0) {
             // one column block per scan workgroup while that leaves the GPU
             // mostly idle, two once there are many (sequence, head) pairs

@@ -211,6 +211,42 @@ def test_gla_short_prompts_several_heads_per_block(zero_init):
     assert np.array_equal(p[untouched], w.pool[untouched])
 
 
+@pytest.mark.parametrize("zero_init", [False, True])
+def test_gdn_short_prompts_several_heads_per_block(zero_init):
+    """The Gated DeltaNet counterpart: pass 2 of unsplit short prompts runs
+    several heads of a segment per block (4 at these sizes), their chunks
+    in one stream, next to split sequences handled by the scan and phase B;
+    empty sequences and a skipped one (slot outside the pool) included."""
+    import gated_deltanet_gla_amd as G
+    rng = np.random.Generator(np.random.PCG64(81 + zero_init))
+    lens = rng.integers(0, 201, size=98).tolist()
+    lens[3] = 0
+    lens[40] = 0
+    lens = lens[:30] + [1200] + lens[30:70] + [1200] + lens[70:]
+    w = synth.random_varlen(21 + zero_init, lens, 16, 128, 128, dtype="bf16", gdn=True, zero_init=zero_init)
+    bad = 7
+    n_slots = w.pool.shape[0]
+    slots = w.slot_idx.copy()
+    slots[bad] = n_slots + 2
+    note(f"gdn short prompts, {len(lens)} sequences x 16 heads, zero_init={zero_init}")
+    q, k, v, a, bt = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.alpha), dev(w.beta)
+    pool = dev(w.pool)
+    o = torch.full(w.q.shape, 7.0, device=DEV)
+    G.gdn_chunk_fwd(q, k, v, a, bt, dev(w.cu_seqlens), pool, dev(slots), chunk=64, o=o, zero_init=zero_init)
+    torch.cuda.synchronize()
+    s0, s1 = int(w.cu_seqlens[bad]), int(w.cu_seqlens[bad + 1])
+    assert torch.all(o[s0:s1] == 7.0)
+    o_ref, pool_ref = run_oracle("gdn", w)
+    keep = np.ones(w.q.shape[0], bool)
+    keep[s0:s1] = False
+    check(host(o)[keep], o_ref[keep], "bf16", "o")
+    p = pool.cpu().numpy()
+    good = np.delete(w.slot_idx, bad)
+    check(p[good], pool_ref[good], "bf16", "state")
+    untouched = sorted(set(range(n_slots)) - set(good.tolist()))
+    assert np.array_equal(p[untouched], w.pool[untouched])
+
+
 def test_gla_prefill_full_size():
     """GLA prefill: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 inputs,
     zero initial state: every output and final state against the oracle."""
