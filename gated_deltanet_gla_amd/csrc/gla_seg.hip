@@ -63,13 +63,16 @@ constexpr int SW = 8;              // waves
 constexpr int ST = SW * 64;        // threads
 constexpr int SD = 128;            // d_k = d_v
 constexpr int SC = 64;             // chunk
-// LDS row strides (bf16 elements).  q is read only along rows (16 lanes on
-// 16 rows, same column): a stride of 4 banks mod 64 spreads them over all
-// banks.  k and v are mostly read with the transpose read, where 8 rows of
-// 32 bytes go out together: a stride of 8 banks mod 64 keeps those apart.
-constexpr int LQ = SD + 8;         // 68 dwords
+// LDS row strides (bf16 elements).  Operand fragments are read as one
+// 16-byte read per lane (16 lanes on 16 rows, 8 consecutive values each)
+// or with the transpose read (8 rows of 32 bytes at once); the LDS serves
+// both at full rate when a row starts 8 banks (72 dwords) or 40 banks
+// (40 dwords) after the one before, and at half rate at 4 banks.  Split
+// 8-byte pairs are avoided altogether: the LDS serves 8-byte reads at a
+// quarter of the 16-byte rate.
+constexpr int LQ = SD + 16;        // 72 dwords
 constexpr int LK = SD + 16;        // 72 dwords
-constexpr int SP = SC + 8;         // LDS line of a P row (36 dwords)
+constexpr int SP = SC + 16;        // LDS line of a P row (40 dwords)
 constexpr int kSegBlocks = 256;    // one workgroup on each of the 256 compute units
 constexpr int kShortChunks = 4;    // batches of sequences this short (mean chunks) ...
 constexpr int kMaxItems = 16;      // ... put up to this many heads in one output-pass block
@@ -272,13 +275,56 @@ __device__ __forceinline__ const float* frag_slot(const float* ws, long slot) {
     return ws + slot * SD * SD + threadIdx.x * 32;
 }
 
-// This wave's 8 state tiles read from a row-major [d][n] state.
+// Which state rows the accumulator tiles hold.  In the output pass, tile mt
+// gives lane group g (tile rows 4g..4g+3) the state rows
+// srow(mt, 4g) + r = 32 (mt / 2) + 8 g + 4 (mt % 2) + r, so that tiles 2s
+// and 2s + 1 hand each lane the 8 consecutive rows 32 s + 8 g .. + 7 as an
+// MFMA operand: S^T then pairs with q fragments in natural order, one
+// 16-byte LDS read each.  Pass 1, which never multiplies S by q, keeps
+// the plain order (tile mt, rows 16 mt + 4 g + r) and reorders its tiles
+// only as it writes them to the workspace.
+__device__ __forceinline__ int srow(int mt, int row0) { return 32 * (mt >> 1) + 2 * row0 + 4 * (mt & 1); }
+
+// Where P's keys sit along an LDS row of P: keys 16 jt + 4 g .. + 3 (key
+// tile jt, lane group g of the tile's MFMA) at 32 (jt / 2) + 8 g + 4 (jt % 2),
+// so that one 16-byte read at 32 ks + 8 g returns keys
+// {32 ks + 4 g .. + 3} u {32 ks + 16 + 4 g .. + 3}, the split k order of the
+// V^T operand.
+__device__ __forceinline__ int p_col(int jt, int g) { return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1); }
+
+// K^T operand (lines = state rows of output-pass tile mt, in the order
+// above; tokens in the split k order) for the state update
+__device__ __forceinline__ bf16x8 frag_kt_out(const uint16_t* base, int ld, int mt, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const uint16_t* p = base + (k0 + (lane >> 4) * 4 + (i >> 2)) * ld + 32 * (mt >> 1) + 8 * (i & 3) + 4 * (mt & 1);
+    return cat8(ld_tr16(p), ld_tr16(p + 16 * ld));
+}
+
+// This wave's 8 state tiles read from a row-major [d][n] state (OUT: the
+// output pass's row order).
+template <bool OUT>
 __device__ __forceinline__ void load_state_rowmajor(f32x4 (&S)[8], const float* src, int col) {
     const AccPos ap;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
+        const int r0 = OUT ? srow(mt, ap.row0) : mt * 16 + ap.row0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[mt][r] = src[(mt * 16 + ap.row0 + r) * SD + col + ap.col];
+        for (int r = 0; r < 4; ++r) S[mt][r] = src[(r0 + r) * SD + col + ap.col];
+    }
+}
+
+// Pass 1's tiles (plain row order) into a workspace slot in the output
+// pass's order: plain tile mt', group g', row r is state row
+// 16 mt' + 4 g' + r, which the output pass holds in tile 2 (mt' / 2) + g' % 2
+// of lane group 2 (mt' % 2) + g' / 2 (same column, same wave).
+__device__ __forceinline__ void store_slot_out_order(float* ws, long slot, const f32x4 (&S)[8]) {
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 4;
+    float* base = ws + slot * SD * SD + (t & ~63) * 32;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        const int dl = (lane & 15) + 16 * (2 * (mt & 1) + (g >> 1));
+        *reinterpret_cast<f32x4*>(base + dl * 32 + (2 * (mt >> 1) + (g & 1)) * 4) = S[mt];
     }
 }
 
@@ -411,12 +457,14 @@ struct SegUpd {
     bf16x8 kf[2][8];
     bf16x8 vh[2], vl[2];
 };
-template <class Buf>
+template <bool OUT, class Buf>
 __device__ __forceinline__ void seg_update_prep(SegUpd& up, f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) up.kf[ks][mt] = frag_km_split(&bb.k[0][0], LK, mt * 16, 32 * ks);
+        for (int mt = 0; mt < 8; ++mt)
+            up.kf[ks][mt] = OUT ? frag_kt_out(&bb.k[0][0], LK, mt, 32 * ks)
+                                : frag_km_split(&bb.k[0][0], LK, mt * 16, 32 * ks);
     __builtin_amdgcn_sched_barrier(0);
     // decayed values for tokens {32ks + 4g + e} u {32ks + 16 + 4g + e}, split
     const int g = (threadIdx.x & 63) >> 4;
@@ -451,7 +499,7 @@ __device__ __forceinline__ void seg_update_mfma(f32x4 (&S)[8], const SegUpd& up)
 template <class Buf>
 __device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
     SegUpd up;
-    seg_update_prep(up, S, bb, vf);
+    seg_update_prep<false>(up, S, bb, vf);
     __builtin_amdgcn_sched_barrier(0);
     seg_update_mfma(S, up);
 }
@@ -477,7 +525,7 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (sg.g == sg.nseg - 1) {                     // last segment's slot: copy of the initial state
-        if (!zero_init) load_state_rowmajor(S, pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD, col);
+        if (!zero_init) load_state_rowmajor<true>(S, pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD, col);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
         if constexpr (NORM) {
@@ -509,8 +557,7 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
         seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
+    store_slot_out_order(wstate, sg.ws_slot, S);
     if (threadIdx.x == 0) wlam[sg.ws_slot] = lam;
     if constexpr (NORM) {
         if (ap.col == 0) {
@@ -560,7 +607,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     if (sg.nseg <= 1) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (!zero_init) load_state_rowmajor(S, Sg, col);
+        if (!zero_init) load_state_rowmajor<true>(S, Sg, col);
     } else {
         const float* s0 = frag_slot(wstate, sg.ws_first + static_cast<long>(sg.nseg - 1) * H);
 #pragma unroll
@@ -586,11 +633,11 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         }
         if (ap.col == 0) *reinterpret_cast<f32x4*>(&zb[0][zr]) = zacc;
     }
-    // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
-    // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
+    // P tiles above the diagonal that P V still reads (rows 0-15 x keys 16-31,
+    // rows 32-47 x keys 48-63) stay zero; the others are rewritten each chunk.
     for (int idx = tid; idx < 2 * 256; idx += ST) {
         const int t = idx >> 8, e = idx & 255;
-        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+        const int row = (t ? 32 : 0) + (e >> 4), cx = p_col(t ? 3 : 1, (e >> 2) & 3) + (e & 3);
         pbuf[0][row][cx] = 0;
         pbuf[1][row][cx] = 0;
     }
@@ -621,7 +668,8 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             const int j = jt * 16 + ap.row0 + r;
             pt[r] = (j <= i) ? pt[r] * hw_exp2(gi - bb.g2[j]) : 0.f;
         }
-        Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
+        const int pc = p_col(jt, ap.row0 >> 2);
+        Op<false>::store4(&pbuf[0][i][pc], &pbuf[1][i][pc], pt);
         if constexpr (NORM) {
             // row i's sum over this tile's 16 keys (spread over the 4 lane groups)
             float rs = (pt[0] + pt[1]) + (pt[2] + pt[3]);
@@ -658,7 +706,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 #pragma unroll
         for (int s = 0; s < SD / 32; ++s)
 #pragma unroll
-            for (int it = 0; it < 4; ++it) qf[s][it] = frag_kc_split(&bb.q[0][0], LQ, it * 16, 32 * s);
+            for (int it = 0; it < 4; ++it) qf[s][it] = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * s);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 sh8[4], sl8[4];
 #pragma unroll
@@ -716,19 +764,19 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         load_vt(vf, bb, col);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            pp[it][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 0);
-            pp[it][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 0);
+            pp[it][0] = frag_kc(&pbuf[0][0][0], SP, it * 16, 0);
+            pp[it][1] = frag_kc(&pbuf[1][0][0], SP, it * 16, 0);
         }
 #pragma unroll
         for (int it = 2; it < 4; ++it) {
-            pp[it + 2][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 32);
-            pp[it + 2][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 32);
+            pp[it + 2][0] = frag_kc(&pbuf[0][0][0], SP, it * 16, 32);
+            pp[it + 2][1] = frag_kc(&pbuf[1][0][0], SP, it * 16, 32);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the state update's operand reads and VALU work go ahead of the
         // P V MFMAs, which do not depend on them, so they can overlap
         SegUpd up;
-        seg_update_prep(up, S, bb, vf);
+        seg_update_prep<true>(up, S, bb, vf);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
@@ -783,11 +831,11 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         const int cs = CKPT && n == SC ? ckpt_slot(ck, sg.b, sg.g * lseg + (c + 1) * SC, n_slots) : -1;
         if (CKPT && cs >= 0) {
             float* Sc = pool + (static_cast<long>(cs) * H + sg.h) * SD * SD +
-                        opaque(ap.row0 * SD + col + ap.col);
+                        opaque(2 * ap.row0 * SD + col + ap.col);
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sc[(mt * 16 + r) * SD] = S[mt][r];
+                for (int r = 0; r < 4; ++r) Sc[(srow(mt, 0) + r) * SD] = S[mt][r];
             }
         }
         lds_barrier();
@@ -798,7 +846,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * SD + col + ap.col] = S[mt][r];
+            for (int r = 0; r < 4; ++r) Sg[(srow(mt, ap.row0) + r) * SD + col + ap.col] = S[mt][r];
         }
         if constexpr (NORM) {
             // z after the last chunk (the loop ends with a barrier)
@@ -869,7 +917,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     f32x4 S[8];
     // a pool state through a buffer resource: the lane's offset in one
     // register, each of its 32 rows a scalar offset (no per-row addresses)
-    const uint32_t lane_off = static_cast<uint32_t>((ap.row0 * SD + col + ap.col) * 4);
+    const uint32_t lane_off = static_cast<uint32_t>((2 * ap.row0 * SD + col + ap.col) * 4);
     auto pool_state = [&](int it) {
         return BufRsrc(pool + (static_cast<long>(sg.slot) * H + sg.h + it) * SD * SD, SD * SD * 4);
     };
@@ -882,7 +930,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (mt * 16 + r) * SD * 4);
+                    for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (srow(mt, 0) + r) * SD * 4);
             }
         } else {
             const float* s0 = frag_slot(wstate, sg.ws_first + it + static_cast<long>(sg.nseg - 1) * H);
@@ -897,12 +945,12 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             }
         }
     };
-    // P tiles above the diagonal that P V still reads (rows 0-15 x cols 16-31,
-    // rows 32-47 x cols 48-63) stay zero; the others are rewritten each chunk.
+    // P tiles above the diagonal that P V still reads (rows 0-15 x keys 16-31,
+    // rows 32-47 x keys 48-63) stay zero; the others are rewritten each chunk.
     auto zero_p_upper = [&]() {
         for (int idx = tid; idx < 2 * 256; idx += ST) {
             const int t = idx >> 8, e = idx & 255;
-            const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+            const int row = (t ? 32 : 0) + (e >> 4), cx = p_col(t ? 3 : 1, (e >> 2) & 3) + (e & 3);
             pbuf[0][row][cx] = 0;
             pbuf[1][row][cx] = 0;
         }
@@ -913,7 +961,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (mt * 16 + r) * SD * 4);
+            for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (srow(mt, 0) + r) * SD * 4);
     };
     // Between item it and item it + 1 (all threads, after a barrier that
     // ends every read of the free chunk buffer fb and of pbuf; ends with the
@@ -934,10 +982,11 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         float* hi = reinterpret_cast<float*>(&pbuf[0][0][0]);
         // lane offsets recomputed here (opaque), not held across the chunk loop
         if (last_seg) {
-            const int wo = opaque(ap.row0 * kRow + col + ap.col);
+            const int wo = opaque(2 * ap.row0 * kRow + col + ap.col);
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
-                float* base = (mt < 6 ? lo + mt * 16 * kRow : hi + (mt - 6) * 16 * kRow) + wo;
+                // state rows srow(mt, .): tiles 0-5 hold rows 0-95, tiles 6 and 7 rows 96-127
+                float* base = (mt < 6 ? lo + srow(mt, 0) * kRow : hi + (srow(mt, 0) - 96) * kRow) + wo;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) base[r * kRow] = S[mt][r];
             }
@@ -999,7 +1048,8 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             const int j = jt * 16 + ap.row0 + r;
             pt[r] = (j <= i) ? pt[r] * hw_exp2(gi - bb.g2[j]) : 0.f;
         }
-        Op<false>::store4(&pbuf[0][i][jt * 16 + ap.row0], &pbuf[1][i][jt * 16 + ap.row0], pt);
+        const int pc = p_col(jt, ap.row0 >> 2);
+        Op<false>::store4(&pbuf[0][i][pc], &pbuf[1][i][pc], pt);
     };
 
     // bf16 outputs of chunk cc of item it: LDS -> HBM, 16 lanes per 256-byte
@@ -1038,7 +1088,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
         for (int s = 0; s < SD / 32; ++s)
 #pragma unroll
-            for (int it = 0; it < 4; ++it) qf[s][it] = frag_kc_split(&bb.q[0][0], LQ, it * 16, 32 * s);
+            for (int it = 0; it < 4; ++it) qf[s][it] = frag_kc(&bb.q[0][0], LQ, it * 16, 32 * s);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 sh8[4], sl8[4];
 #pragma unroll
@@ -1074,19 +1124,19 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         load_vt(vf, bb, col);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            pp[it][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 0);
-            pp[it][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 0);
+            pp[it][0] = frag_kc(&pbuf[0][0][0], SP, it * 16, 0);
+            pp[it][1] = frag_kc(&pbuf[1][0][0], SP, it * 16, 0);
         }
 #pragma unroll
         for (int it = 2; it < 4; ++it) {
-            pp[it + 2][0] = frag_kc_split(&pbuf[0][0][0], SP, it * 16, 32);
-            pp[it + 2][1] = frag_kc_split(&pbuf[1][0][0], SP, it * 16, 32);
+            pp[it + 2][0] = frag_kc(&pbuf[0][0][0], SP, it * 16, 32);
+            pp[it + 2][1] = frag_kc(&pbuf[1][0][0], SP, it * 16, 32);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the state update's operand reads and VALU work go ahead of the
         // P V MFMAs, which do not depend on them, so they can overlap
         SegUpd up;
-        seg_update_prep(up, S, bb, vf);
+        seg_update_prep<true>(up, S, bb, vf);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
