@@ -330,6 +330,34 @@ __device__ __forceinline__ bf16x8 frag_km_split(const uint16_t* base, int ld, in
     const uint16_t* p = base + (k0 + (lane >> 4) * 4 + (i >> 2)) * ld + m0 + 4 * (i & 3);
     return cat8(ld_tr16(p), ld_tr16(p + 16 * ld));
 }
+// A 128-row state held as 8 accumulator tiles in "pair" order: tile mt
+// gives lane group g (tile rows 4g..4g+3) the state rows
+// srow(mt, 4g) + r = 32 (mt / 2) + 8 g + 4 (mt % 2) + r.  Tiles 2s and 2s + 1
+// then hand each lane the 8 consecutive rows 32 s + 8 g .. + 7, so the
+// state as an MFMA operand (S^T Q^T, K S) meets the other operand's
+// fragment in natural order, one 16-byte LDS read per lane; a split order
+// would take two 8-byte reads, which the LDS serves at a quarter of the
+// 16-byte rate.
+__device__ __forceinline__ int srow(int mt, int row0) { return 32 * (mt >> 1) + 2 * row0 + 4 * (mt & 1); }
+
+// K^T operand of the update of pair-order tile mt (lines = its state rows,
+// tokens k0 + {4g .. 4g + 3} u {16 + 4g .. 16 + 4g + 3}): the transpose read
+// with each lane group's 4 columns where srow() puts them.
+__device__ __forceinline__ bf16x8 frag_kt_pair(const uint16_t* base, int ld, int mt, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const uint16_t* p = base + (k0 + (lane >> 4) * 4 + (i >> 2)) * ld + 32 * (mt >> 1) + 8 * (i & 3) + 4 * (mt & 1);
+    return cat8(ld_tr16(p), ld_tr16(p + 16 * ld));
+}
+
+// Where a 64-key matrix (P, T diag(beta)) keeps keys 16 jt + 4 g .. + 3 (key
+// tile jt, lane group g) along its LDS row: at 32 (jt / 2) + 8 g + 4 (jt % 2),
+// so that one 16-byte read at 32 ks + 8 g returns keys
+// {32 ks + 4 g .. + 3} u {32 ks + 16 + 4 g .. + 3}, the split k order in
+// which token-indexed operands come out of the transpose read and of
+// accumulator tile pairs.
+__device__ __forceinline__ int p_col(int jt, int g) { return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1); }
+
 // 16-wide k tail (16x16x16 MFMA, 4 k-values k0 + 4 g .. +3 per lane).
 __device__ __forceinline__ s16x4 frag_kc4(const uint16_t* base, int ld, int line0, int k0) {
     const int lane = threadIdx.x & 63;

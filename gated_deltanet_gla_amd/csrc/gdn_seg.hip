@@ -72,10 +72,12 @@ constexpr int NWV = 8;             // waves
 constexpr int NTH = NWV * 64;      // threads
 constexpr int D = 128;             // d_k = d_v
 constexpr int CH = 64;             // chunk
-constexpr int LQ = D + 8;          // LDS row stride of q (read along rows)
-constexpr int LK = D + 16;         // k, v read with the transpose read and k's 16-byte row reads
-constexpr int LX = D + 8;          // k read in the split order of X = K S (8-byte reads)
-constexpr int LP = CH + 8;         // P and T diag(beta)
+// LDS row strides: 16-byte operand reads (16 lanes on 16 rows) and the
+// transpose read run at full rate with rows 72 dwords (or 40) apart, half
+// rate 68 dwords apart.
+constexpr int LQ = D + 16;         // q
+constexpr int LK = D + 16;         // k, v
+constexpr int LP = CH + 16;        // P and T diag(beta), keys in p_col() order
 constexpr int kTargetBlocks = 256; // about one workgroup per compute unit
 constexpr int kPlaneElems = CH * CH;       // T diag(beta) (fp16) per (chunk, head)
 
@@ -265,7 +267,7 @@ __device__ __forceinline__ void g_rowmajor_load(f32x4 (&S)[8], const float* src,
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[mt][r] = src[(mt * 16 + ap.row0 + r) * D + col + ap.col];
+        for (int r = 0; r < 4; ++r) S[mt][r] = src[(srow(mt, ap.row0) + r) * D + col + ap.col];
 }
 
 // Split a pair of accumulator tiles into bf16 hi / lo operand fragments
@@ -333,7 +335,7 @@ __device__ __forceinline__ Scale form_u(bf16x8 (&uf)[2], bf16x8 (&df)[2], const 
     for (int it = 0; it < 4; ++it) {
         U[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks <= (it >> 1); ++ks) U[it] = mfma_f16(frag_kc_split(&t[0][0], LP, it * 16, 32 * ks), yf[ks], U[it]);
+        for (int ks = 0; ks <= (it >> 1); ++ks) U[it] = mfma_f16(frag_kc(&t[0][0], LP, it * 16, 32 * ks), yf[ks], U[it]);
         m = absmax4(U[it], m);
     }
     // the scale is taken on the true U = uinv U[it]; dec <= 1, so the same
@@ -359,7 +361,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[8], const uint16_t* kbas
     for (int mt = 0; mt < 8; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc = mfma_f16(frag_km_split(kbase, LK, mt * 16, 32 * ks), df[ks], acc);
+        for (int ks = 0; ks < 2; ++ks) acc = mfma_f16(frag_kt_pair(kbase, LK, mt, 32 * ks), df[ks], acc);
         S[mt] = gam * S[mt] + dinv * acc;
     }
 }
@@ -378,8 +380,8 @@ __device__ __forceinline__ void k_times_s(f32x4 (&X)[4], f32x4* ot, const bf16x8
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            X[it] = mfma_f16(frag_kc_split(kbase, LX, it * 16, 32 * s), sf[s], X[it]);
-            if constexpr (WQ) ot[it] = mfma_f16(sf[s], frag_kc_split(qbase, LQ, it * 16, 32 * s), ot[it]);
+            X[it] = mfma_f16(frag_kc(kbase, LK, it * 16, 32 * s), sf[s], X[it]);
+            if constexpr (WQ) ot[it] = mfma_f16(sf[s], frag_kc(qbase, LQ, it * 16, 32 * s), ot[it]);
         }
     }
 }
@@ -394,7 +396,7 @@ __device__ __forceinline__ void k_times_sm(f32x4 (&XS)[4], f32x4 (&XM)[4], const
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const bf16x8 kf = frag_kc_split(kbase, LX, it * 16, 32 * s);
+            const bf16x8 kf = frag_kc(kbase, LK, it * 16, 32 * s);
             XS[it] = mfma_f16(kf, sf[s], XS[it]);
             XM[it] = mfma_f16(kf, mf[s], XM[it]);
         }
@@ -407,7 +409,7 @@ __device__ __forceinline__ void state_update_sm(f32x4 (&S)[8], f32x4 (&M)[8], co
         f32x4 as = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 kt = frag_km_split(kbase, LK, mt * 16, 32 * ks);
+            const bf16x8 kt = frag_kt_pair(kbase, LK, mt, 32 * ks);
             as = mfma_f16(kt, sdf[ks], as);
             am = mfma_f16(kt, mdf[ks], am);
         }
@@ -550,15 +552,17 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
         const Scale sc = range_scale(mloc);
         if (lane == 0) tinv[item] = sc.inv;
         const BufRsrc rp(planes + item * kPlaneElems, kPlaneElems * 2u);
+        // column me of the plane sits at p_col() order (columns 32..63 stay in 32..63)
+        const int pos = p_col(me >> 4, (me >> 2) & 3) + (me & 3);
 #pragma unroll
         for (int r = 0; r < CH; r += 2) {
             // rows r and r + 1 of column `me`: two 2-byte stores
             const uint32_t hv = pk_f16(x[r] * bj * sc.s, x[r + 1] * bj * sc.s);
             const bool skip = r < 32 && me >= 32;
             rp.store_b16(static_cast<uint16_t>(hv & 0xffffu),
-                         skip ? 0x80000000u : static_cast<uint32_t>((r * CH + me) * 2));
+                         skip ? 0x80000000u : static_cast<uint32_t>((r * CH + pos) * 2));
             rp.store_b16(static_cast<uint16_t>(hv >> 16),
-                         skip ? 0x80000000u : static_cast<uint32_t>(((r + 1) * CH + me) * 2));
+                         skip ? 0x80000000u : static_cast<uint32_t>(((r + 1) * CH + pos) * 2));
         }
         wave_sync();       // this wave's A and gate tables are rewritten by its next item
     }
@@ -594,7 +598,6 @@ struct SegArgs {
 // ------------------------------------------------------------------ pass 1
 struct StateBuf {
     alignas(16) uint16_t k[CH][LK];      // fp16
-    alignas(16) uint16_t kx[CH][LX];     // fp16, the same rows at the stride of X's reads
     alignas(16) uint16_t v[CH][LK];      // bf16
     alignas(16) uint16_t t[CH][LP];      // T diag(beta), fp16, scaled
     alignas(16) float eg[CH];
@@ -639,7 +642,7 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
     auto fetch = [&](int c) { g_fetch(pf, src, c, rows(c)); };
     auto stage = [&](StateBuf& bb) {
         g_stage_gates(nullptr, bb.eg, bb.dec, &bb.gamma, pf);
-        g_stage_tile<true>(&bb.k[0][0], LK, pf.k, &bb.kx[0][0], LX);
+        g_stage_tile<true>(&bb.k[0][0], LK, pf.k);
         g_stage_tile<false>(&bb.v[0][0], LK, pf.v);
         g_stage_plane(bb.t, pf.t);
         if (threadIdx.x == 0) bb.tinv = pf.tinv;
@@ -659,7 +662,7 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
         const Scale ss = state_operand(sf, S);
         const Scale sm = state_operand(mf, M);
         f32x4 XS[4], XM[4];
-        k_times_sm(XS, XM, sf, mf, &bb.kx[0][0]);
+        k_times_sm(XS, XM, sf, mf, &bb.k[0][0]);
         bf16x8 yf[2], un[2], sdf[2], mdf[2];
         const Scale sy = form_y<false>(yf, XS, vf, bb.eg, ss.inv);
         const Scale su = form_u<false>(un, sdf, yf, bb.t, bb.dec, bb.tinv * sy.inv);
@@ -734,7 +737,7 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
         if (!zero_init) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[c][r] = src[(wave * 16 + ap.row0 + r) * D + (part * kScanCols + c) * 16 + ap.col];
+                S[c][r] = src[(srow(wave, ap.row0) + r) * D + (part * kScanCols + c) * 16 + ap.col];
         }
         *reinterpret_cast<f32x4*>(s0 + lofs(c)) = S[c];
     }
@@ -812,7 +815,6 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
 // ------------------------------------------------------------------ pass 2
 struct KGate {
     alignas(16) uint16_t k[CH][LK];      // fp16
-    alignas(16) uint16_t kx[CH][LX];     // fp16, the same rows at the stride of X's reads
     alignas(16) float g2[CH];
     alignas(16) float eg[CH];
     alignas(16) float dec[CH];
@@ -885,15 +887,15 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
         g_slot_load(S, src);
     }
     // P tiles above the diagonal that the products still read (rows 0-15 x
-    // columns 16-31, rows 32-47 x columns 48-63) stay zero
+    // keys 16-31, rows 32-47 x keys 48-63) stay zero
     for (int idx = tid; idx < 2 * 256; idx += NTH) {
         const int t = idx >> 8, e = idx & 255;
-        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+        const int row = (t ? 32 : 0) + (e >> 4), cx = p_col(t ? 3 : 1, (e >> 2) & 3) + (e & 3);
         sp[row][cx] = 0;
     }
     auto stage = [&](KGate& kk) {
         g_stage_gates(kk.g2, kk.eg, kk.dec, &kk.gamma, pf);
-        g_stage_tile<true>(&kk.k[0][0], LK, pf.k, &kk.kx[0][0], LX);
+        g_stage_tile<true>(&kk.k[0][0], LK, pf.k);
         g_stage_tile<true>(&sq[0][0], LQ, pf.q);
         g_stage_tile<false>(&sv[0][0], LK, pf.v);
         g_stage_plane(st, pf.t);
@@ -918,7 +920,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
             const int jj = jt * 16 + ap.row0 + r;
             pt[r] = (jj <= i) ? pt[r] * hw_exp2(gi - kk.g2[jj]) : 0.f;
         }
-        *reinterpret_cast<u32x2*>(&sp[i][jt * 16 + ap.row0]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
+        *reinterpret_cast<u32x2*>(&sp[i][p_col(jt, ap.row0 >> 2)]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
     };
     // chunk cc's bf16 outputs: LDS -> HBM, 16 lanes per 256-byte row
     auto flush_o = [&](int cc) {
@@ -945,7 +947,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
         bf16x8 sf[4];
         const Scale ss = state_operand(sf, S);
         f32x4 X[4], ot[4];
-        k_times_s<true>(X, ot, sf, &kk.kx[0][0], &sq[0][0]);
+        k_times_s<true>(X, ot, sf, &kk.k[0][0], &sq[0][0]);
         bf16x8 vf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&sv[0][0], LK, col, 32 * ks);
@@ -961,7 +963,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
         for (int it = 0; it < 4; ++it) {
             f32x4 pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks <= (it >> 1); ++ks) pu = mfma_f16(uf[ks], frag_kc_split(&sp[0][0], LP, it * 16, 32 * ks), pu);
+            for (int ks = 0; ks <= (it >> 1); ++ks) pu = mfma_f16(uf[ks], frag_kc(&sp[0][0], LP, it * 16, 32 * ks), pu);
             ot[it] += su.inv * pu;
         }
         // lane: token it*16 + (lane % 16), columns col + 4 (lane / 16) .. +3
@@ -983,11 +985,11 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
         // checkpoint: this wave's columns of the state after chunk c
         const int cs = CKPT && n == CH ? ckpt_slot(ck, sg.b, sg.g * lseg + (c + 1) * CH, n_slots) : -1;
         if (CKPT && cs >= 0) {
-            float* Sc = pool + (static_cast<long>(cs) * H + h) * D * D + opaque(ap.row0 * D + col + ap.col);
+            float* Sc = pool + (static_cast<long>(cs) * H + h) * D * D + opaque(2 * ap.row0 * D + col + ap.col);
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sc[(mt * 16 + r) * D] = S[mt][r];
+                for (int r = 0; r < 4; ++r) Sc[(srow(mt, 0) + r) * D] = S[mt][r];
             }
         }
         lds_barrier();
@@ -998,7 +1000,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sg[(mt * 16 + ap.row0 + r) * D + col + ap.col] = S[mt][r];
+            for (int r = 0; r < 4; ++r) Sg[(srow(mt, ap.row0) + r) * D + col + ap.col] = S[mt][r];
         }
     }
 }
@@ -1070,7 +1072,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
 
     // pool states through buffer resources: the lane's offset in one
     // register, each of its 32 rows a scalar offset
-    const uint32_t lane_off = static_cast<uint32_t>((ap.row0 * D + col + ap.col) * 4);
+    const uint32_t lane_off = static_cast<uint32_t>((2 * ap.row0 * D + col + ap.col) * 4);
     auto pool_state = [&](int it, bool live) {
         return BufRsrc(pool + (static_cast<long>(sg.slot) * H + h0 + it) * D * D, live ? D * D * 4 : 0u);
     };
@@ -1083,7 +1085,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (mt * 16 + r) * D * 4);
+                for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (srow(mt, 0) + r) * D * 4);
         }
     };
     auto final_state = [&](int it, bool live) {
@@ -1091,7 +1093,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (mt * 16 + r) * D * 4);
+            for (int r = 0; r < 4; ++r) rs.storef(S[mt][r], lane_off, (srow(mt, 0) + r) * D * 4);
     };
     entry(0);
     if (nch == 0) {
@@ -1103,15 +1105,15 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
         return;
     }
     // P tiles above the diagonal that the products still read (rows 0-15 x
-    // columns 16-31, rows 32-47 x columns 48-63) stay zero
+    // keys 16-31, rows 32-47 x keys 48-63) stay zero
     for (int idx = tid; idx < 2 * 256; idx += NTH) {
         const int t = idx >> 8, e = idx & 255;
-        const int row = (t ? 32 : 0) + (e >> 4), cx = (t ? 48 : 16) + (e & 15);
+        const int row = (t ? 32 : 0) + (e >> 4), cx = p_col(t ? 3 : 1, (e >> 2) & 3) + (e & 3);
         sp[row][cx] = 0;
     }
     auto stage = [&](KGate& kk) {
         g_stage_gates(kk.g2, kk.eg, kk.dec, &kk.gamma, pf);
-        g_stage_tile<true>(&kk.k[0][0], LK, pf.k, &kk.kx[0][0], LX);
+        g_stage_tile<true>(&kk.k[0][0], LK, pf.k);
         g_stage_tile<true>(&sq[0][0], LQ, pf.q);
         g_stage_tile<false>(&sv[0][0], LK, pf.v);
         g_stage_plane(st, pf.t);
@@ -1139,7 +1141,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
             const int jj = jt * 16 + ap.row0 + r;
             pt[r] = (jj <= i) ? pt[r] * hw_exp2(gi - kk.g2[jj]) : 0.f;
         }
-        *reinterpret_cast<u32x2*>(&sp[i][jt * 16 + ap.row0]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
+        *reinterpret_cast<u32x2*>(&sp[i][p_col(jt, ap.row0 >> 2)]) = u32x2{pk_f16(pt[0], pt[1]), pk_f16(pt[2], pt[3])};
     };
     // bf16 outputs of chunk cc of item it: LDS -> HBM, 16 lanes per 256-byte row
     auto flush_o = [&](int cc, int it, bool live) {
@@ -1171,7 +1173,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
         bf16x8 sf[4];
         const Scale ss = state_operand(sf, S);
         f32x4 X[4], ot[4];
-        k_times_s<true>(X, ot, sf, &kk.kx[0][0], &sq[0][0]);
+        k_times_s<true>(X, ot, sf, &kk.k[0][0], &sq[0][0]);
         bf16x8 vf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&sv[0][0], LK, col, 32 * ks);
@@ -1187,7 +1189,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
         for (int it = 0; it < 4; ++it) {
             f32x4 pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks <= (it >> 1); ++ks) pu = mfma_f16(uf[ks], frag_kc_split(&sp[0][0], LP, it * 16, 32 * ks), pu);
+            for (int ks = 0; ks <= (it >> 1); ++ks) pu = mfma_f16(uf[ks], frag_kc(&sp[0][0], LP, it * 16, 32 * ks), pu);
             ot[it] += su.inv * pu;
         }
         if constexpr (TO::bytes == 2) {

@@ -275,32 +275,12 @@ __device__ __forceinline__ const float* frag_slot(const float* ws, long slot) {
     return ws + slot * SD * SD + threadIdx.x * 32;
 }
 
-// Which state rows the accumulator tiles hold.  In the output pass, tile mt
-// gives lane group g (tile rows 4g..4g+3) the state rows
-// srow(mt, 4g) + r = 32 (mt / 2) + 8 g + 4 (mt % 2) + r, so that tiles 2s
-// and 2s + 1 hand each lane the 8 consecutive rows 32 s + 8 g .. + 7 as an
-// MFMA operand: S^T then pairs with q fragments in natural order, one
-// 16-byte LDS read each.  Pass 1, which never multiplies S by q, keeps
-// the plain order (tile mt, rows 16 mt + 4 g + r) and reorders its tiles
-// only as it writes them to the workspace.
-__device__ __forceinline__ int srow(int mt, int row0) { return 32 * (mt >> 1) + 2 * row0 + 4 * (mt & 1); }
-
-// Where P's keys sit along an LDS row of P: keys 16 jt + 4 g .. + 3 (key
-// tile jt, lane group g of the tile's MFMA) at 32 (jt / 2) + 8 g + 4 (jt % 2),
-// so that one 16-byte read at 32 ks + 8 g returns keys
-// {32 ks + 4 g .. + 3} u {32 ks + 16 + 4 g .. + 3}, the split k order of the
-// V^T operand.
-__device__ __forceinline__ int p_col(int jt, int g) { return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1); }
-
-// K^T operand (lines = state rows of output-pass tile mt, in the order
-// above; tokens in the split k order) for the state update
-__device__ __forceinline__ bf16x8 frag_kt_out(const uint16_t* base, int ld, int mt, int k0) {
-    const int lane = threadIdx.x & 63;
-    const int i = lane & 15;
-    const uint16_t* p = base + (k0 + (lane >> 4) * 4 + (i >> 2)) * ld + 32 * (mt >> 1) + 8 * (i & 3) + 4 * (mt & 1);
-    return cat8(ld_tr16(p), ld_tr16(p + 16 * ld));
-}
-
+// The output pass holds the state in the accumulator row order srow()
+// (tiles 2s and 2s + 1 give each lane 8 consecutive state rows, which meet
+// q fragments in natural order).  Pass 1, which never multiplies S by q,
+// keeps the plain order (tile mt, rows 16 mt + 4 g + r), in which its
+// transpose reads of K run at full rate, and reorders its tiles only as it
+// writes them to the workspace.
 // This wave's 8 state tiles read from a row-major [d][n] state (OUT: the
 // output pass's row order).
 template <bool OUT>
@@ -463,7 +443,7 @@ __device__ __forceinline__ void seg_update_prep(SegUpd& up, f32x4 (&S)[8], const
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
-            up.kf[ks][mt] = OUT ? frag_kt_out(&bb.k[0][0], LK, mt, 32 * ks)
+            up.kf[ks][mt] = OUT ? frag_kt_pair(&bb.k[0][0], LK, mt, 32 * ks)
                                 : frag_km_split(&bb.k[0][0], LK, mt * 16, 32 * ks);
     __builtin_amdgcn_sched_barrier(0);
     // decayed values for tokens {32ks + 4g + e} u {32ks + 16 + 4g + e}, split
