@@ -78,6 +78,7 @@ constexpr int CH = 64;             // chunk
 constexpr int LQ = D + 16;         // q
 constexpr int LK = D + 16;         // k, v
 constexpr int LP = CH + 16;        // P and T diag(beta), keys in p_col() order
+constexpr int LO = D + 8;          // outputs: 8-byte writes (16 rows x 4 lane groups), row reads
 constexpr int kTargetBlocks = 256; // about one workgroup per compute unit
 constexpr int kPlaneElems = CH * CH;       // T diag(beta) (fp16) per (chunk, head)
 
@@ -828,7 +829,7 @@ struct OutSmem {
     alignas(16) uint16_t sv[CH][LK];      // bf16
     alignas(16) uint16_t st[CH][LP];      // T diag(beta), fp16, scaled
     alignas(16) uint16_t sp[CH][LP];      // P, fp16
-    alignas(16) uint16_t obuf[CH][LQ];    // bf16 outputs of the previous chunk
+    alignas(16) uint16_t obuf[CH][LO];    // bf16 outputs of the previous chunk
 };
 
 // Pass 2 for segment si of head h (bid = si * H + h); SPLIT selects the
@@ -859,7 +860,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
     uint16_t (&sv)[CH][LK] = sm.sv;
     uint16_t (&st)[CH][LP] = sm.st;
     uint16_t (&sp)[CH][LP] = sm.sp;
-    uint16_t (&obuf)[CH][LQ] = sm.obuf;
+    uint16_t (&obuf)[CH][LO] = sm.obuf;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1036,7 +1037,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
     uint16_t (&sv)[CH][LK] = sm.sv;
     uint16_t (&st)[CH][LP] = sm.st;
     uint16_t (&sp)[CH][LP] = sm.sp;
-    uint16_t (&obuf)[CH][LQ] = sm.obuf;
+    uint16_t (&obuf)[CH][LO] = sm.obuf;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -73,6 +73,10 @@ constexpr int SC = 64;             // chunk
 constexpr int LQ = SD + 16;        // 72 dwords
 constexpr int LK = SD + 16;        // 72 dwords
 constexpr int SP = SC + 16;        // LDS line of a P row (40 dwords)
+// The output rows are written 8 bytes a lane (16 rows x 4 lane groups) and
+// read back as whole rows: rows 68 dwords apart keep the 8-byte writes at
+// their best rate, which 72 would halve.
+constexpr int LO = SD + 8;
 constexpr int kSegBlocks = 256;    // one workgroup on each of the 256 compute units
 constexpr int kShortChunks = 4;    // batches of sequences this short (mean chunks) ...
 constexpr int kMaxItems = 16;      // ... put up to this many heads in one output-pass block
@@ -562,7 +566,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     __shared__ QKVBuf buf[2];
     __shared__ uint16_t pbuf[2][SC][SP];           // P = (Q K^T) .* D, hi and lo planes
     // bf16 outputs of the previous chunk, stored to HBM as whole rows
-    __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LQ];
+    __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LO];
     // NORM: z_in by chunk parity, row sums of the 10 P tiles, phi(q_i) . z_in
     __shared__ alignas(16) float zb[NORM ? 2 : 1][NORM ? SD : 1];
     __shared__ float dpart[NORM ? 10 : 1][16];
@@ -859,7 +863,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     __shared__ QKVBuf buf[2];
     __shared__ uint16_t pbuf[2][SC][SP];           // P = (Q K^T) .* D, hi and lo planes
     // bf16 outputs of the previous chunk, stored to HBM as whole rows
-    __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LQ];
+    __shared__ uint16_t obuf[TO::bytes == 2 ? SC : 1][LO];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
