@@ -452,12 +452,12 @@ __device__ __forceinline__ bool seg_bounds(GSeg& sg, int b, int g, int nseg, con
 // T diag(beta) for every (chunk, head), one wave per item, the items strided
 // over a persistent grid.  A = strictly-lower(diag(beta) (K K^T .* D)) comes
 // from the MFMA on K fragments loaded straight from HBM; T = (I + A)^-1 by
-// forward substitution with one lane per column of T (lane j keeps column
-// j in registers and reads row r of A from LDS as a broadcast:
-// x_r = [r == j] - sum_{m < r} A_rm x_m); then column j is scaled by beta_j,
-// the item by a power of two (range guard; its inverse goes to tinv), and
-// written as one fp16 plane, one 128-byte row per store instruction.  Rows
-// 0..31 x columns 32..63 are zero and never read: not written.
+// 16 x 16 blocks (forward substitution on the diagonal blocks, the fp32
+// MFMA for the others); then lane j takes column j of T, scales it by
+// beta_j and the item by a power of two (range guard; its inverse goes to
+// tinv), and the item is written as one fp16 plane, one 128-byte row per
+// store instruction.  Rows 0..31 x columns 32..63 are zero and never read:
+// not written.
 constexpr int PW = 4;              // waves per prep workgroup
 constexpr int LA = CH + 4;         // fp32 row stride of A in LDS
 constexpr int kPrepGroups = 512;   // 2 resident workgroups per compute unit
@@ -469,6 +469,7 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
     __shared__ alignas(16) float As[PW][CH][LA];
     __shared__ alignas(16) float gs[PW][CH];
     __shared__ alignas(16) float bs[PW][CH];
+    __shared__ float Ws[PW][16][17];      // one 16 x 16 product on its way to an MFMA operand
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const AccPos ap;
@@ -522,27 +523,88 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
             }
         }
         wave_sync();
-        // T = (I + A)^-1, column `me` (the lane index, recomputed per item so
-        // the 64 selects below are not hoisted out of the item loop)
+        // T = (I + A)^-1 (A strictly lower triangular, so I + A is unit lower
+        // triangular) by 16 x 16 blocks: the diagonal blocks
+        // T_bb = (I + A_bb)^-1 by forward substitution, lane c of lane group
+        // b solving for column c of T_bb; then, for i > j in order of i - j,
+        //   T_ij = -T_ii (sum over j <= k < i of A_ik T_kj)
+        // on the fp32 MFMA.  A's blocks below the diagonal stay in place;
+        // T goes transposed into the upper half, T[r][c] at As[c][r] for r
+        // in c's block row or below, over A's diagonal blocks once those are
+        // solved.  One wave owns As[wave]: its LDS operations complete in
+        // order, and wave_sync() keeps the compiler from reordering them.
+        {
+            const int bb = lane >> 4, c = lane & 15;
+            float* Ab = &As[wave][16 * bb][16 * bb];
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < r; m += 4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(Ab + r * LA + m);
+                    acc -= a4.x * x[m];
+                    if (m + 1 < r) acc -= a4.y * x[m + 1];
+                    if (m + 2 < r) acc -= a4.z * x[m + 2];
+                    if (m + 3 < r) acc -= a4.w * x[m + 3];
+                }
+                x[r] = acc;
+            }
+            wave_sync();
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(Ab + c * LA + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        }
+        wave_sync();
+        {
+            float* Aw = &As[wave][0][0];
+            float* Wt = &Ws[wave][0][0];
+            const int i16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+            for (int d = 1; d < 4; ++d) {
+#pragma unroll
+                for (int bi = d; bi < 4; ++bi) {
+                    const int bj = bi - d;
+                    // W = sum_k A_ik T_kj: A_ik[i16][4 s + kg] in place, T_kj[4 s + kg][i16] transposed
+                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int bk = bj; bk < bi; ++bk)
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+                            w = mfma_f32(Aw[(16 * bi + i16) * LA + 16 * bk + 4 * s4 + kg],
+                                         Aw[(16 * bj + i16) * LA + 16 * bk + 4 * s4 + kg], w);
+                    // W (lane: column i16, rows 4 kg .. + 3) through LDS into the B layout
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Wt[(4 * kg + r) * 17 + i16] = w[r];
+                    wave_sync();
+                    // T_ii W: T_ii[i16][4 s + kg] transposed, W[4 s + kg][i16]
+                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        t = mfma_f32(Aw[(16 * bi + 4 * s4 + kg) * LA + 16 * bi + i16], Wt[(4 * s4 + kg) * 17 + i16], t);
+                    // T_ij[4 kg + r][i16] = -t[r], transposed into block (j, i)
+                    *reinterpret_cast<f32x4*>(&Aw[(16 * bj + i16) * LA + 16 * bi + 4 * kg]) = -t;
+                    wave_sync();
+                }
+            }
+        }
+        // column `me` of T (the lane index, recomputed per item so the
+        // selects below are not hoisted out of the item loop): row me of As
+        // from me's block on, zero above it
         const int me = opaque(lane);
         float x[CH];
+        {
+            const float* Tc = &As[wave][me][0];
+            const int b0 = me >> 4;
 #pragma unroll
-        for (int r = 0; r < CH; ++r) x[r] = 0.f;
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            float acc = (r == me) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < r; m += 4) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&As[wave][r][m]);
-                acc -= a4.x * x[m];
-                if (m + 1 < r) acc -= a4.y * x[m + 1];
-                if (m + 2 < r) acc -= a4.z * x[m + 2];
-                if (m + 3 < r) acc -= a4.w * x[m + 3];
+            for (int q = 0; q < CH / 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(Tc + 4 * q);
+                const bool keep = (q >> 2) >= b0;
+                x[4 * q] = keep ? v.x : 0.f;
+                x[4 * q + 1] = keep ? v.y : 0.f;
+                x[4 * q + 2] = keep ? v.z : 0.f;
+                x[4 * q + 3] = keep ? v.w : 0.f;
             }
-            x[r] = acc;
-            // keep the next rows' LDS reads from being hoisted (and held in
-            // registers) across this one
-            __builtin_amdgcn_sched_barrier(0);
         }
         // T diag(beta) -> an fp16 plane scaled by a power of two (its
         // inverse kept per item), row r per store instruction
