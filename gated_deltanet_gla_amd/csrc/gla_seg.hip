@@ -81,11 +81,14 @@ constexpr int kSegBlocks = 256;    // one workgroup on each of the 256 compute u
 constexpr int kShortChunks = 4;    // batches of sequences this short (mean chunks) ...
 constexpr int kMaxItems = 16;      // ... put up to this many heads in one output-pass block
 
+// Gate tables of a chunk (seg_stage_gates): dec, the update's weights;
+// smul, what the held state is multiplied by before the update (1: not
+// at all); sig, the state's scale after the update.
 struct KVBuf {                     // pass 1 staging
     alignas(16) uint16_t k[SC][LK];
     alignas(16) uint16_t v[SC][LK];
-    alignas(16) float dec[SC];     // 2^(g2_last - g2)
-    float gamma;                   // 2^g2_last
+    alignas(16) float dec[SC];
+    float smul, sig;
 };
 
 struct QKVBuf {                    // pass 2 staging
@@ -93,9 +96,9 @@ struct QKVBuf {                    // pass 2 staging
     alignas(16) uint16_t k[SC][LK];
     alignas(16) uint16_t v[SC][LK];
     alignas(16) float g2[SC];      // running log2 decay inside the chunk
-    alignas(16) float eg[SC];      // 2^g2
+    alignas(16) float eg[SC];      // 2^g2 times the entry state's scale
     alignas(16) float dec[SC];
-    float gamma;
+    float smul, sig;
 };
 
 template <bool WQ>
@@ -385,10 +388,22 @@ __device__ __forceinline__ void seg_stage_rows(Buf& bb, const SegPrefetch<WQ>& p
     }
 }
 
+// The state is held as S = sigma Shat, sigma a running product of the
+// chunks' total decays gamma = 2^g2_last: the update
+// S <- gamma S + K^T diag(2^(g2_last - g2)) V is then
+// Shat <- Shat + K^T diag(2^(-g2 - log2 sigma)) V with sigma <- gamma sigma, no
+// pass over the state, as long as gamma sigma stays at or above
+// 2^kFoldFloor; a chunk that would take it lower scales Shat by gamma sigma
+// before its update and restarts sigma at 1.  That bounds Shat by
+// 2^-kFoldFloor |S| and the weights by 2^(-2 kFoldFloor).
+constexpr float kFoldFloor = -30.f;
+
 // Wave 0 scans log2(alpha), writes the per-token tables and gets the chunk's
-// total log2 decay back (other waves get 0).
+// total log2 decay back (other waves get 0).  lsig: log2 sigma of the state
+// entering the chunk on wave 0, updated to the state leaving it; reset: the
+// chunk starts a new state (sigma = 1).
 template <bool WQ, bool NORM = false, class Buf>
-__device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>& pf) {
+__device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>& pf, float& lsig, bool reset = false) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     float glast = 0.f;
@@ -396,12 +411,19 @@ __device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>&
         const float a = (!NORM && lane < pf.n) ? pf.a : 1.f;
         const float x = wave_inclusive_sum(__log2f(fmaxf(a, kMinDecay)));
         glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), SC - 1));
+        const float l0 = reset ? 0.f : lsig;
+        const bool fold = l0 + glast >= kFoldFloor;
         if constexpr (WQ) {
             bb.g2[lane] = x;
-            bb.eg[lane] = hw_exp2(x);
+            bb.eg[lane] = hw_exp2(x + l0);
         }
-        bb.dec[lane] = hw_exp2(glast - x);
-        if (lane == 0) bb.gamma = hw_exp2(glast);
+        bb.dec[lane] = hw_exp2(fold ? -x - l0 : glast - x);
+        if (lane == 0) {
+            bb.smul = fold ? 1.f : hw_exp2(l0 + glast);
+            bb.sig = fold ? hw_exp2(l0 + glast) : 1.f;
+        }
+        // wave-uniform: kept in a scalar register across the chunk loop
+        lsig = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, fold ? l0 + glast : 0.f)));
     }
     return glast;
 }
@@ -409,8 +431,8 @@ __device__ __forceinline__ float seg_stage_gates(Buf& bb, const SegPrefetch<WQ>&
 // Registers -> LDS (rows and gate tables); returns the chunk's total log2
 // decay on wave 0.
 template <bool WQ, bool NORM = false, class Buf>
-__device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf) {
-    const float glast = seg_stage_gates<WQ, NORM>(bb, pf);
+__device__ __forceinline__ float seg_stage(Buf& bb, const SegPrefetch<WQ>& pf, float& lsig) {
+    const float glast = seg_stage_gates<WQ, NORM>(bb, pf, lsig);
     seg_stage_rows<WQ, NORM>(bb, pf);
     return glast;
 }
@@ -434,14 +456,17 @@ __device__ __forceinline__ void load_vt(bf16x8 (&vf)[2], const Buf& bb, int col)
     for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&bb.v[0][0], LK, col, 32 * ks);
 }
 
-// State update S (this wave's 16 columns, all 8 row tiles) <- gamma S +
+// State update Shat (this wave's 16 columns, all 8 row tiles) <- smul Shat +
 // K^T diag(dec) V, in two parts: the operand reads and the VALU work
-// (decayed, split values; the gamma scaling), then the MFMAs.
+// (decayed, split values; the smul scaling), then the MFMAs.
 struct SegUpd {
     bf16x8 kf[2][8];
     bf16x8 vh[2], vl[2];
 };
-template <bool OUT, class Buf>
+// SKIP: a block-uniform branch skips the multiply when smul is 1 (where
+// the branch would make the loop's register allocation spill, the multiply
+// by 1 is done instead).
+template <bool OUT, bool SKIP, class Buf>
 __device__ __forceinline__ void seg_update_prep(SegUpd& up, f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -465,9 +490,11 @@ __device__ __forceinline__ void seg_update_prep(SegUpd& up, f32x4 (&S)[8], const
         up.vh[ks] = as_bf16x8(u32x4{hw[0], hw[1], hw[2], hw[3]});
         up.vl[ks] = as_bf16x8(u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
-    const float gam = bb.gamma;
+    const float sm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, bb.smul)));
+    if (!SKIP || sm != 1.f) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] *= gam;
+        for (int mt = 0; mt < 8; ++mt) S[mt] *= sm;
+    }
 }
 __device__ __forceinline__ void seg_update_mfma_half(f32x4 (&S)[8], const SegUpd& up, int ks) {
 #pragma unroll
@@ -483,7 +510,7 @@ __device__ __forceinline__ void seg_update_mfma(f32x4 (&S)[8], const SegUpd& up)
 template <class Buf>
 __device__ __forceinline__ void seg_state_update(f32x4 (&S)[8], const Buf& bb, const bf16x8 (&vf)[2]) {
     SegUpd up;
-    seg_update_prep<false>(up, S, bb, vf);
+    seg_update_prep<false, true>(up, S, bb, vf);
     __builtin_amdgcn_sched_barrier(0);
     seg_update_mfma(S, up);
 }
@@ -526,9 +553,9 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     auto rows = [&](int c) { return c < nch ? min(SC, sg.t1 - sg.t0 - c * SC) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * SC; };
     SegPrefetch<false> pf;
-    float lam = 0.f;
+    float lam = 0.f, lsig = 0.f;
     seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(0), rows(0), sg.h, H);
-    lam += seg_stage<false, NORM>(buf[0], pf);
+    lam += seg_stage<false, NORM>(buf[0], pf, lsig);
     seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(1), rows(1), sg.h, H);
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
@@ -536,11 +563,16 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
         load_vt(vf, buf[c & 1], col);
         seg_state_update(S, buf[c & 1], vf);
         if constexpr (NORM) seg_z_update(zacc, buf[c & 1], wave);
-        const float gl = seg_stage<false, NORM>(buf[(c + 1) & 1], pf);
+        const float gl = seg_stage<false, NORM>(buf[(c + 1) & 1], pf, lsig);
         if (c + 1 < nch) lam += gl;
         seg_fetch<false, !NORM>(pf, nullptr, k, v, alpha, tok(c + 2), rows(c + 2), sg.h, H);
         lds_barrier();
     }
+    // dS = sigma Shat (sigma after the last chunk; the loop's last staging
+    // went to the other buffer)
+    const float sgl = nch > 0 ? buf[(nch - 1) & 1].sig : 1.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] *= sgl;
     store_slot_out_order(wstate, sg.ws_slot, S);
     if (threadIdx.x == 0) wlam[sg.ws_slot] = lam;
     if constexpr (NORM) {
@@ -625,7 +657,8 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         pbuf[0][row][cx] = 0;
         pbuf[1][row][cx] = 0;
     }
-    seg_stage<true, NORM>(buf[0], pf);
+    float lsig = 0.f;                              // log2 sigma on wave 0
+    seg_stage<true, NORM>(buf[0], pf, lsig);
     seg_fetch<true, !NORM>(pf, q, k, v, alpha, tok(1), rows(1), sg.h, H);
     lds_barrier();
 
@@ -760,7 +793,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         // the state update's operand reads and VALU work go ahead of the
         // P V MFMAs, which do not depend on them, so they can overlap
         SegUpd up;
-        seg_update_prep<true>(up, S, bb, vf);
+        seg_update_prep<true, !CKPT>(up, S, bb, vf);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
@@ -800,7 +833,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         seg_update_mfma_half(S, up, 0);
         seg_stage_rows<true, NORM>(buf[(c + 1) & 1], pf);
         seg_update_mfma_half(S, up, 1);
-        seg_stage_gates<true, NORM>(buf[(c + 1) & 1], pf);
+        seg_stage_gates<true, NORM>(buf[(c + 1) & 1], pf, lsig);
         if constexpr (NORM) {
             // z_in of the next chunk = z_in + this chunk's sums of phi(k)
             f32x4 zc = {0.f, 0.f, 0.f, 0.f};
@@ -819,7 +852,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sc[(srow(mt, 0) + r) * SD] = S[mt][r];
+                for (int r = 0; r < 4; ++r) Sc[(srow(mt, 0) + r) * SD] = S[mt][r] * bb.sig;
             }
         }
         lds_barrier();
@@ -827,10 +860,11 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     if (nch > 0) flush_o(nch - 1);
 
     if (sg.g == sg.nseg - 1) {
+        const float sgl = nch > 0 ? buf[(nch - 1) & 1].sig : 1.f;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sg[(srow(mt, ap.row0) + r) * SD + col + ap.col] = S[mt][r];
+            for (int r = 0; r < 4; ++r) Sg[(srow(mt, ap.row0) + r) * SD + col + ap.col] = S[mt][r] * sgl;
         }
         if constexpr (NORM) {
             // z after the last chunk (the loop ends with a barrier)
@@ -961,18 +995,20 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     // a one-segment entry state is zeros: no loads, no wait.
     constexpr int kRow = SD + 4;
     static_assert(96 * kRow * 4 <= sizeof(QKVBuf) && 32 * kRow * 4 <= sizeof(pbuf), "state staging");
+    static_assert(offsetof(QKVBuf, sig) >= 96 * kRow * 4, "the staged state leaves sig in place");
     auto next_item = [&](int it, QKVBuf& fb) {
         float* lo = reinterpret_cast<float*>(&fb);
         float* hi = reinterpret_cast<float*>(&pbuf[0][0][0]);
         // lane offsets recomputed here (opaque), not held across the chunk loop
         if (last_seg) {
+            const float sgl = fb.sig;          // S = sigma Shat after the item's last chunk
             const int wo = opaque(2 * ap.row0 * kRow + col + ap.col);
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
                 // state rows srow(mt, .): tiles 0-5 hold rows 0-95, tiles 6 and 7 rows 96-127
                 float* base = (mt < 6 ? lo + srow(mt, 0) * kRow : hi + (srow(mt, 0) - 96) * kRow) + wo;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) base[r * kRow] = S[mt][r];
+                for (int r = 0; r < 4; ++r) base[r * kRow] = S[mt][r] * sgl;
             }
         }
         if (it + 1 < items) entry(it + 1);
@@ -1001,7 +1037,8 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     };
     entry(0);
     zero_p_upper();
-    seg_stage<true, false>(buf[0], pf);
+    float lsig = 0.f;                              // log2 sigma on wave 0
+    seg_stage<true, false>(buf[0], pf, lsig);
     {
         int c1, i1;
         step(0, 0, 1, c1, i1);
@@ -1120,7 +1157,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         // the state update's operand reads and VALU work go ahead of the
         // P V MFMAs, which do not depend on them, so they can overlap
         SegUpd up;
-        seg_update_prep<true>(up, S, bb, vf);
+        seg_update_prep<true, false>(up, S, bb, vf);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             ot[it] = mfma_bf16(vf[0], pp[it][0], ot[it]);
@@ -1149,8 +1186,8 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         seg_update_mfma_half(S, up, 0);
         seg_stage_rows<true, false>(buf[(vc + 1) & 1], pf);
         seg_update_mfma_half(S, up, 1);
-        seg_stage_gates<true, false>(buf[(vc + 1) & 1], pf);
         const bool item_end = c == nch - 1;
+        seg_stage_gates<true, false>(buf[(vc + 1) & 1], pf, lsig, item_end);
         {
             int c2, i2;
             step(c, item, 2, c2, i2);
