@@ -355,15 +355,46 @@ __device__ __forceinline__ Scale form_u(bf16x8 (&uf)[2], bf16x8 (&df)[2], const 
     return sc;
 }
 
-// S (this wave's columns) <- gamma S + K^T diag(dec) U (df carries dinv).
+// A float that is the same on every lane, in a scalar register.
+__device__ __forceinline__ float uniform_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// The state may be held as S = sigma Shat, sigma a running product of the
+// chunks' decays gamma: the update S <- gamma S + X is then
+// Shat <- Shat + X / (gamma sigma) with sigma <- gamma sigma, no pass over
+// the state, while gamma sigma stays at or above kFoldMin; a chunk that
+// would take it lower scales Shat by gamma sigma first and restarts sigma
+// at 1.  Shat stays within 2^30 |S|.  fold_scale() applies that rule (to S
+// and, if given, M) and returns the factor of X.
+constexpr float kFoldMin = 0x1p-30f;
+__device__ __forceinline__ float fold_scale(f32x4 (&S)[8], f32x4* M, float gam, float& sigma) {
+    const float gs = uniform_f(gam * sigma);
+    const bool fold = gs >= kFoldMin;
+    if (!fold) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            S[mt] *= gs;
+            if (M) M[mt] *= gs;
+        }
+    }
+    sigma = fold ? gs : 1.f;
+    return fold ? __builtin_amdgcn_rcpf(gs) : 1.f;
+}
+
+// S (this wave's columns) <- gamma S + K^T diag(dec) U (df carries dinv);
+// FOLD: S held as sigma Shat (fold_scale).
+template <bool FOLD>
 __device__ __forceinline__ void state_update(f32x4 (&S)[8], const uint16_t* kbase, float gam, const bf16x8 (&df)[2],
-                                             float dinv) {
+                                             float dinv, float& sigma) {
+    float dm = dinv;
+    if constexpr (FOLD) dm *= fold_scale(S, nullptr, gam, sigma);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) acc = mfma_f16(frag_kt_pair(kbase, LK, mt, 32 * ks), df[ks], acc);
-        S[mt] = gam * S[mt] + dinv * acc;
+        S[mt] = FOLD ? S[mt] + dm * acc : gam * S[mt] + dm * acc;
     }
 }
 
@@ -403,8 +434,12 @@ __device__ __forceinline__ void k_times_sm(f32x4 (&XS)[4], f32x4 (&XM)[4], const
         }
     }
 }
+// Pass 1's update of [S | M], both held with the same sigma.
 __device__ __forceinline__ void state_update_sm(f32x4 (&S)[8], f32x4 (&M)[8], const uint16_t* kbase, float gam,
-                                                const bf16x8 (&sdf)[2], float sinv, const bf16x8 (&mdf)[2], float minv) {
+                                                const bf16x8 (&sdf)[2], float sinv, const bf16x8 (&mdf)[2], float minv,
+                                                float& sigma) {
+    const float f = fold_scale(S, M, gam, sigma);
+    const float sd = sinv * f, md = minv * f;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
         f32x4 as = {0.f, 0.f, 0.f, 0.f}, am = {0.f, 0.f, 0.f, 0.f};
@@ -414,8 +449,8 @@ __device__ __forceinline__ void state_update_sm(f32x4 (&S)[8], f32x4 (&M)[8], co
             as = mfma_f16(kt, sdf[ks], as);
             am = mfma_f16(kt, mdf[ks], am);
         }
-        S[mt] = gam * S[mt] + sinv * as;
-        M[mt] = gam * M[mt] + minv * am;
+        S[mt] += sd * as;
+        M[mt] += md * am;
     }
 }
 
@@ -696,6 +731,7 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
 #pragma unroll
         for (int r = 0; r < 4; ++r) M[mt][r] = (mt * 16 + ap.row0 + r == col + ap.col) ? 1.f : 0.f;
     }
+    float sigma = 1.f;          // [S | M] = sigma [Shat | Mhat]
 
     auto rows = [&](int c) { return c < nch ? min(CH, sg.t1 - sg.t0 - c * CH) : 0; };
     auto tok = [&](int c) { return static_cast<long>(sg.t0) + static_cast<long>(c < nch ? c : 0) * CH; };
@@ -727,16 +763,21 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
         f32x4 XS[4], XM[4];
         k_times_sm(XS, XM, sf, mf, &bb.k[0][0]);
         bf16x8 yf[2], un[2], sdf[2], mdf[2];
-        const Scale sy = form_y<false>(yf, XS, vf, bb.eg, ss.inv);
+        const Scale sy = form_y<false>(yf, XS, vf, bb.eg, ss.inv * sigma);
         const Scale su = form_u<false>(un, sdf, yf, bb.t, bb.dec, bb.tinv * sy.inv);
-        const Scale my = form_y<true>(yf, XM, vf, bb.eg, sm.inv);
+        const Scale my = form_y<true>(yf, XM, vf, bb.eg, sm.inv * sigma);
         const Scale mu = form_u<false>(un, mdf, yf, bb.t, bb.dec, bb.tinv * my.inv);
-        state_update_sm(S, M, &bb.k[0][0], bb.gamma, sdf, su.inv, mdf, mu.inv);
+        state_update_sm(S, M, &bb.k[0][0], uniform_f(bb.gamma), sdf, su.inv, mdf, mu.inv, sigma);
         stage(buf[(c + 1) & 1]);
         fetch(c + 2);
         lds_barrier();
     }
     const long slot = (sg.jsplit + g) * H + h;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        S[mt] *= sigma;
+        M[mt] *= sigma;
+    }
     g_slot_store(g_slot(a.wsS, slot), S);
     // M[16 mt + row0 + r][col + ap.col] -> row block mt, column k = col + ap.col
     // (s = wave / 2, h2 = wave % 2), fragment lane row0 + r + 16 (ap.col / 4)
@@ -938,8 +979,9 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
     auto fetch = [&](int c) { g_fetch(pf, src, c, rows(c)); };
     fetch(0);
 
-    // entry state
+    // entry state, held as S = sigma Shat (fold_scale)
     f32x4 S[8];
+    float sigma = 1.f;
     float* Sg = pool + (static_cast<long>(sg.slot) * H + h) * D * D;
     if (sg.nseg <= 1) {
 #pragma unroll
@@ -1015,10 +1057,10 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&sv[0][0], LK, col, 32 * ks);
         bf16x8 yf[2], uf[2], df[2];
-        const Scale sy = form_y<false>(yf, X, vf, kk.eg, ss.inv);
+        const Scale sy = form_y<false>(yf, X, vf, kk.eg, ss.inv * sigma);
         const Scale su = form_u(uf, df, yf, st, kk.dec, kk.tinv * sy.inv);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) ot[it] *= kk.eg[it * 16 + ap.col] * ss.inv;
+        for (int it = 0; it < 4; ++it) ot[it] *= kk.eg[it * 16 + ap.col] * (ss.inv * sigma);
         lds_barrier();
 
         // ---- phase 2: O^T += U^T P^T; outputs; state update; next chunk
@@ -1042,7 +1084,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
                 ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
                               static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
         }
-        state_update(S, &kk.k[0][0], kk.gamma, df, su.inv);
+        state_update<true>(S, &kk.k[0][0], uniform_f(kk.gamma), df, su.inv, sigma);
         stage(kb[(c + 1) & 1]);
         fetch(c + 2);
         // checkpoint: this wave's columns of the state after chunk c
@@ -1052,7 +1094,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sc[(srow(mt, 0) + r) * D] = S[mt][r];
+                for (int r = 0; r < 4; ++r) Sc[(srow(mt, 0) + r) * D] = S[mt][r] * sigma;
             }
         }
         lds_barrier();
@@ -1063,7 +1105,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sg[(srow(mt, ap.row0) + r) * D + col + ap.col] = S[mt][r];
+            for (int r = 0; r < 4; ++r) Sg[(srow(mt, ap.row0) + r) * D + col + ap.col] = S[mt][r] * sigma;
         }
     }
 }
@@ -1140,6 +1182,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
         return BufRsrc(pool + (static_cast<long>(sg.slot) * H + h0 + it) * D * D, live ? D * D * 4 : 0u);
     };
     f32x4 S[8];
+    float sigma = 1.f;           // the update here keeps S itself (no running scale)
     auto entry = [&](int it) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1241,10 +1284,10 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) vf[ks] = frag_km_split(&sv[0][0], LK, col, 32 * ks);
         bf16x8 yf[2], uf[2], df[2];
-        const Scale sy = form_y<false>(yf, X, vf, kk.eg, ss.inv);
+        const Scale sy = form_y<false>(yf, X, vf, kk.eg, ss.inv * sigma);
         const Scale su = form_u(uf, df, yf, st, kk.dec, kk.tinv * sy.inv);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) ot[it] *= kk.eg[it * 16 + ap.col] * ss.inv;
+        for (int it = 0; it < 4; ++it) ot[it] *= kk.eg[it * 16 + ap.col] * (ss.inv * sigma);
         lds_barrier();
 
         // ---- phase 2: O^T += U^T P^T; outputs; state update; next chunk
@@ -1267,7 +1310,7 @@ __device__ __forceinline__ void seg_out_multi(OutSmem& sm, int bid0, int items, 
                 ro.store_b128(__builtin_bit_cast(u32x4, ot[it]),
                               static_cast<uint32_t>(((it * 16 + ap.col) * stride + col + ap.row0) * 4));
         }
-        state_update(S, &kk.k[0][0], kk.gamma, df, su.inv);
+        state_update<false>(S, &kk.k[0][0], kk.gamma, df, su.inv, sigma);
         stage(kb[(vc + 1) & 1]);
         {
             int c2, i2;
