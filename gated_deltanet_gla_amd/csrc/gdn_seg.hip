@@ -495,6 +495,7 @@ __device__ __forceinline__ bool seg_bounds(GSeg& sg, int b, int g, int nseg, con
 // not written.
 constexpr int PW = 4;              // waves per prep workgroup
 constexpr int LA = CH + 4;         // fp32 row stride of A in LDS
+constexpr int kPlRow = CH + 8;     // fp16 row stride of a plane staged in A's place
 constexpr int kPrepGroups = 512;   // 2 resident workgroups per compute unit
 
 __global__ void __launch_bounds__(PW * 64, 2)
@@ -515,28 +516,48 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
-    for (long item = static_cast<long>(blockIdx.x) * PW + wave; item < n_items;
-         item += static_cast<long>(gridDim.x) * PW) {
-        const int h = static_cast<int>(item % H);
-        const int ci = static_cast<int>(item / H);
-        const int b = find_span_owner(coff, n_seqs, ci);
-        const int s0 = clampi(cu[b], 0, n_tokens);
-        const int s1 = clampi(cu[b + 1], s0, n_tokens);
-        const int c0 = (ci - coff[b]) * CH;
-        const int n = max(0, min(CH, s1 - s0 - c0));
-        const long tok0 = s0 + max(c0, 0);
-
-        const BufRsrc rk(k + tok0 * stride + h * D, rows_extent(n, stride * 2, D * 2));
-        u32x4 kf[4][4];
+    // an item's rows: k from row tok0 of head h, n of them valid (none past
+    // the last item: its loads read nothing)
+    struct Item {
+        long tok0;
+        int h, n;
+    };
+    auto locate = [&](long item) {
+        Item it{0, 0, 0};
+        if (item < n_items) {
+            it.h = static_cast<int>(item % H);
+            const int ci = static_cast<int>(item / H);
+            const int b = find_span_owner(coff, n_seqs, ci);
+            const int s0 = clampi(cu[b], 0, n_tokens);
+            const int s1 = clampi(cu[b + 1], s0, n_tokens);
+            const int c0 = (ci - coff[b]) * CH;
+            it.n = max(0, min(CH, s1 - s0 - c0));
+            it.tok0 = s0 + max(c0, 0);
+        }
+        return it;
+    };
+    u32x4 kf[4][4];
+    float a, bt;
+    auto fetch = [&](const Item& it) {
+        const BufRsrc rk(k + it.tok0 * stride + it.h * D, rows_extent(it.n, stride * 2, D * 2));
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 kf[tt][ks] = rk.load16_nt(static_cast<uint32_t>(
                     ((tt * 16 + (lane & 15)) * stride + 32 * ks + (lane >> 4) * 8) * 2));
-        const uint32_t gext = rows_extent(n, static_cast<long>(H) * 4, 4);
-        const float a = BufRsrc(alpha + tok0 * H + h, gext).loadf_nt(static_cast<uint32_t>(lane * H * 4));
-        const float bt = BufRsrc(beta + tok0 * H + h, gext).loadf_nt(static_cast<uint32_t>(lane * H * 4));
+        const uint32_t gext = rows_extent(it.n, static_cast<long>(H) * 4, 4);
+        a = BufRsrc(alpha + it.tok0 * H + it.h, gext).loadf_nt(static_cast<uint32_t>(lane * H * 4));
+        bt = BufRsrc(beta + it.tok0 * H + it.h, gext).loadf_nt(static_cast<uint32_t>(lane * H * 4));
+    };
+    const long step = static_cast<long>(gridDim.x) * PW;
+    long item = static_cast<long>(blockIdx.x) * PW + wave;
+    Item cur = locate(item);
+    fetch(cur);
+    // the next item's loads are issued as soon as this item's A is formed,
+    // so they are in flight during the inversion and the plane stores
+    for (; item < n_items; item += step) {
+        const int n = cur.n;
         gs[wave][lane] = wave_inclusive_sum(__log2f(fmaxf(lane < n ? a : 1.f, kMinDecay)));
         bs[wave][lane] = lane < n ? bt : 0.f;
         wave_sync();
@@ -557,6 +578,9 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
                 }
             }
         }
+        const float bj = bs[wave][lane];        // read before the next item's beta lands
+        const Item nxt = locate(item + step);
+        fetch(nxt);
         wave_sync();
         // T = (I + A)^-1 (A strictly lower triangular, so I + A is unit lower
         // triangular) by 16 x 16 blocks: the diagonal blocks
@@ -642,26 +666,34 @@ gdn_seg_prep(const uint16_t* __restrict__ k, const float* __restrict__ alpha, co
             }
         }
         // T diag(beta) -> an fp16 plane scaled by a power of two (its
-        // inverse kept per item), row r per store instruction
-        const float bj = bs[wave][lane];
+        // inverse kept per item): column me into LDS (over A, all of which
+        // has been read), then whole rows out, 16 bytes a lane
         float mloc = 0.f;
 #pragma unroll
         for (int r = 0; r < CH; ++r) mloc = fmaxf(mloc, fabsf(x[r] * bj));
         const Scale sc = range_scale(mloc);
         if (lane == 0) tinv[item] = sc.inv;
-        const BufRsrc rp(planes + item * kPlaneElems, kPlaneElems * 2u);
         // column me of the plane sits at p_col() order (columns 32..63 stay in 32..63)
         const int pos = p_col(me >> 4, (me >> 2) & 3) + (me & 3);
+        uint16_t* pl = reinterpret_cast<uint16_t*>(&As[wave][0][0]);
+        wave_sync();
 #pragma unroll
         for (int r = 0; r < CH; r += 2) {
-            // rows r and r + 1 of column `me`: two 2-byte stores
             const uint32_t hv = pk_f16(x[r] * bj * sc.s, x[r + 1] * bj * sc.s);
-            const bool skip = r < 32 && me >= 32;
-            rp.store_b16(static_cast<uint16_t>(hv & 0xffffu),
-                         skip ? 0x80000000u : static_cast<uint32_t>((r * CH + pos) * 2));
-            rp.store_b16(static_cast<uint16_t>(hv >> 16),
-                         skip ? 0x80000000u : static_cast<uint32_t>(((r + 1) * CH + pos) * 2));
+            pl[r * kPlRow + pos] = static_cast<uint16_t>(hv & 0xffffu);
+            pl[(r + 1) * kPlRow + pos] = static_cast<uint16_t>(hv >> 16);
         }
+        wave_sync();
+        const BufRsrc rp(planes + item * kPlaneElems, kPlaneElems * 2u);
+#pragma unroll
+        for (int u = 0; u < CH * CH / 8 / 64; ++u) {
+            const int vix = lane + 64 * u, row = vix >> 3, cb = vix & 7;
+            // rows 0..31 x columns 32..63 are never read: not written
+            const bool skip = row < 32 && cb >= 4;
+            rp.store_b128(*reinterpret_cast<const u32x4*>(pl + row * kPlRow + 8 * cb),
+                          skip ? 0x80000000u : static_cast<uint32_t>((row * CH + 8 * cb) * 2));
+        }
+        cur = nxt;
         wave_sync();       // this wave's A and gate tables are rewritten by its next item
     }
 }
