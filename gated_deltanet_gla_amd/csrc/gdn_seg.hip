@@ -48,16 +48,19 @@
 // enters a segment: S_out = M S_in + dS, where dS is the segment's state
 // from S_in = 0 and M (d_k x d_k) its transition, the product of the chunks'
 // exp(g_last) I - K^T diag(exp(g_last - g)) T diag(b) diag(exp g) K.  So:
-//   pass 1 (gdn_seg_state): for every segment but the last of a sequence cut
-//     into several, dS and M, by running the state update alone on [S | M]
-//     from [0 | I] (M takes no values: its Y is -diag(exp g) K M);
-//   scan (gdn_seg_scan): per (sequence, head), S_in(0) = the pool state and
-//     S_in(j + 1) = M_j S_in(j) + dS_j, written over dS_j (S_in(0) to a slot
-//     of its own);
-//   pass 2 (gdn_seg_out): every segment from its S_in, outputs included; the
-//     last one writes the final state to the pool.
+//   phase A: every segment but the last of a sequence cut into several runs
+//     pass 1 (gdn_seg_state): dS and M, by running the state update alone
+//     on [S | M] from [0 | I] (M takes no values: its Y is
+//     -diag(exp g) K M).  In batches of many (sequence, head) pairs the
+//     first segment runs pass 2 here instead (it needs no M: its entry
+//     state is the pool's), and its end state S_in(1) goes to the workspace;
+//   scan (gdn_seg_scan): per (sequence, head),
+//     S_in(j + 1) = M_j S_in(j) + dS_j, written over dS_j, from S_in(0) =
+//     the pool state (copied to a slot of its own) or from S_in(1);
+//   phase B: pass 2 for the remaining segments from their S_in; the last one
+//     writes the final state to the pool.
 // A sequence of one segment is handled by pass 2 alone, reading and writing
-// the pool.  State slots in the workspace are tile-major (a wave reads or
+// the pool, in phase A.  State slots in the workspace are tile-major (a wave reads or
 // writes one accumulator tile as one contiguous 1 KiB); M is stored as the
 // scan's A operand fragments.
 #include <algorithm>
@@ -721,6 +724,7 @@ struct SegArgs {
     float* wsS;                   // per (split segment, head): dS, then the entry state of the next segment
     float* wsM;                   // per (split segment, head): M, as the scan's operand fragments
     float* wsI;                   // per split sequence (at its first split segment) and head: S_in(0)
+    int first_in_a;               // the first segment of a split sequence runs in phase A (see launch_gdn_seg)
     Ckpt ck;
     void* o;
 };
@@ -822,8 +826,11 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
 }
 
 // ------------------------------------------------------------------ scan
-// Per (split sequence, head): S_in(0) = the pool state (or 0), then
-// S_in(j + 1) = M_j S_in(j) + dS_j.  The state's columns are independent, so
+// Per (split sequence, head): S_in(j + 1) = M_j S_in(j) + dS_j over the split
+// segments, from S_in(1) in the sequence's first split slot when phase A ran
+// the first segment (from_first), else from S_in(0) = the pool state (or
+// 0), which also goes to the sequence's slot in wsI.  The state's columns
+// are independent, so
 // kScanGroups workgroups share a (sequence, head), each with kScanCols
 // 16-column blocks, at equal blockIdx % 8 (one XCD, so M_j is fetched into
 // one L2).  Wave w forms rows 16 w .. 16 w + 15 of its workgroup's blocks:
@@ -833,8 +840,7 @@ __device__ __forceinline__ void seg_state_body(StateBuf (&buf)[2], int bid, cons
 // workgroup reads all of M_j each step: wider workgroups move fewer bytes
 // from L2 and lengthen each step's LDS reads and MFMA chains.
 // The products take bf16 hi + lo pairs (three MFMAs per 32-deep block).
-// S_in(j + 1) overwrites dS_j (each word by the lane that read it) and
-// S_in(0) goes to the sequence's slot in wsI.
+// S_in(j + 1) overwrites dS_j (each word by the lane that read it).
 // kScanCols: 16-column blocks per workgroup (1 or 2, the latter when there
 // are many (sequence, head) pairs; kScanGroups = 8 / kScanCols workgroups
 // per pair).
@@ -842,7 +848,7 @@ template <int kScanCols>
 __global__ void __launch_bounds__(NTH)
 gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
              int zero_init, const int32_t* __restrict__ split_off, long nsplit_max, float* __restrict__ wsS,
-             const float* __restrict__ wsM, float* __restrict__ wsI) {
+             const float* __restrict__ wsM, float* __restrict__ wsI, int from_first) {
     constexpr int kScanGroups = 8 / kScanCols;
     const int x = blockIdx.x;
     const int part = (x >> 3) % kScanGroups;         // which kScanCols column blocks
@@ -856,7 +862,10 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
     const int nsplit = split_off[b + 1] - split_off[b];
     if (static_cast<long>(j) + nsplit > nsplit_max) return;      // malformed cu_seqlens only
     const int slot = slot_idx[b];
-    if (slot < 0 || slot >= n_slots) return;
+    if (slot < 0 || slot >= n_slots) return;        // a sequence skipped by the passes
+    const int s0 = from_first ? 1 : 0;              // the first split segment stepped over
+    const int nsteps = nsplit - s0;
+    if (nsteps <= 0) return;
 
     __shared__ f32x4 xs[2][kScanCols][NWV][64];      // S_in by column block and row block
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -865,17 +874,24 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
     // this lane's words of a state slot in column block c of the workgroup
     auto lofs = [&](int c) { return g_tile(part * kScanCols + c, wave, lane); };
     f32x4 S[kScanCols];
-    const float* src = pool + (static_cast<long>(slot) * H + h) * D * D;
-    float* s0 = wsI + (static_cast<long>(j) * H + h) * D * D;
+    if (from_first) {
+        const float* s1 = wsS + (static_cast<long>(j) * H + h) * D * D;
 #pragma unroll
-    for (int c = 0; c < kScanCols; ++c) {
-        S[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (!zero_init) {
+        for (int c = 0; c < kScanCols; ++c) S[c] = *reinterpret_cast<const f32x4*>(s1 + lofs(c));
+    } else {
+        // position 16 wave + row0 + r of the pair-order slot is state row srow(wave, row0) + r
+        const float* src = pool + (static_cast<long>(slot) * H + h) * D * D;
+        float* si = wsI + (static_cast<long>(j) * H + h) * D * D;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[c][r] = src[(srow(wave, ap.row0) + r) * D + (part * kScanCols + c) * 16 + ap.col];
+        for (int c = 0; c < kScanCols; ++c) {
+            S[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!zero_init) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[c][r] = src[(srow(wave, ap.row0) + r) * D + (part * kScanCols + c) * 16 + ap.col];
+            }
+            *reinterpret_cast<f32x4*>(si + lofs(c)) = S[c];
         }
-        *reinterpret_cast<f32x4*>(s0 + lofs(c)) = S[c];
     }
 
     // M_j row 16 wave + lane % 16 at columns 32 s + 4 g + (0..3) and
@@ -884,8 +900,9 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
         f32x4 m[8];
         f32x4 d[kScanCols];
     };
+    // step s is split segment j + s0 + s
     auto load = [&](Pf& p, int step) {
-        const long sl = (static_cast<long>(j) + step) * H + h;
+        const long sl = (static_cast<long>(j) + s0 + step) * H + h;
         const float* mp = wsM + sl * D * D;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -920,7 +937,7 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
                 acc[c] = mfma_bf16(al, bh, acc[c]);
             }
         }
-        float* dst = wsS + ((static_cast<long>(j) + step) * H + h) * D * D;
+        float* dst = wsS + ((static_cast<long>(j) + s0 + step) * H + h) * D * D;
 #pragma unroll
         for (int c = 0; c < kScanCols; ++c) {
             S[c] = acc[c];
@@ -933,19 +950,19 @@ gdn_seg_scan(int n_seqs, int H, const float* __restrict__ pool, int n_slots, con
     // so the load-counter wait before each step covers only that step's set
     Pf pa, pb, pc;
     load(pa, 0);
-    load(pb, min(1, nsplit - 1));
-    load(pc, min(2, nsplit - 1));
+    load(pb, min(1, nsteps - 1));
+    load(pc, min(2, nsteps - 1));
     int step = 0;
-    for (; step + 2 < nsplit; step += 3) {
+    for (; step + 2 < nsteps; step += 3) {
         run(pa, step);
-        load(pa, min(step + 3, nsplit - 1));
+        load(pa, min(step + 3, nsteps - 1));
         run(pb, step + 1);
-        load(pb, min(step + 4, nsplit - 1));
+        load(pb, min(step + 4, nsteps - 1));
         run(pc, step + 2);
-        load(pc, min(step + 5, nsplit - 1));
+        load(pc, min(step + 5, nsteps - 1));
     }
-    if (step < nsplit) run(pa, step);
-    if (step + 1 < nsplit) run(pb, step + 1);
+    if (step < nsteps) run(pa, step);
+    if (step + 1 < nsteps) run(pb, step + 1);
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -967,9 +984,16 @@ struct OutSmem {
     alignas(16) uint16_t obuf[CH][LO];    // bf16 outputs of the previous chunk
 };
 
-// Pass 2 for segment si of head h (bid = si * H + h); SPLIT selects the
-// segments of sequences cut into several (true) or of those that are not.
-template <class TO, bool CKPT, bool SPLIT>
+// Which segments a pass-2 call takes: those of sequences that are not cut
+// (the pool in and out), the first segment of a cut sequence run in phase A
+// (the pool in, its end state out to the workspace slot the scan starts
+// from), or the segments of a cut sequence after the scan (its entry state
+// in, the pool out after the last one; the first segment among them when it
+// did not run in phase A).
+enum SegMode { kWhole = 0, kFirst = 1, kLater = 2 };
+
+// Pass 2 for segment si of head h (bid = si * H + h) if it is of kind MODE.
+template <class TO, bool CKPT, int MODE>
 __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs& a) {
     const int H = a.H;
     const int h = bid % H;
@@ -978,7 +1002,8 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
     const int b = find_span_owner(a.seg_off, a.n_seqs, si);
     const int g = si - a.seg_off[b];
     const int nseg = a.seg_off[b + 1] - a.seg_off[b];
-    if ((nseg > 1) != SPLIT) return;
+    const int mode = nseg <= 1 ? kWhole : (g == 0 && a.first_in_a ? kFirst : kLater);
+    if (mode != MODE) return;
     GSeg sg;
     if (!seg_bounds(sg, b, g, nseg, a.cu, a.n_tokens, a.coff, a.split_off, a.slot_idx, a.n_slots, a.lseg,
                     a.nsplit_max))
@@ -1015,7 +1040,7 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
     f32x4 S[8];
     float sigma = 1.f;
     float* Sg = pool + (static_cast<long>(sg.slot) * H + h) * D * D;
-    if (sg.nseg <= 1) {
+    if (MODE != kLater) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!a.zero_init) g_rowmajor_load(S, Sg, col);
@@ -1133,7 +1158,12 @@ __device__ __forceinline__ void seg_out_body(OutSmem& sm, int bid, const SegArgs
     }
     if (nch > 0) flush_o(nch - 1);
 
-    if (sg.g == sg.nseg - 1) {
+    if (MODE == kFirst) {
+        // S_in of the second segment, where the scan starts
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) S[mt] *= sigma;
+        g_slot_store(g_slot(a.wsS, sg.jsplit * H + h), S);
+    } else if (sg.g == sg.nseg - 1) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -1379,40 +1409,58 @@ union SegSmem {
     OutSmem out;
 };
 
-// Phase A: pass 1 for the split segments (blocks [0, n1)), which the scan
-// waits for, and next to it pass 2 for sequences that are not split, which
-// depend on nothing else (blocks [n1, ...)).
+// Phase A block bid < n1: split segment j = bid / H (every segment but the
+// last of a cut sequence).  With first_in_a, the first segment of a cut
+// sequence, which needs no transition (its entry state is the pool's), runs
+// pass 2 here and its end state seeds the scan; the others run pass 1.
+template <class TO, bool CKPT>
+__device__ __forceinline__ void phase_a_split(SegSmem& sm, int bid, const SegArgs& a) {
+    const int j = bid / a.H;
+    if (j >= a.split_off[a.n_seqs]) return;
+    const int b = find_span_owner(a.split_off, a.n_seqs, j);
+    if (a.first_in_a && j == a.split_off[b])
+        seg_out_body<TO, CKPT, kFirst>(sm.out, a.seg_off[b] * a.H + bid % a.H, a);
+    else
+        seg_state_body(sm.st, bid, a);
+}
+
+// Phase A: the split segments (blocks [0, n1)), which the scan waits for,
+// and next to them pass 2 for sequences that are not split, which depend
+// on nothing else (blocks [n1, ...)).
 template <class TO, bool CKPT>
 __global__ void __launch_bounds__(NTH)
 gdn_seg_a(SegArgs a, int n1) {
     __shared__ SegSmem sm;
-    if (static_cast<int>(blockIdx.x) < n1) seg_state_body(sm.st, blockIdx.x, a);
-    else seg_out_body<TO, CKPT, false>(sm.out, blockIdx.x - n1, a);
+    if (static_cast<int>(blockIdx.x) < n1) phase_a_split<TO, CKPT>(sm, blockIdx.x, a);
+    else seg_out_body<TO, CKPT, kWhole>(sm.out, blockIdx.x - n1, a);
 }
 
-// Phase A for batches of short prompts: pass 1 as above, and pass 2 for
-// unsplit sequences with `items` heads per block.
+// Phase A for batches of short prompts: the split segments as above, and
+// pass 2 for unsplit sequences with `items` heads per block.
 template <class TO, bool ZERO>
 __global__ void __launch_bounds__(NTH)
 gdn_seg_a_multi(SegArgs a, int n1, int items) {
     __shared__ SegSmem sm;
-    if (static_cast<int>(blockIdx.x) < n1) seg_state_body(sm.st, blockIdx.x, a);
+    if (static_cast<int>(blockIdx.x) < n1) phase_a_split<TO, false>(sm, blockIdx.x, a);
     else seg_out_multi<TO, ZERO>(sm.out, (blockIdx.x - n1) * items, items, a);
 }
 
-// Phase B (after the scan): pass 2 for the segments of split sequences,
-// block j being segment j / H of their concatenated segment lists (a batch
-// of short prompts launches no idle blocks here).
+// Phase B (after the scan): pass 2 for the segments of split sequences
+// that phase A did not run (a batch of short prompts launches no idle
+// blocks here).  With first_in_a, block j is split segment j / H, whose
+// i-th of a sequence stands for its segment i + 1; otherwise block j is
+// segment j / H of the split sequences' concatenated segment lists.
 template <class TO, bool CKPT>
 __global__ void __launch_bounds__(NTH)
 gdn_seg_b(SegArgs a) {
     __shared__ SegSmem sm;
     const int h = blockIdx.x % a.H;
-    const int jj = blockIdx.x / a.H;
-    if (jj >= a.splitseg_off[a.n_seqs]) return;
-    const int b = find_span_owner(a.splitseg_off, a.n_seqs, jj);
-    const int si = a.seg_off[b] + (jj - a.splitseg_off[b]);
-    seg_out_body<TO, CKPT, true>(sm.out, si * a.H + h, a);
+    const int j = blockIdx.x / a.H;
+    const int32_t* off = a.first_in_a ? a.split_off : a.splitseg_off;
+    if (j >= off[a.n_seqs]) return;
+    const int b = find_span_owner(off, a.n_seqs, j);
+    const int si = a.seg_off[b] + (j - off[b]) + (a.first_in_a ? 1 : 0);
+    seg_out_body<TO, CKPT, kLater>(sm.out, si * a.H + h, a);
 }
 
 // Segment length: whole chunks, at least 4 of them, such that the call
@@ -1446,9 +1494,10 @@ __host__ __device__ constexpr size_t al256(size_t x) { return (x + 255) & ~size_
 
 // Workspace of the segmented path beyond the chunk offsets and T planes:
 // segment offsets, split-segment offsets, offsets among the segments of
-// split sequences, and three 64 KiB state slots per
-// (split segment, head): dS, M and (at a sequence's first) S_in(0).  A sequence of s >= 2 segments is longer than
-// (s - 1) * lseg tokens, so split segments number at most n_tokens / lseg.
+// split sequences, and three 64 KiB state slots per (split segment, head):
+// dS (then S_in of the next segment), M and (at a sequence's first)
+// S_in(0).  A sequence of s >= 2 segments is longer than (s - 1) * lseg
+// tokens, so split segments number at most n_tokens / lseg.
 size_t gdn_seg_workspace(int n_seqs, int n_tokens, int n_heads) {
     const long nsplit = n_tokens / g_seg_len(n_seqs, n_tokens, n_heads);
     return 3 * al256(sizeof(int32_t) * (n_seqs + 1)) +
@@ -1502,16 +1551,26 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
     float* wsS = reinterpret_cast<float*>(ws);
     float* wsM = wsS + static_cast<size_t>(nsplit) * a.n_heads * D * D;
     float* wsI = wsM + static_cast<size_t>(nsplit) * a.n_heads * D * D;
+    // The first segment of a split sequence needs no pass 1 (its entry
+    // state is the pool's): run in phase A as pass 2 it saves that work, but
+    // puts a pass-2 chain (slower per chunk than pass 1) into phase A.  That
+    // pays when the phases are throughput-bound (many (sequence, head) pairs,
+    // more workgroups than compute units), not for a few long prompts, where
+    // each phase is one segment's chain.
+    const int first_in_a = static_cast<long>(a.n_seqs) * a.n_heads >= 2 * kTargetBlocks;
     const SegArgs sa{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.alpha, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads,
                      a.pool, a.n_slots, a.slot_idx, a.zero_init, lseg, coff, seg_off, split_off, splitseg_off,
                      planes, plane_scales(planes, n_chunks_max, a.n_heads), n_chunks_max, nsplit, wsS, wsM, wsI,
+                     first_in_a,
                      Ckpt{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride}, a.o};
     const int n1 = static_cast<int>(nsplit * a.n_heads);
     const dim3 grid_a(static_cast<unsigned>(n1 + maxseg * a.n_heads));
-    // a sequence of k >= 2 segments is longer than (k - 1) lseg tokens and
-    // k <= 2 (k - 1): the segments of split sequences number at most 2 nsplit
-    const dim3 grid_b(static_cast<unsigned>(std::min(maxseg, 2 * nsplit) * a.n_heads));
+    // phase B: with first_in_a the later segments of split sequences, one
+    // per split segment (at most nsplit); otherwise all their segments (a
+    // sequence of k >= 2 segments is longer than (k - 1) lseg tokens and
+    // k <= 2 (k - 1): at most 2 nsplit)
+    const dim3 grid_b(static_cast<unsigned>((first_in_a ? nsplit : std::min(maxseg, 2 * nsplit)) * a.n_heads));
     // several heads per block for batches of short prompts (no checkpoints)
     const int items = sa.ck.slots ? 1 : g_seg_items(a.n_seqs, a.n_tokens, a.n_heads, maxseg);
     auto passes = [&](auto ka, auto kb) {
@@ -1534,7 +1593,7 @@ hipError_t launch_gdn_seg(const ChunkArgs& a, const int32_t* coff, const uint16_
             auto scan = [&](auto kern, int groups) {
                 hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((n1 + 7) / 8 * 8 * groups)), dim3(NTH), 0, s,
                                    a.n_seqs, a.n_heads, a.pool, a.n_slots, a.slot_idx, a.zero_init, split_off,
-                                   nsplit, wsS, wsM, wsI);
+                                   nsplit, wsS, wsM, wsI, first_in_a);
             };
             if (static_cast<long>(a.n_seqs) * a.n_heads <= 32) scan(gdn_seg_scan<1>, 8);
             else scan(gdn_seg_scan<2>, 4);

@@ -163,7 +163,9 @@ GLA_API int gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
  * each segment's state contribution and its d_k x d_k transition, a scan
  * over the segments forms every segment's entry state, and the second pass
  * produces the outputs (the state hand-off of "Chunked prefill comes for
- * free", used inside one call).  That path multiplies fp16 operands with
+ * free", used inside one call); in batches of at least 512 (sequence, head)
+ * pairs the first segment of a cut sequence runs straight from the pool
+ * state instead, next to the first pass.  That path multiplies fp16 operands with
  * fp32 accumulation, each fp32-derived operand scaled by a power of two
  * into fp16's range; it needs |q_i| |k_j| < 2^15 and |q|, |k| entries
  * below 2^15 (true for L2-normalised q and k) and gives results about 5e-4

@@ -247,6 +247,34 @@ def test_gdn_short_prompts_several_heads_per_block(zero_init):
     assert np.array_equal(p[untouched], w.pool[untouched])
 
 
+def test_gdn_first_segments_run_before_the_scan():
+    """A Gated DeltaNet batch of many (sequence, head) pairs (40 x 16) with
+    three prompts cut into 4, 4 and 3 segments: there the first segment of
+    a cut prompt runs its outputs next to the other segments' first pass
+    and its end state seeds the scan, which then starts one segment later.
+    Outputs and final states against the recurrence."""
+    rng = np.random.Generator(np.random.PCG64(83))
+    lens = rng.integers(260, 341, size=37).tolist()
+    lens = lens[:5] + [2000] + lens[5:20] + [1990] + lens[20:] + [1500]
+    w = synth.random_varlen(23, lens, 16, 128, 128, dtype="bf16", gdn=True)
+    note(f"gdn large batch with cut prompts, {len(lens)} sequences x 16 heads, {sum(lens)} tokens")
+    o, pool = run_chunk("gdn", w)
+    o_ref, pool_ref = run_oracle("gdn", w)
+    cu = w.cu_seqlens
+    cut = np.zeros(o_ref.shape[0], bool)
+    for b in (5, 21, 39):
+        cut[cu[b]:cu[b + 1]] = True
+    oh = host(o)
+    print(f"rel err o: cut prompts {rel_err(oh[cut], o_ref[cut]):.2e}, others {rel_err(oh[~cut], o_ref[~cut]):.2e}")
+    check(oh, o_ref, "bf16", "o")
+    p = pool.cpu().numpy()
+    check(p[w.slot_idx], pool_ref[w.slot_idx], "bf16", "state")
+    spare = sorted(set(range(p.shape[0])) - set(w.slot_idx.tolist()))
+    assert np.array_equal(p[spare], w.pool[spare])
+    o16, p16 = run_chunk("gdn", w, out_dtype="bf16")
+    assert torch.equal(o16.cpu(), rne_bf16(o))
+
+
 def test_gla_prefill_full_size():
     """GLA prefill: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 inputs,
     zero initial state: every output and final state against the oracle."""
