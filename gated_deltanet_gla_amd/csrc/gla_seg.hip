@@ -768,9 +768,17 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
                 acc += __uint_as_float(qw.z << 16) * z1.x + __uint_as_float(qw.z & 0xffff0000u) * z1.y;
                 acc += __uint_as_float(qw.w << 16) * z1.z + __uint_as_float(qw.w & 0xffff0000u) * z1.w;
             }
-            acc += __shfl_xor(acc, 1, 64);
-            acc += __shfl_xor(acc, 2, 64);
-            acc += __shfl_xor(acc, 4, 64);
+            // sum over the row's 8 lanes by DPP: partners 1 and 2 apart, then
+            // the other quad (the half-row mirror; its lanes hold equal sums)
+            auto dpp_add = [](float x, int ctrl) {
+                const int y = ctrl == 0xb1 ? __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false)
+                            : ctrl == 0x4e ? __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false)
+                                           : __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false);
+                return x + __int_as_float(y);
+            };
+            acc = dpp_add(acc, 0xb1);     // quad_perm [1,0,3,2]
+            acc = dpp_add(acc, 0x4e);     // quad_perm [2,3,0,1]
+            acc = dpp_add(acc, 0x141);    // row_half_mirror
             if ((tq & 7) == 0) qzb[i] = acc;
         }
         lds_barrier();
@@ -812,7 +820,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
                 float den = qzb[i] + eps;
 #pragma unroll
                 for (int jt = 0; jt <= it; ++jt) den += dpart[it * (it + 1) / 2 + jt][lc];
-                ot[it] *= 1.f / den;
+                ot[it] *= __builtin_amdgcn_rcpf(den);   // hardware reciprocal (1 ulp), not a division
             }
         }
         // lane: token it*16 + (lane % 16), columns col + 4 (lane / 16) .. +3
