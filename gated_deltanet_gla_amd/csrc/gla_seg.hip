@@ -11,11 +11,15 @@
 //   pass 1 (gla_seg_state): for each segment but the last, its local state
 //     contribution dS_g = sum over its tokens of exp(G_end - G_t) k_t^T v_t
 //     (the state it would produce from S = 0) and its total log-decay
-//     Lambda_g; the last segment's slot receives a copy of the initial state;
-//   pass 2 (gla_seg_out): each segment folds its entry state
-//     S_in(g) = 2^Lambda_{g-1} S_in(g-1) + dS_{g-1} from those, then runs the
-//     chunked form over its chunks; the last segment writes the final state
-//     back to the pool.
+//     Lambda_g; the first segment starts from the initial state instead, so
+//     its slot holds the entry state of the second, S_in(1), and it leaves a
+//     copy of the initial state in the last segment's slot (not for a zero
+//     initial state);
+//   pass 2 (gla_seg_out): each later segment folds its entry state
+//     S_in(g) = 2^Lambda_{g-1} S_in(g-1) + dS_{g-1} from those (g slot reads),
+//     the first reads the copy (the pool slot itself is rewritten by the
+//     last segment in the same pass); then each runs the chunked form over
+//     its chunks; the last segment writes the final state back to the pool.
 //
 // Within a workgroup (8 waves) each wave owns 16 columns of the 128x128
 // fp32 state (held in MFMA accumulators).  Q S, P V and the state update are
@@ -527,26 +531,30 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     __shared__ int sh[2 * SW + 4];
     SegGeom sg;
     if (!split_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, maxseg, sh)) return;
-    if (sg.nseg <= 1) return;                      // no split: pass 2 reads the pool itself
+    // no split: pass 2 reads the pool itself; the last segment's local
+    // state is never used
+    if (sg.nseg <= 1 || sg.g == sg.nseg - 1) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const AccPos ap;
     const int col = wave * 16;
-    float* dst = frag_slot(wstate, sg.ws_slot);
     f32x4 S[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (sg.g == sg.nseg - 1) {                     // last segment's slot: copy of the initial state
-        if (!zero_init) load_state_rowmajor<true>(S, pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD, col);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + mt * 4) = S[mt];
-        if constexpr (NORM) {
-            if (threadIdx.x < SD)
-                wz[sg.ws_slot * SD + threadIdx.x] =
-                    zero_init ? 0.f : zpool[(static_cast<long>(sg.slot) * H + sg.h) * SD + threadIdx.x];
-        }
-        return;
-    }
     f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+    // The first segment runs from the initial state (sigma = 1), so that its
+    // slot holds the second segment's entry state S_in(1); it also copies
+    // the initial state to the last segment's slot, from which pass 2's
+    // first segment reads it.
+    if (sg.g == 0 && !zero_init) {
+        const long pslot = static_cast<long>(sg.slot) * H + sg.h;
+        const long last = sg.ws_first + static_cast<long>(sg.nseg - 1) * H;
+        load_state_rowmajor<false>(S, pool + pslot * SD * SD, col);
+        store_slot_out_order(wstate, last, S);
+        if constexpr (NORM) {
+            zacc = *reinterpret_cast<const f32x4*>(zpool + pslot * SD + wave * 16 + ap.row0);
+            if (threadIdx.x < SD) wz[last * SD + threadIdx.x] = zpool[pslot * SD + threadIdx.x];
+        }
+    }
 
     __shared__ KVBuf buf[2];
     const int nch = (sg.t1 - sg.t0 + SC - 1) / SC;
@@ -620,15 +628,17 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
     // ---- entry state of this segment
     f32x4 S[8];
     float* Sg = pool + (static_cast<long>(sg.slot) * H + sg.h) * SD * SD;
-    if (sg.nseg <= 1) {
+    if (sg.nseg <= 1 || (sg.g == 0 && zero_init)) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!zero_init) load_state_rowmajor<true>(S, Sg, col);
     } else {
-        const float* s0 = frag_slot(wstate, sg.ws_first + static_cast<long>(sg.nseg - 1) * H);
+        // first segment: the copy of the initial state in the last
+        // segment's slot; later ones: slot 0 holds S_in(1)
+        const float* s0 = frag_slot(wstate, sg.ws_first + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
-        for (int j = 0; j < sg.g; ++j) {
+        for (int j = 1; j < sg.g; ++j) {
             const long sj = sg.ws_first + static_cast<long>(j) * H;
             const float dcy = hw_exp2(wlam[sj]);
             const float* dS = frag_slot(wstate, sj);
@@ -640,11 +650,12 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         // entry normaliser z_in: rows wave*16 + row0 .. + 3
         const int zr = wave * 16 + ap.row0;
         f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
-        if (sg.nseg <= 1) {
+        if (sg.nseg <= 1 || (sg.g == 0 && zero_init)) {
             if (!zero_init) zacc = *reinterpret_cast<const f32x4*>(zpool + zoff + zr);
         } else {
-            zacc = *reinterpret_cast<const f32x4*>(wz + (sg.ws_first + static_cast<long>(sg.nseg - 1) * H) * SD + zr);
-            for (int j = 0; j < sg.g; ++j)
+            zacc = *reinterpret_cast<const f32x4*>(
+                wz + (sg.ws_first + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L)) * SD + zr);
+            for (int j = 1; j < sg.g; ++j)
                 zacc += *reinterpret_cast<const f32x4*>(wz + (sg.ws_first + static_cast<long>(j) * H) * SD + zr);
         }
         if (ap.col == 0) *reinterpret_cast<f32x4*>(&zb[0][zr]) = zacc;
@@ -948,7 +959,7 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         return BufRsrc(pool + (static_cast<long>(sg.slot) * H + sg.h + it) * SD * SD, SD * SD * 4);
     };
     auto entry = [&](int it) {
-        if (sg.nseg <= 1) {
+        if (sg.nseg <= 1 || (ZERO && sg.g == 0)) {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (!ZERO) {
@@ -959,10 +970,13 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                     for (int r = 0; r < 4; ++r) S[mt][r] = rs.loadf(lane_off, (srow(mt, 0) + r) * SD * 4);
             }
         } else {
-            const float* s0 = frag_slot(wstate, sg.ws_first + it + static_cast<long>(sg.nseg - 1) * H);
+            // first segment: the copy of the initial state in the last
+            // segment's slot; later ones: slot 0 holds S_in(1)
+            const float* s0 =
+                frag_slot(wstate, sg.ws_first + it + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L));
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
-            for (int j = 0; j < sg.g; ++j) {
+            for (int j = 1; j < sg.g; ++j) {
                 const long sj = sg.ws_first + it + static_cast<long>(j) * H;
                 const float dcy = hw_exp2(wlam[sj]);
                 const float* dS = frag_slot(wstate, sj);
