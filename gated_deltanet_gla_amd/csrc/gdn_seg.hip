@@ -193,6 +193,16 @@ __device__ __forceinline__ bf16x8 f16_pair(const f32x4& a, const f32x4& b, float
     return as_bf16x8(u32x4{pk_f16(a.x * sc, a.y * sc), pk_f16(a.z * sc, a.w * sc), pk_f16(b.x * sc, b.y * sc),
                            pk_f16(b.z * sc, b.w * sc)});
 }
+// The same for a wave-uniform power of two s: x s is exact, and written as an
+// fma with a zero addend it compiles to the mixed-precision fma that rounds
+// to fp16 into one half of the packed register (one instruction per value
+// instead of a multiply per value and a pack per two).  Only the sign of a
+// zero product can differ (+0 for -0), which no product with it sees.
+__device__ __forceinline__ bf16x8 f16_pair_scaled(const f32x4& a, const f32x4& b, float sc) {
+    auto m = [sc](float x) { return __builtin_fmaf(x, sc, 0.f); };
+    return as_bf16x8(u32x4{pk_f16(m(a.x), m(a.y)), pk_f16(m(a.z), m(a.w)), pk_f16(m(b.x), m(b.y)),
+                           pk_f16(m(b.z), m(b.w))});
+}
 // Range guard: a power of two s with (largest |x| of the wave) * s < 2^15,
 // and 1 / s (both exact; s is capped at 2^126 for tiny or zero slices).
 struct Scale {
@@ -292,7 +302,7 @@ __device__ __forceinline__ Scale state_operand(bf16x8 (&sf)[4], const f32x4 (&S)
     for (int mt = 0; mt < 8; ++mt) m = absmax4(S[mt], m);
     const Scale sc = range_scale(m);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sf[s] = f16_pair(S[2 * s], S[2 * s + 1], sc.s);
+    for (int s = 0; s < 4; ++s) sf[s] = f16_pair_scaled(S[2 * s], S[2 * s + 1], sc.s);
     return sc;
 }
 
@@ -322,7 +332,7 @@ __device__ __forceinline__ Scale form_y(bf16x8 (&yf)[2], const f32x4 (&X)[4], co
     }
     const Scale sc = range_scale(m);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) yf[ks] = f16_pair(y[2 * ks], y[2 * ks + 1], sc.s);
+    for (int ks = 0; ks < 2; ++ks) yf[ks] = f16_pair_scaled(y[2 * ks], y[2 * ks + 1], sc.s);
     return sc;
 }
 
