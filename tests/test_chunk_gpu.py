@@ -176,17 +176,18 @@ def test_gla_segmented_no_split_sequences():
 def test_gla_short_prompts_several_heads_per_block(zero_init):
     """Batches of short prompts run the output pass with several heads of
     one segment per block, their chunks in one stream (4 heads per block at
-    these sizes): 98 sequences of 0..200 tokens (empty ones included) and
-    two of 1200 tokens that split into two segments (entry states folded
-    between heads), 16 heads, and one sequence whose slot is outside the
-    pool: it is skipped (its outputs and the pool untouched), the others
-    match the recurrence."""
+    these sizes): 98 sequences of 0..200 tokens (empty ones included), one
+    of 1200 tokens that splits into two segments and one of 3000 that splits
+    into four (entry states folded between heads, from the copy of the
+    initial state and from up to three segment slots), 16 heads, and one
+    sequence whose slot is outside the pool: it is skipped (its outputs and
+    the pool untouched), the others match the recurrence."""
     import gated_deltanet_gla_amd as G
     rng = np.random.Generator(np.random.PCG64(79 + zero_init))
     lens = rng.integers(0, 201, size=98).tolist()
     lens[3] = 0
     lens[40] = 0
-    lens = lens[:30] + [1200] + lens[30:70] + [1200] + lens[70:]
+    lens = lens[:30] + [1200] + lens[30:70] + [3000] + lens[70:]
     w = synth.random_varlen(19 + zero_init, lens, 16, 128, 128, dtype="bf16", zero_init=zero_init)
     bad = 7
     n_slots = w.pool.shape[0]
