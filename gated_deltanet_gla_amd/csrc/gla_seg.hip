@@ -84,6 +84,7 @@ constexpr int LO = SD + 8;
 constexpr int kSegBlocks = 256;    // one workgroup on each of the 256 compute units
 constexpr int kShortChunks = 4;    // batches of sequences this short (mean chunks) ...
 constexpr int kMaxItems = 16;      // ... put up to this many heads in one output-pass block
+constexpr int kScanMinSegs = 6;    // mean segments per sequence from which the entry states are scanned
 
 // Gate tables of a chunk (seg_stage_gates): dec, the update's weights;
 // smul, what the held state is multiplied by before the update (1: not
@@ -591,6 +592,62 @@ gla_seg_state(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     }
 }
 
+// ------------------------------------------------------------------ scan
+// Entry states by a scan over pass 1's slots, for calls whose sequences
+// have many segments: folded in pass 2 instead, segment g would read g
+// slots, a number of reads quadratic in the segments.  Slot j >= 1 of a
+// split sequence becomes S_in(j + 1) = 2^Lambda_j S_in(j) + dS_j, from
+// slot 0 = S_in(1), so pass 2's segment g >= 1 reads slot g - 1 alone
+// (and z_in likewise, without decay).  Block (s, c) runs on pass 1's
+// geometry (s as there; only a sequence's first segment does the scan) and
+// takes floats [c * 2048, (c + 1) * 2048) of every slot, 4 per thread: the
+// scan is elementwise, so any split of a slot will do.  Slot loads are
+// issued kScanBatch at a time ahead of the chained multiply-adds.
+constexpr int kScanCols = 8;       // blocks per sequence and head
+constexpr int kScanBatch = 8;
+template <bool NORM>
+__global__ void __launch_bounds__(ST)
+gla_seg_scan(const int32_t* __restrict__ cu, int n_seqs, int n_tokens, int H, int lseg,
+             const int32_t* __restrict__ slot_idx, int n_slots, int maxseg, float* __restrict__ wstate,
+             const float* __restrict__ wlam, float* __restrict__ wz) {
+    __shared__ int sh[2 * SW + 4];
+    SegGeom sg;
+    if (!split_geometry(sg, cu, n_seqs, n_tokens, H, lseg, slot_idx, n_slots, maxseg, sh)) return;
+    if (sg.nseg <= 2 || sg.g != 0) return;        // nothing to scan
+    const int n = sg.nseg - 1;                     // slots 0 .. n - 1 of this sequence
+    const long off = static_cast<long>(blockIdx.y) * (SD * SD / kScanCols) + threadIdx.x * 4;
+    auto slot = [&](int j) { return wstate + (sg.ws_first + static_cast<long>(j) * H) * SD * SD + off; };
+    f32x4 S = *reinterpret_cast<const f32x4*>(slot(0));
+    for (int j0 = 1; j0 < n; j0 += kScanBatch) {
+        f32x4 L[kScanBatch];
+        float lam[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            if (j0 + u < n) {
+                L[u] = *reinterpret_cast<const f32x4*>(slot(j0 + u));
+                lam[u] = wlam[sg.ws_first + static_cast<long>(j0 + u) * H];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            if (j0 + u < n) {
+                S = hw_exp2(lam[u]) * S + L[u];
+                *reinterpret_cast<f32x4*>(slot(j0 + u)) = S;
+            }
+        }
+    }
+    if constexpr (NORM) {
+        if (blockIdx.y == 0 && threadIdx.x < SD) {
+            float* z = wz + sg.ws_first * SD + threadIdx.x;
+            float acc = z[0];
+            for (int j = 1; j < n; ++j) {
+                acc += z[static_cast<long>(j) * H * SD];
+                z[static_cast<long>(j) * H * SD] = acc;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ pass 2
 template <class TO, bool CKPT, bool NORM>
 __global__ void __launch_bounds__(ST)
@@ -598,7 +655,7 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
             const float* __restrict__ alpha, const int32_t* __restrict__ cu, int n_seqs, int n_tokens,
             int H, float* __restrict__ pool, int n_slots, const int32_t* __restrict__ slot_idx,
             int zero_init, int lseg, const float* __restrict__ wstate, const float* __restrict__ wlam,
-            Ckpt ck, float* __restrict__ zpool, const float* __restrict__ wz, float eps,
+            int scanned, Ckpt ck, float* __restrict__ zpool, const float* __restrict__ wz, float eps,
             typename TO::T* __restrict__ o) {
     __shared__ int sh[SW + 4];
     SegGeom sg;
@@ -634,11 +691,13 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         if (!zero_init) load_state_rowmajor<true>(S, Sg, col);
     } else {
         // first segment: the copy of the initial state in the last
-        // segment's slot; later ones: slot 0 holds S_in(1)
-        const float* s0 = frag_slot(wstate, sg.ws_first + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L));
+        // segment's slot; later ones: slot 0 holds S_in(1), and after the
+        // scan slot g - 1 holds S_in(g)
+        const long s_in = sg.g == 0 ? static_cast<long>(sg.nseg - 1) : (scanned ? sg.g - 1 : 0);
+        const float* s0 = frag_slot(wstate, sg.ws_first + s_in * H);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
-        for (int j = 1; j < sg.g; ++j) {
+        for (int j = 1; j < (scanned ? 0 : sg.g); ++j) {
             const long sj = sg.ws_first + static_cast<long>(j) * H;
             const float dcy = hw_exp2(wlam[sj]);
             const float* dS = frag_slot(wstate, sj);
@@ -653,9 +712,9 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         if (sg.nseg <= 1 || (sg.g == 0 && zero_init)) {
             if (!zero_init) zacc = *reinterpret_cast<const f32x4*>(zpool + zoff + zr);
         } else {
-            zacc = *reinterpret_cast<const f32x4*>(
-                wz + (sg.ws_first + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L)) * SD + zr);
-            for (int j = 1; j < sg.g; ++j)
+            const long z_in = sg.g == 0 ? static_cast<long>(sg.nseg - 1) : (scanned ? sg.g - 1 : 0);
+            zacc = *reinterpret_cast<const f32x4*>(wz + (sg.ws_first + z_in * H) * SD + zr);
+            for (int j = 1; j < (scanned ? 0 : sg.g); ++j)
                 zacc += *reinterpret_cast<const f32x4*>(wz + (sg.ws_first + static_cast<long>(j) * H) * SD + zr);
         }
         if (ap.col == 0) *reinterpret_cast<f32x4*>(&zb[0][zr]) = zacc;
@@ -1295,6 +1354,15 @@ hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
     // k <= 2 (k - 1), so the segments of split sequences number at most
     // 2 * (n_tokens / lseg); pass 1 launches no more blocks than that.
     const long nsplit = std::min(maxseg, 2L * (a.n_tokens / lseg));
+    const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
+    // several heads per block for batches of short prompts (plain GLA; the
+    // checkpoint and normalised variants keep one)
+    const int items = NORM || ck.slots ? 1 : seg_items(a.n_seqs, a.n_tokens, a.n_heads, maxseg);
+    // the scan of the entry states pays its launch where sequences have
+    // kScanMinSegs segments or more on average (never with several heads
+    // per block, which fold: their batches are of short prompts)
+    const int scanned =
+        items == 1 && nsplit > 0 && a.n_tokens / lseg >= static_cast<long>(kScanMinSegs) * a.n_seqs;
     if (nsplit > 0) {
         hipLaunchKernelGGL(gla_seg_state<NORM>, dim3(static_cast<unsigned>(nsplit * a.n_heads)), dim3(ST), 0,
                            s, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), alpha,
@@ -1303,11 +1371,14 @@ hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const Ckpt ck{a.ckpt_slots, a.ckpt_interval, a.ckpt_stride};
-    // several heads per block for batches of short prompts (plain GLA; the
-    // checkpoint and normalised variants keep one)
+    if (scanned) {
+        hipLaunchKernelGGL(gla_seg_scan<NORM>, dim3(static_cast<unsigned>(nsplit * a.n_heads), kScanCols), dim3(ST),
+                           0, s, a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, lseg, a.slot_idx, a.n_slots,
+                           static_cast<int>(maxseg), wstate, wlam, wz);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if constexpr (!NORM) {
-        const int items = ck.slots ? 1 : seg_items(a.n_seqs, a.n_tokens, a.n_heads, maxseg);
         if (items > 1) {
             auto multi = [&](auto kern, auto* o) {
                 hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(maxseg * a.n_heads / items)), dim3(ST), 0, s,
@@ -1329,7 +1400,7 @@ hipError_t launch_seg(const ChunkArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(kern, grid, dim3(ST), 0, s, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), alpha,
                            a.cu_seqlens, a.n_seqs, a.n_tokens, a.n_heads, a.pool, a.n_slots, a.slot_idx,
-                           a.zero_init, lseg, wstate, wlam, ck, a.zpool, wz, a.eps, o);
+                           a.zero_init, lseg, wstate, wlam, scanned, ck, a.zpool, wz, a.eps, o);
     };
     // the checkpoint stores are compiled in only where they are asked for
     if constexpr (!NORM) {

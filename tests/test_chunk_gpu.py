@@ -156,6 +156,26 @@ def test_gla_segmented_many_sequences(zero_init):
     assert torch.equal(p16, pool)
 
 
+@pytest.mark.parametrize("zero_init", [False, True])
+def test_gla_segmented_entry_scan(zero_init):
+    """Few sequences of many segments (here 16, 10 and 13 segments of 256
+    tokens, an empty sequence between them, last segments of 160, 1 and 28
+    tokens): the entry states are scanned once over the first pass's slots
+    instead of folded in every segment of the output pass.  Outputs and final
+    states against the recurrence; bf16 outputs are the RNE of the fp32 ones."""
+    lens = [4000, 2305, 0, 3100]
+    w = synth.random_varlen(23 + zero_init, lens, 2, 128, 128, dtype="bf16", zero_init=zero_init)
+    note(f"gla segmented entry scan, lengths {lens}, zero_init={zero_init}")
+    o, pool = run_chunk("gla", w)
+    o_ref, pool_ref = run_oracle("gla", w)
+    check(host(o), o_ref, "bf16", "o")
+    p = pool.cpu().numpy()
+    check(p[w.slot_idx], pool_ref[w.slot_idx], "bf16", "state")
+    o16, p16 = run_chunk("gla", w, out_dtype="bf16")
+    assert torch.equal(o16.cpu(), rne_bf16(o))
+    assert torch.equal(p16, pool)
+
+
 def test_gla_segmented_no_split_sequences():
     """Many prompts of one segment each (1..256 tokens, under the 320-token
     segment at this size): the first pass launches blocks, none of which

@@ -73,11 +73,12 @@ def test_lin_attn_chunk_zero_init_and_eps(dtype):
 
 @pytest.mark.parametrize("zero_init", [False, True])
 @pytest.mark.parametrize("lengths,H", [([1000, 77, 0, 640, 300], 2), ([2050, 256, 64], 3),
-                                       ([257, 1], 1)])
+                                       ([257, 1], 1), ([3000, 1800], 2)])
 def test_lin_attn_segmented_parity(lengths, H, zero_init):
     """bf16, d = 128, chunk 64: sequences cut into segments of 256 tokens
     (several per sequence here), each segment's sum of phi(k) handed on
-    with its state."""
+    with its state (the last case has 12 and 8 segments a sequence: its
+    entry states and normalisers are scanned once instead of folded)."""
     note(f"lin_attn segmented lengths={lengths} H={H} zero_init={zero_init}")
     w = synth.lin_attn_varlen(650 + H + len(lengths), lengths, H, 128, 128, dtype="bf16", chunk=64,
                               zero_init=zero_init)
