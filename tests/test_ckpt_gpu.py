@@ -59,6 +59,8 @@ CASES = [
     ("bf16", 128, 128, 64, 2, [1000, 77, 0, 640, 300], 64, 16),
     ("bf16", 128, 128, 64, 2, [1000, 513, 129], 192, 4),
     ("bf16", 128, 128, 64, 3, [2050, 256], 256, 9),
+    # 11 and 7 segments a sequence: the GLA entry states are scanned, not folded
+    ("bf16", 128, 128, 64, 2, [2600, 1700], 128, 21),
     ("bf16", 64, 64, 32, 2, [300, 31, 160], 96, 3),
     ("f32", 32, 32, 16, 2, [100, 16, 47], 16, 7),
     ("f32", 16, 64, 16, 1, [64, 63], 32, 2),
