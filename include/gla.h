@@ -109,8 +109,10 @@ enum { GLA_ZERO_INIT = 1u };  /* ignore the pool's contents: S_0 = 0 */
  * sequences are also cut into segments of whole chunks that run in
  * parallel: a first pass writes each segment's state contribution and total
  * decay to the workspace, and each segment folds its entry state from them
- * (the same hand-off of the state, inside one call).  Contents of the
- * workspace are scratch; it must not be shared by calls that overlap.
+ * (the same hand-off of the state, inside one call; where sequences average
+ * six or more segments, a scan forms the entry states once instead).
+ * Contents of the workspace are scratch; it must not be shared by calls
+ * that overlap.
  */
 GLA_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                   const int32_t* cu_seqlens, int32_t n_seqs, int32_t n_tokens,
