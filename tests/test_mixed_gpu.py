@@ -59,11 +59,13 @@ def test_mixed_step_small():
 
 def test_mixed_step_full_size_sampled_heads():
     """48 prompts of log-uniform length in [16, 32768] + 512 decodes, 16 heads,
-    1024-slot pool: heads 0 and 7 of every request against the oracle."""
+    1024-slot pool: heads 0, 7 and 12 of every request against the oracle,
+    and every head's outputs and states finite."""
     w = synth.mixed_varlen()
     note(f"mixed full ({int(w.cu_seqlens[-1])} tokens)")
     o, pool, cache, st = _run_step(w)
-    heads = [0, 7]
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(pool).all())
+    heads = [0, 7, 12]
     o_ref, pool_ref, y_ref, c_ref, ch = _oracle(w, heads)
     check_bf16_storage(host(st.y)[:, ch], y_ref, "conv y")
     check(host(o)[:, heads], o_ref, "bf16", "o")
