@@ -197,7 +197,7 @@ __device__ __forceinline__ bf16x8 f16_pair(const f32x4& a, const f32x4& b, float
 // fma with a zero addend it compiles to the mixed-precision fma that rounds
 // to fp16 into one half of the packed register (one instruction per value
 // instead of a multiply per value and a pack per two).  Only the sign of a
-// zero product can differ (+0 for -0), which no product with it sees.
+// zero product can differ (+0 for -0), which changes no MFMA product.
 __device__ __forceinline__ bf16x8 f16_pair_scaled(const f32x4& a, const f32x4& b, float sc) {
     auto m = [sc](float x) { return __builtin_fmaf(x, sc, 0.f); };
     return as_bf16x8(u32x4{pk_f16(m(a.x), m(a.y)), pk_f16(m(a.z), m(a.w)), pk_f16(m(b.x), m(b.y)),

@@ -16,7 +16,8 @@
 //     copy of the initial state in the last segment's slot (not for a zero
 //     initial state);
 //   pass 2 (gla_seg_out): each later segment folds its entry state
-//     S_in(g) = 2^Lambda_{g-1} S_in(g-1) + dS_{g-1} from those (g slot reads),
+//     S_in(g) = 2^Lambda_{g-1} S_in(g-1) + dS_{g-1} from those (g slot reads;
+//     one, where a scan between the passes has formed the entry states),
 //     the first reads the copy (the pool slot itself is rewritten by the
 //     last segment in the same pass); then each runs the chunked form over
 //     its chunks; the last segment writes the final state back to the pool.
