@@ -51,6 +51,15 @@ def test_noalloc_equals_workspace_call_twice_then_smaller():
     assert np.array_equal(p1[rest], w.pool[rest])
 
 
+def test_noalloc_many_segments_scanned():
+    """One 5000-token sequence over 16 heads is cut into 16 segments, so the
+    entry states are scanned between the passes, in the fixed array too."""
+    w = synth.random_varlen(75, [5000], 16, 128, 128, dtype="bf16", n_slots=3)
+    note("noalloc gla, 1 sequence of 5000 tokens x 16 heads (scanned entry states)")
+    o1, o2, p1, p2 = _both(w)
+    assert np.array_equal(o1, o2) and np.array_equal(p1, p2)
+
+
 def test_noalloc_shapes_without_segments():
     """fp32 inputs and small heads run the generic kernel, which needs no
     workspace: the call is then gla_chunk_fwd with nothing extra."""
