@@ -363,6 +363,32 @@ def test_prefill_then_decode(kind):
 
 
 @pytest.mark.parametrize("kind", ["gla", "gdn"])
+@pytest.mark.parametrize("reset", [False, True])
+def test_degenerate_gates_many_segments(kind, reset):
+    """The gates of test_degenerate_gates (alpha = 1 on a tenth of the
+    tokens, with ``reset`` alpha = 0 on another tenth; for Gated DeltaNet
+    beta = 0 or 1 on a tenth each) in two long bf16 sequences cut into
+    many segments (GLA: 11 and 7 segments of 256 tokens, entry states
+    scanned): segment decay totals that underflow to zero and state scales
+    restarted mid-segment, against the recurrence."""
+    w = synth.random_varlen(31 + reset, [2600, 1700], 2, 128, 128, dtype="bf16", gdn=(kind == "gdn"),
+                            chunk=64)
+    rng = np.random.Generator(np.random.PCG64(32))
+    u = rng.random(w.alpha.shape)
+    w.alpha = np.where(u < 0.1, 0.0 if reset else w.alpha, np.where(u > 0.9, 1.0, w.alpha)).astype(np.float32)
+    if kind == "gdn":
+        u = rng.random(w.beta.shape)
+        w.beta = np.where(u < 0.1, 0.0, np.where(u > 0.9, 1.0, w.beta)).astype(np.float32)
+    note(f"chunk {kind} bf16 many segments, degenerate gates reset={reset}")
+    o, pool = run_chunk(kind, w)
+    o_ref, pool_ref = run_oracle(kind, w)
+    p = pool.cpu().numpy()[w.slot_idx]
+    assert np.all(np.isfinite(host(o))) and np.all(np.isfinite(p))
+    check(host(o), o_ref, "bf16", "o")
+    check(p, pool_ref[w.slot_idx], "bf16", "state")
+
+
+@pytest.mark.parametrize("kind", ["gla", "gdn"])
 @pytest.mark.parametrize("dtype,d,C", [("bf16", 128, 64), ("f32", 32, 16)])
 @pytest.mark.parametrize("reset", [False, True])
 def test_degenerate_gates(kind, dtype, d, C, reset):
