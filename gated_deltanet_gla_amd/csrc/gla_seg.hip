@@ -278,14 +278,16 @@ __device__ __forceinline__ bool split_geometry(SegGeom& sg, const int32_t* cu, i
 }
 
 // A state slot in the workspace holds the 128x128 state as the MFMA
-// accumulator fragments of the 8 waves: lane l of wave w keeps its 8 tiles x
-// 4 values (32 floats, 128 contiguous bytes) at ((w * 64 + l) * 32), so a
-// slot is written and read with 16-byte accesses.
+// accumulator fragments of the 8 waves, tile-major: tile mt of lane l of
+// wave w (4 values) at ((w * 8 + mt) * 64 + l) * 4, so a wave reads or
+// writes one tile as one contiguous 1 KiB (16 bytes a lane).  frag_slot()
+// is this lane's tile 0; tile mt is kSlotTile * mt floats further on.
+constexpr int kSlotTile = 64 * 4;
 __device__ __forceinline__ float* frag_slot(float* ws, long slot) {
-    return ws + slot * SD * SD + threadIdx.x * 32;
+    return ws + slot * SD * SD + ((threadIdx.x >> 6) * 8 * 64 + (threadIdx.x & 63)) * 4;
 }
 __device__ __forceinline__ const float* frag_slot(const float* ws, long slot) {
-    return ws + slot * SD * SD + threadIdx.x * 32;
+    return ws + slot * SD * SD + ((threadIdx.x >> 6) * 8 * 64 + (threadIdx.x & 63)) * 4;
 }
 
 // The output pass holds the state in the accumulator row order srow()
@@ -313,11 +315,11 @@ __device__ __forceinline__ void load_state_rowmajor(f32x4 (&S)[8], const float* 
 // of lane group 2 (mt' % 2) + g' / 2 (same column, same wave).
 __device__ __forceinline__ void store_slot_out_order(float* ws, long slot, const f32x4 (&S)[8]) {
     const int t = threadIdx.x, lane = t & 63, g = lane >> 4;
-    float* base = ws + slot * SD * SD + (t & ~63) * 32;
+    float* base = ws + slot * SD * SD + (t >> 6) * 8 * kSlotTile;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
         const int dl = (lane & 15) + 16 * (2 * (mt & 1) + (g >> 1));
-        *reinterpret_cast<f32x4*>(base + dl * 32 + (2 * (mt >> 1) + (g & 1)) * 4) = S[mt];
+        *reinterpret_cast<f32x4*>(base + (2 * (mt >> 1) + (g & 1)) * kSlotTile + dl * 4) = S[mt];
     }
 }
 
@@ -697,13 +699,13 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         const long s_in = sg.g == 0 ? static_cast<long>(sg.nseg - 1) : (scanned ? sg.g - 1 : 0);
         const float* s0 = frag_slot(wstate, sg.ws_first + s_in * H);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
+        for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * kSlotTile);
         for (int j = 1; j < (scanned ? 0 : sg.g); ++j) {
             const long sj = sg.ws_first + static_cast<long>(j) * H;
             const float dcy = hw_exp2(wlam[sj]);
             const float* dS = frag_slot(wstate, sj);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
+            for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * kSlotTile);
         }
     }
     if constexpr (NORM) {
@@ -1035,13 +1037,13 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             const float* s0 =
                 frag_slot(wstate, sg.ws_first + it + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L));
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * 4);
+            for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * kSlotTile);
             for (int j = 1; j < sg.g; ++j) {
                 const long sj = sg.ws_first + it + static_cast<long>(j) * H;
                 const float dcy = hw_exp2(wlam[sj]);
                 const float* dS = frag_slot(wstate, sj);
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * 4);
+                for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * kSlotTile);
             }
         }
     };
