@@ -280,15 +280,22 @@ __device__ __forceinline__ bool split_geometry(SegGeom& sg, const int32_t* cu, i
 // A state slot in the workspace holds the 128x128 state as the MFMA
 // accumulator fragments of the 8 waves, tile-major: tile mt of lane l of
 // wave w (4 values) at ((w * 8 + mt) * 64 + l) * 4, so a wave reads or
-// writes one tile as one contiguous 1 KiB (16 bytes a lane).  frag_slot()
-// is this lane's tile 0; tile mt is kSlotTile * mt floats further on.
+// writes one tile as one contiguous 1 KiB (16 bytes a lane); tile mt is
+// kSlotTile * mt floats after tile 0.
 constexpr int kSlotTile = 64 * 4;
-__device__ __forceinline__ float* frag_slot(float* ws, long slot) {
-    return ws + slot * SD * SD + ((threadIdx.x >> 6) * 8 * 64 + (threadIdx.x & 63)) * 4;
-}
-__device__ __forceinline__ const float* frag_slot(const float* ws, long slot) {
-    return ws + slot * SD * SD + ((threadIdx.x >> 6) * 8 * 64 + (threadIdx.x & 63)) * 4;
-}
+// This lane's 8 tiles of a slot, through a buffer resource: the tile
+// offsets (up to 7 KiB) go in the scalar offset, so the eight loads share
+// one address register.
+struct SlotReader {
+    BufRsrc rs;
+    uint32_t lo;
+    __device__ __forceinline__ SlotReader(const float* ws, long slot)
+        : rs(ws + slot * SD * SD, SD * SD * 4),
+          lo(static_cast<uint32_t>(((threadIdx.x >> 6) * 8 * 64 + (threadIdx.x & 63)) * 16)) {}
+    __device__ __forceinline__ f32x4 tile(int mt) const {
+        return __builtin_bit_cast(f32x4, rs.load16(lo, static_cast<uint32_t>(mt * kSlotTile * 4)));
+    }
+};
 
 // The output pass holds the state in the accumulator row order srow()
 // (tiles 2s and 2s + 1 give each lane 8 consecutive state rows, which meet
@@ -697,15 +704,15 @@ gla_seg_out(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, cons
         // segment's slot; later ones: slot 0 holds S_in(1), and after the
         // scan slot g - 1 holds S_in(g)
         const long s_in = sg.g == 0 ? static_cast<long>(sg.nseg - 1) : (scanned ? sg.g - 1 : 0);
-        const float* s0 = frag_slot(wstate, sg.ws_first + s_in * H);
+        const SlotReader s0(wstate, sg.ws_first + s_in * H);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * kSlotTile);
+        for (int mt = 0; mt < 8; ++mt) S[mt] = s0.tile(mt);
         for (int j = 1; j < (scanned ? 0 : sg.g); ++j) {
             const long sj = sg.ws_first + static_cast<long>(j) * H;
             const float dcy = hw_exp2(wlam[sj]);
-            const float* dS = frag_slot(wstate, sj);
+            const SlotReader dS(wstate, sj);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * kSlotTile);
+            for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + dS.tile(mt);
         }
     }
     if constexpr (NORM) {
@@ -1034,16 +1041,15 @@ gla_seg_out_multi(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         } else {
             // first segment: the copy of the initial state in the last
             // segment's slot; later ones: slot 0 holds S_in(1)
-            const float* s0 =
-                frag_slot(wstate, sg.ws_first + it + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L));
+            const SlotReader s0(wstate, sg.ws_first + it + (sg.g == 0 ? static_cast<long>(sg.nseg - 1) * H : 0L));
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(s0 + mt * kSlotTile);
+            for (int mt = 0; mt < 8; ++mt) S[mt] = s0.tile(mt);
             for (int j = 1; j < sg.g; ++j) {
                 const long sj = sg.ws_first + it + static_cast<long>(j) * H;
                 const float dcy = hw_exp2(wlam[sj]);
-                const float* dS = frag_slot(wstate, sj);
+                const SlotReader dS(wstate, sj);
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + *reinterpret_cast<const f32x4*>(dS + mt * kSlotTile);
+                for (int mt = 0; mt < 8; ++mt) S[mt] = dcy * S[mt] + dS.tile(mt);
             }
         }
     };
