@@ -156,16 +156,17 @@ def test_gla_segmented_many_sequences(zero_init):
     assert torch.equal(p16, pool)
 
 
-@pytest.mark.parametrize("zero_init", [False, True])
-def test_gla_segmented_entry_scan(zero_init):
+@pytest.mark.parametrize("zero_init,H", [(False, 2), (True, 2), (False, 5)])
+def test_gla_segmented_entry_scan(zero_init, H):
     """Few sequences of many segments (here 16, 10 and 13 segments of 256
     tokens, an empty sequence between them, last segments of 160, 1 and 28
-    tokens): the entry states are scanned once over the first pass's slots
+    tokens; H = 5 does not divide the 256 workgroups the segment length
+    aims at): the entry states are scanned once over the first pass's slots
     instead of folded in every segment of the output pass.  Outputs and final
     states against the recurrence; bf16 outputs are the RNE of the fp32 ones."""
     lens = [4000, 2305, 0, 3100]
-    w = synth.random_varlen(23 + zero_init, lens, 2, 128, 128, dtype="bf16", zero_init=zero_init)
-    note(f"gla segmented entry scan, lengths {lens}, zero_init={zero_init}")
+    w = synth.random_varlen(23 + zero_init + 3 * H, lens, H, 128, 128, dtype="bf16", zero_init=zero_init)
+    note(f"gla segmented entry scan, lengths {lens}, H={H}, zero_init={zero_init}")
     o, pool = run_chunk("gla", w)
     o_ref, pool_ref = run_oracle("gla", w)
     check(host(o), o_ref, "bf16", "o")
